@@ -1,0 +1,271 @@
+"""Pins for the oracle's decode step (CPU only).
+
+* Brute force: a cache-free, page-free causal recompute of the whole sequence,
+  written here with explicit loops and a complex-number form of RoPE, must
+  equal the oracle's cached decode (unrounded cache) at every position.
+* Special cases: GQA equals MHA with each KV head repeated; paging is
+  invisible under any block permutation; one key returns V.
+* Cache placement: a step changes exactly the new token's slots.
+* Ledger: the MAC count is 2 P per token plus attention, and agrees with the
+  product's closed-form FLOP model.
+* Planted mistakes: plausible errors put into the oracle make the brute-force
+  comparison fail, so the comparison has teeth.
+"""
+
+import cmath
+import math
+
+import numpy as np
+import pytest
+
+from oracle import codecs
+from oracle import decoder as D
+from memory_bound_transformer_decode_amd import perfmodel
+
+
+# ------------------------------------------------------------------ tiny random model
+
+def tiny_model(seed=0, L=2, d=16, Hq=4, Hkv=2, dh=4, dff=24, V=11, fmt="f64"):
+    rng = np.random.default_rng(seed)
+
+    def mat(r, c, s=0.3):
+        w = rng.standard_normal((r, c)) * s
+        if fmt == "f64":
+            return D.Matrix(r, c, "f64", codes=w)
+        return D.Matrix(r, c, "bf16", codes=codecs.bf16_encode(w))
+
+    return D.Model(
+        n_layers=L, d_model=d, n_q_heads=Hq, n_kv_heads=Hkv, d_head=dh, d_ff=dff, vocab=V,
+        rms_eps=1e-5, rope_theta=1e4,
+        embed=mat(V, d, 1.0), attn_norm=1 + 0.2 * rng.standard_normal((L, d)),
+        qkv=[mat((Hq + 2 * Hkv) * dh, d) for _ in range(L)],
+        o=[mat(d, Hq * dh) for _ in range(L)],
+        mlp_norm=1 + 0.2 * rng.standard_normal((L, d)),
+        gate_up=[mat(2 * dff, d) for _ in range(L)],
+        down=[mat(d, dff) for _ in range(L)],
+        final_norm=1 + 0.2 * rng.standard_normal(d), lm_head=mat(V, d))
+
+
+def new_cache(m, nblk, fmt="f64", bs=4):
+    dt = {"f64": np.float64, "bf16": np.uint16, "fp8": np.uint8}[fmt]
+    pool = np.zeros((m.n_layers, 2, nblk, m.n_kv_heads, bs, m.d_head), dtype=dt)
+    return D.PagedKVCache(pool, fmt, block_size=bs)
+
+
+# ------------------------------------------------------------------ brute force
+
+def brute_force_logits(m, tokens):
+    """Logits at every position of `tokens`, recomputing the full causal prefix with
+    plain loops: no cache, no paging, RoPE as complex rotation of adjacent pairs."""
+    W = lambda mat: mat.decoded()  # noqa: E731
+    n, d, dh = len(tokens), m.d_model, m.d_head
+    Hq, Hkv = m.n_q_heads, m.n_kv_heads
+    g = Hq // Hkv
+
+    def norm(v, gain):
+        ms = sum(t * t for t in v) / len(v)
+        r = 1.0 / math.sqrt(ms + m.rms_eps)
+        return [gain[i] * v[i] * r for i in range(len(v))]
+
+    def rot(vec, pos):
+        out = []
+        for i in range(dh // 2):
+            z = complex(vec[2 * i], vec[2 * i + 1]) * cmath.exp(
+                1j * pos * m.rope_theta ** (-2.0 * i / dh))
+            out += [z.real, z.imag]
+        return out
+
+    def mv(Wm, v):
+        return [sum(Wm[r, c] * v[c] for c in range(len(v))) for r in range(Wm.shape[0])]
+
+    E = W(m.embed)
+    hs = [list(E[t]) for t in tokens]
+    for l in range(m.n_layers):
+        Wqkv, Wo, Wgu, Wd = W(m.qkv[l]), W(m.o[l]), W(m.gate_up[l]), W(m.down[l])
+        qs, ks, vs = [], [], []
+        for i in range(n):
+            y = mv(Wqkv, norm(hs[i], m.attn_norm[l]))
+            qs.append([rot(y[j * dh:(j + 1) * dh], i) for j in range(Hq)])
+            ks.append([rot(y[(Hq + c) * dh:(Hq + c + 1) * dh], i) for c in range(Hkv)])
+            vs.append([y[(Hq + Hkv + c) * dh:(Hq + Hkv + c + 1) * dh] for c in range(Hkv)])
+        for i in range(n):
+            o = []
+            for j in range(Hq):
+                c = j // g
+                sc = [sum(qs[i][j][e] * ks[t][c][e] for e in range(dh)) / math.sqrt(dh)
+                      for t in range(i + 1)]
+                mx = max(sc)
+                ex = [math.exp(s - mx) for s in sc]
+                tot = sum(ex)
+                o += [sum(ex[t] / tot * vs[t][c][e] for t in range(i + 1)) for e in range(dh)]
+            hs[i] = [hs[i][r] + v for r, v in enumerate(mv(Wo, o))]
+            x = norm(hs[i], m.mlp_norm[l])
+            gu = mv(Wgu, x)
+            a = [gu[f] / (1 + math.exp(-gu[f])) * gu[m.d_ff + f] for f in range(m.d_ff)]
+            hs[i] = [hs[i][r] + v for r, v in enumerate(mv(Wd, a))]
+    Wl = W(m.lm_head)
+    return np.array([mv(Wl, norm(hs[i], m.final_norm)) for i in range(n)])
+
+
+def oracle_sequence(m, tokens, block_table, cache):
+    return np.stack([D.decode_step(m, cache, [t], [p], np.array([block_table]))[0]
+                     for p, t in enumerate(tokens)])
+
+
+TOKENS = [3, 7, 0, 10, 5, 5, 2, 9, 1]
+
+
+def test_cached_decode_equals_full_causal_recompute():
+    m = tiny_model()
+    bt = [5, 0, 3]  # logical blocks of 4 positions mapped to scattered physical blocks
+    got = oracle_sequence(m, TOKENS, bt, new_cache(m, 6))
+    ref = brute_force_logits(m, TOKENS)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+
+
+def test_batched_step_equals_single_sequence_steps():
+    m = tiny_model(seed=1)
+    bts = np.array([[1, 4], [0, 2], [5, 3]])
+    ctx = [[2, 8, 1, 4, 4], [9], [0, 1, 2]]
+    # run each sequence's context alone, then one batched step
+    cache_b = new_cache(m, 6, bs=4)
+    singles = []
+    for b, seq in enumerate(ctx):
+        cache_s = new_cache(m, 6, bs=4)
+        for p, t in enumerate(seq):
+            D.decode_step(m, cache_s, [t], [p], bts[b:b + 1])
+            D.decode_step(m, cache_b, [t], [p], bts[b:b + 1])
+        singles.append(D.decode_step(m, cache_s, [6], [len(seq)], bts[b:b + 1])[0])
+    batched = D.decode_step(m, cache_b, [6, 6, 6], [len(s) for s in ctx], bts)
+    np.testing.assert_allclose(batched, np.stack(singles), rtol=0, atol=1e-13)
+
+
+def test_paging_invisible_under_block_permutation():
+    m = tiny_model(seed=2)
+    a = oracle_sequence(m, TOKENS, [0, 1, 2], new_cache(m, 3))
+    b = oracle_sequence(m, TOKENS, [2, 0, 1], new_cache(m, 3))
+    np.testing.assert_array_equal(a, b)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    m = tiny_model(seed=3, Hq=4, Hkv=2, dh=4)
+    Hq, Hkv, dh, g = 4, 2, 4, 2
+    mha_qkv = []
+    for l in range(m.n_layers):
+        w = m.qkv[l].decoded()
+        q = w[:Hq * dh]
+        k = w[Hq * dh:(Hq + Hkv) * dh].reshape(Hkv, dh, -1)
+        v = w[(Hq + Hkv) * dh:].reshape(Hkv, dh, -1)
+        k4 = np.repeat(k, g, axis=0).reshape(Hq * dh, -1)  # kv head c serves q heads c*g..c*g+g-1
+        v4 = np.repeat(v, g, axis=0).reshape(Hq * dh, -1)
+        mha_qkv.append(D.Matrix(3 * Hq * dh, m.d_model, "f64",
+                                codes=np.concatenate([q, k4, v4])))
+    import dataclasses
+    mha = dataclasses.replace(m, n_kv_heads=Hq, qkv=mha_qkv)
+    a = oracle_sequence(m, TOKENS, [0, 1, 2], new_cache(m, 3))
+    b = oracle_sequence(mha, TOKENS, [0, 1, 2], new_cache(mha, 3))
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_first_token_attention_returns_rounded_v():
+    """The first token's cached V is the definition's v rounded to the cache format
+    (the value single-key attention then returns exactly)."""
+    m = tiny_model(seed=4, fmt="bf16", L=1)
+    cache = new_cache(m, 2, fmt="bf16")
+    D.decode_step(m, cache, [4], [0], np.array([[1, 0]]))
+    # recompute the layer-0 V the definition gives, rounded to bf16
+    x = D.rmsnorm(m.embed.row(4), m.attn_norm[0], m.rms_eps)
+    y = m.qkv[0].decoded() @ x
+    Hq, Hkv, dh = m.n_q_heads, m.n_kv_heads, m.d_head
+    v = y[(Hq + Hkv) * dh:].reshape(Hkv, dh)
+    np.testing.assert_array_equal(cache.read(0, 1, [1, 0], 1, 0), codecs.bf16_round(v[0:1]))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_cache_writes_exactly_the_new_slots(fmt):
+    m = tiny_model(seed=5, fmt="bf16")
+    cache = new_cache(m, 8, fmt=fmt)
+    canary = 0x7FC1 if fmt == "bf16" else 0x7F
+    cache.pool[...] = canary
+    bts = np.array([[3, 6], [1, 7]])
+    pos = [5, 2]
+    rng = np.random.default_rng(0)
+    for b, p in enumerate(pos):  # context positions 0 .. p-1 hold real values
+        for t in range(p):
+            for l in range(m.n_layers):
+                for kv in (0, 1):
+                    for c in range(m.n_kv_heads):
+                        cache.write(l, kv, bts[b], t, c, rng.standard_normal(m.d_head))
+    before = cache.pool.copy()
+    D.decode_step(m, cache, [1, 2], pos, bts)
+    changed = np.argwhere(np.any(cache.pool != before, axis=-1))
+    expect = sorted((l, kv, int(bts[b][p // 4]), c, p % 4)
+                    for l in range(m.n_layers) for kv in (0, 1)
+                    for b, p in enumerate(pos) for c in range(m.n_kv_heads))
+    assert sorted(map(tuple, changed.tolist())) == expect
+
+
+# ------------------------------------------------------------------ ledger
+
+def test_mac_ledger_is_2P_per_token_plus_attention():
+    m = tiny_model(seed=6, fmt="bf16")
+    led = D.Ledger()
+    cache = new_cache(m, 4, fmt="bf16")
+    pos = [3, 0]
+    D.decode_step(m, cache, [1, 2], pos, np.array([[0, 1], [2, 3]]), ledger=led)
+    shape = perfmodel.Shape(m.n_layers, m.d_model, m.n_q_heads, m.n_kv_heads, m.d_head,
+                            m.d_ff, m.vocab)
+    assert led.macs == 2 * shape.matmul_params()
+    assert led.attn_macs == sum(2 * m.n_q_heads * m.d_head * (p + 1) * m.n_layers for p in pos)
+    assert 2 * (led.macs + led.attn_macs) == shape.step_flops(pos)
+
+
+# ------------------------------------------------------------------ planted mistakes
+
+def _rope_half_split(x, pos, theta):
+    x = np.asarray(x, dtype=np.float64)
+    dh = x.shape[-1]
+    phi = D.rope_angles(pos, dh, theta)
+    c, s = np.cos(phi), np.sin(phi)
+    a, b = x[..., : dh // 2], x[..., dh // 2:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+_real_rope, _real_attend, _real_rmsnorm, _real_silu = D.rope, D.attend, D.rmsnorm, D.silu
+
+MISTAKES = {
+    "rope_half_split": ("rope", _rope_half_split),
+    # (a constant position offset is no mistake: it cancels in q.k, RoPE's relative property)
+    "rope_frequency_exponent": ("rope", lambda x, p, t: _real_rope(x, p, t * t)),
+    "rope_sign_flipped": ("rope", lambda x, p, t: _real_rope(x, -p, t)),
+    "attention_unscaled": ("attend", lambda q, K, V: D.softmax(K @ q) @ V),
+    "attention_drops_self": ("attend", lambda q, K, V: _real_attend(q, K[:-1], V[:-1])
+                             if len(K) > 1 else V[0]),
+    "rmsnorm_no_gain": ("rmsnorm", lambda v, g, e: _real_rmsnorm(v, np.ones_like(g), e)),
+    "rmsnorm_centred": ("rmsnorm", lambda v, g, e: _real_rmsnorm(
+        v - np.mean(v, axis=-1, keepdims=True), g, e)),
+    "silu_is_sigmoid": ("silu", lambda z: 1.0 / (1.0 + np.exp(-np.asarray(z)))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MISTAKES))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    fn_name, bad = MISTAKES[name]
+    m = tiny_model(seed=7)
+    ref = brute_force_logits(m, TOKENS[:6])
+    monkeypatch.setattr(D, fn_name, bad)
+    got = oracle_sequence(m, TOKENS[:6], [0, 1], new_cache(m, 2))
+    assert np.max(np.abs(got - ref)) > 1e-6
+
+
+class _WrongSlotCache(D.PagedKVCache):
+    def write(self, layer, kv, block_table, pos, head, values):
+        super().write(layer, kv, block_table, (pos + 1) % (len(block_table) * self.bs), head, values)
+
+
+def test_planted_cache_slot_mistake_is_caught():
+    m = tiny_model(seed=8)
+    ref = brute_force_logits(m, TOKENS[:6])
+    bad = _WrongSlotCache(np.zeros((m.n_layers, 2, 2, m.n_kv_heads, 4, m.d_head)), "f64", 4)
+    got = oracle_sequence(m, TOKENS[:6], [0, 1], bad)
+    assert np.max(np.abs(got - ref)) > 1e-6
