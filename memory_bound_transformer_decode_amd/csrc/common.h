@@ -1,0 +1,134 @@
+// Device helpers shared by the decode-step kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dec {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+constexpr int KV_BLOCK = 16;  // positions per paged KV block
+
+// ---------------------------------------------------------------- loads
+
+// Weights are read exactly once per step: stream them past the caches.
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// ---------------------------------------------------------------- number formats
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp32 -> OCP E4M3 code: round to nearest even, finite values saturate to +-448.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;           // NaN
+  float af = __uint_as_float(a);
+  if (af >= 448.0f) return sign | 0x7Eu;              // saturate (incl. inf)
+  if (af < 0.015625f) {                               // below 2^-6: multiples of 2^-9
+    return sign | (uint32_t)__builtin_rintf(af * 512.0f);  // rint: ties to even; 8 -> 2^-6 (code 8)
+  }
+  uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;  // (biased exp << 3) | 3-bit mantissa, RNE
+  uint32_t code = r - ((127u - 7u) << 3);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// two E4M3 codes (bytes 0,1 or bytes 2,3 of w) -> two bf16 (exact: E4M3 values are bf16 values)
+template <bool HI>
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
+
+// two E4M3 codes -> two fp32 (exact)
+template <bool HI>
+__device__ __forceinline__ f32x2 e4m3x2_to_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
+// ---------------------------------------------------------------- dot products
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         acc, false);
+}
+__device__ __forceinline__ float dot2_bf16v(bf16x2 a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+// 8 bf16 weights . 8 bf16 activations
+__device__ __forceinline__ float dot8_bf16(const u32x4& w, const u32x4& x, float acc) {
+  acc = dot2_bf16(w.x, x.x, acc);
+  acc = dot2_bf16(w.y, x.y, acc);
+  acc = dot2_bf16(w.z, x.z, acc);
+  acc = dot2_bf16(w.w, x.w, acc);
+  return acc;
+}
+
+// 4 E4M3 weights (one u32) . 4 bf16 activations (two u32)
+__device__ __forceinline__ float dot4_e4m3(uint32_t w, uint32_t x01, uint32_t x23, float acc) {
+  acc = dot2_bf16v(e4m3x2_to_bf16x2<false>(w), x01, acc);
+  acc = dot2_bf16v(e4m3x2_to_bf16x2<true>(w), x23, acc);
+  return acc;
+}
+
+// 16 E4M3 weights . 16 bf16 activations (xa: elements 0..7, xb: 8..15)
+__device__ __forceinline__ float dot16_e4m3(const u32x4& w, const u32x4& xa, const u32x4& xb, float acc) {
+  acc = dot4_e4m3(w.x, xa.x, xa.y, acc);
+  acc = dot4_e4m3(w.y, xa.z, xa.w, acc);
+  acc = dot4_e4m3(w.z, xb.x, xb.y, acc);
+  acc = dot4_e4m3(w.w, xb.z, xb.w, acc);
+  return acc;
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Sum over a 256-thread block; every thread gets the total.  `red` holds 4 floats.
+__device__ __forceinline__ float block256_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+__device__ __forceinline__ int64_t kv_offset(int layer, int kv, int block, int head, int slot, int e,
+                                             int num_blocks, int n_kv_heads, int d_head) {
+  return ((((int64_t)layer * 2 + kv) * num_blocks + block) * n_kv_heads + head) * (int64_t)(KV_BLOCK * d_head) +
+         (int64_t)slot * d_head + e;
+}
+
+}  // namespace dec

@@ -1,0 +1,615 @@
+// Host runtime behind include/dec.h: validation, workspace layout, pinned staging
+// of the per-step inputs, the kernel plan of one step, and one captured hipGraph
+// per batch-size bucket.
+//
+// The engine step the pages describe has the CPU prepare the batch, block tables
+// and metadata, copy them into static device buffers, and replay a graph captured
+// once per batch size, padding the live batch up to the nearest captured size
+// (ladder 1, 2, 4, then every 8); eager launches stay available for debugging and
+// measurement ("Kernels, Fusion & CUDA Graphs", Fix 2: CUDA graphs and The serving
+// engine's kernel stack; "CUDA graphs & kernel fusion", Direct answer and Deep
+// dive).  Everything that varies per step is read by the kernels from device
+// buffers, so one graph per bucket serves every step.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dec.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr int LADDER[] = {1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64};
+constexpr int N_BUCKETS = sizeof(LADDER) / sizeof(LADDER[0]);
+constexpr int MAX_SPLIT = 64;
+constexpr int ATTN_TARGET_GROUPS = 1024;  // work groups per attention launch to aim for
+constexpr uint32_t KNOWN_FLAGS = DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL;
+constexpr uint32_t MODE_FLAGS = DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA;  // flags that change the kernel plan
+
+int bucket_index(int n) {
+  for (int i = 0; i < N_BUCKETS; ++i)
+    if (LADDER[i] >= n) return i;
+  return -1;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int blocks_per_seq(const dec_config& c) { return (c.max_seq_len + 15) / 16; }
+
+int n_split_for(const dec_config& c, int Bp) {
+  int ns = (ATTN_TARGET_GROUPS + Bp * c.n_kv_heads - 1) / (Bp * c.n_kv_heads);
+  const int bps = blocks_per_seq(c);
+  if (ns > bps) ns = bps;
+  if (ns > MAX_SPLIT) ns = MAX_SPLIT;
+  return ns < 1 ? 1 : ns;
+}
+
+struct Layout {
+  size_t ids, lens, bt, static_bytes;  // static region: ids | lens | block tables
+  size_t h, x, q, part_o, part_ml, o, a, rope, total;
+};
+
+Layout layout_of(const dec_config& c) {
+  Layout L{};
+  const size_t MB = (size_t)c.max_batch;
+  const size_t bps = (size_t)blocks_per_seq(c);
+  size_t off = 0;
+  L.ids = off;
+  off += MB * 4;
+  L.lens = off;
+  off += MB * 4;
+  L.bt = off;
+  off += MB * bps * 4;
+  L.static_bytes = off;
+  off = align256(off);
+  L.h = off;
+  off = align256(off + MB * c.d_model * 4);
+  L.x = off;
+  off = align256(off + MB * c.d_model * 2);
+  L.q = off;
+  off = align256(off + MB * c.n_q_heads * c.d_head * 4);
+  size_t rows_split = 0;  // max over buckets of Bp * n_split
+  for (int i = 0; i < N_BUCKETS && LADDER[i] <= c.max_batch; ++i) {
+    const size_t r = (size_t)LADDER[i] * n_split_for(c, LADDER[i]);
+    if (r > rows_split) rows_split = r;
+  }
+  L.part_o = off;
+  off = align256(off + rows_split * c.n_q_heads * c.d_head * 4);
+  L.part_ml = off;
+  off = align256(off + rows_split * c.n_q_heads * 2 * 4);
+  L.o = off;
+  off = align256(off + MB * c.n_q_heads * c.d_head * 2);
+  L.a = off;
+  off = align256(off + MB * c.d_ff * 2);
+  L.rope = off;
+  off = align256(off + (size_t)c.max_seq_len * (c.d_head / 2) * 8);
+  L.total = off;
+  return L;
+}
+
+int validate_config(const dec_config* c) {
+  if (!c) return fail(DEC_E_INVALID, "config is NULL");
+  if (c->n_layers < 0) return fail(DEC_E_INVALID, "n_layers must be >= 0 (got %d)", c->n_layers);
+  if (c->d_model <= 0 || c->d_model % 16) return fail(DEC_E_INVALID, "d_model must be a positive multiple of 16 (got %d)", c->d_model);
+  if (c->d_ff <= 0 || c->d_ff % 16) return fail(DEC_E_INVALID, "d_ff must be a positive multiple of 16 (got %d)", c->d_ff);
+  if (c->n_kv_heads <= 0 || c->n_q_heads <= 0 || c->n_q_heads % c->n_kv_heads)
+    return fail(DEC_E_INVALID, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", c->n_q_heads, c->n_kv_heads);
+  if (c->n_q_heads / c->n_kv_heads > 8)
+    return fail(DEC_E_UNSUPPORTED, "query heads per KV head must be <= 8 (got %d)", c->n_q_heads / c->n_kv_heads);
+  if (c->d_head != 64 && c->d_head != 128) return fail(DEC_E_UNSUPPORTED, "d_head must be 64 or 128 (got %d)", c->d_head);
+  if (c->vocab <= 0 || c->vocab % 2) return fail(DEC_E_INVALID, "vocab must be positive and even (got %d)", c->vocab);
+  if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(DEC_E_INVALID, "rms_eps must be a positive finite number");
+  if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta)) return fail(DEC_E_INVALID, "rope_theta must be finite and > 1");
+  if ((c->weight_dtype != DEC_BF16 && c->weight_dtype != DEC_FP8_E4M3) || (c->kv_dtype != DEC_BF16 && c->kv_dtype != DEC_FP8_E4M3))
+    return fail(DEC_E_INVALID, "weight_dtype / kv_dtype must be DEC_BF16 or DEC_FP8_E4M3");
+  if (c->block_size != 16) return fail(DEC_E_UNSUPPORTED, "block_size must be 16 (got %d)", c->block_size);
+  if (c->num_blocks <= 0) return fail(DEC_E_INVALID, "num_blocks must be positive (got %d)", c->num_blocks);
+  if (bucket_index(c->max_batch) < 0 || LADDER[bucket_index(c->max_batch)] != c->max_batch)
+    return fail(DEC_E_INVALID, "max_batch must be one of 1, 2, 4, 8, 16, 24, ..., 64 (got %d)", c->max_batch);
+  if (c->max_seq_len <= 0) return fail(DEC_E_INVALID, "max_seq_len must be positive (got %d)", c->max_seq_len);
+  if (c->flags & ~KNOWN_FLAGS) return fail(DEC_E_INVALID, "unknown flag bits 0x%x", c->flags & ~KNOWN_FLAGS);
+  if (c->flags & DEC_FLAG_UNFUSED) return fail(DEC_E_UNSUPPORTED, "DEC_FLAG_UNFUSED is not implemented in this build");
+  return DEC_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+struct dec_ctx {
+  dec_config cfg{};
+  hipStream_t stream = nullptr;
+  hipStream_t cap_stream = nullptr;
+  int device = 0;
+  void* pool = nullptr;
+  uint8_t* ws = nullptr;
+  float* logits = nullptr;
+  Layout L{};
+  bool loaded = false;
+  bool failed = false;
+  // weights
+  dec_mat embed{}, lm{};
+  std::vector<dec_mat> qkv, o, gu, down;
+  const float* attn_norm = nullptr;
+  const float* mlp_norm = nullptr;
+  const float* final_norm = nullptr;
+  // host staging of the per-step inputs (double-buffered, pinned)
+  uint8_t* pinned[2] = {nullptr, nullptr};
+  hipEvent_t slot_ev[2] = {nullptr, nullptr};
+  bool slot_pending[2] = {false, false};
+  int slot = 0;
+  // graphs per (bucket, plan flags)
+  hipGraphExec_t graphs[N_BUCKETS][4] = {};
+  dec_info info{};
+};
+
+namespace {
+
+template <typename T>
+T* ws_ptr(dec_ctx* c, size_t off) {
+  return reinterpret_cast<T*>(c->ws + off);
+}
+
+int hip_fail(dec_ctx* c, hipError_t e, const char* what) {
+  if (c) c->failed = true;
+  return fail(DEC_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIPCHK(ctx, call, what)                       \
+  do {                                                \
+    hipError_t e_ = (call);                           \
+    if (e_ != hipSuccess) return hip_fail(ctx, e_, what); \
+  } while (0)
+
+// Parameters of the matrix kernel `which` (dec_matrix) of layer l for a padded batch Bp.
+dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) {
+  const dec_config& g = c->cfg;
+  const int d = g.d_model, dh = g.d_head, Hq = g.n_q_heads, Hkv = g.n_kv_heads;
+  dec::MatmulParams p{};
+  p.Bp = Bp;
+  p.seq_lens = ws_ptr<int32_t>(c, c->L.lens);
+  p.bt = ws_ptr<int32_t>(c, c->L.bt);
+  p.rope = ws_ptr<float2>(c, c->L.rope);
+  p.pool = c->pool;
+  p.q = ws_ptr<float>(c, c->L.q);
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.dh = dh;
+  p.num_blocks = g.num_blocks;
+  p.bps = blocks_per_seq(g);
+  p.d_ff = g.d_ff;
+  p.layer = l;
+  uint16_t* x = ws_ptr<uint16_t>(c, c->L.x);
+  float* h = ws_ptr<float>(c, c->L.h);
+  switch (which) {
+    case DEC_MAT_QKV:  // [q; k; v] = W_qkv x, RoPE, K/V -> cache
+      p.W = c->qkv[l].w;
+      p.scale = c->qkv[l].scale;
+      p.N = (Hq + 2 * Hkv) * dh;
+      p.K = d;
+      p.x = x;
+      p.ldx = d;
+      *epi = dec::EPI_QKV;
+      break;
+    case DEC_MAT_O:  // h += W_o o
+      p.W = c->o[l].w;
+      p.scale = c->o[l].scale;
+      p.N = d;
+      p.K = Hq * dh;
+      p.x = ws_ptr<uint16_t>(c, c->L.o);
+      p.ldx = Hq * dh;
+      p.out = h;
+      p.ldo = d;
+      *epi = dec::EPI_RESID;
+      break;
+    case DEC_MAT_GATE_UP:  // a = silu(W_gate x) * (W_up x)
+      p.W = c->gu[l].w;
+      p.scale = c->gu[l].scale;
+      p.N = 2 * g.d_ff;
+      p.K = d;
+      p.x = x;
+      p.ldx = d;
+      p.act = ws_ptr<uint16_t>(c, c->L.a);
+      p.ldact = g.d_ff;
+      *epi = dec::EPI_SILU;
+      break;
+    case DEC_MAT_DOWN:  // h += W_down a
+      p.W = c->down[l].w;
+      p.scale = c->down[l].scale;
+      p.N = d;
+      p.K = g.d_ff;
+      p.x = ws_ptr<uint16_t>(c, c->L.a);
+      p.ldx = g.d_ff;
+      p.out = h;
+      p.ldo = d;
+      *epi = dec::EPI_RESID;
+      break;
+    default:  // logits = W_lm x
+      p.W = c->lm.w;
+      p.scale = c->lm.scale;
+      p.N = g.vocab;
+      p.K = d;
+      p.x = x;
+      p.ldx = d;
+      p.out = c->logits;
+      p.ldo = g.vocab;
+      *epi = dec::EPI_LOGITS;
+      break;
+  }
+  return p;
+}
+
+hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s) {
+  const dec_config& g = c->cfg;
+  int epi = 0;
+  const dec::MatmulParams p = matmul_params(c, which, l, Bp, &epi);
+  const bool mfma = !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
+  return dec::launch_matmul(p, epi, g.weight_dtype == DEC_FP8_E4M3, g.kv_dtype == DEC_FP8_E4M3, mfma, s);
+}
+
+// Enqueue the fused plan of one step for a padded batch of Bp rows on stream s.
+hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
+  const dec_config& g = c->cfg;
+  const bool wfp8 = g.weight_dtype == DEC_FP8_E4M3, kvfp8 = g.kv_dtype == DEC_FP8_E4M3;
+  const int bps = blocks_per_seq(g);
+  int32_t* ids = ws_ptr<int32_t>(c, c->L.ids);
+  int32_t* lens = ws_ptr<int32_t>(c, c->L.lens);
+  int32_t* bt = ws_ptr<int32_t>(c, c->L.bt);
+  float* h = ws_ptr<float>(c, c->L.h);
+  uint16_t* x = ws_ptr<uint16_t>(c, c->L.x);
+  float* q = ws_ptr<float>(c, c->L.q);
+  uint16_t* o = ws_ptr<uint16_t>(c, c->L.o);
+  const int d = g.d_model, dh = g.d_head, Hq = g.n_q_heads, Hkv = g.n_kv_heads;
+  hipError_t e;
+
+  dec::NormParams np{};
+  np.h = h;
+  np.h_out = h;
+  np.x = x;
+  np.d = d;
+  np.Bp = Bp;
+  np.eps = g.rms_eps;
+  np.E = c->embed.w;
+  np.E_scale = c->embed.scale;
+  np.ids = ids;
+  np.gain = g.n_layers > 0 ? c->attn_norm : c->final_norm;
+  if ((e = dec::launch_embed_norm(np, wfp8, s)) != hipSuccess) return e;
+
+  dec::AttnParams ap{};
+  ap.q = q;
+  ap.pool = c->pool;
+  ap.seq_lens = lens;
+  ap.bt = bt;
+  ap.part_o = ws_ptr<float>(c, c->L.part_o);
+  ap.part_ml = ws_ptr<float>(c, c->L.part_ml);
+  ap.o = o;
+  ap.Bp = Bp;
+  ap.Hq = Hq;
+  ap.Hkv = Hkv;
+  ap.dh = dh;
+  ap.num_blocks = g.num_blocks;
+  ap.bps = bps;
+  ap.n_split = n_split_for(g, Bp);
+
+  for (int l = 0; l < g.n_layers; ++l) {
+    if (l > 0) {
+      np.gain = c->attn_norm + (size_t)l * d;
+      if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
+    }
+    if ((e = run_matmul(c, DEC_MAT_QKV, l, Bp, s)) != hipSuccess) return e;
+    // attention over positions 0..p
+    ap.layer = l;
+    if ((e = dec::launch_attention(ap, kvfp8, s)) != hipSuccess) return e;
+    if ((e = run_matmul(c, DEC_MAT_O, l, Bp, s)) != hipSuccess) return e;
+    // x = RMSNorm(h) g_mlp
+    np.gain = c->mlp_norm + (size_t)l * d;
+    if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
+    if ((e = run_matmul(c, DEC_MAT_GATE_UP, l, Bp, s)) != hipSuccess) return e;
+    if ((e = run_matmul(c, DEC_MAT_DOWN, l, Bp, s)) != hipSuccess) return e;
+  }
+  if (g.n_layers > 0) {
+    np.gain = c->final_norm;
+    if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
+  }
+  if ((e = run_matmul(c, DEC_MAT_LM_HEAD, 0, Bp, s)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+void drop_graphs(dec_ctx* c) {
+  for (auto& row : c->graphs)
+    for (auto& ge : row)
+      if (ge) {
+        (void)hipGraphExecDestroy(ge);
+        ge = nullptr;
+      }
+}
+
+int capture(dec_ctx* c, int bi, int mode) {
+  hipGraph_t graph = nullptr;
+  HIPCHK(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+  hipError_t e = enqueue_step(c, LADDER[bi], c->cap_stream);
+  hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
+  if (e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return hip_fail(c, e, "kernel launch during capture");
+  }
+  if (e2 != hipSuccess) return hip_fail(c, e2, "hipStreamEndCapture");
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess) return hip_fail(c, e, "hipGraphInstantiate");
+  c->graphs[bi][mode] = exec;
+  return DEC_OK;
+}
+
+int check_mat(const dec_mat& m, bool fp8, const char* name, int layer) {
+  if (!m.w) return fail(DEC_E_INVALID, "%s[%d].w is NULL", name, layer);
+  if (!aligned16(m.w)) return fail(DEC_E_INVALID, "%s[%d].w is not 16-byte aligned", name, layer);
+  if (fp8 && !m.scale) return fail(DEC_E_INVALID, "%s[%d].scale is NULL for E4M3 weights", name, layer);
+  if (!fp8 && m.scale) return fail(DEC_E_INVALID, "%s[%d].scale must be NULL for bf16 weights", name, layer);
+  return DEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dec_last_error(void) { return g_err.c_str(); }
+
+size_t dec_workspace_bytes(const dec_config* cfg) {
+  if (validate_config(cfg) != DEC_OK) return 0;
+  return layout_of(*cfg).total;
+}
+
+int dec_create(const dec_config* cfg, void* hip_stream, void* kv_pool, void* workspace, size_t workspace_bytes,
+               float* logits, dec_ctx** out) {
+  if (!out) return fail(DEC_E_INVALID, "out is NULL");
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc != DEC_OK) return rc;
+  if (!kv_pool || !workspace || !logits) return fail(DEC_E_INVALID, "kv_pool, workspace and logits must be non-NULL");
+  if (!aligned16(kv_pool) || !aligned16(logits)) return fail(DEC_E_INVALID, "kv_pool and logits must be 16-byte aligned");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(DEC_E_INVALID, "workspace must be 256-byte aligned");
+  const Layout L = layout_of(*cfg);
+  if (workspace_bytes < L.total)
+    return fail(DEC_E_INVALID, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+
+  dec_ctx* c = new dec_ctx();
+  c->cfg = *cfg;
+  c->stream = static_cast<hipStream_t>(hip_stream);
+  c->pool = kv_pool;
+  c->ws = static_cast<uint8_t*>(workspace);
+  c->logits = logits;
+  c->L = L;
+  hipError_t e;
+  if ((e = hipGetDevice(&c->device)) != hipSuccess || (e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking)) != hipSuccess) {
+    rc = hip_fail(nullptr, e, "dec_create: device / capture stream");
+    delete c;
+    return rc;
+  }
+  for (int i = 0; i < 2; ++i) {
+    if ((e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned[i]), L.static_bytes, hipHostMallocDefault)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->slot_ev[i], hipEventDisableTiming)) != hipSuccess) {
+      rc = hip_fail(nullptr, e, "dec_create: pinned staging");
+      dec_destroy(c);
+      return rc;
+    }
+    std::memset(c->pinned[i], 0, L.static_bytes);
+  }
+  // RoPE table once; static region starts zeroed (ids 0, every row padded until set)
+  if ((e = dec::launch_rope_table(ws_ptr<float2>(c, L.rope), cfg->max_seq_len, cfg->d_head, (double)cfg->rope_theta,
+                                  c->stream)) != hipSuccess ||
+      (e = hipMemsetAsync(c->ws, 0, L.static_bytes, c->stream)) != hipSuccess ||
+      (e = hipStreamSynchronize(c->stream)) != hipSuccess) {
+    rc = hip_fail(nullptr, e, "dec_create: initialising the workspace");
+    dec_destroy(c);
+    return rc;
+  }
+  c->info.flags = cfg->flags;
+  *out = c;
+  return DEC_OK;
+}
+
+int dec_load_weights(dec_ctx* c, const dec_weights* w) {
+  if (!c || !w) return fail(DEC_E_INVALID, "ctx or weights is NULL");
+  if (c->failed) return fail(DEC_E_STATE, "context has failed; destroy it");
+  const dec_config& g = c->cfg;
+  const bool fp8 = g.weight_dtype == DEC_FP8_E4M3;
+  int rc;
+  if ((rc = check_mat(w->embed, fp8, "embed", 0)) != DEC_OK) return rc;
+  if ((rc = check_mat(w->lm_head, fp8, "lm_head", 0)) != DEC_OK) return rc;
+  if (!w->final_norm) return fail(DEC_E_INVALID, "final_norm is NULL");
+  if (g.n_layers > 0) {
+    if (!w->attn_norm || !w->mlp_norm || !w->qkv || !w->o || !w->gate_up || !w->down)
+      return fail(DEC_E_INVALID, "per-layer weight arrays must be non-NULL");
+    for (int l = 0; l < g.n_layers; ++l) {
+      if ((rc = check_mat(w->qkv[l], fp8, "qkv", l)) != DEC_OK || (rc = check_mat(w->o[l], fp8, "o", l)) != DEC_OK ||
+          (rc = check_mat(w->gate_up[l], fp8, "gate_up", l)) != DEC_OK ||
+          (rc = check_mat(w->down[l], fp8, "down", l)) != DEC_OK)
+        return rc;
+    }
+  }
+  drop_graphs(c);
+  c->embed = w->embed;
+  c->lm = w->lm_head;
+  c->attn_norm = w->attn_norm;
+  c->mlp_norm = w->mlp_norm;
+  c->final_norm = w->final_norm;
+  c->qkv.assign(w->qkv, w->qkv + g.n_layers);
+  c->o.assign(w->o, w->o + g.n_layers);
+  c->gu.assign(w->gate_up, w->gate_up + g.n_layers);
+  c->down.assign(w->down, w->down + g.n_layers);
+  c->loaded = true;
+  c->info.graphs_captured = 0;
+  return DEC_OK;
+}
+
+int dec_set_flags(dec_ctx* c, uint32_t flags) {
+  if (!c) return fail(DEC_E_INVALID, "ctx is NULL");
+  if (flags & ~KNOWN_FLAGS) return fail(DEC_E_INVALID, "unknown flag bits 0x%x", flags & ~KNOWN_FLAGS);
+  if (flags & DEC_FLAG_UNFUSED) return fail(DEC_E_UNSUPPORTED, "DEC_FLAG_UNFUSED is not implemented in this build");
+  c->cfg.flags = flags;
+  c->info.flags = flags;
+  return DEC_OK;
+}
+
+int dec_step(dec_ctx* c, const dec_step_args* a) {
+  if (!c || !a) return fail(DEC_E_INVALID, "ctx or args is NULL");
+  if (c->failed) return fail(DEC_E_STATE, "context has failed; destroy it");
+  if (!c->loaded) return fail(DEC_E_STATE, "dec_step before dec_load_weights");
+  const dec_config& g = c->cfg;
+  const int n = a->n_seqs;
+  if (n < 1) return fail(DEC_E_INVALID, "n_seqs must be >= 1 (got %d)", n);
+  if (n > g.max_batch) return fail(DEC_E_CAPACITY, "n_seqs %d exceeds max_batch %d", n, g.max_batch);
+  if (!a->token_ids || !a->seq_lens || !a->block_tables)
+    return fail(DEC_E_INVALID, "token_ids, seq_lens and block_tables must be non-NULL");
+  const int bps = blocks_per_seq(g);
+  for (int b = 0; b < n; ++b) {
+    const int t = a->token_ids[b], p = a->seq_lens[b];
+    if (t < 0 || t >= g.vocab) return fail(DEC_E_INVALID, "token_ids[%d] = %d outside [0, %d)", b, t, g.vocab);
+    if (p < 0) return fail(DEC_E_INVALID, "seq_lens[%d] = %d is negative", b, p);
+    if (p >= g.max_seq_len) return fail(DEC_E_CAPACITY, "seq_lens[%d] = %d: position must be < max_seq_len %d", b, p, g.max_seq_len);
+    for (int k = 0; k <= p / 16; ++k) {
+      const int blk = a->block_tables[(size_t)b * bps + k];
+      if (blk < 0 || blk >= g.num_blocks)
+        return fail(DEC_E_CAPACITY, "block_tables[%d][%d] = %d outside [0, %d)", b, k, blk, g.num_blocks);
+    }
+  }
+  const int bi = bucket_index(n);
+  const int Bp = LADDER[bi];
+
+  // stage into the pinned slot (wait until the copy that last used it has finished)
+  const int s = c->slot;
+  c->slot ^= 1;
+  if (c->slot_pending[s]) HIPCHK(c, hipEventSynchronize(c->slot_ev[s]), "waiting for a staging slot");
+  uint8_t* st = c->pinned[s];
+  int32_t* ids = reinterpret_cast<int32_t*>(st + c->L.ids);
+  int32_t* lens = reinterpret_cast<int32_t*>(st + c->L.lens);
+  int32_t* bt = reinterpret_cast<int32_t*>(st + c->L.bt);
+  std::memcpy(ids, a->token_ids, (size_t)n * 4);
+  std::memcpy(lens, a->seq_lens, (size_t)n * 4);
+  std::memcpy(bt, a->block_tables, (size_t)n * bps * 4);
+  for (int b = n; b < Bp; ++b) {  // padded rows: token 0, position -1 (no cache write, no attention)
+    ids[b] = 0;
+    lens[b] = -1;
+    std::memset(bt + (size_t)b * bps, 0, (size_t)bps * 4);
+  }
+  HIPCHK(c, hipMemcpyAsync(c->ws, st, c->L.static_bytes, hipMemcpyHostToDevice, c->stream), "staging copy");
+  HIPCHK(c, hipEventRecord(c->slot_ev[s], c->stream), "hipEventRecord");
+  c->slot_pending[s] = true;
+
+  const int mode = (int)(g.flags & MODE_FLAGS) >> 1;
+  if (g.flags & DEC_FLAG_EAGER) {
+    hipError_t e = enqueue_step(c, Bp, c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
+    c->info.used_graph = 0;
+  } else {
+    if (g.flags & DEC_FLAG_CAPTURE_ALL) {
+      for (int i = 0; i < N_BUCKETS && LADDER[i] <= g.max_batch; ++i)
+        if (!c->graphs[i][mode]) {
+          int rc = capture(c, i, mode);
+          if (rc != DEC_OK) return rc;
+        }
+    }
+    if (!c->graphs[bi][mode]) {
+      int rc = capture(c, bi, mode);
+      if (rc != DEC_OK) return rc;
+    }
+    HIPCHK(c, hipGraphLaunch(c->graphs[bi][mode], c->stream), "hipGraphLaunch");
+    c->info.used_graph = 1;
+  }
+  int ncap = 0;
+  for (auto& row : c->graphs)
+    for (auto& ge : row) ncap += ge != nullptr;
+  const bool mfma = !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
+  const int slices = (!mfma && Bp > 8) ? Bp / 8 : 1;
+  const int L = g.n_layers;
+  c->info.kernels_per_step = 2 + (L > 0 ? 8 * L : 0) + (slices - 1) * (4 * L + 1);
+  c->info.bucket = Bp;
+  c->info.attn_splits = n_split_for(g, Bp);
+  c->info.used_mfma = mfma ? 1 : 0;
+  c->info.graphs_captured = ncap;
+  c->info.flags = g.flags;
+  return DEC_OK;
+}
+
+int dec_launch_matmul(dec_ctx* c, int which, int layer) {
+  if (!c) return fail(DEC_E_INVALID, "ctx is NULL");
+  if (c->failed) return fail(DEC_E_STATE, "context has failed; destroy it");
+  if (!c->loaded || c->info.bucket == 0) return fail(DEC_E_STATE, "dec_launch_matmul needs a previous dec_step");
+  if (which < DEC_MAT_O || which > DEC_MAT_LM_HEAD)
+    return fail(DEC_E_INVALID, "which must be DEC_MAT_O, DEC_MAT_GATE_UP, DEC_MAT_DOWN or DEC_MAT_LM_HEAD");
+  if (which != DEC_MAT_LM_HEAD && (layer < 0 || layer >= c->cfg.n_layers))
+    return fail(DEC_E_INVALID, "layer %d outside [0, %d)", layer, c->cfg.n_layers);
+  hipError_t e = run_matmul(c, which, which == DEC_MAT_LM_HEAD ? 0 : layer, c->info.bucket, c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
+  return DEC_OK;
+}
+
+int dec_get_info(const dec_ctx* c, dec_info* out) {
+  if (!c || !out) return fail(DEC_E_INVALID, "ctx or out is NULL");
+  *out = c->info;
+  return DEC_OK;
+}
+
+int dec_destroy(dec_ctx* c) {
+  if (!c) return DEC_OK;
+  int rc = DEC_OK;
+  if (c->stream || c->cap_stream) {
+    hipError_t e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) rc = fail(DEC_E_HIP, "dec_destroy: %s", hipGetErrorString(e));
+  }
+  drop_graphs(c);
+  for (int i = 0; i < 2; ++i) {
+    if (c->slot_ev[i]) (void)hipEventDestroy(c->slot_ev[i]);
+    if (c->pinned[i]) (void)hipHostFree(c->pinned[i]);
+  }
+  if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+  delete c;
+  return rc;
+}
+
+int dec_bw_probe(const void* buf, size_t bytes, int reps, void* hip_stream, double* out) {
+  if (!buf || !out || reps < 1 || bytes < 16 || bytes % 16 || !aligned16(buf))
+    return fail(DEC_E_INVALID, "dec_bw_probe: need a 16-byte aligned buffer, bytes a positive multiple of 16, reps >= 1");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e;
+  double best = 0.0;
+  if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess) goto done;
+  for (int r = 0; r < reps + 1; ++r) {
+    if ((e = hipEventRecord(e0, s)) != hipSuccess) goto done;
+    if ((e = dec::launch_bw_probe(buf, bytes, nullptr, s)) != hipSuccess) goto done;
+    if ((e = hipEventRecord(e1, s)) != hipSuccess) goto done;
+    if ((e = hipEventSynchronize(e1)) != hipSuccess) goto done;
+    float ms = 0.f;
+    if ((e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess) goto done;
+    if (r > 0 && ms > 0.f && bytes / (ms * 1e-3) > best) best = bytes / (ms * 1e-3);  // first run warms up
+  }
+done:
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return fail(DEC_E_HIP, "dec_bw_probe: %s", hipGetErrorString(e));
+  *out = best;
+  return DEC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Host-side launchers of the decode-step kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dec {
+
+// What the matrix kernels do with the fp32 row sums y[b][n] = scale[n] * sum_k W[n][k] x[b][k].
+enum Epilogue : int {
+  EPI_LOGITS = 0,  // out[b][n] = y                                   (LM head)
+  EPI_RESID = 1,   // out[b][n] += y                                  (O and down: residual add)
+  EPI_SILU = 2,    // act[b][i] = bf16(silu(y_gate[i]) * y_up[i])     (gate+up rows i, d_ff + i)
+  EPI_QKV = 3      // RoPE on q/k rows, q -> fp32 buffer, k/v -> paged KV cache (QKV rows)
+};
+
+struct MatmulParams {
+  const void* W;         // [N][K] bf16 or E4M3
+  const float* scale;    // [N] or nullptr (bf16)
+  int N, K;              // weight rows, columns
+  int d_ff;              // EPI_SILU: up rows start at d_ff (N = 2 d_ff)
+  const uint16_t* x;     // bf16 activations [Bp][ldx]
+  int ldx;
+  int Bp;                // padded batch (bucket)
+  float* out;            // EPI_LOGITS / EPI_RESID: [Bp][ldo]
+  int ldo;
+  uint16_t* act;         // EPI_SILU: bf16 [Bp][ldact]
+  int ldact;
+  // EPI_QKV
+  float* q;              // [Bp][Hq][dh]
+  void* pool;            // KV pool (bf16 or E4M3 elements)
+  int layer;
+  const int32_t* seq_lens;  // [Bp]; < 0 marks a padded row (no cache write)
+  const int32_t* bt;        // [Bp][bps]
+  const float2* rope;       // [max_seq_len][dh / 2] (cos, sin)
+  int Hq, Hkv, dh, num_blocks, bps;
+};
+
+// y = matrix x for one of the epilogues; gemv kernels for Bp <= 8, MFMA tiles for
+// Bp >= 16 unless no_mfma.  Returns the number of kernels launched through *n.
+hipError_t launch_matmul(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, bool mfma,
+                         hipStream_t s);
+
+struct NormParams {
+  const float* h;       // [Bp][d] fp32 (input, or output for the embedding kernel)
+  float* h_out;         // embed: h written here
+  const float* gain;    // [d]
+  uint16_t* x;          // [Bp][d] bf16 out
+  int d, Bp;
+  float eps;
+  // embedding
+  const void* E; const float* E_scale; const int32_t* ids;
+};
+
+// h = E[ids[b]] (dequantized), x = RMSNorm(h) g
+hipError_t launch_embed_norm(const NormParams& p, bool w_fp8, hipStream_t s);
+// x = RMSNorm(h) g
+hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
+
+struct AttnParams {
+  const float* q;         // [Bp][Hq][dh] fp32 (RoPE applied)
+  const void* pool;
+  int layer;
+  const int32_t* seq_lens;  // [Bp]
+  const int32_t* bt;        // [Bp][bps]
+  float* part_o;          // [Bp][Hq][n_split][dh]
+  float* part_ml;         // [Bp][Hq][n_split][2]
+  uint16_t* o;            // [Bp][Hq * dh] bf16 out
+  int Bp, Hq, Hkv, dh, num_blocks, bps, n_split;
+};
+
+// split-K paged GQA decode attention + log-sum-exp combine (2 kernels)
+hipError_t launch_attention(const AttnParams& p, bool kv_fp8, hipStream_t s);
+
+// (cos, sin)(p * theta^(-2i/dh)) for p < max_seq, i < dh/2, evaluated in double
+hipError_t launch_rope_table(float2* rope, int max_seq, int dh, double theta, hipStream_t s);
+
+// streaming read used to measure the device's HBM read bandwidth
+hipError_t launch_bw_probe(const void* buf, size_t bytes, float* sink, hipStream_t s);
+
+}  // namespace dec

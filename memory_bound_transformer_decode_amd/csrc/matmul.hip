@@ -1,0 +1,387 @@
+// Weight-streaming matrix kernels of the decode step: y = s (.) (W x) for a skinny
+// activation block x [Bp][K], with the step's fused epilogues.
+//
+// Decode reads every weight once per step to produce one column of activations per
+// sequence, so these kernels are HBM-bound (intensity 2B/b_w FLOP/byte; "GPU
+// Inference Internals", Roofline: Why Decode Is Memory-Bound).  Two shapes:
+//
+//  * k_gemv (Bp <= 8): one wave per work group; a wave owns a contiguous range of
+//    row pairs and streams both rows with 16-byte non-temporal loads, U loads per
+//    row in flight; activations come from L2 (they are tiny and shared by every
+//    wave); bf16 products use v_dot2_f32_bf16, E4M3 weights are widened to bf16 in
+//    registers (exact) and the per-row scale is applied once in the epilogue
+//    ("dequantization fused into the matmul ... converted in-register",
+//    kernel-fusion architecture study, section 11).
+//  * k_gemm_mfma (Bp >= 16): the batch is wide enough to make this a dense
+//    contraction, so 16x16x32 bf16 MFMA tiles do the products.  A work group owns
+//    a 16-row tile; its waves split K and reduce through LDS.
+//
+// Fused epilogues (fused-kernel table of "Kernels, Fusion & CUDA Graphs", Fix 1):
+// QKV + RoPE + paged KV-cache write, gate+up + SiLU x mul, residual add (O, down),
+// and plain fp32 logits (LM head).
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dec {
+
+// ---------------------------------------------------------------- epilogues
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// Rows (r0, r0 + 1) of the fused QKV matrix for batch row b, values v0, v1 (scaled).
+__device__ __forceinline__ void qkv_pair_out(const MatmulParams& p, bool kv_fp8, int b, int r0,
+                                             float v0, float v1) {
+  const int dh = p.dh;
+  const int qrows = p.Hq * dh, krows = p.Hkv * dh;
+  const int pos = p.seq_lens[b];
+  const int pr = pos < 0 ? 0 : pos;
+  if (r0 < qrows + krows) {  // q or k: rotate the adjacent pair (r0 even)
+    const int e = r0 % dh;
+    const float2 cs = p.rope[(int64_t)pr * (dh / 2) + (e >> 1)];
+    const float y0 = v0 * cs.x - v1 * cs.y;
+    const float y1 = v0 * cs.y + v1 * cs.x;
+    v0 = y0;
+    v1 = y1;
+  }
+  if (r0 < qrows) {
+    const int j = r0 / dh, e = r0 % dh;
+    float* qd = p.q + ((int64_t)b * p.Hq + j) * dh + e;
+    qd[0] = v0;
+    qd[1] = v1;
+    return;
+  }
+  if (pos < 0) return;  // padded row: no cache write
+  const int kv = r0 < qrows + krows ? 0 : 1;
+  const int rr = r0 - qrows - kv * krows;
+  const int c = rr / dh, e = rr % dh;
+  const int blk = p.bt[(int64_t)b * p.bps + pos / KV_BLOCK];
+  const int64_t off = kv_offset(p.layer, kv, blk, c, pos % KV_BLOCK, e, p.num_blocks, p.Hkv, dh);
+  if (kv_fp8) {
+    const uint32_t c0 = f32_to_e4m3(v0), c1 = f32_to_e4m3(v1);
+    *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.pool) + off) = (uint16_t)(c0 | (c1 << 8));
+  } else {
+    const uint32_t w = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.pool) + off) = w;
+  }
+}
+
+// Epilogue for one row pair (r0, r1) and batch row b; a0/a1 are unscaled sums.
+template <int EPI>
+__device__ __forceinline__ void pair_epilogue(const MatmulParams& p, bool kv_fp8, int b, int item, int r0,
+                                              int r1, float a0, float a1) {
+  const float s0 = p.scale ? p.scale[r0] : 1.0f;
+  const float s1 = p.scale ? p.scale[r1] : 1.0f;
+  const float y0 = a0 * s0, y1 = a1 * s1;
+  if (EPI == EPI_LOGITS) {
+    float* o = p.out + (int64_t)b * p.ldo;
+    o[r0] = y0;
+    o[r1] = y1;
+  } else if (EPI == EPI_RESID) {
+    float* o = p.out + (int64_t)b * p.ldo;
+    o[r0] += y0;
+    o[r1] += y1;
+  } else if (EPI == EPI_SILU) {
+    p.act[(int64_t)b * p.ldact + item] = f32_to_bf16(silu_f(y0) * y1);
+  } else {
+    qkv_pair_out(p, kv_fp8, b, r0, y0, y1);
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void item_rows(const MatmulParams& p, int item, int& r0, int& r1) {
+  if (EPI == EPI_SILU) {
+    r0 = item;
+    r1 = item + p.d_ff;
+  } else {
+    r0 = 2 * item;
+    r1 = 2 * item + 1;
+  }
+}
+
+// ---------------------------------------------------------------- gemv (Bp <= 8)
+
+template <int BT>
+struct GemvUnroll {
+  static constexpr int U = BT == 1 ? 16 : BT == 2 ? 8 : 4;
+};
+
+template <int BT, bool FP8, int EPI, bool KVFP8>
+__global__ __launch_bounds__(64) void k_gemv(MatmulParams p, int n_items) {
+  constexpr int U = GemvUnroll<BT>::U;
+  constexpr int EPV = FP8 ? 16 : 8;  // weight elements per 16-byte vector
+  const int lane = threadIdx.x;
+  const int i0 = (int)((int64_t)n_items * blockIdx.x / gridDim.x);
+  const int i1 = (int)((int64_t)n_items * (blockIdx.x + 1) / gridDim.x);
+  const int KV = p.K / EPV;  // 16-byte vectors per weight row (K % EPV == 0)
+  const u32x4* W = static_cast<const u32x4*>(p.W);
+
+  for (int it = i0; it < i1; ++it) {
+    int r0, r1;
+    item_rows<EPI>(p, it, r0, r1);
+    const u32x4* w0p = W + (int64_t)r0 * KV;
+    const u32x4* w1p = W + (int64_t)r1 * KV;
+    float acc0[BT], acc1[BT];
+#pragma unroll
+    for (int b = 0; b < BT; ++b) acc0[b] = acc1[b] = 0.0f;
+
+    for (int kb = lane; kb < KV; kb += WAVE * U) {
+      u32x4 w0[U], w1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = kb + WAVE * u;
+        if (kk < KV) {
+          w0[u] = ld_stream(w0p + kk);
+          w1[u] = ld_stream(w1p + kk);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = kb + WAVE * u;
+        if (kk < KV) {
+#pragma unroll
+          for (int b = 0; b < BT; ++b) {
+            const uint16_t* xb = p.x + (int64_t)b * p.ldx + (int64_t)kk * EPV;
+            if (FP8) {
+              const u32x4 xa = ld16(xb), xc = ld16(xb + 8);
+              acc0[b] = dot16_e4m3(w0[u], xa, xc, acc0[b]);
+              acc1[b] = dot16_e4m3(w1[u], xa, xc, acc1[b]);
+            } else {
+              const u32x4 xa = ld16(xb);
+              acc0[b] = dot8_bf16(w0[u], xa, acc0[b]);
+              acc1[b] = dot8_bf16(w1[u], xa, acc1[b]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      acc0[b] = wave_sum(acc0[b]);
+      acc1[b] = wave_sum(acc1[b]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int b = 0; b < BT; ++b) pair_epilogue<EPI>(p, KVFP8, b, it, r0, r1, acc0[b], acc1[b]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- MFMA tiles (Bp >= 16)
+//
+// v_mfma_f32_16x16x32_bf16: lane l supplies A[l % 16][8 k-values] and B[8 k-values][l % 16];
+// the four lane groups l / 16 cover four disjoint sets of 8 k-values; lane l receives
+// D[4 (l / 16) + j][l % 16], j = 0..3.  Which k-values a lane group covers is free as long
+// as A and B agree, so each lane takes a contiguous run (32 bytes of a weight row: 16 bf16
+// or 32 E4M3 codes) and 4 lanes cover a whole 128-byte line of each of the tile's rows.
+
+constexpr int MFMA_WAVES = 8;  // waves per work group; they split K
+
+template <int NT, bool FP8, int EPI, bool KVFP8>
+__global__ __launch_bounds__(WAVE * MFMA_WAVES) void k_gemm_mfma(MatmulParams p) {
+  constexpr int NA = EPI == EPI_SILU ? 2 : 1;  // A tiles per work group (gate + up)
+  constexpr int EPL = FP8 ? 32 : 16;           // weight elements per lane per step
+  constexpr int KSTEP = 4 * EPL;               // k per step (4 lane groups)
+  constexpr int NM = EPL / 8;                  // MFMAs per step per (A tile, column tile)
+  const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+  const int m = lane % 16, kg = lane / 16;
+  const int tile = blockIdx.x;
+
+  // rows of this lane's A operand
+  int arow[NA];
+  bool arow_ok[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const int r = (EPI == EPI_SILU ? a * p.d_ff : 0) + tile * 16 + m;
+    const int lim = EPI == EPI_SILU ? (a + 1) * p.d_ff : p.N;
+    arow_ok[a] = r < lim;
+    arow[a] = arow_ok[a] ? r : 0;
+  }
+  // k range of this wave
+  const int nsteps = (p.K + KSTEP - 1) / KSTEP;
+  const int per = (nsteps + MFMA_WAVES - 1) / MFMA_WAVES;
+  const int s0 = wave * per, s1 = min(nsteps, s0 + per);
+
+  f32x4 acc[NA][NT];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const size_t wrow_bytes = FP8 ? (size_t)p.K : (size_t)p.K * 2;
+  const uint8_t* Wb = static_cast<const uint8_t*>(p.W);
+
+  for (int st = s0; st < s1; ++st) {
+    const int k0 = st * KSTEP + kg * EPL;  // first k of this lane's run
+    // A: 32 bytes per lane per A tile, as two 16-byte halves (each half all-in or all-out of K)
+    u32x4 wa[NA][2];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int kh = k0 + hh * (EPL / 2);
+        if (arow_ok[a] && kh < p.K)
+          wa[a][hh] = ld_stream(reinterpret_cast<const u32x4*>(Wb + (size_t)arow[a] * wrow_bytes +
+                                                               (size_t)kh * (FP8 ? 1 : 2)));
+        else
+          wa[a][hh] = u32x4{0u, 0u, 0u, 0u};
+      }
+    // B: EPL bf16 activations per lane per column tile
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int col = t * 16 + m;
+      u32x4 xb[EPL / 8];
+#pragma unroll
+      for (int v = 0; v < EPL / 8; ++v) {
+        const int kv = k0 + v * 8;
+        if (col < p.Bp && kv < p.K)
+          xb[v] = ld16(p.x + (int64_t)col * p.ldx + kv);
+        else
+          xb[v] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+#pragma unroll
+        for (int mm = 0; mm < NM; ++mm) {
+          bf16x8 av;
+          if (FP8) {
+            // 8 codes: bytes [8 mm, 8 mm + 8) of the lane's 32-byte run
+            const u32x4& h = wa[a][mm / 2];
+            const uint32_t c0 = (mm & 1) ? h.z : h.x, c1 = (mm & 1) ? h.w : h.y;
+            const bf16x2 p0 = e4m3x2_to_bf16x2<false>(c0), p1 = e4m3x2_to_bf16x2<true>(c0);
+            const bf16x2 p2 = e4m3x2_to_bf16x2<false>(c1), p3 = e4m3x2_to_bf16x2<true>(c1);
+            av = bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+          } else {
+            av = __builtin_bit_cast(bf16x8, wa[a][mm]);
+          }
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, xb[mm]);
+          acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[a][t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // reduce the waves' partial tiles through LDS: red[wave][a][t][lane][j]
+  __shared__ float red[MFMA_WAVES * NA * NT * 64 * 4];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[(((wave * NA + a) * NT + t) * 64 + lane) * 4 + j] = acc[a][t][j];
+  __syncthreads();
+
+  auto total = [&](int a, int t, int l, int j) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < MFMA_WAVES; ++w) s += red[(((w * NA + a) * NT + t) * 64 + l) * 4 + j];
+    return s;
+  };
+  if (EPI == EPI_QKV) {
+    // pairs (j, j + 1) are rows (2i, 2i + 1) of the same lane
+    for (int idx = tid; idx < NT * 64 * 2; idx += WAVE * MFMA_WAVES) {
+      const int t = idx / 128, l = (idx / 2) % 64, jp = (idx % 2) * 2;
+      const int col = t * 16 + l % 16, row = tile * 16 + 4 * (l / 16) + jp;
+      if (col >= p.Bp || row >= p.N) continue;
+      const float s0 = p.scale ? p.scale[row] : 1.f, s1 = p.scale ? p.scale[row + 1] : 1.f;
+      qkv_pair_out(p, KVFP8, col, row, total(0, t, l, jp) * s0, total(0, t, l, jp + 1) * s1);
+    }
+  } else {
+    for (int idx = tid; idx < NT * 64 * 4; idx += WAVE * MFMA_WAVES) {
+      const int t = idx / 256, l = (idx / 4) % 64, j = idx % 4;
+      const int col = t * 16 + l % 16, r = tile * 16 + 4 * (l / 16) + j;
+      if (col >= p.Bp) continue;
+      if (EPI == EPI_SILU) {
+        if (r >= p.d_ff) continue;
+        const float sg = p.scale ? p.scale[r] : 1.f, su = p.scale ? p.scale[p.d_ff + r] : 1.f;
+        const float g = total(0, t, l, j) * sg, u = total(1, t, l, j) * su;
+        p.act[(int64_t)col * p.ldact + r] = f32_to_bf16(silu_f(g) * u);
+      } else {
+        if (r >= p.N) continue;
+        const float y = total(0, t, l, j) * (p.scale ? p.scale[r] : 1.f);
+        float* o = p.out + (int64_t)col * p.ldo + r;
+        if (EPI == EPI_RESID)
+          *o += y;
+        else
+          *o = y;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+namespace {
+
+constexpr int GEMV_MAX_WAVES = 256 * 8;  // 8 waves per CU on 256 CUs
+
+template <int BT, bool FP8, int EPI, bool KVFP8>
+hipError_t gemv_go(const MatmulParams& p, hipStream_t s) {
+  const int n_items = EPI == EPI_SILU ? p.d_ff : p.N / 2;
+  const int grid = n_items < GEMV_MAX_WAVES ? n_items : GEMV_MAX_WAVES;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8>), dim3(grid), dim3(WAVE), 0, s, p, n_items);
+  return hipGetLastError();
+}
+
+template <int NT, bool FP8, int EPI, bool KVFP8>
+hipError_t mfma_go(const MatmulParams& p, hipStream_t s) {
+  const int rows = EPI == EPI_SILU ? p.d_ff : p.N;
+  const int grid = (rows + 15) / 16;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_mfma<NT, FP8, EPI, KVFP8>), dim3(grid), dim3(WAVE * MFMA_WAVES), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool FP8, int EPI, bool KVFP8>
+hipError_t dispatch_bt(const MatmulParams& p, bool mfma, hipStream_t s) {
+  if (p.Bp <= 8 || !mfma) {
+    if (p.Bp <= 1) return gemv_go<1, FP8, EPI, KVFP8>(p, s);
+    if (p.Bp <= 2) return gemv_go<2, FP8, EPI, KVFP8>(p, s);
+    if (p.Bp <= 4) return gemv_go<4, FP8, EPI, KVFP8>(p, s);
+    if (p.Bp <= 8) return gemv_go<8, FP8, EPI, KVFP8>(p, s);
+    // no-MFMA mode above 8 rows: run the 8-row gemv on slices of the batch
+    for (int b0 = 0; b0 < p.Bp; b0 += 8) {
+      MatmulParams q = p;
+      q.x = p.x + (int64_t)b0 * p.ldx;
+      q.Bp = p.Bp - b0 < 8 ? p.Bp - b0 : 8;
+      q.out = p.out ? p.out + (int64_t)b0 * p.ldo : nullptr;
+      q.act = p.act ? p.act + (int64_t)b0 * p.ldact : nullptr;
+      q.q = p.q ? p.q + (int64_t)b0 * p.Hq * p.dh : nullptr;
+      q.seq_lens = p.seq_lens ? p.seq_lens + b0 : nullptr;
+      q.bt = p.bt ? p.bt + (int64_t)b0 * p.bps : nullptr;
+      hipError_t e;
+      if (q.Bp <= 1) e = gemv_go<1, FP8, EPI, KVFP8>(q, s);
+      else if (q.Bp <= 2) e = gemv_go<2, FP8, EPI, KVFP8>(q, s);
+      else if (q.Bp <= 4) e = gemv_go<4, FP8, EPI, KVFP8>(q, s);
+      else e = gemv_go<8, FP8, EPI, KVFP8>(q, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  if (p.Bp <= 16) return mfma_go<1, FP8, EPI, KVFP8>(p, s);
+  if (p.Bp <= 32) return mfma_go<2, FP8, EPI, KVFP8>(p, s);
+  if (p.Bp <= 48) return mfma_go<3, FP8, EPI, KVFP8>(p, s);
+  return mfma_go<4, FP8, EPI, KVFP8>(p, s);
+}
+
+template <bool FP8, bool KVFP8>
+hipError_t dispatch_epi(const MatmulParams& p, int epi, bool mfma, hipStream_t s) {
+  switch (epi) {
+    case EPI_LOGITS: return dispatch_bt<FP8, EPI_LOGITS, KVFP8>(p, mfma, s);
+    case EPI_RESID: return dispatch_bt<FP8, EPI_RESID, KVFP8>(p, mfma, s);
+    case EPI_SILU: return dispatch_bt<FP8, EPI_SILU, KVFP8>(p, mfma, s);
+    default: return dispatch_bt<FP8, EPI_QKV, KVFP8>(p, mfma, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_matmul(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, bool mfma, hipStream_t s) {
+  // the cache dtype only matters for the QKV epilogue; keep one instance otherwise
+  if (epi != EPI_QKV) kv_fp8 = false;
+  if (w_fp8) return kv_fp8 ? dispatch_epi<true, true>(p, epi, mfma, s) : dispatch_epi<true, false>(p, epi, mfma, s);
+  return kv_fp8 ? dispatch_epi<false, true>(p, epi, mfma, s) : dispatch_epi<false, false>(p, epi, mfma, s);
+}
+
+}  // namespace dec

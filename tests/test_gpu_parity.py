@@ -1,0 +1,224 @@
+"""Parity of the HIP decode step with the fp64 oracle (needs an MI355X).
+
+Every case draws its inputs from the seeded generator, runs the step through
+the C ABI (ctypes binding) and the oracle, and checks logits, greedy argmax and
+KV-cache placement (see harness.py for the bars).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from memory_bound_transformer_decode_amd import synth
+
+from harness import Case, assert_ok, log, make_case, require_gpu, run_parity
+
+pytestmark = pytest.mark.gpu
+
+# A small model whose shapes are ragged for every kernel: d = 320 is not a
+# multiple of the 512-element wave stride, vocab 1000 is not a multiple of the
+# 16-row MFMA tile, g = 5 query heads per KV head.
+MINI = synth.ModelConfig("mini", 7, n_layers=2, d_model=320, n_q_heads=10, n_kv_heads=2,
+                         d_head=64, d_ff=1040, vocab=1000)
+MINI128 = synth.ModelConfig("mini128", 8, n_layers=2, d_model=256, n_q_heads=8, n_kv_heads=1,
+                            d_head=128, d_ff=512, vocab=512)
+
+
+def fmt(cfg, w, kv):
+    return dataclasses.replace(cfg, weight_dtype=w, kv_dtype=kv, name=f"{cfg.name}-{w}-{kv}")
+
+
+@pytest.fixture(scope="module")
+def dec():
+    return require_gpu()
+
+
+def ctx_mix(B, rng, hi=100):
+    base = [0, 15, 16, 17, 1, 31, 32, 33]
+    lens = [base[i] if i < len(base) else int(rng.integers(0, hi)) for i in range(B)]
+    return lens
+
+
+# ------------------------------------------------------------------ LM-head path only
+
+@pytest.mark.parametrize("wdt", ["bf16", "fp8"])
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 13, 16, 24, 40, 64])
+def test_zero_layer_embed_norm_lmhead(dec, wdt, B):
+    cfg = fmt(MINI, wdt, "bf16").with_layers(0)
+    case = make_case(cfg, [0] * B, 16, seed=1, gains="random")
+    ids = synth.make_token_ids(cfg, 1, B, seed=1)
+    log(f"zero-layer {wdt} B={B}")
+    assert_ok(run_parity(case, ids), cfg)
+
+
+# ------------------------------------------------------------------ the tiny workload
+
+def test_tiny_workload(dec):
+    """1 layer, d 256, 4/4 heads of 64, batch 1, 32 prefilled positions, 8 decode steps."""
+    wl = synth.WORKLOADS["tiny"]
+    cfg = wl.model
+    case = make_case(cfg, [32], wl.max_seq_len, seed=0)
+    ids = synth.make_token_ids(cfg, wl.decode_steps, 1, seed=0)
+    log("tiny workload")
+    assert_ok(run_parity(case, ids), cfg)
+
+
+# ------------------------------------------------------------------ ragged mini models
+
+@pytest.mark.parametrize("w,kv", [("bf16", "bf16"), ("fp8", "fp8"), ("bf16", "fp8")])
+@pytest.mark.parametrize("B", [1, 3, 8, 13, 24, 64])
+def test_mini_model(dec, w, kv, B):
+    cfg = fmt(MINI, w, kv)
+    rng = np.random.default_rng(B)
+    case = make_case(cfg, ctx_mix(B, rng), 128, seed=2, gains="random")
+    ids = synth.make_token_ids(cfg, 3, B, seed=2)
+    log(f"mini {w}/{kv} B={B}")
+    assert_ok(run_parity(case, ids), cfg)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("B", [1, 5, 16])
+def test_mini_dh128_group8(dec, kv, B):
+    cfg = fmt(MINI128, "bf16" if kv == "bf16" else "fp8", kv)
+    rng = np.random.default_rng(10 + B)
+    case = make_case(cfg, ctx_mix(B, rng, hi=200), 256, seed=3, gains="random")
+    ids = synth.make_token_ids(cfg, 3, B, seed=3)
+    log(f"mini128 {kv} B={B}")
+    assert_ok(run_parity(case, ids), cfg)
+
+
+def test_decode_from_empty_cache(dec):
+    """Prefill by decode: 40 steps starting at position 0 (the cache holds only what
+    the step itself wrote)."""
+    cfg = fmt(MINI, "bf16", "bf16")
+    case = make_case(cfg, [0, 0, 0], 64, seed=4, gains="random")
+    ids = synth.make_token_ids(cfg, 40, 3, seed=4)
+    log("decode from empty cache")
+    assert_ok(run_parity(case, ids, kv_every_step=False), cfg)
+
+
+# ------------------------------------------------------------------ execution invariants
+
+def _one_step(dec, case, ids, lens, flags, max_batch=None):
+    d = dec.Decoder(case.cfg, case.weights, num_blocks=case.num_blocks,
+                    max_batch=max_batch or dec.ladder_bucket(len(ids)),
+                    max_seq_len=case.max_seq_len, flags=flags, kv_pool=case.pool.clone())
+    z = d.step(ids, lens, case.block_tables[: len(ids)]).clone()
+    torch.cuda.synchronize()
+    pool = d.kv_pool.clone()
+    info = d.info()
+    d.close()
+    return z, pool, info
+
+
+@pytest.mark.parametrize("B", [5, 24])
+def test_graph_replay_equals_eager_bitwise(dec, B):
+    cfg = fmt(MINI, "bf16", "bf16")
+    rng = np.random.default_rng(20)
+    case = make_case(cfg, ctx_mix(B, rng), 128, seed=5)
+    ids = synth.make_token_ids(cfg, 1, B, seed=5)[0]
+    ze, pe, ie = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_EAGER)
+    zg, pg, ig = _one_step(dec, case, ids, case.ctx_lens, 0)
+    assert ie.used_graph == 0 and ig.used_graph == 1
+    assert torch.equal(ze.view(torch.int32), zg.view(torch.int32))
+    assert torch.equal(pe.view(torch.uint8), pg.view(torch.uint8))
+    assert ie.kernels_per_step == ig.kernels_per_step == 8 * cfg.n_layers + 2
+
+
+def test_repeated_steps_are_deterministic(dec):
+    cfg = fmt(MINI, "fp8", "fp8")
+    case = make_case(cfg, [9, 40, 3], 128, seed=6)
+    ids = synth.make_token_ids(cfg, 1, 3, seed=6)[0]
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=4,
+                    max_seq_len=128, kv_pool=case.pool.clone())
+    outs = [d.step(ids, case.ctx_lens, case.block_tables).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    d.close()
+    for z in outs[1:]:
+        assert torch.equal(z.view(torch.int32), outs[0].view(torch.int32))
+
+
+@pytest.mark.parametrize("b_small,b_big", [(5, 7), (13, 15), (17, 23)])
+def test_padding_rows_are_inert(dec, b_small, b_big):
+    """Rows padded up to the bucket do not change the live rows' logits (bitwise)."""
+    cfg = fmt(MINI, "bf16", "bf16")
+    rng = np.random.default_rng(30)
+    lens = ctx_mix(b_big, rng)
+    case = make_case(cfg, lens, 128, seed=7)
+    ids = synth.make_token_ids(cfg, 1, b_big, seed=7)[0]
+    mb = dec.ladder_bucket(b_big)
+    zs, _, _ = _one_step(dec, case, ids[:b_small], case.ctx_lens[:b_small], 0, max_batch=mb)
+    zb, _, _ = _one_step(dec, case, ids, case.ctx_lens, 0, max_batch=mb)
+    assert torch.equal(zs.view(torch.int32), zb[:b_small].view(torch.int32))
+
+
+def test_gemv_path_matches_mfma_path(dec):
+    cfg = fmt(MINI, "bf16", "bf16")
+    rng = np.random.default_rng(40)
+    case = make_case(cfg, ctx_mix(24, rng), 128, seed=8, gains="random")
+    ids = synth.make_token_ids(cfg, 2, 24, seed=8)
+    assert_ok(run_parity(case, ids, flags=dec.FLAG_NO_MFMA), cfg)
+    za, _, ia = _one_step(dec, case, ids[0], case.ctx_lens, 0)
+    zb, _, ib = _one_step(dec, case, ids[0], case.ctx_lens, dec.FLAG_NO_MFMA)
+    assert ia.used_mfma == 1 and ib.used_mfma == 0
+    zo = za.double().cpu().numpy()
+    R = zo.max(axis=1) - zo.min(axis=1)
+    assert np.max(np.abs(za.double().cpu().numpy() - zb.double().cpu().numpy()) / R[:, None]) < 1e-2
+
+
+# ------------------------------------------------------------------ error paths on a live context
+
+def test_step_argument_errors(dec):
+    cfg = fmt(MINI, "bf16", "bf16")
+    case = make_case(cfg, [3, 5], 64, seed=9)
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=2, max_seq_len=64,
+                    kv_pool=case.pool.clone())
+    bt = case.block_tables
+    with pytest.raises(dec.DecError) as e:
+        d.step([3, cfg.vocab], [3, 5], bt)
+    assert e.value.code == dec.DEC_E_INVALID
+    with pytest.raises(dec.DecError) as e:
+        d.step([3, 4], [3, 64], bt)
+    assert e.value.code == dec.DEC_E_CAPACITY
+    bad = bt.copy()
+    bad[1, 0] = case.num_blocks
+    with pytest.raises(dec.DecError) as e:
+        d.step([3, 4], [3, 5], bad)
+    assert e.value.code == dec.DEC_E_CAPACITY
+    with pytest.raises(dec.DecError) as e:
+        d.step([1, 2, 3], [1, 2, 3], np.zeros((3, 4), np.int32))
+    assert e.value.code == dec.DEC_E_CAPACITY
+    # a rejected call has no side effects: the context still steps correctly
+    z = d.step([3, 4], [3, 5], bt)
+    torch.cuda.synchronize()
+    assert torch.isfinite(z).all()
+    d.close()
+
+
+# ------------------------------------------------------------------ workload shapes
+
+def test_1b_workload_shapes(dec):
+    """The ~1B workload at batch 1: 16 layers, 128 prefilled positions, 6 decode steps."""
+    wl = synth.WORKLOADS["1B"]
+    cfg = wl.model
+    case = make_case(cfg, [128], wl.max_seq_len, seed=0)
+    ids = synth.make_token_ids(cfg, 6, 1, seed=0)
+    log("1B workload")
+    assert_ok(run_parity(case, ids, keep_decoded=True, kv_every_step=False), cfg)
+
+
+@pytest.mark.parametrize("name,layers,B", [("8B", 2, 1), ("8B", 2, 8), ("8B", 1, 32),
+                                           ("32B", 1, 1), ("32B", 1, 13), ("32B", 1, 64),
+                                           ("70B", 1, 1), ("70B", 1, 64)])
+def test_large_workload_widths(dec, name, layers, B):
+    """Full widths and vocabulary of the 8B / 32B / 70B workloads at truncated depth,
+    at each workload's batch sizes and context mix, 2 decode steps."""
+    wl = synth.WORKLOADS[name]
+    cfg = wl.model.with_layers(layers)
+    lens = synth.make_context_lengths(wl, B, seed=0)
+    case = make_case(cfg, lens, wl.max_seq_len, seed=0)
+    ids = synth.make_token_ids(cfg, 2, B, seed=0)
+    log(f"{name} L={layers} B={B}")
+    assert_ok(run_parity(case, ids, stream_weights=True, kv_every_step=False), cfg)
