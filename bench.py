@@ -103,17 +103,26 @@ def run_batch(wl, B: int, steps: int, warmup: int, seed: int, want_eager: bool, 
         "tok_s": B * steps / wall, "ms_per_step": 1e3 * wall / steps,
         "bytes_per_step": step_bytes / steps, "achieved_gbps": step_bytes / wall / 1e9,
         "kernels_per_step": info.kernels_per_step, "bucket": info.bucket, "used_mfma": info.used_mfma,
+        "persistent": bool(info.persistent),
         "attn_splits": info.attn_splits, "graph": bool(info.used_graph),
         "flops_per_step": sum(shape.step_flops(lens0 + t) for t in range(steps)) / steps,
     }
     res["frac_of_peak"] = res["achieved_gbps"] / PEAK_GBPS
+    if info.persistent:
+        # the step is a single kernel: its duration is the event time per step (which
+        # also holds the small H2D copy of the step inputs that precedes the kernel)
+        res["kernel"] = {"name": "k_step (whole step, one persistent kernel)", "avg_s": ev / steps,
+                         "bytes": step_bytes / steps, "gbps": step_bytes / ev / 1e9, "launches": steps}
     if want_eager:
-        ew, _ = timed(dec.FLAG_EAGER)
-        res["eager_tok_s"] = B * steps / ew
-        res["eager_ms_per_step"] = 1e3 * ew / steps
-        res["graph_speedup"] = ew / wall
+        plans = {}
+        for name, flags in (("multi_kernel_graph", dec.FLAG_MULTI_KERNEL),
+                            ("multi_kernel_eager", dec.FLAG_MULTI_KERNEL | dec.FLAG_EAGER)):
+            w2, _ = timed(flags)
+            plans[name] = {"tok_s": B * steps / w2, "ms_per_step": 1e3 * w2 / steps,
+                           "kernels_per_step": d.info().kernels_per_step}
+        res["plans"] = plans
         d.set_flags(0)
-    if want_kernel:
+    if want_kernel and "kernel" not in res:
         # the dominant kernel alone, one launch per layer (distinct weights each launch,
         # so no launch is served from the 256 MB last-level cache), events per launch
         L = cfg.n_layers
@@ -130,7 +139,8 @@ def run_batch(wl, B: int, steps: int, warmup: int, seed: int, want_eager: bool, 
                 durs += [a.elapsed_time(b) / 1e3 for a, b in evs]
         avg = float(np.mean(durs))
         nbytes = gate_up_bytes(cfg, B)
-        res["kernel"] = {"avg_s": avg, "bytes": nbytes, "gbps": nbytes / avg / 1e9, "launches": len(durs)}
+        res["kernel"] = {"name": ("k_gemm_mfma" if B >= 16 else "k_gemv") + " gate+up + SiLU x mul",
+                         "avg_s": avg, "bytes": nbytes, "gbps": nbytes / avg / 1e9, "launches": len(durs)}
     d.close()
     del pool
     return res, weights
@@ -253,6 +263,7 @@ def main() -> int:
                          f"{args.steps} decode steps; hipGraph replay per step"),
             "batch": args.batch,
             "kernels_per_step": main_res["kernels_per_step"],
+            "persistent_step": main_res["persistent"],
             "attn_splits": main_res["attn_splits"],
         },
         "hbm": {"achieved_gbps": round(main_res["achieved_gbps"], 1),
@@ -261,16 +272,19 @@ def main() -> int:
                 "probe_read_gbps": round(probe, 1) if probe else None},
         "roofline": {"bound": "hbm", "achieved": round(k["gbps"], 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(k["gbps"] / PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "k_gemv gate+up + SiLU x mul (batch <= 8 path)" if args.batch <= 8 else
-                     "k_gemm_mfma gate+up + SiLU x mul",
-                     "bytes_per_launch": k["bytes"], "avg_us": round(k["avg_s"] * 1e6, 2),
+                     "kernel": k["name"],
+                     "bytes_per_launch": int(k["bytes"]), "avg_us": round(k["avg_s"] * 1e6, 2),
                      "launches": k["launches"]},
         "cpu_baseline": cpu,
     }
-    if "eager_tok_s" in main_res:
-        line["graph_vs_eager"] = {"eager_tok_s": round(main_res["eager_tok_s"], 3),
-                                  "eager_ms_per_step": round(main_res["eager_ms_per_step"], 4),
-                                  "graph_speedup": round(main_res["graph_speedup"], 4)}
+    if "plans" in main_res:
+        pl = {"persistent_graph" if main_res["persistent"] else "default_graph":
+              {"tok_s": round(main_res["tok_s"], 3), "ms_per_step": round(main_res["ms_per_step"], 4),
+               "kernels_per_step": main_res["kernels_per_step"]}}
+        for k2, v in main_res["plans"].items():
+            pl[k2] = {"tok_s": round(v["tok_s"], 3), "ms_per_step": round(v["ms_per_step"], 4),
+                      "kernels_per_step": v["kernels_per_step"]}
+        line["plans"] = pl
     if second:
         line[f"batch{second['batch']}"] = {
             "value": round(second["tok_s"], 2), "unit": "tokens/s",

@@ -69,7 +69,9 @@ enum {
   DEC_FLAG_EAGER = 1u,       /* launch kernels one by one instead of replaying a captured graph */
   DEC_FLAG_UNFUSED = 2u,     /* one kernel per op, intermediates through HBM (measurement only) */
   DEC_FLAG_NO_MFMA = 4u,     /* matrix-vector kernels at every batch size (no MFMA tiles) */
-  DEC_FLAG_CAPTURE_ALL = 8u  /* capture every batch bucket at the first step instead of lazily */
+  DEC_FLAG_CAPTURE_ALL = 8u, /* capture every batch bucket at the first step instead of lazily */
+  DEC_FLAG_MULTI_KERNEL = 16u /* one kernel per fused op at every batch size; without it a padded
+                                 batch of <= 8 runs the whole step as one persistent kernel */
 };
 
 typedef struct dec_config {
@@ -130,7 +132,7 @@ typedef struct dec_info {
   int32_t used_graph;        /* 1 if the last step replayed a captured graph              */
   int32_t graphs_captured;   /* buckets with a live captured graph                        */
   uint32_t flags;            /* current DEC_FLAG_* set                                    */
-  int32_t reserved;
+  int32_t persistent;        /* 1 if the last step ran as one persistent kernel            */
 } dec_info;
 
 /* Bytes of device workspace a context with this config needs (0 on an invalid

@@ -18,10 +18,50 @@ constexpr int KV_BLOCK = 16;  // positions per paged KV block
 
 // ---------------------------------------------------------------- loads
 
+// Global-memory accesses through pointers the compiler cannot place (read from
+// memory, or passed around generically) would become flat instructions, which also
+// count against the LDS counter and so make every LDS read wait for in-flight global
+// loads.  These helpers address global memory explicitly.
+#define DEC_GLOBAL __attribute__((address_space(1)))
+
+template <typename T>
+__device__ __forceinline__ T gld(const T* p) { return *(const DEC_GLOBAL T*)p; }
+template <typename T>
+__device__ __forceinline__ void gst(T* p, T v) { *(DEC_GLOBAL T*)p = v; }
+
 // Weights are read exactly once per step: stream them past the caches.
-__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load((const DEC_GLOBAL u32x4*)p); }
+// 16 bytes from global memory
+__device__ __forceinline__ u32x4 gld16(const void* p) { return gld(reinterpret_cast<const u32x4*>(p)); }
+// 16 bytes from LDS or global memory (the caller's pointer decides)
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// Data one work group writes and another work group of the same kernel reads (the
+// persistent step's residual stream, q, attention partials, activations, the new
+// token's K/V) goes through device-coherent accesses: each L2 (one per XCD) is not
+// coherent with the others, so these stores write through it and these loads bypass
+// it.  No cache flush or invalidate is then needed at a grid barrier, only that the
+// stores have completed (see the barrier in the persistent step).
+template <typename T>
+__device__ __forceinline__ T cld(const T* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename T>
+__device__ __forceinline__ void cst(T* p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ u32x4 cld16(const void* p) {
+  const uint64_t* q = static_cast<const uint64_t*>(p);
+  const uint64_t a = cld(q), b = cld(q + 1);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+__device__ __forceinline__ void cst_f2(float* p, float x, float y) {
+  cst(reinterpret_cast<uint64_t*>(p), (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32));
+}
+__device__ __forceinline__ void cst_f4(float* p, float x, float y, float z, float w) {
+  cst_f2(p, x, y);
+  cst_f2(p + 2, z, w);
+}
+__device__ __forceinline__ f32x4 cld_f4(const float* p) {
+  const u32x4 v = cld16(p);
+  return f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+}
 
 // ---------------------------------------------------------------- number formats
 

@@ -41,8 +41,18 @@ constexpr int LADDER[] = {1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64};
 constexpr int N_BUCKETS = sizeof(LADDER) / sizeof(LADDER[0]);
 constexpr int MAX_SPLIT = 64;
 constexpr int ATTN_TARGET_GROUPS = 1024;  // work groups per attention launch to aim for
-constexpr uint32_t KNOWN_FLAGS = DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL;
-constexpr uint32_t MODE_FLAGS = DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA;  // flags that change the kernel plan
+constexpr uint32_t KNOWN_FLAGS =
+    DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL | DEC_FLAG_MULTI_KERNEL;
+constexpr int N_MODES = 8;  // plan-changing flag combinations (UNFUSED, NO_MFMA, MULTI_KERNEL)
+constexpr int PERSIST_MAX_BATCH = 8;
+constexpr size_t PERSIST_XS_BUDGET = 128 * 1024;  // LDS for one layer input block
+constexpr int PERSIST_ASSUMED_WAVES = 256 * 8;    // sizes the attention split count
+constexpr double BARRIER_TIMEOUT_S = 0.25;
+
+int mode_of(uint32_t flags) {
+  return (int)(((flags & DEC_FLAG_UNFUSED) ? 1 : 0) | ((flags & DEC_FLAG_NO_MFMA) ? 2 : 0) |
+               ((flags & DEC_FLAG_MULTI_KERNEL) ? 4 : 0));
+}
 
 int bucket_index(int n) {
   for (int i = 0; i < N_BUCKETS; ++i)
@@ -62,9 +72,29 @@ int n_split_for(const dec_config& c, int Bp) {
   return ns < 1 ? 1 : ns;
 }
 
+// context splits of the persistent step's attention: about two (sequence, head, split)
+// units per wave
+int n_split_persistent(const dec_config& c, int Bp) {
+  int ns = (2 * PERSIST_ASSUMED_WAVES + Bp * c.n_q_heads - 1) / (Bp * c.n_q_heads);
+  const int bps = blocks_per_seq(c);
+  if (ns > bps) ns = bps;
+  if (ns > MAX_SPLIT) ns = MAX_SPLIT;
+  return ns < 1 ? 1 : ns;
+}
+
+// the persistent step holds one layer input block [Bp][K] of bf16 in LDS
+bool persistent_fits(const dec_config& c, int Bp) {
+  size_t k = (size_t)c.d_model;
+  if ((size_t)c.n_q_heads * c.d_head > k) k = (size_t)c.n_q_heads * c.d_head;
+  if ((size_t)c.d_ff > k) k = (size_t)c.d_ff;
+  return Bp <= PERSIST_MAX_BATCH && (size_t)Bp * k * 2 <= PERSIST_XS_BUDGET;
+}
+
 struct Layout {
   size_t ids, lens, bt, static_bytes;  // static region: ids | lens | block tables
-  size_t h, x, q, part_o, part_ml, o, a, rope, total;
+  size_t h, x, q, part_o, part_ml, o, a, rope;
+  size_t mats, bar, attn_cnt, err;     // persistent-step state
+  size_t total;
 };
 
 Layout layout_of(const dec_config& c) {
@@ -88,8 +118,10 @@ Layout layout_of(const dec_config& c) {
   off = align256(off + MB * c.n_q_heads * c.d_head * 4);
   size_t rows_split = 0;  // max over buckets of Bp * n_split
   for (int i = 0; i < N_BUCKETS && LADDER[i] <= c.max_batch; ++i) {
-    const size_t r = (size_t)LADDER[i] * n_split_for(c, LADDER[i]);
+    size_t r = (size_t)LADDER[i] * n_split_for(c, LADDER[i]);
     if (r > rows_split) rows_split = r;
+    r = (size_t)LADDER[i] * n_split_persistent(c, LADDER[i]);
+    if (persistent_fits(c, LADDER[i]) && r > rows_split) rows_split = r;
   }
   L.part_o = off;
   off = align256(off + rows_split * c.n_q_heads * c.d_head * 4);
@@ -101,6 +133,14 @@ Layout layout_of(const dec_config& c) {
   off = align256(off + MB * c.d_ff * 2);
   L.rope = off;
   off = align256(off + (size_t)c.max_seq_len * (c.d_head / 2) * 8);
+  L.mats = off;  // device copies of the per-layer weight pointers: 4 arrays of n_layers
+  off = align256(off + (size_t)4 * (c.n_layers > 0 ? c.n_layers : 1) * sizeof(dec::DevMat));
+  L.bar = off;
+  off = align256(off + 2 * 4);
+  L.attn_cnt = off;
+  off = align256(off + MB * c.n_q_heads * 4);
+  L.err = off;
+  off = align256(off + 4);
   L.total = off;
   return L;
 }
@@ -130,6 +170,27 @@ int validate_config(const dec_config* c) {
   return DEC_OK;
 }
 
+// waves of one work group that share a row pair's K range in a persistent product
+// phase: the smallest S in {1, 2, 4, 8} that spreads the rows evenly over the waves
+int choose_split(int items, int groups) {
+  const int pw = dec::step_waves_per_group();
+  int best = 1;
+  double best_eff = 0.0;
+  for (int S = 1; S <= pw; S *= 2) {
+    const int wg_items = (items + groups - 1) / groups;
+    const int slots = pw / S;
+    const int per_slot = (wg_items + slots - 1) / slots;
+    if (S > 1 && per_slot > dec::step_max_rounds()) continue;
+    const double work = (double)per_slot / S;
+    const double eff = ((double)items / ((double)groups * pw)) / work;
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = S;
+    }
+  }
+  return best;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
@@ -157,8 +218,13 @@ struct dec_ctx {
   bool slot_pending[2] = {false, false};
   int slot = 0;
   // graphs per (bucket, plan flags)
-  hipGraphExec_t graphs[N_BUCKETS][4] = {};
+  hipGraphExec_t graphs[N_BUCKETS][N_MODES] = {};
   dec_info info{};
+  // persistent step
+  int n_cu = 0;
+  uint64_t timeout_ticks = 0;
+  unsigned* err_host = nullptr;      // pinned, written by the device on a barrier timeout
+  unsigned* err_host_dev = nullptr;  // its device address
 };
 
 namespace {
@@ -265,8 +331,70 @@ hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s) {
   return dec::launch_matmul(p, epi, g.weight_dtype == DEC_FP8_E4M3, g.kv_dtype == DEC_FP8_E4M3, mfma, s);
 }
 
-// Enqueue the fused plan of one step for a padded batch of Bp rows on stream s.
+bool use_persistent(const dec_ctx* c, int Bp) {
+  return !(c->cfg.flags & (DEC_FLAG_MULTI_KERNEL | DEC_FLAG_UNFUSED)) && persistent_fits(c->cfg, Bp);
+}
+
+// The whole step as one persistent kernel (Bp <= 8).
+hipError_t enqueue_persistent(dec_ctx* c, int Bp, hipStream_t s) {
+  const dec_config& g = c->cfg;
+  dec::StepParams p{};
+  p.L = g.n_layers;
+  p.d = g.d_model;
+  p.Hq = g.n_q_heads;
+  p.Hkv = g.n_kv_heads;
+  p.dh = g.d_head;
+  p.dff = g.d_ff;
+  p.V = g.vocab;
+  p.Bp = Bp;
+  p.num_blocks = g.num_blocks;
+  p.bps = blocks_per_seq(g);
+  p.n_split = n_split_persistent(g, Bp);
+  p.eps = g.rms_eps;
+  const int G = c->n_cu;
+  p.split[0] = choose_split((g.n_q_heads + 2 * g.n_kv_heads) * g.d_head / 2, G);
+  p.split[1] = choose_split(g.d_model / 2, G);
+  p.split[2] = choose_split(g.d_ff, G);
+  p.split[3] = choose_split(g.d_model / 2, G);
+  p.split[4] = choose_split(g.vocab / 2, G);
+  size_t k = (size_t)g.d_model;
+  if ((size_t)g.n_q_heads * g.d_head > k) k = (size_t)g.n_q_heads * g.d_head;
+  if ((size_t)g.d_ff > k) k = (size_t)g.d_ff;
+  p.xs_bytes = (int)(((size_t)Bp * k * 2 + 15) & ~(size_t)15);
+  const dec::DevMat* mats = ws_ptr<dec::DevMat>(c, c->L.mats);
+  const int Ls = g.n_layers > 0 ? g.n_layers : 1;
+  p.w_qkv = mats;
+  p.w_o = mats + Ls;
+  p.w_gu = mats + 2 * Ls;
+  p.w_down = mats + 3 * Ls;
+  p.embed = dec::DevMat{c->embed.w, c->embed.scale};
+  p.lm = dec::DevMat{c->lm.w, c->lm.scale};
+  p.attn_norm = c->attn_norm;
+  p.mlp_norm = c->mlp_norm;
+  p.final_norm = c->final_norm;
+  p.ids = ws_ptr<int32_t>(c, c->L.ids);
+  p.lens = ws_ptr<int32_t>(c, c->L.lens);
+  p.bt = ws_ptr<int32_t>(c, c->L.bt);
+  p.h = ws_ptr<float>(c, c->L.h);
+  p.q = ws_ptr<float>(c, c->L.q);
+  p.part_o = ws_ptr<float>(c, c->L.part_o);
+  p.part_ml = ws_ptr<float>(c, c->L.part_ml);
+  p.o = ws_ptr<uint16_t>(c, c->L.o);
+  p.a = ws_ptr<uint16_t>(c, c->L.a);
+  p.rope = ws_ptr<float2>(c, c->L.rope);
+  p.pool = c->pool;
+  p.logits = c->logits;
+  p.bar = ws_ptr<unsigned>(c, c->L.bar);
+  p.attn_cnt = ws_ptr<unsigned>(c, c->L.attn_cnt);
+  p.err_dev = ws_ptr<unsigned>(c, c->L.err);
+  p.err_host = c->err_host_dev;
+  p.timeout_ticks = c->timeout_ticks;
+  return dec::launch_step(p, g.weight_dtype == DEC_FP8_E4M3, g.kv_dtype == DEC_FP8_E4M3, G, s);
+}
+
+// Enqueue the plan of one step for a padded batch of Bp rows on stream s.
 hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
+  if (use_persistent(c, Bp)) return enqueue_persistent(c, Bp, s);
   const dec_config& g = c->cfg;
   const bool wfp8 = g.weight_dtype == DEC_FP8_E4M3, kvfp8 = g.kv_dtype == DEC_FP8_E4M3;
   const int bps = blocks_per_seq(g);
@@ -405,6 +533,18 @@ int dec_create(const dec_config* cfg, void* hip_stream, void* kv_pool, void* wor
     delete c;
     return rc;
   }
+  int wall_khz = 0;
+  if ((e = hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device)) != hipSuccess ||
+      (e = hipHostMalloc(reinterpret_cast<void**>(&c->err_host), 64, hipHostMallocMapped)) != hipSuccess ||
+      (e = hipHostGetDevicePointer(reinterpret_cast<void**>(&c->err_host_dev), c->err_host, 0)) != hipSuccess) {
+    rc = hip_fail(nullptr, e, "dec_create: device attributes / error word");
+    dec_destroy(c);
+    return rc;
+  }
+  *reinterpret_cast<volatile unsigned*>(c->err_host) = 0u;
+  if (hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, c->device) != hipSuccess || wall_khz <= 0)
+    wall_khz = 100000;  // the s_memrealtime counter runs at 100 MHz on this family
+  c->timeout_ticks = (uint64_t)((double)wall_khz * 1e3 * BARRIER_TIMEOUT_S);
   for (int i = 0; i < 2; ++i) {
     if ((e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned[i]), L.static_bytes, hipHostMallocDefault)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&c->slot_ev[i], hipEventDisableTiming)) != hipSuccess) {
@@ -418,6 +558,7 @@ int dec_create(const dec_config* cfg, void* hip_stream, void* kv_pool, void* wor
   if ((e = dec::launch_rope_table(ws_ptr<float2>(c, L.rope), cfg->max_seq_len, cfg->d_head, (double)cfg->rope_theta,
                                   c->stream)) != hipSuccess ||
       (e = hipMemsetAsync(c->ws, 0, L.static_bytes, c->stream)) != hipSuccess ||
+      (e = hipMemsetAsync(c->ws + L.bar, 0, L.total - L.bar, c->stream)) != hipSuccess ||
       (e = hipStreamSynchronize(c->stream)) != hipSuccess) {
     rc = hip_fail(nullptr, e, "dec_create: initialising the workspace");
     dec_destroy(c);
@@ -457,6 +598,20 @@ int dec_load_weights(dec_ctx* c, const dec_weights* w) {
   c->o.assign(w->o, w->o + g.n_layers);
   c->gu.assign(w->gate_up, w->gate_up + g.n_layers);
   c->down.assign(w->down, w->down + g.n_layers);
+  // device copies of the per-layer pointers for the persistent step
+  if (g.n_layers > 0) {
+    std::vector<dec::DevMat> host(4 * (size_t)g.n_layers);
+    for (int l = 0; l < g.n_layers; ++l) {
+      host[l] = dec::DevMat{c->qkv[l].w, c->qkv[l].scale};
+      host[g.n_layers + l] = dec::DevMat{c->o[l].w, c->o[l].scale};
+      host[2 * g.n_layers + l] = dec::DevMat{c->gu[l].w, c->gu[l].scale};
+      host[3 * g.n_layers + l] = dec::DevMat{c->down[l].w, c->down[l].scale};
+    }
+    hipError_t e = hipMemcpyAsync(c->ws + c->L.mats, host.data(), host.size() * sizeof(dec::DevMat),
+                                  hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "dec_load_weights: uploading layer pointers");
+  }
   c->loaded = true;
   c->info.graphs_captured = 0;
   return DEC_OK;
@@ -475,6 +630,10 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   if (!c || !a) return fail(DEC_E_INVALID, "ctx or args is NULL");
   if (c->failed) return fail(DEC_E_STATE, "context has failed; destroy it");
   if (!c->loaded) return fail(DEC_E_STATE, "dec_step before dec_load_weights");
+  if (*reinterpret_cast<volatile unsigned*>(c->err_host) != 0u) {
+    c->failed = true;
+    return fail(DEC_E_HIP, "a grid-wide barrier of an earlier step timed out; the context is unusable");
+  }
   const dec_config& g = c->cfg;
   const int n = a->n_seqs;
   if (n < 1) return fail(DEC_E_INVALID, "n_seqs must be >= 1 (got %d)", n);
@@ -516,7 +675,7 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   HIPCHK(c, hipEventRecord(c->slot_ev[s], c->stream), "hipEventRecord");
   c->slot_pending[s] = true;
 
-  const int mode = (int)(g.flags & MODE_FLAGS) >> 1;
+  const int mode = mode_of(g.flags);
   if (g.flags & DEC_FLAG_EAGER) {
     hipError_t e = enqueue_step(c, Bp, c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
@@ -539,13 +698,15 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   int ncap = 0;
   for (auto& row : c->graphs)
     for (auto& ge : row) ncap += ge != nullptr;
-  const bool mfma = !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
+  const bool persist = use_persistent(c, Bp);
+  const bool mfma = !persist && !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
   const int slices = (!mfma && Bp > 8) ? Bp / 8 : 1;
   const int L = g.n_layers;
-  c->info.kernels_per_step = 2 + (L > 0 ? 8 * L : 0) + (slices - 1) * (4 * L + 1);
+  c->info.kernels_per_step = persist ? 1 : 2 + (L > 0 ? 8 * L : 0) + (slices - 1) * (4 * L + 1);
   c->info.bucket = Bp;
-  c->info.attn_splits = n_split_for(g, Bp);
+  c->info.attn_splits = persist ? n_split_persistent(g, Bp) : n_split_for(g, Bp);
   c->info.used_mfma = mfma ? 1 : 0;
+  c->info.persistent = persist ? 1 : 0;
   c->info.graphs_captured = ncap;
   c->info.flags = g.flags;
   return DEC_OK;
@@ -583,6 +744,7 @@ int dec_destroy(dec_ctx* c) {
     if (c->pinned[i]) (void)hipHostFree(c->pinned[i]);
   }
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+  if (c->err_host) (void)hipHostFree(c->err_host);
   delete c;
   return rc;
 }

@@ -72,6 +72,51 @@ struct AttnParams {
 // split-K paged GQA decode attention + log-sum-exp combine (2 kernels)
 hipError_t launch_attention(const AttnParams& p, bool kv_fp8, hipStream_t s);
 
+// ---------------------------------------------------------------- persistent step (Bp <= 8)
+
+struct DevMat {
+  const void* w;
+  const float* scale;
+};
+
+struct StepParams {
+  int L, d, Hq, Hkv, dh, dff, V, Bp, num_blocks, bps, n_split;
+  float eps;
+  int split[5];           // waves sharing one row pair's K range: QKV, O, gate+up, down, LM head
+  int xs_bytes;           // LDS bytes for the activation block
+  const DevMat* w_qkv;    // device arrays [L]
+  const DevMat* w_o;
+  const DevMat* w_gu;
+  const DevMat* w_down;
+  DevMat embed, lm;
+  const float* attn_norm;
+  const float* mlp_norm;
+  const float* final_norm;
+  const int32_t* ids;
+  const int32_t* lens;
+  const int32_t* bt;
+  float* h;
+  float* q;
+  float* part_o;
+  float* part_ml;
+  uint16_t* o;
+  uint16_t* a;
+  const float2* rope;
+  void* pool;
+  float* logits;
+  unsigned* bar;          // [count, generation] of the grid barrier
+  unsigned* attn_cnt;     // [Bp][Hq] splits finished per head (self-resetting)
+  unsigned* err_dev;      // barrier timeout flag, device copy
+  unsigned* err_host;     // barrier timeout flag, pinned host copy
+  uint64_t timeout_ticks; // bound on one barrier wait, in s_memrealtime ticks
+};
+
+// One launch of the whole step: grid = one work group per CU, all resident.
+hipError_t launch_step(const StepParams& p, bool w_fp8, bool kv_fp8, int grid, hipStream_t s);
+size_t step_lds_bytes(const StepParams& p);
+int step_max_rounds();
+int step_waves_per_group();
+
 // (cos, sin)(p * theta^(-2i/dh)) for p < max_seq, i < dh/2, evaluated in double
 hipError_t launch_rope_table(float2* rope, int max_seq, int dh, double theta, hipStream_t s);
 

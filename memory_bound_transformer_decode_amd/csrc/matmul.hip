@@ -21,83 +21,10 @@
 // and plain fp32 logits (LM head).
 
 #include "common.h"
+#include "epilogue.h"
 #include "kernels.h"
 
 namespace dec {
-
-// ---------------------------------------------------------------- epilogues
-
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-
-// Rows (r0, r0 + 1) of the fused QKV matrix for batch row b, values v0, v1 (scaled).
-__device__ __forceinline__ void qkv_pair_out(const MatmulParams& p, bool kv_fp8, int b, int r0,
-                                             float v0, float v1) {
-  const int dh = p.dh;
-  const int qrows = p.Hq * dh, krows = p.Hkv * dh;
-  const int pos = p.seq_lens[b];
-  const int pr = pos < 0 ? 0 : pos;
-  if (r0 < qrows + krows) {  // q or k: rotate the adjacent pair (r0 even)
-    const int e = r0 % dh;
-    const float2 cs = p.rope[(int64_t)pr * (dh / 2) + (e >> 1)];
-    const float y0 = v0 * cs.x - v1 * cs.y;
-    const float y1 = v0 * cs.y + v1 * cs.x;
-    v0 = y0;
-    v1 = y1;
-  }
-  if (r0 < qrows) {
-    const int j = r0 / dh, e = r0 % dh;
-    float* qd = p.q + ((int64_t)b * p.Hq + j) * dh + e;
-    qd[0] = v0;
-    qd[1] = v1;
-    return;
-  }
-  if (pos < 0) return;  // padded row: no cache write
-  const int kv = r0 < qrows + krows ? 0 : 1;
-  const int rr = r0 - qrows - kv * krows;
-  const int c = rr / dh, e = rr % dh;
-  const int blk = p.bt[(int64_t)b * p.bps + pos / KV_BLOCK];
-  const int64_t off = kv_offset(p.layer, kv, blk, c, pos % KV_BLOCK, e, p.num_blocks, p.Hkv, dh);
-  if (kv_fp8) {
-    const uint32_t c0 = f32_to_e4m3(v0), c1 = f32_to_e4m3(v1);
-    *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.pool) + off) = (uint16_t)(c0 | (c1 << 8));
-  } else {
-    const uint32_t w = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
-    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.pool) + off) = w;
-  }
-}
-
-// Epilogue for one row pair (r0, r1) and batch row b; a0/a1 are unscaled sums.
-template <int EPI>
-__device__ __forceinline__ void pair_epilogue(const MatmulParams& p, bool kv_fp8, int b, int item, int r0,
-                                              int r1, float a0, float a1) {
-  const float s0 = p.scale ? p.scale[r0] : 1.0f;
-  const float s1 = p.scale ? p.scale[r1] : 1.0f;
-  const float y0 = a0 * s0, y1 = a1 * s1;
-  if (EPI == EPI_LOGITS) {
-    float* o = p.out + (int64_t)b * p.ldo;
-    o[r0] = y0;
-    o[r1] = y1;
-  } else if (EPI == EPI_RESID) {
-    float* o = p.out + (int64_t)b * p.ldo;
-    o[r0] += y0;
-    o[r1] += y1;
-  } else if (EPI == EPI_SILU) {
-    p.act[(int64_t)b * p.ldact + item] = f32_to_bf16(silu_f(y0) * y1);
-  } else {
-    qkv_pair_out(p, kv_fp8, b, r0, y0, y1);
-  }
-}
-
-template <int EPI>
-__device__ __forceinline__ void item_rows(const MatmulParams& p, int item, int& r0, int& r1) {
-  if (EPI == EPI_SILU) {
-    r0 = item;
-    r1 = item + p.d_ff;
-  } else {
-    r0 = 2 * item;
-    r1 = 2 * item + 1;
-  }
-}
 
 // ---------------------------------------------------------------- gemv (Bp <= 8)
 

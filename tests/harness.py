@@ -171,8 +171,10 @@ def run_parity(case: Case, batch_ids: np.ndarray, *, flags: int = 0, max_batch: 
         if cfg.n_layers > 0 and (kv_every_step or t == steps - 1):
             compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol)
         lens = lens + 1
+    info = d.info()
     d.close()
-    log(f"{cfg.name} B={B} steps={steps} flags={flags}: max rel err {rep.max_rel_err:.3e} "
+    log(f"{cfg.name} B={B} steps={steps} flags={flags} persistent={info.persistent} "
+        f"mfma={info.used_mfma}: max rel err {rep.max_rel_err:.3e} "
         f"(tol {tol}), argmax {rep.argmax_checked - rep.argmax_mismatch}/{rep.argmax_checked}, "
         f"kv elements off the oracle's code {rep.kv_neighbour}")
     return rep
