@@ -70,8 +70,9 @@ enum {
   DEC_FLAG_UNFUSED = 2u,     /* one kernel per op, intermediates through HBM (measurement only) */
   DEC_FLAG_NO_MFMA = 4u,     /* matrix-vector kernels at every batch size (no MFMA tiles) */
   DEC_FLAG_CAPTURE_ALL = 8u, /* capture every batch bucket at the first step instead of lazily */
-  DEC_FLAG_MULTI_KERNEL = 16u /* one kernel per fused op at every batch size; without it a padded
-                                 batch of <= 8 runs the whole step as one persistent kernel */
+  DEC_FLAG_PERSISTENT = 16u  /* a padded batch of <= 8 whose layer input fits in LDS runs the
+                                whole step as one persistent kernel with grid barriers; without
+                                it (the default) every batch runs one kernel per fused op */
 };
 
 typedef struct dec_config {

@@ -16,13 +16,19 @@
 // V row; scores are reduced over the lanes of a row, then the running max m, sum l
 // and output o are updated (base-2 exponentials with log2(e) folded into q).  The
 // waves merge in LDS and the work group writes (m, l, o) for each of its heads.
-// k_attn_combine: o = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j, M = max_j m_j,
-// as bf16; a sequence with no positions (a padded row) gets o = 0.
+// The last work group of a (sequence, kv head) to finish -- counted by a
+// self-resetting arrival counter -- combines the splits:
+// o = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j, M = max_j m_j, as bf16; a
+// sequence with no positions (a padded row) gets o = 0.  Partials go through
+// device-coherent stores and loads, since the work groups of one (sequence, kv
+// head) run on different XCDs, whose L2 caches are not coherent with each other.
 
 #include "common.h"
 #include "kernels.h"
 
 namespace dec {
+
+constexpr int MAX_SPLIT = 64;  // splits per (sequence, kv head); the host keeps n_split within it
 
 template <int DH, bool FP8, int G>
 __global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
@@ -183,31 +189,56 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
       }
     }
     const int64_t row = ((int64_t)b * p.Hq + c * G + h) * p.n_split + split;
-    p.part_o[row * DH + e] = O;
-    if (e == 0) {
-      p.part_ml[row * 2] = M;
-      p.part_ml[row * 2 + 1] = L;
-    }
+    cst(p.part_o + row * DH + e, O);
+    if (e == 0) cst_f2(p.part_ml + row * 2, M, L);
   }
-}
 
-template <int DH>
-__global__ __launch_bounds__(DH) void k_attn_combine(AttnParams p) {
-  const int j = blockIdx.x, b = blockIdx.y, e = threadIdx.x;
-  const int64_t row0 = ((int64_t)b * p.Hq + j) * p.n_split;
-  float M = -INFINITY;
-  for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, p.part_ml[(row0 + s) * 2]);
-  float out = 0.f;
-  if (M != -INFINITY) {
-    float O = 0.f, L = 0.f;
-    for (int s = 0; s < p.n_split; ++s) {
-      const float f = exp2f(p.part_ml[(row0 + s) * 2] - M);
-      O = fmaf(f, p.part_o[(row0 + s) * DH + e], O);
-      L = fmaf(f, p.part_ml[(row0 + s) * 2 + 1], L);
-    }
-    out = O / L;
+  // arrival: the partial stores of every wave complete before this work group counts
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __shared__ int last;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* cnt = p.cnt + (int64_t)b * p.Hkv + c;
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == (unsigned)p.n_split - 1;
+    if (last) cst(cnt, 0u);  // ready for the next launch
   }
-  p.o[((int64_t)b * p.Hq + j) * DH + e] = f32_to_bf16(out);
+  __syncthreads();
+  if (!last) return;
+
+  // combine the n_split partials of the group's G heads
+  __shared__ float cm[G][MAX_SPLIT], cl[G][MAX_SPLIT], cM[G];
+  for (int idx = threadIdx.x; idx < G * p.n_split; idx += NW * WAVE) {
+    const int h = idx / p.n_split, sp = idx % p.n_split;
+    const int64_t row = ((int64_t)b * p.Hq + c * G + h) * p.n_split + sp;
+    const uint64_t ml = cld(reinterpret_cast<const uint64_t*>(p.part_ml + row * 2));
+    cm[h][sp] = __uint_as_float((uint32_t)ml);
+    cl[h][sp] = __uint_as_float((uint32_t)(ml >> 32));
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < p.n_split; ++sp) M = fmaxf(M, cm[threadIdx.x][sp]);
+    cM[threadIdx.x] = M;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * DH; idx += NW * WAVE) {
+    const int h = idx / DH, e = idx % DH;
+    const float M = cM[h];
+    const int64_t row0 = ((int64_t)b * p.Hq + c * G + h) * p.n_split;
+    float out = 0.f;
+    if (M != -INFINITY) {
+      float O = 0.f, L = 0.f;
+#pragma unroll 8
+      for (int sp = 0; sp < p.n_split; ++sp) {
+        const float f = exp2f(cm[h][sp] - M);
+        O = fmaf(f, cld(p.part_o + (row0 + sp) * DH + e), O);
+        L = fmaf(f, cl[h][sp], L);
+      }
+      out = O / L;
+    }
+    p.o[((int64_t)b * p.Hq + c * G + h) * DH + e] = f32_to_bf16(out);
+  }
 }
 
 namespace {
@@ -226,9 +257,6 @@ hipError_t attn_go(const AttnParams& p, hipStream_t s) {
     case 8: hipLaunchKernelGGL((k_attn_split<DH, FP8, 8>), grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_attn_combine<DH>), dim3(p.Hq, p.Bp), dim3(DH), 0, s, p);
   return hipGetLastError();
 }
 }  // namespace

@@ -42,8 +42,8 @@ constexpr int N_BUCKETS = sizeof(LADDER) / sizeof(LADDER[0]);
 constexpr int MAX_SPLIT = 64;
 constexpr int ATTN_TARGET_GROUPS = 1024;  // work groups per attention launch to aim for
 constexpr uint32_t KNOWN_FLAGS =
-    DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL | DEC_FLAG_MULTI_KERNEL;
-constexpr int N_MODES = 8;  // plan-changing flag combinations (UNFUSED, NO_MFMA, MULTI_KERNEL)
+    DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL | DEC_FLAG_PERSISTENT;
+constexpr int N_MODES = 8;  // plan-changing flag combinations (UNFUSED, NO_MFMA, PERSISTENT)
 constexpr int PERSIST_MAX_BATCH = 8;
 constexpr size_t PERSIST_XS_BUDGET = 128 * 1024;  // LDS for one layer input block
 constexpr int PERSIST_ASSUMED_WAVES = 256 * 8;    // sizes the attention split count
@@ -51,7 +51,7 @@ constexpr double BARRIER_TIMEOUT_S = 0.25;
 
 int mode_of(uint32_t flags) {
   return (int)(((flags & DEC_FLAG_UNFUSED) ? 1 : 0) | ((flags & DEC_FLAG_NO_MFMA) ? 2 : 0) |
-               ((flags & DEC_FLAG_MULTI_KERNEL) ? 4 : 0));
+               ((flags & DEC_FLAG_PERSISTENT) ? 4 : 0));
 }
 
 int bucket_index(int n) {
@@ -66,8 +66,9 @@ int blocks_per_seq(const dec_config& c) { return (c.max_seq_len + 15) / 16; }
 
 int n_split_for(const dec_config& c, int Bp) {
   int ns = (ATTN_TARGET_GROUPS + Bp * c.n_kv_heads - 1) / (Bp * c.n_kv_heads);
-  const int bps = blocks_per_seq(c);
-  if (ns > bps) ns = bps;
+  // at least one block per wave of a split (4 waves) at the longest context
+  const int bps = blocks_per_seq(c), by_len = (bps + 3) / 4;
+  if (ns > by_len) ns = by_len;
   if (ns > MAX_SPLIT) ns = MAX_SPLIT;
   return ns < 1 ? 1 : ns;
 }
@@ -332,7 +333,7 @@ hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s) {
 }
 
 bool use_persistent(const dec_ctx* c, int Bp) {
-  return !(c->cfg.flags & (DEC_FLAG_MULTI_KERNEL | DEC_FLAG_UNFUSED)) && persistent_fits(c->cfg, Bp);
+  return (c->cfg.flags & DEC_FLAG_PERSISTENT) && !(c->cfg.flags & DEC_FLAG_UNFUSED) && persistent_fits(c->cfg, Bp);
 }
 
 // The whole step as one persistent kernel (Bp <= 8).
@@ -436,6 +437,7 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
   ap.num_blocks = g.num_blocks;
   ap.bps = bps;
   ap.n_split = n_split_for(g, Bp);
+  ap.cnt = ws_ptr<unsigned>(c, c->L.attn_cnt);
 
   for (int l = 0; l < g.n_layers; ++l) {
     if (l > 0) {
@@ -702,7 +704,7 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   const bool mfma = !persist && !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
   const int slices = (!mfma && Bp > 8) ? Bp / 8 : 1;
   const int L = g.n_layers;
-  c->info.kernels_per_step = persist ? 1 : 2 + (L > 0 ? 8 * L : 0) + (slices - 1) * (4 * L + 1);
+  c->info.kernels_per_step = persist ? 1 : 2 + (L > 0 ? 7 * L : 0) + (slices - 1) * (4 * L + 1);
   c->info.bucket = Bp;
   c->info.attn_splits = persist ? n_split_persistent(g, Bp) : n_split_for(g, Bp);
   c->info.used_mfma = mfma ? 1 : 0;

@@ -66,10 +66,12 @@ struct AttnParams {
   float* part_o;          // [Bp][Hq][n_split][dh]
   float* part_ml;         // [Bp][Hq][n_split][2]
   uint16_t* o;            // [Bp][Hq * dh] bf16 out
+  unsigned* cnt;          // [Bp][Hkv] split arrival counters, zero between launches
   int Bp, Hq, Hkv, dh, num_blocks, bps, n_split;
 };
 
-// split-K paged GQA decode attention + log-sum-exp combine (2 kernels)
+// split-K paged GQA decode attention; the last split of each (sequence, kv head)
+// combines (one kernel)
 hipError_t launch_attention(const AttnParams& p, bool kv_fp8, hipStream_t s);
 
 // ---------------------------------------------------------------- persistent step (Bp <= 8)

@@ -9,53 +9,86 @@
 
 namespace dec {
 
-// one work group of 256 threads per batch row
-template <bool EMBED, bool FP8>
+// One work group of 256 threads per batch row.  Each thread keeps its NV float4 of the
+// row in registers, so the row is read once and the kernel costs one load round trip
+// plus a block reduction (NV * 1024 >= d; NV = 0 selects a two-pass loop for wider rows).
+template <bool EMBED, bool FP8, int NV>
 __global__ __launch_bounds__(256) void k_norm(NormParams p) {
   __shared__ float red[4];
-  const int b = blockIdx.x;
-  const int d = p.d;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int d = p.d;  // a multiple of 16
   const float* hrow = p.h + (int64_t)b * d;
   float* hout = p.h_out ? p.h_out + (int64_t)b * d : nullptr;
-  float ss = 0.f;
-  float e_scale = 1.f;
+  uint16_t* xrow = p.x + (int64_t)b * d;
   const int64_t id = EMBED ? (int64_t)p.ids[b] : 0;
-  if (EMBED && FP8) e_scale = p.E_scale[id];
-  // pass 1: (gather) and sum of squares; each thread covers elements tid, tid + 256, ...
-  for (int i = threadIdx.x; i < d; i += 256) {
-    float v;
-    if (EMBED) {
-      if (FP8) {
-        const uint8_t c = static_cast<const uint8_t*>(p.E)[id * d + i];
-        v = e4m3x2_to_f32x2<false>((uint32_t)c).x * e_scale;
-      } else {
-        v = bf16_to_f32(static_cast<const uint16_t*>(p.E)[id * d + i]);
-      }
-      hout[i] = v;
+  const float e_scale = (EMBED && FP8) ? p.E_scale[id] : 1.f;
+  // 4 consecutive elements of the row starting at i (embedding rows are dequantized)
+  auto load4 = [&](int i) -> f32x4 {
+    if (!EMBED) return *reinterpret_cast<const f32x4*>(hrow + i);
+    f32x4 v;
+    if (FP8) {
+      const uint32_t c = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.E) + id * d + i);
+      const f32x2 lo = e4m3x2_to_f32x2<false>(c), hi = e4m3x2_to_f32x2<true>(c);
+      v = f32x4{lo.x * e_scale, lo.y * e_scale, hi.x * e_scale, hi.y * e_scale};
     } else {
-      v = hrow[i];
+      const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.E) + id * d + i);
+      v = f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
     }
-    ss += v * v;
+    *reinterpret_cast<f32x4*>(hout + i) = v;
+    return v;
+  };
+  auto store4 = [&](int i, f32x4 v, float r) {
+    const f32x4 g = *reinterpret_cast<const f32x4*>(p.gain + i);
+    const uint32_t lo = (uint32_t)f32_to_bf16(v.x * r * g.x) | ((uint32_t)f32_to_bf16(v.y * r * g.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(v.z * r * g.z) | ((uint32_t)f32_to_bf16(v.w * r * g.w) << 16);
+    *reinterpret_cast<u32x2*>(xrow + i) = u32x2{lo, hi};
+  };
+  float ss = 0.f;
+  if (NV > 0) {
+    f32x4 v[NV > 0 ? NV : 1];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i = (j * 256 + tid) * 4;
+      v[j] = i < d ? load4(i) : f32x4{0.f, 0.f, 0.f, 0.f};
+      ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    }
+    ss = block256_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)d + p.eps);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i = (j * 256 + tid) * 4;
+      if (i < d) store4(i, v[j], r);
+    }
+  } else {
+    for (int i = tid * 4; i < d; i += 1024) {
+      const f32x4 v = load4(i);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = block256_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)d + p.eps);
+    const float* src = EMBED ? hout : hrow;  // this thread's own values, re-read
+    for (int i = tid * 4; i < d; i += 1024) store4(i, *reinterpret_cast<const f32x4*>(src + i), r);
   }
-  ss = block256_sum(ss, red);
-  const float r = 1.0f / sqrtf(ss / (float)d + p.eps);
-  // pass 2: normalize (re-reading our own values)
-  const float* src = EMBED ? hout : hrow;
-  for (int i = threadIdx.x; i < d; i += 256) p.x[(int64_t)b * d + i] = f32_to_bf16(src[i] * r * p.gain[i]);
 }
+
+namespace {
+template <bool EMBED, bool FP8>
+hipError_t norm_go(const NormParams& p, hipStream_t s) {
+  const int nv = (p.d + 1023) / 1024;
+  if (nv <= 1) hipLaunchKernelGGL((k_norm<EMBED, FP8, 1>), dim3(p.Bp), dim3(256), 0, s, p);
+  else if (nv <= 2) hipLaunchKernelGGL((k_norm<EMBED, FP8, 2>), dim3(p.Bp), dim3(256), 0, s, p);
+  else if (nv <= 4) hipLaunchKernelGGL((k_norm<EMBED, FP8, 4>), dim3(p.Bp), dim3(256), 0, s, p);
+  else if (nv <= 8) hipLaunchKernelGGL((k_norm<EMBED, FP8, 8>), dim3(p.Bp), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((k_norm<EMBED, FP8, 0>), dim3(p.Bp), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+}  // namespace
 
 hipError_t launch_embed_norm(const NormParams& p, bool w_fp8, hipStream_t s) {
-  if (w_fp8)
-    hipLaunchKernelGGL((k_norm<true, true>), dim3(p.Bp), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((k_norm<true, false>), dim3(p.Bp), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return w_fp8 ? norm_go<true, true>(p, s) : norm_go<true, false>(p, s);
 }
 
-hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((k_norm<false, false>), dim3(p.Bp), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
+hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s) { return norm_go<false, false>(p, s); }
 
 // RoPE angles phi = p * theta^(-2i/dh) (RoFormer, adjacent pairs), in double precision
 __global__ void k_rope_table(float2* rope, int max_seq, int half, double theta) {

@@ -33,7 +33,10 @@ namespace dec {
 
 constexpr int PW = 8;           // waves per work group
 constexpr int PT = PW * WAVE;   // threads per work group
-constexpr int PU = 8;           // 16-byte vectors per row per lane per chunk
+#ifndef DEC_PU
+#define DEC_PU 8
+#endif
+constexpr int PU = DEC_PU;      // 16-byte vectors per row per lane per chunk
 constexpr int MAX_ROUNDS = 8;   // items per wave when a phase splits K over waves
 
 // the wave's index in its work group, as a wave-uniform (scalar) value
@@ -91,6 +94,7 @@ __device__ __forceinline__ void wait_stores(int n_loads) {
   // s_waitcnt immediates: vmcnt = n (bits 3:0 and 15:14), expcnt and lgkmcnt left open
   if (n_loads >= 32) __builtin_amdgcn_s_waitcnt(0x8F70);        // vmcnt(32)
   else if (n_loads >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
+  else if (n_loads >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
   else __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
 }
 
@@ -190,7 +194,7 @@ struct Chunk {
 };
 
 // loads issued by unit_load(k, 0) and unit_load(k, 1)
-static_assert(PU == 8, "wait_stores encodes counts of 16 and 32 prefetch loads");
+static_assert(PU == 8 || PU == 4, "wait_stores encodes counts of 8, 16 and 32 prefetch loads");
 __device__ __forceinline__ int prefetch_loads(const PWork& k) {
   return (k.n > 0 ? 2 * PU : 0) + (k.n > 1 ? 2 * PU : 0);
 }

@@ -113,34 +113,34 @@ def _one_step(dec, case, ids, lens, flags, max_batch=None):
     return z, pool, info
 
 
-@pytest.mark.parametrize("B,multi", [(5, False), (5, True), (24, False)])
-def test_graph_replay_equals_eager_bitwise(dec, B, multi):
+@pytest.mark.parametrize("B,persist", [(5, False), (5, True), (24, False)])
+def test_graph_replay_equals_eager_bitwise(dec, B, persist):
     cfg = fmt(MINI, "bf16", "bf16")
     rng = np.random.default_rng(20)
     case = make_case(cfg, ctx_mix(B, rng), 128, seed=5)
     ids = synth.make_token_ids(cfg, 1, B, seed=5)[0]
-    base = dec.FLAG_MULTI_KERNEL if multi else 0
+    base = dec.FLAG_PERSISTENT if persist else 0
     ze, pe, ie = _one_step(dec, case, ids, case.ctx_lens, base | dec.FLAG_EAGER)
     zg, pg, ig = _one_step(dec, case, ids, case.ctx_lens, base)
     assert ie.used_graph == 0 and ig.used_graph == 1
     assert torch.equal(ze.view(torch.int32), zg.view(torch.int32))
     assert torch.equal(pe.view(torch.uint8), pg.view(torch.uint8))
-    persistent = B <= 8 and not multi
+    persistent = B <= 8 and persist
     assert ie.persistent == ig.persistent == int(persistent)
-    expect = 1 if persistent else 8 * cfg.n_layers + 2
+    expect = 1 if persistent else 7 * cfg.n_layers + 2
     assert ie.kernels_per_step == ig.kernels_per_step == expect
 
 
 @pytest.mark.parametrize("w,kv", [("bf16", "bf16"), ("fp8", "fp8")])
 @pytest.mark.parametrize("B", [1, 3, 8])
-def test_mini_model_multi_kernel_plan(dec, w, kv, B):
-    """The per-op kernel plan at small batches (the persistent step is the default there)."""
+def test_mini_model_persistent_plan(dec, w, kv, B):
+    """The persistent one-kernel step at small batches (opt-in)."""
     cfg = fmt(MINI, w, kv)
     rng = np.random.default_rng(50 + B)
     case = make_case(cfg, ctx_mix(B, rng), 128, seed=12, gains="random")
     ids = synth.make_token_ids(cfg, 3, B, seed=12)
-    log(f"mini multi-kernel {w}/{kv} B={B}")
-    assert_ok(run_parity(case, ids, flags=dec.FLAG_MULTI_KERNEL), cfg)
+    log(f"mini persistent {w}/{kv} B={B}")
+    assert_ok(run_parity(case, ids, flags=dec.FLAG_PERSISTENT), cfg)
 
 
 @pytest.mark.parametrize("B", [1, 2, 4, 8])
@@ -150,8 +150,8 @@ def test_persistent_step_matches_multi_kernel(dec, B):
     rng = np.random.default_rng(60 + B)
     case = make_case(cfg, ctx_mix(B, rng), 128, seed=13, gains="random")
     ids = synth.make_token_ids(cfg, 1, B, seed=13)[0]
-    zp, pp, ip = _one_step(dec, case, ids, case.ctx_lens, 0)
-    zm, pm, im = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_MULTI_KERNEL)
+    zp, pp, ip = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_PERSISTENT)
+    zm, pm, im = _one_step(dec, case, ids, case.ctx_lens, 0)
     assert ip.persistent == 1 and im.persistent == 0
     a, b = zp.double().cpu().numpy(), zm.double().cpu().numpy()
     R = a.max(axis=1) - a.min(axis=1)
@@ -259,12 +259,12 @@ def test_large_workload_widths(dec, name, layers, B):
 
 
 @pytest.mark.parametrize("name,B", [("8B", 1), ("70B", 1)])
-def test_large_workload_widths_multi_kernel(dec, name, B):
-    """The per-op plan at the same widths (the benchmark reports both plans)."""
+def test_large_workload_widths_persistent(dec, name, B):
+    """The persistent step at the same widths (the benchmark reports both plans)."""
     wl = synth.WORKLOADS[name]
     cfg = wl.model.with_layers(1)
     lens = synth.make_context_lengths(wl, B, seed=0)
     case = make_case(cfg, lens, wl.max_seq_len, seed=0)
     ids = synth.make_token_ids(cfg, 2, B, seed=0)
-    assert_ok(run_parity(case, ids, flags=dec.FLAG_MULTI_KERNEL, stream_weights=True,
+    assert_ok(run_parity(case, ids, flags=dec.FLAG_PERSISTENT, stream_weights=True,
                          kv_every_step=False), cfg)
