@@ -28,14 +28,8 @@ namespace dec {
 
 // ---------------------------------------------------------------- gemv (Bp <= 8)
 
-template <int BT>
-struct GemvUnroll {
-  static constexpr int U = BT == 1 ? 16 : BT == 2 ? 8 : 4;
-};
-
-template <int BT, bool FP8, int EPI, bool KVFP8>
+template <int BT, bool FP8, int EPI, bool KVFP8, int U>
 __global__ __launch_bounds__(64) void k_gemv(MatmulParams p, int n_items) {
-  constexpr int U = GemvUnroll<BT>::U;
   constexpr int EPV = FP8 ? 16 : 8;  // weight elements per 16-byte vector
   const int lane = threadIdx.x;
   const int i0 = (int)((int64_t)n_items * blockIdx.x / gridDim.x);
@@ -240,14 +234,22 @@ __global__ __launch_bounds__(WAVE * MFMA_WAVES) void k_gemm_mfma(MatmulParams p)
 
 namespace {
 
-constexpr int GEMV_MAX_WAVES = 256 * 8;  // 8 waves per CU on 256 CUs
-
+// One row pair per work group: more work groups than the CUs hold at once, so the
+// hardware dispatcher hands out the rest as work groups retire and no CU is left with
+// a long static share at the end.  U (16-byte loads per row per lane in flight) covers
+// a whole row for K <= 64 U vectors, fewer loop trips beyond.
 template <int BT, bool FP8, int EPI, bool KVFP8>
 hipError_t gemv_go(const MatmulParams& p, hipStream_t s) {
   const int n_items = EPI == EPI_SILU ? p.d_ff : p.N / 2;
-  const int grid = n_items < GEMV_MAX_WAVES ? n_items : GEMV_MAX_WAVES;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8>), dim3(grid), dim3(WAVE), 0, s, p, n_items);
+  if (n_items <= 0) return hipSuccess;
+  const int kv = p.K / (FP8 ? 16 : 8);
+  const dim3 grid(n_items), block(WAVE);
+  if (kv <= 64 * 4)
+    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, 4>), grid, block, 0, s, p, n_items);
+  else if (kv <= 64 * 8 || BT > 2)
+    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, 8>), grid, block, 0, s, p, n_items);
+  else
+    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, 16>), grid, block, 0, s, p, n_items);
   return hipGetLastError();
 }
 
