@@ -28,62 +28,87 @@ namespace dec {
 
 // ---------------------------------------------------------------- gemv (Bp <= 8)
 
-template <int BT, bool FP8, int EPI, bool KVFP8, int U>
-__global__ __launch_bounds__(64) void k_gemv(MatmulParams p, int n_items) {
+// Work group = one row pair (item blockIdx.x), S waves; wave w takes the contiguous
+// slice [KV w / S, KV (w + 1) / S) of the 16-byte vectors of both rows, with U loads
+// per row per lane in flight; the slices' sums are added in LDS in wave order.
+template <int BT, bool FP8, int EPI, bool KVFP8, int U, int S>
+__global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
   constexpr int EPV = FP8 ? 16 : 8;  // weight elements per 16-byte vector
-  const int lane = threadIdx.x;
-  const int i0 = (int)((int64_t)n_items * blockIdx.x / gridDim.x);
-  const int i1 = (int)((int64_t)n_items * (blockIdx.x + 1) / gridDim.x);
+  const int lane = threadIdx.x % WAVE;
+  const int w = S == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const int it = blockIdx.x;
   const int KV = p.K / EPV;  // 16-byte vectors per weight row (K % EPV == 0)
+  const int kb = (int)((int64_t)KV * w / S), ke = (int)((int64_t)KV * (w + 1) / S);
   const u32x4* W = static_cast<const u32x4*>(p.W);
-
-  for (int it = i0; it < i1; ++it) {
-    int r0, r1;
-    item_rows<EPI>(p, it, r0, r1);
-    const u32x4* w0p = W + (int64_t)r0 * KV;
-    const u32x4* w1p = W + (int64_t)r1 * KV;
-    float acc0[BT], acc1[BT];
+  int r0, r1;
+  item_rows<EPI>(p, it, r0, r1);
+  const u32x4* w0p = W + (int64_t)r0 * KV;
+  const u32x4* w1p = W + (int64_t)r1 * KV;
+  float acc0[BT], acc1[BT];
 #pragma unroll
-    for (int b = 0; b < BT; ++b) acc0[b] = acc1[b] = 0.0f;
+  for (int b = 0; b < BT; ++b) acc0[b] = acc1[b] = 0.0f;
 
-    for (int kb = lane; kb < KV; kb += WAVE * U) {
-      u32x4 w0[U], w1[U];
+  for (int k0 = kb + lane; k0 < ke; k0 += WAVE * U) {
+    u32x4 w0[U], w1[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = kb + WAVE * u;
-        if (kk < KV) {
-          w0[u] = ld_stream(w0p + kk);
-          w1[u] = ld_stream(w1p + kk);
-        }
+    for (int u = 0; u < U; ++u) {
+      const int kk = k0 + WAVE * u;
+      if (kk < ke) {
+        w0[u] = ld_stream(w0p + kk);
+        w1[u] = ld_stream(w1p + kk);
       }
+    }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = kb + WAVE * u;
-        if (kk < KV) {
+    for (int u = 0; u < U; ++u) {
+      const int kk = k0 + WAVE * u;
+      if (kk < ke) {
 #pragma unroll
-          for (int b = 0; b < BT; ++b) {
-            const uint16_t* xb = p.x + (int64_t)b * p.ldx + (int64_t)kk * EPV;
-            if (FP8) {
-              const u32x4 xa = ld16(xb), xc = ld16(xb + 8);
-              acc0[b] = dot16_e4m3(w0[u], xa, xc, acc0[b]);
-              acc1[b] = dot16_e4m3(w1[u], xa, xc, acc1[b]);
-            } else {
-              const u32x4 xa = ld16(xb);
-              acc0[b] = dot8_bf16(w0[u], xa, acc0[b]);
-              acc1[b] = dot8_bf16(w1[u], xa, acc1[b]);
-            }
+        for (int b = 0; b < BT; ++b) {
+          const uint16_t* xb = p.x + (int64_t)b * p.ldx + (int64_t)kk * EPV;
+          if (FP8) {
+            const u32x4 xa = gld16(xb), xc = gld16(xb + 8);
+            acc0[b] = dot16_e4m3(w0[u], xa, xc, acc0[b]);
+            acc1[b] = dot16_e4m3(w1[u], xa, xc, acc1[b]);
+          } else {
+            const u32x4 xa = gld16(xb);
+            acc0[b] = dot8_bf16(w0[u], xa, acc0[b]);
+            acc1[b] = dot8_bf16(w1[u], xa, acc1[b]);
           }
         }
       }
     }
+  }
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      acc0[b] = wave_sum(acc0[b]);
-      acc1[b] = wave_sum(acc1[b]);
-    }
+  for (int b = 0; b < BT; ++b) {
+    acc0[b] = wave_sum(acc0[b]);
+    acc1[b] = wave_sum(acc1[b]);
+  }
+  if (S == 1) {
     if (lane == 0) {
 #pragma unroll
       for (int b = 0; b < BT; ++b) pair_epilogue<EPI>(p, KVFP8, b, it, r0, r1, acc0[b], acc1[b]);
+    }
+  } else {
+    __shared__ float red[S][2][BT];
+    if (lane == 0) {
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        red[w][0][b] = acc0[b];
+        red[w][1][b] = acc1[b];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < S; ++ww) {
+          s0 += red[ww][0][b];
+          s1 += red[ww][1][b];
+        }
+        pair_epilogue<EPI>(p, KVFP8, b, it, r0, r1, s0, s1);
+      }
     }
   }
 }
@@ -236,21 +261,31 @@ namespace {
 
 // One row pair per work group: more work groups than the CUs hold at once, so the
 // hardware dispatcher hands out the rest as work groups retire and no CU is left with
-// a long static share at the end.  U (16-byte loads per row per lane in flight) covers
-// a whole row for K <= 64 U vectors, fewer loop trips beyond.
+// a long static share at the end.  Rows longer than one pass of a wave (64 U vectors)
+// are split over S waves of the work group, so that every wave issues all of its loads
+// at once.
+template <int BT, bool FP8, int EPI, bool KVFP8, int U>
+hipError_t gemv_s(const MatmulParams& p, int n_items, int kv, hipStream_t s) {
+  const int need = (kv + WAVE * U - 1) / (WAVE * U);
+  const dim3 grid(n_items);
+  if (need <= 1)
+    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, U, 1>), grid, dim3(WAVE), 0, s, p);
+  else if (need <= 2)
+    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, U, 2>), grid, dim3(2 * WAVE), 0, s, p);
+  else if (need <= 4)
+    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, U, 4>), grid, dim3(4 * WAVE), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, U, 8>), grid, dim3(8 * WAVE), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int BT, bool FP8, int EPI, bool KVFP8>
 hipError_t gemv_go(const MatmulParams& p, hipStream_t s) {
   const int n_items = EPI == EPI_SILU ? p.d_ff : p.N / 2;
   if (n_items <= 0) return hipSuccess;
   const int kv = p.K / (FP8 ? 16 : 8);
-  const dim3 grid(n_items), block(WAVE);
-  if (kv <= 64 * 4)
-    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, 4>), grid, block, 0, s, p, n_items);
-  else if (kv <= 64 * 8 || BT > 2)
-    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, 8>), grid, block, 0, s, p, n_items);
-  else
-    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, 16>), grid, block, 0, s, p, n_items);
-  return hipGetLastError();
+  if (kv <= WAVE * 4) return gemv_s<BT, FP8, EPI, KVFP8, 4>(p, n_items, kv, s);
+  return gemv_s<BT, FP8, EPI, KVFP8, 8>(p, n_items, kv, s);
 }
 
 template <int NT, bool FP8, int EPI, bool KVFP8>
