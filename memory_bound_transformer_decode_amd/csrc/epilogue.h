@@ -67,6 +67,88 @@ __device__ __forceinline__ void pair_epilogue(const MatmulParams& p, bool kv_fp8
   }
 }
 
+// The per-op kernels fetch what their epilogue reads (scales, the residual rows, the
+// token's position, RoPE angles and cache block) when they start, so that these loads
+// overlap the weight stream instead of following it.
+template <int EPI, int BT>
+struct EpiInputs {
+  float s0, s1;
+  float h0[EPI == EPI_RESID ? BT : 1], h1[EPI == EPI_RESID ? BT : 1];
+  int pos[EPI == EPI_QKV ? BT : 1], blk[EPI == EPI_QKV ? BT : 1];
+  f32x2 cs[EPI == EPI_QKV ? BT : 1];
+};
+
+template <int EPI, int BT>
+__device__ __forceinline__ void epi_fetch(const MatmulParams& p, int r0, int r1, EpiInputs<EPI, BT>& in) {
+  in.s0 = p.scale ? gld(p.scale + r0) : 1.0f;
+  in.s1 = p.scale ? gld(p.scale + r1) : 1.0f;
+  if (EPI == EPI_RESID) {
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      const float* o = p.out + (int64_t)b * p.ldo;
+      in.h0[b] = gld(o + r0);
+      in.h1[b] = gld(o + r1);
+    }
+  }
+  if (EPI == EPI_QKV) {
+    const int qrows = p.Hq * p.dh, krows = p.Hkv * p.dh;
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      in.pos[b] = gld(p.seq_lens + b);
+      const int pr = in.pos[b] < 0 ? 0 : in.pos[b];
+      in.cs[b] = r0 < qrows + krows
+                     ? gld(reinterpret_cast<const f32x2*>(p.rope + (int64_t)pr * (p.dh / 2) + ((r0 % p.dh) >> 1)))
+                     : f32x2{1.f, 0.f};
+      in.blk[b] = r0 >= qrows && in.pos[b] >= 0 ? gld(p.bt + (int64_t)b * p.bps + in.pos[b] / KV_BLOCK) : 0;
+    }
+  }
+}
+
+// pair_epilogue with the inputs fetched by epi_fetch (per-op kernels only: plain stores)
+template <int EPI, int BT>
+__device__ __forceinline__ void pair_epilogue_pre(const MatmulParams& p, bool kv_fp8, const EpiInputs<EPI, BT>& in,
+                                                  int b, int item, int r0, int r1, float a0, float a1) {
+  float y0 = a0 * in.s0, y1 = a1 * in.s1;
+  if (EPI == EPI_LOGITS) {
+    float* o = p.out + (int64_t)b * p.ldo;
+    gst(o + r0, y0);
+    gst(o + r1, y1);
+  } else if (EPI == EPI_RESID) {
+    float* o = p.out + (int64_t)b * p.ldo;
+    gst(o + r0, in.h0[b] + y0);
+    gst(o + r1, in.h1[b] + y1);
+  } else if (EPI == EPI_SILU) {
+    gst(p.act + (int64_t)b * p.ldact + item, f32_to_bf16(silu_f(y0) * y1));
+  } else {
+    const int dh = p.dh, qrows = p.Hq * dh, krows = p.Hkv * dh;
+    if (r0 < qrows + krows) {  // q or k: rotate the adjacent pair (r0 even)
+      const f32x2 cs = in.cs[b];
+      const float z0 = y0 * cs.x - y1 * cs.y;
+      const float z1 = y0 * cs.y + y1 * cs.x;
+      y0 = z0;
+      y1 = z1;
+    }
+    if (r0 < qrows) {
+      const int j = r0 / dh, e = r0 % dh;
+      gst(reinterpret_cast<f32x2*>(p.q + ((int64_t)b * p.Hq + j) * dh + e), f32x2{y0, y1});
+      return;
+    }
+    const int pos = in.pos[b];
+    if (pos < 0) return;  // padded row: no cache write
+    const int kv = r0 < qrows + krows ? 0 : 1;
+    const int rr = r0 - qrows - kv * krows;
+    const int c = rr / dh, e = rr % dh;
+    const int64_t off = kv_offset(p.layer, kv, in.blk[b], c, pos % KV_BLOCK, e, p.num_blocks, p.Hkv, dh);
+    if (kv_fp8) {
+      const uint32_t c0 = f32_to_e4m3(y0), c1 = f32_to_e4m3(y1);
+      gst(reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.pool) + off), (uint16_t)(c0 | (c1 << 8)));
+    } else {
+      const uint32_t w = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+      gst(reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.pool) + off), w);
+    }
+  }
+}
+
 template <int EPI>
 __device__ __forceinline__ void item_rows(const MatmulParams& p, int item, int& r0, int& r1) {
   if (EPI == EPI_SILU) {

@@ -44,6 +44,8 @@ __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
   item_rows<EPI>(p, it, r0, r1);
   const u32x4* w0p = W + (int64_t)r0 * KV;
   const u32x4* w1p = W + (int64_t)r1 * KV;
+  EpiInputs<EPI, BT> ein;
+  if (threadIdx.x == 0) epi_fetch<EPI, BT>(p, r0, r1, ein);
   float acc0[BT], acc1[BT];
 #pragma unroll
   for (int b = 0; b < BT; ++b) acc0[b] = acc1[b] = 0.0f;
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
   if (S == 1) {
     if (lane == 0) {
 #pragma unroll
-      for (int b = 0; b < BT; ++b) pair_epilogue<EPI>(p, KVFP8, b, it, r0, r1, acc0[b], acc1[b]);
+      for (int b = 0; b < BT; ++b) pair_epilogue_pre<EPI, BT>(p, KVFP8, ein, b, it, r0, r1, acc0[b], acc1[b]);
     }
   } else {
     __shared__ float red[S][2][BT];
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
           s0 += red[ww][0][b];
           s1 += red[ww][1][b];
         }
-        pair_epilogue<EPI>(p, KVFP8, b, it, r0, r1, s0, s1);
+        pair_epilogue_pre<EPI, BT>(p, KVFP8, ein, b, it, r0, r1, s0, s1);
       }
     }
   }
