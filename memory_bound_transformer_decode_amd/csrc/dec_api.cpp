@@ -324,13 +324,23 @@ dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) 
   return p;
 }
 
-hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s) {
+// norm_gain: when set, the kernel computes x = RMSNorm(h) norm_gain itself (fused_norm)
+hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const float* norm_gain = nullptr) {
   const dec_config& g = c->cfg;
   int epi = 0;
-  const dec::MatmulParams p = matmul_params(c, which, l, Bp, &epi);
+  dec::MatmulParams p = matmul_params(c, which, l, Bp, &epi);
+  if (norm_gain) {
+    p.nh = ws_ptr<float>(c, c->L.h);
+    p.ng = norm_gain;
+    p.eps = g.rms_eps;
+  }
   const bool mfma = !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
   return dec::launch_matmul(p, epi, g.weight_dtype == DEC_FP8_E4M3, g.kv_dtype == DEC_FP8_E4M3, mfma, s);
 }
+
+// Batches of <= 8 rows run matrix-vector kernels that normalize their own input in
+// LDS ([Bp][d] bf16 must fit in 128 KB)
+bool fused_norm(const dec_config& g, int Bp) { return Bp <= 8 && (size_t)Bp * g.d_model * 2 <= 128 * 1024; }
 
 bool use_persistent(const dec_ctx* c, int Bp) {
   return (c->cfg.flags & DEC_FLAG_PERSISTENT) && !(c->cfg.flags & DEC_FLAG_UNFUSED) && persistent_fits(c->cfg, Bp);
@@ -439,27 +449,33 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
   ap.n_split = n_split_for(g, Bp);
   ap.cnt = ws_ptr<unsigned>(c, c->L.attn_cnt);
 
+  // the matrix-vector kernels normalize their own input (no RMSNorm kernels)
+  const bool fn = fused_norm(g, Bp);
   for (int l = 0; l < g.n_layers; ++l) {
-    if (l > 0) {
-      np.gain = c->attn_norm + (size_t)l * d;
+    const float* an = c->attn_norm + (size_t)l * d;
+    if (l > 0 && !fn) {
+      np.gain = an;
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
-    if ((e = run_matmul(c, DEC_MAT_QKV, l, Bp, s)) != hipSuccess) return e;
+    if ((e = run_matmul(c, DEC_MAT_QKV, l, Bp, s, fn ? an : nullptr)) != hipSuccess) return e;
     // attention over positions 0..p
     ap.layer = l;
     if ((e = dec::launch_attention(ap, kvfp8, s)) != hipSuccess) return e;
     if ((e = run_matmul(c, DEC_MAT_O, l, Bp, s)) != hipSuccess) return e;
     // x = RMSNorm(h) g_mlp
-    np.gain = c->mlp_norm + (size_t)l * d;
-    if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
-    if ((e = run_matmul(c, DEC_MAT_GATE_UP, l, Bp, s)) != hipSuccess) return e;
+    const float* mn = c->mlp_norm + (size_t)l * d;
+    if (!fn) {
+      np.gain = mn;
+      if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
+    }
+    if ((e = run_matmul(c, DEC_MAT_GATE_UP, l, Bp, s, fn ? mn : nullptr)) != hipSuccess) return e;
     if ((e = run_matmul(c, DEC_MAT_DOWN, l, Bp, s)) != hipSuccess) return e;
   }
-  if (g.n_layers > 0) {
+  if (g.n_layers > 0 && !fn) {
     np.gain = c->final_norm;
     if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
   }
-  if ((e = run_matmul(c, DEC_MAT_LM_HEAD, 0, Bp, s)) != hipSuccess) return e;
+  if ((e = run_matmul(c, DEC_MAT_LM_HEAD, 0, Bp, s, fn ? c->final_norm : nullptr)) != hipSuccess) return e;
   return hipSuccess;
 }
 
@@ -704,7 +720,8 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   const bool mfma = !persist && !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
   const int slices = (!mfma && Bp > 8) ? Bp / 8 : 1;
   const int L = g.n_layers;
-  c->info.kernels_per_step = persist ? 1 : 2 + (L > 0 ? 7 * L : 0) + (slices - 1) * (4 * L + 1);
+  const int per_layer = fused_norm(g, Bp) ? 5 : 7;  // without fusion: two RMSNorm kernels
+  c->info.kernels_per_step = persist ? 1 : 2 + per_layer * L + (slices - 1) * (4 * L + 1);
   c->info.bucket = Bp;
   c->info.attn_splits = persist ? n_split_persistent(g, Bp) : n_split_for(g, Bp);
   c->info.used_mfma = mfma ? 1 : 0;

@@ -34,6 +34,11 @@ struct MatmulParams {
   const int32_t* bt;        // [Bp][bps]
   const float2* rope;       // [max_seq_len][dh / 2] (cos, sin)
   int Hq, Hkv, dh, num_blocks, bps;
+  // RMSNorm fused into the matrix kernel (Bp <= 8, matrix-vector path): when nh is set,
+  // x = bf16(RMSNorm(nh) ng) is computed by each work group into LDS and p.x is unused
+  const float* nh;        // [Bp][K] fp32 residual stream
+  const float* ng;        // [K] gain
+  float eps;
 };
 
 // y = matrix x for one of the epilogues; gemv kernels for Bp <= 8, MFMA tiles for

@@ -115,6 +115,125 @@ __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
   }
 }
 
+// The same products with the activations x = bf16(h g / sqrt(mean(h^2) + eps)) computed
+// by the work group itself from the fp32 residual stream h into LDS, so that the
+// RMSNorm of the layer input costs no kernel of its own (h is a few KB per row and
+// L2-resident; the kernel-fusion study's section 8 on intermediates round-tripping
+// through HBM).  IPW waves per work group, one row pair per wave.  The first pass's
+// weight loads are issued before the norm, so the norm runs under the weight stream.
+template <int BT, bool FP8, int EPI, bool KVFP8, int U, int IPW>
+__global__ __launch_bounds__(WAVE * IPW) void k_gemv_norm(MatmulParams p, int n_items) {
+  extern __shared__ __align__(16) uint8_t gemv_smem[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(gemv_smem);  // [BT][K] bf16
+  __shared__ float red[IPW][BT];
+  constexpr int EPV = FP8 ? 16 : 8;
+  constexpr int NT = WAVE * IPW;
+  const int tid = threadIdx.x, lane = tid % WAVE;
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int K = p.K, KV = K / EPV;
+  const int it = blockIdx.x * IPW + w;
+  const bool have = it < n_items;
+  int r0, r1;
+  item_rows<EPI>(p, have ? it : n_items - 1, r0, r1);  // a wave without an item loads a valid row
+  const u32x4* W = static_cast<const u32x4*>(p.W);
+  const u32x4* w0p = W + (int64_t)r0 * KV;
+  const u32x4* w1p = W + (int64_t)r1 * KV;
+
+  // sum of squares of this thread's elements of each row (issued first: L2 hits that
+  // complete ahead of the weight loads)
+  float ss[BT];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) ss[b] = 0.f;
+  for (int i = tid * 4; i < K; i += NT * 4) {
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      const f32x4 v = gld(reinterpret_cast<const f32x4*>(p.nh + (int64_t)b * K + i));
+      ss[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+  }
+  EpiInputs<EPI, BT> ein;
+  if (lane == 0) epi_fetch<EPI, BT>(p, r0, r1, ein);
+
+  u32x4 w0[U], w1[U];
+  auto load_pass = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k0 + WAVE * u;
+      if (kk < KV) {
+        w0[u] = ld_stream(w0p + kk);
+        w1[u] = ld_stream(w1p + kk);
+      }
+    }
+  };
+  float acc0[BT], acc1[BT];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) acc0[b] = acc1[b] = 0.0f;
+  auto compute_pass = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k0 + WAVE * u;
+      if (kk < KV) {
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          const uint16_t* xb = xs + b * K + kk * EPV;
+          if (FP8) {
+            const u32x4 xa = *reinterpret_cast<const u32x4*>(xb), xc = *reinterpret_cast<const u32x4*>(xb + 8);
+            acc0[b] = dot16_e4m3(w0[u], xa, xc, acc0[b]);
+            acc1[b] = dot16_e4m3(w1[u], xa, xc, acc1[b]);
+          } else {
+            const u32x4 xa = *reinterpret_cast<const u32x4*>(xb);
+            acc0[b] = dot8_bf16(w0[u], xa, acc0[b]);
+            acc1[b] = dot8_bf16(w1[u], xa, acc1[b]);
+          }
+        }
+      }
+    }
+  };
+  load_pass(lane);
+
+  // the norm: reduce the sums over the work group, then write x into LDS
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    const float t = wave_sum(ss[b]);
+    if (lane == 0) red[w][b] = t;
+  }
+  __syncthreads();
+  float r[BT];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    float t = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < IPW; ++ww) t += red[ww][b];
+    r[b] = 1.0f / sqrtf(t / (float)K + p.eps);
+  }
+  for (int i = tid * 4; i < K; i += NT * 4) {
+    const f32x4 g = gld(reinterpret_cast<const f32x4*>(p.ng + i));
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      const f32x4 v = gld(reinterpret_cast<const f32x4*>(p.nh + (int64_t)b * K + i));
+      const uint32_t lo = (uint32_t)f32_to_bf16(v.x * r[b] * g.x) | ((uint32_t)f32_to_bf16(v.y * r[b] * g.y) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(v.z * r[b] * g.z) | ((uint32_t)f32_to_bf16(v.w * r[b] * g.w) << 16);
+      *reinterpret_cast<u32x2*>(xs + b * K + i) = u32x2{lo, hi};
+    }
+  }
+  __syncthreads();
+
+  compute_pass(lane);
+  for (int k0 = lane + WAVE * U; k0 < KV; k0 += WAVE * U) {
+    load_pass(k0);
+    compute_pass(k0);
+  }
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    acc0[b] = wave_sum(acc0[b]);
+    acc1[b] = wave_sum(acc1[b]);
+  }
+  if (lane == 0 && have) {
+#pragma unroll
+    for (int b = 0; b < BT; ++b) pair_epilogue_pre<EPI, BT>(p, KVFP8, ein, b, it, r0, r1, acc0[b], acc1[b]);
+  }
+}
+
 // ---------------------------------------------------------------- MFMA tiles (Bp >= 16)
 //
 // v_mfma_f32_16x16x32_bf16: lane l supplies A[l % 16][8 k-values] and B[8 k-values][l % 16];
@@ -281,11 +400,33 @@ hipError_t gemv_s(const MatmulParams& p, int n_items, int kv, hipStream_t s) {
   return hipGetLastError();
 }
 
+constexpr int NORM_IPW = 8;  // waves (row pairs) per work group of the norm-fused kernel
+
+template <int BT, bool FP8, int EPI, bool KVFP8, int U>
+hipError_t gemv_norm_go(const MatmulParams& p, int n_items, hipStream_t s) {
+  auto kern = k_gemv_norm<BT, FP8, EPI, KVFP8, U, NORM_IPW>;
+  const size_t lds = (size_t)BT * p.K * 2;
+  static size_t allowed = 64 * 1024;  // per instance: the dynamic LDS size enabled so far
+  if (lds > allowed) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    allowed = lds;
+  }
+  const int grid = (n_items + NORM_IPW - 1) / NORM_IPW;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVE * NORM_IPW), lds, s, p, n_items);
+  return hipGetLastError();
+}
+
 template <int BT, bool FP8, int EPI, bool KVFP8>
 hipError_t gemv_go(const MatmulParams& p, hipStream_t s) {
   const int n_items = EPI == EPI_SILU ? p.d_ff : p.N / 2;
   if (n_items <= 0) return hipSuccess;
   const int kv = p.K / (FP8 ? 16 : 8);
+  if (p.nh) {
+    if (kv <= WAVE * 4) return gemv_norm_go<BT, FP8, EPI, KVFP8, 4>(p, n_items, s);
+    return gemv_norm_go<BT, FP8, EPI, KVFP8, 8>(p, n_items, s);
+  }
   if (kv <= WAVE * 4) return gemv_s<BT, FP8, EPI, KVFP8, 4>(p, n_items, kv, s);
   return gemv_s<BT, FP8, EPI, KVFP8, 8>(p, n_items, kv, s);
 }
@@ -310,6 +451,7 @@ hipError_t dispatch_bt(const MatmulParams& p, bool mfma, hipStream_t s) {
     for (int b0 = 0; b0 < p.Bp; b0 += 8) {
       MatmulParams q = p;
       q.x = p.x + (int64_t)b0 * p.ldx;
+      q.nh = p.nh ? p.nh + (int64_t)b0 * p.K : nullptr;
       q.Bp = p.Bp - b0 < 8 ? p.Bp - b0 : 8;
       q.out = p.out ? p.out + (int64_t)b0 * p.ldo : nullptr;
       q.act = p.act ? p.act + (int64_t)b0 * p.ldact : nullptr;

@@ -127,7 +127,9 @@ def test_graph_replay_equals_eager_bitwise(dec, B, persist):
     assert torch.equal(pe.view(torch.uint8), pg.view(torch.uint8))
     persistent = B <= 8 and persist
     assert ie.persistent == ig.persistent == int(persistent)
-    expect = 1 if persistent else 7 * cfg.n_layers + 2
+    # per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the
+    # matrix-vector kernels (batch <= 8) normalize their own input
+    expect = 1 if persistent else (5 if B <= 8 else 7) * cfg.n_layers + 2
     assert ie.kernels_per_step == ig.kernels_per_step == expect
 
 
