@@ -50,14 +50,49 @@ def log(msg: str) -> None:
 
 def gate_up_bytes(cfg, B: int) -> int:
     """Algorithmic bytes of one gate+up launch: the weights once (+ fp8 row scales),
-    the batch's bf16 activations read, the bf16 SiLU x mul output written."""
+    the input read once -- the fp32 residual rows and the norm gain where the kernel
+    normalizes its own input (batch <= 8), else the bf16 activations -- and the bf16
+    SiLU x mul output written."""
     b = 1 if cfg.weight_dtype == "fp8" else 2
     w = 2 * cfg.d_ff * cfg.d_model * b + (2 * cfg.d_ff * 4 if cfg.weight_dtype == "fp8" else 0)
-    return w + B * cfg.d_model * 2 + B * cfg.d_ff * 2
+    x = B * cfg.d_model * 4 + cfg.d_model * 4 if B <= 8 else B * cfg.d_model * 2
+    return w + x + B * cfg.d_ff * 2
+
+
+def traffic_file(workload: str, B: int) -> str:
+    return os.path.join(ROOT, "profiles", f"k_gemv_norm_gate_up_{workload}_b{B}_traffic.txt")
+
+
+def measured_traffic(workload: str, B: int):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+    or None when there is none or it was taken on other kernel sources."""
+    from memory_bound_transformer_decode_amd import profile_summary as ps
+
+    path = traffic_file(workload, B)
+    if not os.path.exists(path):
+        return None
+    t = ps.read_traffic(path)
+    if t.get("source_sha256") != ps.kernel_source_sha256():
+        log(f"{os.path.basename(path)} was measured on other kernel sources: traffic not reported")
+        return None
+    return int(float(t["traffic_bytes_per_dispatch"]))
+
+
+def copy_calibration(nbytes: int) -> int:
+    """Device-to-device copies of a known size, for scaling the HBM byte counters."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "copies": 3}), flush=True)
+    return 0
 
 
 def run_batch(wl, B: int, steps: int, warmup: int, seed: int, want_eager: bool, want_kernel: bool,
-              weights=None):
+              weights=None, base_flags: int = 0):
     import torch
 
     from memory_bound_transformer_decode_amd import dec, perfmodel, synth
@@ -95,7 +130,7 @@ def run_batch(wl, B: int, steps: int, warmup: int, seed: int, want_eager: bool, 
         wall = time.perf_counter() - t0
         return wall, e0.elapsed_time(e1) / 1e3
 
-    wall, ev = timed(0)
+    wall, ev = timed(base_flags)
     info = d.info()
     step_bytes = sum(shape.step_bytes(lens0 + t) for t in range(steps))
     res = {
@@ -123,24 +158,25 @@ def run_batch(wl, B: int, steps: int, warmup: int, seed: int, want_eager: bool, 
         res["plans"] = plans
         d.set_flags(0)
     if want_kernel and "kernel" not in res:
-        # the dominant kernel alone, one launch per layer (distinct weights each launch,
-        # so no launch is served from the 256 MB last-level cache), events per launch
+        # the dominant kernel alone: one launch per layer back to back (distinct weights
+        # each launch, so no launch is served from a cache), timed with events on the
+        # library's stream (the torch stream the decoder was created on) around all L
+        # launches; the average includes the short gaps between launches
         L = cfg.n_layers
         durs = []
-        for rep in range(3):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(L)]
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             for l in range(L):
-                evs[l][0].record()
                 d.launch_matmul(dec.MAT_GATE_UP, l)
-                evs[l][1].record()
+            e1.record()
             torch.cuda.synchronize()
             if rep > 0:
-                durs += [a.elapsed_time(b) / 1e3 for a, b in evs]
+                durs.append(e0.elapsed_time(e1) / 1e3 / L)
         avg = float(np.mean(durs))
         nbytes = gate_up_bytes(cfg, B)
-        res["kernel"] = {"name": ("k_gemm_mfma" if B >= 16 else "k_gemv") + " gate+up + SiLU x mul",
-                         "avg_s": avg, "bytes": nbytes, "gbps": nbytes / avg / 1e9, "launches": len(durs)}
+        res["kernel"] = {"name": ("k_gemm_mfma" if B >= 16 else "k_gemv_norm") + " gate+up + SiLU x mul",
+                         "avg_s": avg, "bytes": nbytes, "gbps": nbytes / avg / 1e9, "launches": len(durs) * L}
     d.close()
     del pool
     return res, weights
@@ -201,6 +237,10 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip eager, kernel and probe legs")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the main leg's kernels one by one (for counter collection)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES device-to-device 3 times (scales the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -216,12 +256,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
     wl = synth.WORKLOADS[args.workload]
     cfg = wl.model
     extras = not args.no_extras
     log(f"workload {args.workload} batch {args.batch}, {args.steps} steps, {args.warmup} warmup")
     main_res, weights = run_batch(wl, args.batch, args.steps, args.warmup, args.seed,
-                                  want_eager=extras, want_kernel=True)
+                                  want_eager=extras, want_kernel=True,
+                                  base_flags=dec.FLAG_EAGER if args.eager else 0)
     log(f"batch {args.batch}: {main_res['tok_s']:.1f} tok/s, {main_res['ms_per_step']:.3f} ms/step, "
         f"{main_res['achieved_gbps']:.0f} GB/s ({100 * main_res['frac_of_peak']:.1f}% of 8 TB/s)")
     second = None
@@ -271,7 +314,8 @@ def main() -> int:
                 "bytes_per_step": int(main_res["bytes_per_step"]),
                 "probe_read_gbps": round(probe, 1) if probe else None},
         "roofline": {"bound": "hbm", "achieved": round(k["gbps"], 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(k["gbps"] / PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(k["gbps"] / PEAK_GBPS, 4),
+                     "traffic": measured_traffic(args.workload, args.batch) if args.batch <= 8 else None,
                      "kernel": k["name"],
                      "bytes_per_launch": int(k["bytes"]), "avg_us": round(k["avg_s"] * 1e6, 2),
                      "launches": k["launches"]},

@@ -739,7 +739,13 @@ int dec_launch_matmul(dec_ctx* c, int which, int layer) {
     return fail(DEC_E_INVALID, "which must be DEC_MAT_O, DEC_MAT_GATE_UP, DEC_MAT_DOWN or DEC_MAT_LM_HEAD");
   if (which != DEC_MAT_LM_HEAD && (layer < 0 || layer >= c->cfg.n_layers))
     return fail(DEC_E_INVALID, "layer %d outside [0, %d)", layer, c->cfg.n_layers);
-  hipError_t e = run_matmul(c, which, which == DEC_MAT_LM_HEAD ? 0 : layer, c->info.bucket, c->stream);
+  // the same kernel as in the step: a fused RMSNorm where the step fuses it
+  const float* ng = nullptr;
+  if (fused_norm(c->cfg, c->info.bucket)) {
+    if (which == DEC_MAT_GATE_UP) ng = c->mlp_norm + (size_t)layer * c->cfg.d_model;
+    if (which == DEC_MAT_LM_HEAD) ng = c->final_norm;
+  }
+  hipError_t e = run_matmul(c, which, which == DEC_MAT_LM_HEAD ? 0 : layer, c->info.bucket, c->stream, ng);
   if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
   return DEC_OK;
 }

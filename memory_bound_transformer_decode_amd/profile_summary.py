@@ -1,0 +1,144 @@
+"""Short text summaries of rocprofv3 output, for the profiles/ folder.
+
+Kernel durations (from ``rocprofv3 --kernel-trace --stats --output-format csv``)::
+
+    python -m memory_bound_transformer_decode_amd.profile_summary stats DIR \
+        --command "<the rocprofv3 command>" [--top 12] > profiles/<kernel>_<workload>.md
+
+HBM traffic of one kernel per dispatch, from two counter runs of the benchmark
+(``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``) and two of a device-to-device copy of
+known size (the same counters; they give the bytes-per-reported-unit factors)::
+
+    python -m memory_bound_transformer_decode_amd.profile_summary traffic \
+        --fetch DIR1 --write DIR2 --copy-fetch DIR3 --copy-write DIR4 --copy-bytes N \
+        --kernel SUBSTRING --commands "<...>" > profiles/<kernel>_<workload>_traffic.txt
+
+The traffic file ends with ``source_sha256`` of the kernel's sources, which bench.py
+compares with the tree it runs from: counters taken on another version of the kernel
+are not reported.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import sys
+from typing import Dict, List
+
+# sources of the matrix-vector kernels (the benchmark's dominant kernel)
+KERNEL_SOURCES = ("csrc/matmul.hip", "csrc/epilogue.h", "csrc/common.h", "csrc/kernels.h")
+
+
+def kernel_source_sha256() -> str:
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(here, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[-1]
+
+
+def _col(row: Dict[str, str], *names: str) -> str:
+    low = {k.lower(): v for k, v in row.items()}
+    for n in names:
+        if n.lower() in low:
+            return low[n.lower()]
+    raise KeyError(f"none of {names} in {list(row)}")
+
+
+def stats(args) -> None:
+    path = _find(args.dir, "kernel_stats.csv")
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(_col(r, "TotalDurationNs")))
+    print("# Kernel durations (rocprofv3 --kernel-trace --stats)\n")
+    print(f"Command: `{args.command}`\n")
+    print("| kernel | calls | average us | min us | max us | share % |")
+    print("|---|---|---|---|---|---|")
+    for r in rows[: args.top]:
+        name = _col(r, "Name", "KernelName")
+        print(f"| `{name[:110]}` | {_col(r, 'Calls')} | {float(_col(r, 'AverageNs')) / 1e3:.2f} | "
+              f"{float(_col(r, 'MinNs')) / 1e3:.2f} | {float(_col(r, 'MaxNs')) / 1e3:.2f} | "
+              f"{float(_col(r, 'Percentage')):.2f} |")
+
+
+def _counter(d: str, counter: str, kernel: str) -> List[float]:
+    path = _find(d, "counter_collection.csv")
+    vals = []
+    for r in csv.DictReader(open(path)):
+        if _col(r, "Counter_Name", "CounterName") != counter:
+            continue
+        if kernel in _col(r, "Kernel_Name", "KernelName"):
+            vals.append(float(_col(r, "Counter_Value", "CounterValue")))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel!r} in {path}")
+    return vals
+
+
+def traffic(args) -> None:
+    kib = 1024.0
+    f = _counter(args.fetch, "FETCH_SIZE", args.kernel)
+    w = _counter(args.write, "WRITE_SIZE", args.kernel)
+    cf = _counter(args.copy_fetch, "FETCH_SIZE", args.copy_kernel)
+    cw = _counter(args.copy_write, "WRITE_SIZE", args.copy_kernel)
+    # the copy moves copy_bytes in and copy_bytes out: bytes per reported KiB
+    ffac = args.copy_bytes / (max(cf) * kib)
+    wfac = args.copy_bytes / (max(cw) * kib)
+    fetch = sum(f) / len(f) * kib * ffac
+    write = sum(w) / len(w) * kib * wfac
+    print("# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
+    print(f"# commands: {args.commands}")
+    print(f"kernel: {args.kernel}")
+    print(f"dispatches: {len(f)} (fetch), {len(w)} (write)")
+    print(f"fetch_kib_per_dispatch: {sum(f) / len(f):.1f}")
+    print(f"write_kib_per_dispatch: {sum(w) / len(w):.1f}")
+    print(f"copy_bytes: {args.copy_bytes}")
+    print(f"copy_fetch_kib: {max(cf):.1f}")
+    print(f"copy_write_kib: {max(cw):.1f}")
+    print(f"fetch_factor: {ffac:.4f}")
+    print(f"write_factor: {wfac:.4f}")
+    print(f"fetch_bytes_per_dispatch: {fetch:.0f}")
+    print(f"write_bytes_per_dispatch: {write:.0f}")
+    print(f"traffic_bytes_per_dispatch: {fetch + write:.0f}")
+    print(f"source_sha256: {kernel_source_sha256()}")
+
+
+def read_traffic(path: str) -> Dict[str, str]:
+    out = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--command", required=True)
+    s.add_argument("--top", type=int, default=12)
+    t = sub.add_parser("traffic")
+    for name in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--commands"):
+        t.add_argument(name, required=True)
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--copy-kernel", default="copyBuffer")
+    args = ap.parse_args(argv)
+    (stats if args.cmd == "stats" else traffic)(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
