@@ -10,12 +10,14 @@
 // Inference Internals", Batching Economics), so every K/V tile is read once and
 // shared by the g = Hq / Hkv query heads of its group.
 //
-// k_attn_split: work group (split j, kv head c, sequence b), 4 waves.  The blocks
-// of positions 0..p are divided evenly between n_split work groups; each wave of a
-// work group takes every 4th block.  A lane holds 16 bytes of one position's K and
-// V row; scores are reduced over the lanes of a row, then the running max m, sum l
-// and output o are updated (base-2 exponentials with log2(e) folded into q).  The
-// waves merge in LDS and the work group writes (m, l, o) for each of its heads.
+// k_attn_split: work group (split j, kv head c, sequence b), 8 waves.  The blocks
+// of positions 0..p are divided evenly between n_split work groups (one, unless the
+// context is long and the batch small); wave w of a work group takes blocks w, w + 8,
+// ..., with the next block's loads in flight while it works on the current one (the
+// physical block ids are fetched once, one per lane).  A lane holds 8 elements of one
+// position's K and V row; scores are reduced over the lanes of a row, then the
+// running max m, sum l and output o are updated (base-2 exponentials with log2(e)
+// folded into q).  The waves merge in LDS; with one split the work group writes o.
 // The last work group of a (sequence, kv head) to finish -- counted by a
 // self-resetting arrival counter -- combines the splits:
 // o = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j, M = max_j m_j, as bf16; a
@@ -29,24 +31,114 @@
 namespace dec {
 
 constexpr int MAX_SPLIT = 64;  // splits per (sequence, kv head); the host keeps n_split within it
+#ifndef DEC_ATTN_WAVES
+#define DEC_ATTN_WAVES 8
+#endif
+constexpr int ATTN_WAVES = DEC_ATTN_WAVES;  // waves per work group
 
-template <int DH, bool FP8, int G>
-__global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
-  constexpr int EPL = FP8 ? 16 : 8;  // cache elements per 16-byte load
+// K and V of one block of one kv head for this lane: NPASS 16-byte loads each
+// (a lane holds 8 cache elements of a row: 16 bytes of bf16 or 8 bytes of E4M3, in .x .y)
+template <int DH, bool FP8, int NPASS, int PPP>
+__device__ __forceinline__ void attn_load(const uint8_t* pool, int64_t kbase, int64_t vbase, int prow, int eoff,
+                                          u32x4 (&kr)[NPASS], u32x4 (&vr)[NPASS]) {
+  constexpr int ESZ = FP8 ? 1 : 2;
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int64_t off = (int64_t)(ps * PPP + prow) * DH + eoff;
+    if (FP8) {
+      const u32x2 k2 = gld(reinterpret_cast<const u32x2*>(pool + (kbase + off)));
+      const u32x2 v2 = gld(reinterpret_cast<const u32x2*>(pool + (vbase + off)));
+      kr[ps] = u32x4{k2.x, k2.y, 0u, 0u};
+      vr[ps] = u32x4{v2.x, v2.y, 0u, 0u};
+    } else {
+      kr[ps] = gld16(pool + (kbase + off) * ESZ);
+      vr[ps] = gld16(pool + (vbase + off) * ESZ);
+    }
+  }
+}
+
+// the 8 cache elements a lane holds, as fp32
+template <bool FP8>
+__device__ __forceinline__ void attn_widen(const u32x4& r, float (&f)[8]) {
+  if (FP8) {
+    const f32x2 a = e4m3x2_to_f32x2<false>(r.x), b = e4m3x2_to_f32x2<true>(r.x);
+    const f32x2 c = e4m3x2_to_f32x2<false>(r.y), d = e4m3x2_to_f32x2<true>(r.y);
+    f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y; f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
+  } else {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(w[i]); f[2 * i + 1] = bf16_hi(w[i]); }
+  }
+}
+
+// online-softmax update of the G heads' (m, l, o) with one block (positions blk*16 ..)
+template <int DH, bool FP8, int G, int NPASS, int PPP, int LPP, int EPL>
+__device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const float (&qv)[G][EPL],
+                                            const u32x4 (&kr)[NPASS], const u32x4 (&vr)[NPASS], float (&m)[G],
+                                            float (&l)[G], float (&o)[G][EPL]) {
+  float sc[NPASS][G];
+  bool vld[NPASS];  // slots past the last position may hold anything (even NaN): mask them
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    float kf[EPL];
+    attn_widen<FP8>(kr[ps], kf);
+    const bool valid = blk * KV_BLOCK + ps * PPP + prow < ntok;
+    vld[ps] = valid;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s = fmaf(qv[h][e], kf[e], s);
+#pragma unroll
+      for (int off = 1; off < LPP; off <<= 1) s += __shfl_xor(s, off);
+      sc[ps][h] = valid ? s : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float bm = sc[0][h];
+#pragma unroll
+    for (int ps = 1; ps < NPASS; ++ps) bm = fmaxf(bm, sc[ps][h]);
+#pragma unroll
+    for (int off = LPP; off < WAVE; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
+    const float mn = fmaxf(m[h], bm);  // finite: the block's first position is valid
+    const float alpha = exp2f(m[h] - mn);
+    m[h] = mn;
+    l[h] *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const float pr = exp2f(sc[ps][h] - mn);
+      l[h] += pr;
+      float vf[EPL];
+      attn_widen<FP8>(vr[ps], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pr, vld[ps] ? vf[e] : 0.f, o[h][e]);
+    }
+  }
+}
+
+template <int DH, bool FP8, int G, int NW>
+__global__ __launch_bounds__(WAVE * NW) void k_attn_split(AttnParams p) {
+  constexpr int EPL = 8;             // cache elements per lane per row
   constexpr int LPP = DH / EPL;      // lanes per position row
   constexpr int PPP = WAVE / LPP;    // positions per pass
   constexpr int NPASS = KV_BLOCK / PPP;
-  constexpr int NW = 4;
   const int split = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = threadIdx.x % WAVE;
   const int prow = lane / LPP, eoff = (lane % LPP) * EPL;
 
-  const int pos = p.seq_lens[b];
+  const int pos = gld(p.seq_lens + b);
   const int ntok = pos + 1;  // 0 for a padded row
   const int nblk = pos >= 0 ? pos / KV_BLOCK + 1 : 0;
   const int per = (nblk + p.n_split - 1) / p.n_split;
   const int blk0 = split * per;
   const int blk1 = min(nblk, blk0 + per);
+  // this wave's blocks: blk0 + wave + i NW, i < nb; lane i holds the physical id of the i-th
+  const int nb = blk0 + wave < blk1 ? (blk1 - blk0 - wave + NW - 1) / NW : 0;
+  const int my_blk = blk0 + wave + lane * NW;
+  const int my_phys = lane < nb ? gld(p.bt + (int64_t)b * p.bps + my_blk) : 0;
 
   const float qscale = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
   float qv[G][EPL];
@@ -55,7 +147,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
     const float* qh = p.q + ((int64_t)b * p.Hq + c * G + h) * DH + eoff;
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) {
-      const float4 t = *reinterpret_cast<const float4*>(qh + e);
+      const f32x4 t = gld(reinterpret_cast<const f32x4*>(qh + e));
       qv[h][e] = t.x * qscale;
       qv[h][e + 1] = t.y * qscale;
       qv[h][e + 2] = t.z * qscale;
@@ -73,80 +165,34 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
   }
 
   const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
-  constexpr int ESZ = FP8 ? 1 : 2;
-
-  for (int blk = blk0 + wave; blk < blk1; blk += NW) {
-    const int phys = p.bt[(int64_t)b * p.bps + blk];
-    const int64_t kbase = kv_offset(p.layer, 0, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
-    const int64_t vbase = kv_offset(p.layer, 1, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
-    u32x4 kr[NPASS], vr[NPASS];
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int64_t off = (int64_t)(ps * PPP + prow) * DH + eoff;
-      kr[ps] = ld16(pool + (kbase + off) * ESZ);
-      vr[ps] = ld16(pool + (vbase + off) * ESZ);
+  auto bases = [&](int i, int64_t& kb, int64_t& vb) {
+    const int phys = __shfl(my_phys, i);
+    kb = kv_offset(p.layer, 0, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
+    vb = kv_offset(p.layer, 1, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
+  };
+  if (nb > 0 && G > 6) {
+    // wide groups: the per-head state leaves no room for a second block in registers
+    u32x4 ka[NPASS], va[NPASS];
+    int64_t kbase, vbase;
+    for (int i = 0; i < nb; ++i) {
+      bases(i, kbase, vbase);
+      attn_load<DH, FP8, NPASS, PPP>(pool, kbase, vbase, prow, eoff, ka, va);
+      attn_update<DH, FP8, G, NPASS, PPP, LPP, EPL>(blk0 + wave + i * NW, ntok, prow, qv, ka, va, m, l, o);
     }
-    float sc[NPASS][G];
-    bool vld[NPASS];  // slots past the last position may hold anything (even NaN): mask them
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      float kf[EPL];
-      if (FP8) {
-        const uint32_t w[4] = {kr[ps].x, kr[ps].y, kr[ps].z, kr[ps].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x2 lo = e4m3x2_to_f32x2<false>(w[i]), hi = e4m3x2_to_f32x2<true>(w[i]);
-          kf[4 * i] = lo.x; kf[4 * i + 1] = lo.y; kf[4 * i + 2] = hi.x; kf[4 * i + 3] = hi.y;
-        }
-      } else {
-        const uint32_t w[4] = {kr[ps].x, kr[ps].y, kr[ps].z, kr[ps].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { kf[2 * i] = bf16_lo(w[i]); kf[2 * i + 1] = bf16_hi(w[i]); }
-      }
-      const bool valid = blk * KV_BLOCK + ps * PPP + prow < ntok;
-      vld[ps] = valid;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) s = fmaf(qv[h][e], kf[e], s);
-#pragma unroll
-        for (int off = 1; off < LPP; off <<= 1) s += __shfl_xor(s, off);
-        sc[ps][h] = valid ? s : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float bm = sc[0][h];
-#pragma unroll
-      for (int ps = 1; ps < NPASS; ++ps) bm = fmaxf(bm, sc[ps][h]);
-#pragma unroll
-      for (int off = LPP; off < WAVE; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
-      const float mn = fmaxf(m[h], bm);  // finite: the block's first position is valid
-      const float alpha = exp2f(m[h] - mn);
-      m[h] = mn;
-      l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
-#pragma unroll
-      for (int ps = 0; ps < NPASS; ++ps) {
-        const float pr = exp2f(sc[ps][h] - mn);
-        l[h] += pr;
-        float vf[EPL];
-        const uint32_t w[4] = {vr[ps].x, vr[ps].y, vr[ps].z, vr[ps].w};
-        if (FP8) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x2 lo = e4m3x2_to_f32x2<false>(w[i]), hi = e4m3x2_to_f32x2<true>(w[i]);
-            vf[4 * i] = lo.x; vf[4 * i + 1] = lo.y; vf[4 * i + 2] = hi.x; vf[4 * i + 3] = hi.y;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { vf[2 * i] = bf16_lo(w[i]); vf[2 * i + 1] = bf16_hi(w[i]); }
-        }
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pr, vld[ps] ? vf[e] : 0.f, o[h][e]);
-      }
+  } else if (nb > 0) {
+    // two blocks in flight: the next block's loads are issued before this one's math
+    u32x4 ka[NPASS], va[NPASS], kb2[NPASS], vb2[NPASS];
+    int64_t kbase, vbase;
+    bases(0, kbase, vbase);
+    attn_load<DH, FP8, NPASS, PPP>(pool, kbase, vbase, prow, eoff, ka, va);
+    for (int i = 0; i < nb; i += 2) {
+      bases(min(i + 1, nb - 1), kbase, vbase);
+      attn_load<DH, FP8, NPASS, PPP>(pool, kbase, vbase, prow, eoff, kb2, vb2);
+      attn_update<DH, FP8, G, NPASS, PPP, LPP, EPL>(blk0 + wave + i * NW, ntok, prow, qv, ka, va, m, l, o);
+      if (i + 1 >= nb) break;
+      bases(min(i + 2, nb - 1), kbase, vbase);
+      attn_load<DH, FP8, NPASS, PPP>(pool, kbase, vbase, prow, eoff, ka, va);
+      attn_update<DH, FP8, G, NPASS, PPP, LPP, EPL>(blk0 + wave + (i + 1) * NW, ntok, prow, qv, kb2, vb2, m, l, o);
     }
   }
 
@@ -174,6 +220,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
       for (int e = 0; e < EPL; ++e) so[wave][h][eoff + e] = o[h][e];
   }
   __syncthreads();
+  const bool single = p.n_split == 1;
   for (int idx = threadIdx.x; idx < G * DH; idx += NW * WAVE) {
     const int h = idx / DH, e = idx % DH;
     float M = sm[0][h];
@@ -188,10 +235,16 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
         L = fmaf(f, sl[w][h], L);
       }
     }
+    if (single) {
+      // the whole context in this work group: o directly
+      p.o[((int64_t)b * p.Hq + c * G + h) * DH + e] = f32_to_bf16(M != -INFINITY ? O / L : 0.f);
+      continue;
+    }
     const int64_t row = ((int64_t)b * p.Hq + c * G + h) * p.n_split + split;
     cst(p.part_o + row * DH + e, O);
     if (e == 0) cst_f2(p.part_ml + row * 2, M, L);
   }
+  if (single) return;
 
   // arrival: the partial stores of every wave complete before this work group counts
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -242,22 +295,26 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
 }
 
 namespace {
+template <int DH, bool FP8, int G>
+hipError_t attn_g(const AttnParams& p, hipStream_t s) {
+  const dim3 grid(p.n_split, p.Hkv, p.Bp);
+  hipLaunchKernelGGL((k_attn_split<DH, FP8, G, ATTN_WAVES>), grid, dim3(WAVE * ATTN_WAVES), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int DH, bool FP8>
 hipError_t attn_go(const AttnParams& p, hipStream_t s) {
-  const int g = p.Hq / p.Hkv;
-  const dim3 grid(p.n_split, p.Hkv, p.Bp);
-  switch (g) {
-    case 1: hipLaunchKernelGGL((k_attn_split<DH, FP8, 1>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_attn_split<DH, FP8, 2>), grid, dim3(256), 0, s, p); break;
-    case 3: hipLaunchKernelGGL((k_attn_split<DH, FP8, 3>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_attn_split<DH, FP8, 4>), grid, dim3(256), 0, s, p); break;
-    case 5: hipLaunchKernelGGL((k_attn_split<DH, FP8, 5>), grid, dim3(256), 0, s, p); break;
-    case 6: hipLaunchKernelGGL((k_attn_split<DH, FP8, 6>), grid, dim3(256), 0, s, p); break;
-    case 7: hipLaunchKernelGGL((k_attn_split<DH, FP8, 7>), grid, dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((k_attn_split<DH, FP8, 8>), grid, dim3(256), 0, s, p); break;
+  switch (p.Hq / p.Hkv) {
+    case 1: return attn_g<DH, FP8, 1>(p, s);
+    case 2: return attn_g<DH, FP8, 2>(p, s);
+    case 3: return attn_g<DH, FP8, 3>(p, s);
+    case 4: return attn_g<DH, FP8, 4>(p, s);
+    case 5: return attn_g<DH, FP8, 5>(p, s);
+    case 6: return attn_g<DH, FP8, 6>(p, s);
+    case 7: return attn_g<DH, FP8, 7>(p, s);
+    case 8: return attn_g<DH, FP8, 8>(p, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 }  // namespace
 

@@ -40,7 +40,10 @@ int fail(int code, const char* fmt, ...) {
 constexpr int LADDER[] = {1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64};
 constexpr int N_BUCKETS = sizeof(LADDER) / sizeof(LADDER[0]);
 constexpr int MAX_SPLIT = 64;
-constexpr int ATTN_TARGET_GROUPS = 1024;  // work groups per attention launch to aim for
+constexpr int ATTN_TARGET_GROUPS = 256;   // work groups per attention launch to aim for
+constexpr int ATTN_BLOCKS_PER_SPLIT = 8;  // context blocks one attention work group takes alone
+constexpr int ATTN_WAVES_ = 8;            // waves per attention work group (attention.hip)
+constexpr int WAVE_ = 64;
 constexpr uint32_t KNOWN_FLAGS =
     DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL | DEC_FLAG_PERSISTENT;
 constexpr int N_MODES = 8;  // plan-changing flag combinations (UNFUSED, NO_MFMA, PERSISTENT)
@@ -64,11 +67,17 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int blocks_per_seq(const dec_config& c) { return (c.max_seq_len + 15) / 16; }
 
+// Context splits per (sequence, kv head) of the attention kernel.  A split costs a
+// round of partial stores, an arrival counter and a combine; a longer split costs
+// more blocks per wave in sequence.  Split only past ATTN_BLOCKS_PER_SPLIT blocks
+// (at the longest context), and only while there are few (sequence, head) groups.
 int n_split_for(const dec_config& c, int Bp) {
   int ns = (ATTN_TARGET_GROUPS + Bp * c.n_kv_heads - 1) / (Bp * c.n_kv_heads);
-  // at least one block per wave of a split (4 waves) at the longest context
-  const int bps = blocks_per_seq(c), by_len = (bps + 3) / 4;
+  const int bps = blocks_per_seq(c), by_len = (bps + ATTN_BLOCKS_PER_SPLIT - 1) / ATTN_BLOCKS_PER_SPLIT;
   if (ns > by_len) ns = by_len;
+  // a wave holds the block ids of its share in its 64 lanes
+  const int min_ns = (bps + WAVE_ * ATTN_WAVES_ - 1) / (WAVE_ * ATTN_WAVES_);
+  if (ns < min_ns) ns = min_ns;
   if (ns > MAX_SPLIT) ns = MAX_SPLIT;
   return ns < 1 ? 1 : ns;
 }
