@@ -400,11 +400,14 @@ hipError_t gemv_s(const MatmulParams& p, int n_items, int kv, hipStream_t s) {
   return hipGetLastError();
 }
 
-constexpr int NORM_IPW = 8;  // waves (row pairs) per work group of the norm-fused kernel
+// Waves (row pairs) per work group of the norm-fused kernel: 8, so that one
+// normalization serves 8 row pairs (smaller work groups measured slower: the
+// normalization's L2 reads grow with the number of work groups).
+constexpr int NORM_IPW = 8;
 
-template <int BT, bool FP8, int EPI, bool KVFP8, int U>
-hipError_t gemv_norm_go(const MatmulParams& p, int n_items, hipStream_t s) {
-  auto kern = k_gemv_norm<BT, FP8, EPI, KVFP8, U, NORM_IPW>;
+template <int BT, bool FP8, int EPI, bool KVFP8, int U, int IPW>
+hipError_t gemv_norm_ipw(const MatmulParams& p, int n_items, hipStream_t s) {
+  auto kern = k_gemv_norm<BT, FP8, EPI, KVFP8, U, IPW>;
   const size_t lds = (size_t)BT * p.K * 2;
   static size_t allowed = 64 * 1024;  // per instance: the dynamic LDS size enabled so far
   if (lds > allowed) {
@@ -413,9 +416,14 @@ hipError_t gemv_norm_go(const MatmulParams& p, int n_items, hipStream_t s) {
     if (e != hipSuccess) return e;
     allowed = lds;
   }
-  const int grid = (n_items + NORM_IPW - 1) / NORM_IPW;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVE * NORM_IPW), lds, s, p, n_items);
+  const int grid = (n_items + IPW - 1) / IPW;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVE * IPW), lds, s, p, n_items);
   return hipGetLastError();
+}
+
+template <int BT, bool FP8, int EPI, bool KVFP8, int U>
+hipError_t gemv_norm_go(const MatmulParams& p, int n_items, hipStream_t s) {
+  return gemv_norm_ipw<BT, FP8, EPI, KVFP8, U, NORM_IPW>(p, n_items, s);
 }
 
 template <int BT, bool FP8, int EPI, bool KVFP8>
