@@ -383,8 +383,8 @@ namespace {
 // One row pair per work group: more work groups than the CUs hold at once, so the
 // hardware dispatcher hands out the rest as work groups retire and no CU is left with
 // a long static share at the end.  Rows longer than one pass of a wave (64 U vectors)
-// are split over S waves of the work group, so that every wave issues all of its loads
-// at once.
+// are split over S <= 8 waves of the work group (a wave takes more than one pass only
+// beyond 8 passes' worth).
 template <int BT, bool FP8, int EPI, bool KVFP8, int U>
 hipError_t gemv_s(const MatmulParams& p, int n_items, int kv, hipStream_t s) {
   const int need = (kv + WAVE * U - 1) / (WAVE * U);
@@ -431,12 +431,15 @@ hipError_t gemv_go(const MatmulParams& p, hipStream_t s) {
   const int n_items = EPI == EPI_SILU ? p.d_ff : p.N / 2;
   if (n_items <= 0) return hipSuccess;
   const int kv = p.K / (FP8 ? 16 : 8);
-  if (p.nh) {
-    if (kv <= WAVE * 4) return gemv_norm_go<BT, FP8, EPI, KVFP8, 4>(p, n_items, s);
-    return gemv_norm_go<BT, FP8, EPI, KVFP8, 8>(p, n_items, s);
-  }
-  if (kv <= WAVE * 4) return gemv_s<BT, FP8, EPI, KVFP8, 4>(p, n_items, kv, s);
-  return gemv_s<BT, FP8, EPI, KVFP8, 8>(p, n_items, kv, s);
+  // one wave per row pair, 4 loads per row per lane in flight and as many passes as the
+  // row needs (measured faster than one deeper pass, or than splitting the row over
+  // waves, which multiplies the normalizations per row pair)
+  if (p.nh) return gemv_norm_go<BT, FP8, EPI, KVFP8, 4>(p, n_items, s);
+  // shallow per-wave load depth and many waves measured best (more waves resident per
+  // CU): U = 4 for rows up to 1024 vectors (two waves per row pair at K = 4096 bf16),
+  // U = 2 beyond (eight waves, two passes each, for the d_ff-long rows)
+  if (kv <= 1024) return gemv_s<BT, FP8, EPI, KVFP8, 4>(p, n_items, kv, s);
+  return gemv_s<BT, FP8, EPI, KVFP8, 2>(p, n_items, kv, s);
 }
 
 template <int NT, bool FP8, int EPI, bool KVFP8>
