@@ -278,34 +278,35 @@ __global__ __launch_bounds__(WAVE * MFMA_WAVES) void k_gemm_mfma(MatmulParams p)
   const size_t wrow_bytes = FP8 ? (size_t)p.K : (size_t)p.K * 2;
   const uint8_t* Wb = static_cast<const uint8_t*>(p.W);
 
-  for (int st = s0; st < s1; ++st) {
+  // One step: 32 bytes of each A row per lane (two 16-byte halves) and EPL activations
+  // per lane per column tile.  Every load is unconditional at a clamped address: rows
+  // past the matrix feed columns the epilogue drops, activations past the batch feed
+  // batch columns it drops, and activations past K are replaced by zeros, so that the
+  // re-read weights there contribute nothing.
+  auto load_step = [&](int st, u32x4 (&wa)[NA][2], u32x4 (&xb)[NT][EPL / 8]) {
     const int k0 = st * KSTEP + kg * EPL;  // first k of this lane's run
-    // A: 32 bytes per lane per A tile, as two 16-byte halves (each half all-in or all-out of K)
-    u32x4 wa[NA][2];
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int kh = k0 + hh * (EPL / 2);
-        if (arow_ok[a] && kh < p.K)
-          wa[a][hh] = ld_stream(reinterpret_cast<const u32x4*>(Wb + (size_t)arow[a] * wrow_bytes +
-                                                               (size_t)kh * (FP8 ? 1 : 2)));
-        else
-          wa[a][hh] = u32x4{0u, 0u, 0u, 0u};
+        const int kh = min(k0 + hh * (EPL / 2), p.K - EPL / 2);
+        wa[a][hh] = ld_stream(reinterpret_cast<const u32x4*>(Wb + (size_t)arow[a] * wrow_bytes +
+                                                             (size_t)kh * (FP8 ? 1 : 2)));
       }
-    // B: EPL bf16 activations per lane per column tile
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int col = t * 16 + m;
-      u32x4 xb[EPL / 8];
+      const int col = min(t * 16 + m, p.Bp - 1);
 #pragma unroll
       for (int v = 0; v < EPL / 8; ++v) {
         const int kv = k0 + v * 8;
-        if (col < p.Bp && kv < p.K)
-          xb[v] = ld16(p.x + (int64_t)col * p.ldx + kv);
-        else
-          xb[v] = u32x4{0u, 0u, 0u, 0u};
+        const u32x4 xv = gld16(p.x + (int64_t)col * p.ldx + min(kv, p.K - 8));
+        xb[t][v] = kv < p.K ? xv : u32x4{0u, 0u, 0u, 0u};
       }
+    }
+  };
+  auto mma_step = [&](const u32x4 (&wa)[NA][2], const u32x4 (&xb)[NT][EPL / 8]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
 #pragma unroll
@@ -321,10 +322,22 @@ __global__ __launch_bounds__(WAVE * MFMA_WAVES) void k_gemm_mfma(MatmulParams p)
           } else {
             av = __builtin_bit_cast(bf16x8, wa[a][mm]);
           }
-          const bf16x8 bv = __builtin_bit_cast(bf16x8, xb[mm]);
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, xb[t][mm]);
           acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[a][t], 0, 0, 0);
         }
       }
+    }
+  };
+  // two steps in flight: the next step's loads are issued before this step's products
+  if (s0 < s1) {
+    u32x4 wa0[NA][2], wa1[NA][2], xb0[NT][EPL / 8], xb1[NT][EPL / 8];
+    load_step(s0, wa0, xb0);
+    for (int st = s0; st < s1; st += 2) {
+      if (st + 1 < s1) load_step(st + 1, wa1, xb1);
+      mma_step(wa0, xb0);
+      if (st + 1 >= s1) break;
+      if (st + 2 < s1) load_step(st + 2, wa0, xb0);
+      mma_step(wa1, xb1);
     }
   }
 
