@@ -41,6 +41,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/sec at batch 1 and 32; achieved HBM GB/s vs ~8 TB/s peak"
+REPS_CPU = 5  # repeats of the CPU oracle's timed truncations (about 10 s of host work at 8B)
 PEAK_GBPS = 8000.0
 
 
@@ -151,7 +152,9 @@ def run_batch(wl, B: int, steps: int, warmup: int, seed: int, want_eager: bool, 
     if want_eager:
         plans = {}
         for name, flags in (("persistent_graph", dec.FLAG_PERSISTENT),
-                            ("multi_kernel_eager", dec.FLAG_EAGER)):
+                            ("multi_kernel_eager", dec.FLAG_EAGER),
+                            ("unfused_graph", dec.FLAG_UNFUSED),
+                            ("unfused_eager", dec.FLAG_UNFUSED | dec.FLAG_EAGER)):
             w2, _ = timed(flags)
             plans[name] = {"tok_s": B * steps / w2, "ms_per_step": 1e3 * w2 / steps,
                            "kernels_per_step": d.info().kernels_per_step}
@@ -210,19 +213,20 @@ def cpu_baseline(wl, B: int, weights, seed: int, budget_s: float):
     del pool
     m = OI.model(weights, n_layers=2)  # host copies of the codes (transfer not timed)
     ids = synth.make_token_ids(cfg, 1, B, seed=seed)[0]
-    times = {}
-    for L in (1, 2):
-        cache = OI.cache(c2, codes)
-        t0 = time.perf_counter()
-        OD.decode_step(m, cache, ids, lens, bt, n_layers=L)
-        times[L] = time.perf_counter() - t0
+    times = {1: float("inf"), 2: float("inf")}
+    for rep in range(REPS_CPU):  # best of a few repeats of each truncation
+        for L in (1, 2):
+            cache = OI.cache(c2, codes)
+            t0 = time.perf_counter()
+            OD.decode_step(m, cache, ids, lens, bt, n_layers=L)
+            times[L] = min(times[L], time.perf_counter() - t0)
     per_layer = max(times[2] - times[1], 1e-9)
     step = times[1] + (cfg.n_layers - 1) * per_layer
     torch.cuda.empty_cache()
     return {"value": B / step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"one {cfg.name} decode step at batch {B}: embedding, 1 and 2 layers, final "
-                       f"norm and LM head timed ({times[1]:.1f}s, {times[2]:.1f}s), extrapolated "
-                       f"linearly to {cfg.n_layers} layers = {step:.1f}s per step"),
+                       f"norm and LM head, best of {REPS_CPU} runs each ({times[1]:.1f}s, {times[2]:.1f}s), "
+                       f"extrapolated linearly to {cfg.n_layers} layers = {step:.1f}s per step"),
             "host_cpus": os.cpu_count()}
 
 

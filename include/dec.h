@@ -67,7 +67,9 @@ typedef enum { DEC_BF16 = 0, DEC_FP8_E4M3 = 1 } dec_dtype;
 
 enum {
   DEC_FLAG_EAGER = 1u,       /* launch kernels one by one instead of replaying a captured graph */
-  DEC_FLAG_UNFUSED = 2u,     /* one kernel per op, intermediates through HBM (measurement only) */
+  DEC_FLAG_UNFUSED = 2u,     /* one kernel per op, intermediates through HBM (measurement only):
+                                RMSNorm kernels, the matrix kernels with fp32 outputs, then RoPE +
+                                KV write, SiLU x mul and residual adds as kernels of their own */
   DEC_FLAG_NO_MFMA = 4u,     /* matrix-vector kernels at every batch size (no MFMA tiles) */
   DEC_FLAG_CAPTURE_ALL = 8u, /* capture every batch bucket at the first step instead of lazily */
   DEC_FLAG_PERSISTENT = 16u  /* a padded batch of <= 8 whose layer input fits in LDS runs the

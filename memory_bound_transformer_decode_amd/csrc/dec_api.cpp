@@ -103,6 +103,7 @@ bool persistent_fits(const dec_config& c, int Bp) {
 struct Layout {
   size_t ids, lens, bt, static_bytes;  // static region: ids | lens | block tables
   size_t h, x, q, part_o, part_ml, o, a, rope;
+  size_t uf;                           // unfused step: fp32 product rows [MB][max(N)]
   size_t mats, bar, attn_cnt, err;     // persistent-step state
   size_t total;
 };
@@ -143,6 +144,13 @@ Layout layout_of(const dec_config& c) {
   off = align256(off + MB * c.d_ff * 2);
   L.rope = off;
   off = align256(off + (size_t)c.max_seq_len * (c.d_head / 2) * 8);
+  L.uf = off;  // largest product row: QKV, gate+up or d_model
+  {
+    size_t n = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.d_head;
+    if ((size_t)2 * c.d_ff > n) n = (size_t)2 * c.d_ff;
+    if ((size_t)c.d_model > n) n = c.d_model;
+    off = align256(off + MB * n * 4);
+  }
   L.mats = off;  // device copies of the per-layer weight pointers: 4 arrays of n_layers
   off = align256(off + (size_t)4 * (c.n_layers > 0 ? c.n_layers : 1) * sizeof(dec::DevMat));
   L.bar = off;
@@ -176,7 +184,6 @@ int validate_config(const dec_config* c) {
     return fail(DEC_E_INVALID, "max_batch must be one of 1, 2, 4, 8, 16, 24, ..., 64 (got %d)", c->max_batch);
   if (c->max_seq_len <= 0) return fail(DEC_E_INVALID, "max_seq_len must be positive (got %d)", c->max_seq_len);
   if (c->flags & ~KNOWN_FLAGS) return fail(DEC_E_INVALID, "unknown flag bits 0x%x", c->flags & ~KNOWN_FLAGS);
-  if (c->flags & DEC_FLAG_UNFUSED) return fail(DEC_E_UNSUPPORTED, "DEC_FLAG_UNFUSED is not implemented in this build");
   return DEC_OK;
 }
 
@@ -413,8 +420,82 @@ hipError_t enqueue_persistent(dec_ctx* c, int Bp, hipStream_t s) {
 }
 
 // Enqueue the plan of one step for a padded batch of Bp rows on stream s.
+// The unfused step (DEC_FLAG_UNFUSED, measurement only): RMSNorm kernels, the matrix
+// kernels with a plain fp32 output, and the elementwise work as kernels of its own.
+hipError_t enqueue_unfused(dec_ctx* c, int Bp, hipStream_t s) {
+  const dec_config& g = c->cfg;
+  const bool wfp8 = g.weight_dtype == DEC_FP8_E4M3, kvfp8 = g.kv_dtype == DEC_FP8_E4M3;
+  const bool mfma = !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
+  const int d = g.d_model;
+  float* h = ws_ptr<float>(c, c->L.h);
+  float* uf = ws_ptr<float>(c, c->L.uf);
+  hipError_t e;
+  dec::NormParams np{};
+  np.h = h;
+  np.h_out = h;
+  np.x = ws_ptr<uint16_t>(c, c->L.x);
+  np.d = d;
+  np.Bp = Bp;
+  np.eps = g.rms_eps;
+  np.E = c->embed.w;
+  np.E_scale = c->embed.scale;
+  np.ids = ws_ptr<int32_t>(c, c->L.ids);
+  np.gain = g.n_layers > 0 ? c->attn_norm : c->final_norm;
+  if ((e = dec::launch_embed_norm(np, wfp8, s)) != hipSuccess) return e;
+  // the product of `which` with its rows written plainly to uf [Bp][N]
+  auto plain = [&](int which, int l, dec::MatmulParams* keep) -> hipError_t {
+    int epi = 0;
+    dec::MatmulParams p = matmul_params(c, which, l, Bp, &epi);
+    if (keep) *keep = p;
+    p.out = uf;
+    p.ldo = p.N;
+    return dec::launch_matmul(p, dec::EPI_LOGITS, wfp8, kvfp8, mfma, s);
+  };
+  dec::AttnParams ap{};
+  ap.q = ws_ptr<float>(c, c->L.q);
+  ap.pool = c->pool;
+  ap.seq_lens = ws_ptr<int32_t>(c, c->L.lens);
+  ap.bt = ws_ptr<int32_t>(c, c->L.bt);
+  ap.part_o = ws_ptr<float>(c, c->L.part_o);
+  ap.part_ml = ws_ptr<float>(c, c->L.part_ml);
+  ap.o = ws_ptr<uint16_t>(c, c->L.o);
+  ap.cnt = ws_ptr<unsigned>(c, c->L.attn_cnt);
+  ap.Bp = Bp;
+  ap.Hq = g.n_q_heads;
+  ap.Hkv = g.n_kv_heads;
+  ap.dh = g.d_head;
+  ap.num_blocks = g.num_blocks;
+  ap.bps = blocks_per_seq(g);
+  ap.n_split = n_split_for(g, Bp);
+  for (int l = 0; l < g.n_layers; ++l) {
+    if (l > 0) {
+      np.gain = c->attn_norm + (size_t)l * d;
+      if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
+    }
+    dec::MatmulParams qp{};
+    if ((e = plain(DEC_MAT_QKV, l, &qp)) != hipSuccess) return e;
+    if ((e = dec::launch_rope_kv(qp, uf, kvfp8, s)) != hipSuccess) return e;
+    ap.layer = l;
+    if ((e = dec::launch_attention(ap, kvfp8, s)) != hipSuccess) return e;
+    if ((e = plain(DEC_MAT_O, l, nullptr)) != hipSuccess) return e;
+    if ((e = dec::launch_add(h, uf, Bp * d, s)) != hipSuccess) return e;
+    np.gain = c->mlp_norm + (size_t)l * d;
+    if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
+    if ((e = plain(DEC_MAT_GATE_UP, l, nullptr)) != hipSuccess) return e;
+    if ((e = dec::launch_silu_mul(uf, g.d_ff, Bp, ws_ptr<uint16_t>(c, c->L.a), g.d_ff, s)) != hipSuccess) return e;
+    if ((e = plain(DEC_MAT_DOWN, l, nullptr)) != hipSuccess) return e;
+    if ((e = dec::launch_add(h, uf, Bp * d, s)) != hipSuccess) return e;
+  }
+  if (g.n_layers > 0) {
+    np.gain = c->final_norm;
+    if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
+  }
+  return run_matmul(c, DEC_MAT_LM_HEAD, 0, Bp, s);
+}
+
 hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
   if (use_persistent(c, Bp)) return enqueue_persistent(c, Bp, s);
+  if (c->cfg.flags & DEC_FLAG_UNFUSED) return enqueue_unfused(c, Bp, s);
   const dec_config& g = c->cfg;
   const bool wfp8 = g.weight_dtype == DEC_FP8_E4M3, kvfp8 = g.kv_dtype == DEC_FP8_E4M3;
   const int bps = blocks_per_seq(g);
@@ -647,7 +728,6 @@ int dec_load_weights(dec_ctx* c, const dec_weights* w) {
 int dec_set_flags(dec_ctx* c, uint32_t flags) {
   if (!c) return fail(DEC_E_INVALID, "ctx is NULL");
   if (flags & ~KNOWN_FLAGS) return fail(DEC_E_INVALID, "unknown flag bits 0x%x", flags & ~KNOWN_FLAGS);
-  if (flags & DEC_FLAG_UNFUSED) return fail(DEC_E_UNSUPPORTED, "DEC_FLAG_UNFUSED is not implemented in this build");
   c->cfg.flags = flags;
   c->info.flags = flags;
   return DEC_OK;
@@ -729,7 +809,11 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   const bool mfma = !persist && !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
   const int slices = (!mfma && Bp > 8) ? Bp / 8 : 1;
   const int L = g.n_layers;
-  const int per_layer = fused_norm(g, Bp) ? 5 : 7;  // without fusion: two RMSNorm kernels
+  // per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the
+  // matrix-vector kernels fuse them; unfused: also RoPE + KV write, SiLU x mul and two
+  // residual adds
+  const bool unfused = (g.flags & DEC_FLAG_UNFUSED) != 0;
+  const int per_layer = unfused ? 11 : fused_norm(g, Bp) ? 5 : 7;
   c->info.kernels_per_step = persist ? 1 : 2 + per_layer * L + (slices - 1) * (4 * L + 1);
   c->info.bucket = Bp;
   c->info.attn_splits = persist ? n_split_persistent(g, Bp) : n_split_for(g, Bp);

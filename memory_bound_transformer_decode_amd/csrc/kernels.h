@@ -124,6 +124,13 @@ size_t step_lds_bytes(const StepParams& p);
 int step_max_rounds();
 int step_waves_per_group();
 
+// Elementwise kernels of the unfused step (measurement only): RoPE + KV-cache write of
+// the fp32 QKV rows qkv [Bp][N] (p: the QKV product's parameters), SiLU x mul of the
+// fp32 gate+up rows gu [Bp][2 d_ff] into a, and h += delta over n elements.
+hipError_t launch_rope_kv(const MatmulParams& p, const float* qkv, bool kv_fp8, hipStream_t s);
+hipError_t launch_silu_mul(const float* gu, int d_ff, int Bp, uint16_t* a, int lda, hipStream_t s);
+hipError_t launch_add(float* h, const float* delta, int n, hipStream_t s);
+
 // (cos, sin)(p * theta^(-2i/dh)) for p < max_seq, i < dh/2, evaluated in double
 hipError_t launch_rope_table(float2* rope, int max_seq, int dh, double theta, hipStream_t s);
 

@@ -111,11 +111,19 @@ def test_null_context_calls():
     assert lib.dec_bw_probe(None, 16, 1, None, ctypes.byref(out)) == dec.DEC_E_INVALID
 
 
-def test_unfused_flag_reported_unsupported():
+def test_unknown_flag_bits_rejected():
     from memory_bound_transformer_decode_amd import dec
     lib = dec.load_library()
-    c = _cfg(flags=dec.FLAG_UNFUSED)
+    c = _cfg(flags=1 << 20)
     ctx = ctypes.c_void_p()
     rc = lib.dec_create(ctypes.byref(c), None, ctypes.c_void_p(16), ctypes.c_void_p(256), 1 << 30,
                         ctypes.c_void_p(16), ctypes.byref(ctx))
-    assert rc == dec.DEC_E_UNSUPPORTED
+    assert rc == dec.DEC_E_INVALID
+    assert b"flag" in lib.dec_last_error()
+
+
+def test_unfused_flag_accepted_by_the_workspace_query():
+    from memory_bound_transformer_decode_amd import dec
+    lib = dec.load_library()
+    c = _cfg(flags=dec.FLAG_UNFUSED)
+    assert lib.dec_workspace_bytes(ctypes.byref(c)) > 0

@@ -145,6 +145,38 @@ def test_mini_model_persistent_plan(dec, w, kv, B):
     assert_ok(run_parity(case, ids, flags=dec.FLAG_PERSISTENT), cfg)
 
 
+@pytest.mark.parametrize("w,kv", [("bf16", "bf16"), ("fp8", "fp8")])
+@pytest.mark.parametrize("B", [1, 3, 16])
+def test_mini_model_unfused_plan(dec, w, kv, B):
+    """The unfused step (one kernel per op, intermediates through HBM; measurement only)."""
+    cfg = fmt(MINI, w, kv)
+    rng = np.random.default_rng(70 + B)
+    case = make_case(cfg, ctx_mix(B, rng), 128, seed=14, gains="random")
+    ids = synth.make_token_ids(cfg, 2, B, seed=14)
+    log(f"mini unfused {w}/{kv} B={B}")
+    assert_ok(run_parity(case, ids, flags=dec.FLAG_UNFUSED), cfg)
+
+
+def test_unfused_step_matches_fused(dec):
+    """Same step, fused and unfused: close results (summation and rounding order only),
+    the same cache slots, and 11 kernels per layer unfused."""
+    cfg = fmt(MINI, "bf16", "bf16")
+    B = 5
+    rng = np.random.default_rng(80)
+    case = make_case(cfg, ctx_mix(B, rng), 128, seed=15, gains="random")
+    ids = synth.make_token_ids(cfg, 1, B, seed=15)[0]
+    zf, pf, inf_ = _one_step(dec, case, ids, case.ctx_lens, 0)
+    zu, pu, inu = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_UNFUSED)
+    assert inu.kernels_per_step == 11 * cfg.n_layers + 2
+    a, b = zf.double().cpu().numpy(), zu.double().cpu().numpy()
+    R = a.max(axis=1) - a.min(axis=1)
+    assert np.max(np.abs(a - b) / R[:, None]) < 5e-3
+    canary = synth.KV_CANARY_BF16
+    gf = synth.kv_codes_numpy(pf) != canary
+    gu = synth.kv_codes_numpy(pu) != canary
+    assert np.array_equal(gf, gu)
+
+
 @pytest.mark.parametrize("B", [1, 2, 4, 8])
 def test_persistent_step_matches_multi_kernel(dec, B):
     """Both plans of the same step agree closely (different summation orders only)."""
