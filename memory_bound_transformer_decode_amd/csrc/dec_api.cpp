@@ -40,7 +40,10 @@ int fail(int code, const char* fmt, ...) {
 constexpr int LADDER[] = {1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64};
 constexpr int N_BUCKETS = sizeof(LADDER) / sizeof(LADDER[0]);
 constexpr int MAX_SPLIT = 64;
-constexpr int ATTN_TARGET_GROUPS = 256;   // work groups per attention launch to aim for
+#ifndef DEC_ATTN_GROUPS
+#define DEC_ATTN_GROUPS 256
+#endif
+constexpr int ATTN_TARGET_GROUPS = DEC_ATTN_GROUPS;  // work groups per attention launch to aim for
 constexpr int ATTN_BLOCKS_PER_SPLIT = 8;  // context blocks one attention work group takes alone
 constexpr int ATTN_WAVES_ = 8;            // waves per attention work group (attention.hip)
 constexpr int WAVE_ = 64;

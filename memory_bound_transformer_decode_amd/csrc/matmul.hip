@@ -244,25 +244,27 @@ __global__ __launch_bounds__(WAVE * IPW) void k_gemv_norm(MatmulParams p, int n_
 
 constexpr int MFMA_WAVES = 8;  // waves per work group; they split K
 
-template <int NT, bool FP8, int EPI, bool KVFP8>
+template <int NT, bool FP8, int EPI, bool KVFP8, int RT>
 __global__ __launch_bounds__(WAVE * MFMA_WAVES) void k_gemm_mfma(MatmulParams p) {
-  constexpr int NA = EPI == EPI_SILU ? 2 : 1;  // A tiles per work group (gate + up)
+  extern __shared__ __align__(16) float mfma_red[];   // [waves][NA][NT][64][4]
+  constexpr int NG = EPI == EPI_SILU ? 2 : 1;  // row groups (gate, up)
+  constexpr int NA = NG * RT;                  // A tiles per work group: RT 16-row tiles per group
   constexpr int EPL = FP8 ? 32 : 16;           // weight elements per lane per step
   constexpr int KSTEP = 4 * EPL;               // k per step (4 lane groups)
   constexpr int NM = EPL / 8;                  // MFMAs per step per (A tile, column tile)
   const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
   const int m = lane % 16, kg = lane / 16;
-  const int tile = blockIdx.x;
+  const int tile = blockIdx.x;  // RT * 16 rows (per group)
 
-  // rows of this lane's A operand
+  // rows of this lane's A operands: tile a = (group a / RT, 16-row tile a % RT); rows past
+  // the matrix are clamped (their results are dropped by the epilogue)
   int arow[NA];
-  bool arow_ok[NA];
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
-    const int r = (EPI == EPI_SILU ? a * p.d_ff : 0) + tile * 16 + m;
-    const int lim = EPI == EPI_SILU ? (a + 1) * p.d_ff : p.N;
-    arow_ok[a] = r < lim;
-    arow[a] = arow_ok[a] ? r : 0;
+    const int gidx = a / RT;
+    const int r = (EPI == EPI_SILU ? gidx * p.d_ff : 0) + (tile * RT + a % RT) * 16 + m;
+    const int lim = EPI == EPI_SILU ? (gidx + 1) * p.d_ff : p.N;
+    arow[a] = min(r, lim - 1);
   }
   // k range of this wave
   const int nsteps = (p.K + KSTEP - 1) / KSTEP;
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(WAVE * MFMA_WAVES) void k_gemm_mfma(MatmulParams p)
   }
 
   // reduce the waves' partial tiles through LDS: red[wave][a][t][lane][j]
-  __shared__ float red[MFMA_WAVES * NA * NT * 64 * 4];
+  float* red = mfma_red;
 #pragma unroll
   for (int a = 0; a < NA; ++a)
 #pragma unroll
@@ -359,26 +361,26 @@ __global__ __launch_bounds__(WAVE * MFMA_WAVES) void k_gemm_mfma(MatmulParams p)
   };
   if (EPI == EPI_QKV) {
     // pairs (j, j + 1) are rows (2i, 2i + 1) of the same lane
-    for (int idx = tid; idx < NT * 64 * 2; idx += WAVE * MFMA_WAVES) {
-      const int t = idx / 128, l = (idx / 2) % 64, jp = (idx % 2) * 2;
-      const int col = t * 16 + l % 16, row = tile * 16 + 4 * (l / 16) + jp;
+    for (int idx = tid; idx < RT * NT * 64 * 2; idx += WAVE * MFMA_WAVES) {
+      const int rt = idx / (NT * 128), t = (idx / 128) % NT, l = (idx / 2) % 64, jp = (idx % 2) * 2;
+      const int col = t * 16 + l % 16, row = (tile * RT + rt) * 16 + 4 * (l / 16) + jp;
       if (col >= p.Bp || row >= p.N) continue;
       const float s0 = p.scale ? p.scale[row] : 1.f, s1 = p.scale ? p.scale[row + 1] : 1.f;
-      qkv_pair_out(p, KVFP8, col, row, total(0, t, l, jp) * s0, total(0, t, l, jp + 1) * s1);
+      qkv_pair_out(p, KVFP8, col, row, total(rt, t, l, jp) * s0, total(rt, t, l, jp + 1) * s1);
     }
   } else {
-    for (int idx = tid; idx < NT * 64 * 4; idx += WAVE * MFMA_WAVES) {
-      const int t = idx / 256, l = (idx / 4) % 64, j = idx % 4;
-      const int col = t * 16 + l % 16, r = tile * 16 + 4 * (l / 16) + j;
+    for (int idx = tid; idx < RT * NT * 64 * 4; idx += WAVE * MFMA_WAVES) {
+      const int rt = idx / (NT * 256), t = (idx / 256) % NT, l = (idx / 4) % 64, j = idx % 4;
+      const int col = t * 16 + l % 16, r = (tile * RT + rt) * 16 + 4 * (l / 16) + j;
       if (col >= p.Bp) continue;
       if (EPI == EPI_SILU) {
         if (r >= p.d_ff) continue;
         const float sg = p.scale ? p.scale[r] : 1.f, su = p.scale ? p.scale[p.d_ff + r] : 1.f;
-        const float g = total(0, t, l, j) * sg, u = total(1, t, l, j) * su;
+        const float g = total(rt, t, l, j) * sg, u = total(RT + rt, t, l, j) * su;
         p.act[(int64_t)col * p.ldact + r] = f32_to_bf16(silu_f(g) * u);
       } else {
         if (r >= p.N) continue;
-        const float y = total(0, t, l, j) * (p.scale ? p.scale[r] : 1.f);
+        const float y = total(rt, t, l, j) * (p.scale ? p.scale[r] : 1.f);
         float* o = p.out + (int64_t)col * p.ldo + r;
         if (EPI == EPI_RESID)
           *o += y;
@@ -455,13 +457,31 @@ hipError_t gemv_go(const MatmulParams& p, hipStream_t s) {
   return gemv_s<BT, FP8, EPI, KVFP8, 2>(p, n_items, kv, s);
 }
 
+// RT 16-row tiles per work group: the activations each wave loads serve RT times the
+// rows (their L2 reads fall from Bp/16 to Bp/(16 RT) of the weight bytes)
+template <int NT, bool FP8, int EPI, bool KVFP8, int RT>
+hipError_t mfma_rt(const MatmulParams& p, hipStream_t s) {
+  constexpr int NA = (EPI == EPI_SILU ? 2 : 1) * RT;
+  const size_t lds = (size_t)MFMA_WAVES * NA * NT * 64 * 4 * sizeof(float);
+  auto kern = k_gemm_mfma<NT, FP8, EPI, KVFP8, RT>;
+  static bool attr = false;
+  if (!attr && lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int rows = EPI == EPI_SILU ? p.d_ff : p.N;
+  const int grid = (rows + 16 * RT - 1) / (16 * RT);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVE * MFMA_WAVES), lds, s, p);
+  return hipGetLastError();
+}
+
+// one 16-row tile per work group (two measured no faster at batch 32)
 template <int NT, bool FP8, int EPI, bool KVFP8>
 hipError_t mfma_go(const MatmulParams& p, hipStream_t s) {
-  const int rows = EPI == EPI_SILU ? p.d_ff : p.N;
-  const int grid = (rows + 15) / 16;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_mfma<NT, FP8, EPI, KVFP8>), dim3(grid), dim3(WAVE * MFMA_WAVES), 0, s, p);
-  return hipGetLastError();
+  return mfma_rt<NT, FP8, EPI, KVFP8, 1>(p, s);
 }
 
 template <bool FP8, int EPI, bool KVFP8>
