@@ -140,15 +140,35 @@ __global__ __launch_bounds__(WAVE * IPW) void k_gemv_norm(MatmulParams p, int n_
   const u32x4* w1p = W + (int64_t)r1 * KV;
 
   // sum of squares of this thread's elements of each row (issued first: L2 hits that
-  // complete ahead of the weight loads)
+  // complete ahead of the weight loads).  For small batches the thread keeps its h and
+  // gain values in registers, so that x can be written without a second read, which
+  // would queue behind the weight loads.
+  constexpr int NHR = BT <= 2 ? 2 : 1;  // float4 of h per row held per thread (K <= 4096)
+  const bool held = BT <= 2 && K <= NHR * NT * 4;
+  f32x4 hv[BT][NHR], gv[NHR];
   float ss[BT];
 #pragma unroll
   for (int b = 0; b < BT; ++b) ss[b] = 0.f;
-  for (int i = tid * 4; i < K; i += NT * 4) {
+  if (held) {
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      const f32x4 v = gld(reinterpret_cast<const f32x4*>(p.nh + (int64_t)b * K + i));
-      ss[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    for (int j = 0; j < NHR; ++j) {
+      const int i = min((j * NT + tid) * 4, K - 4);  // past K: a re-read that is not counted
+      const bool in = (j * NT + tid) * 4 < K;
+      gv[j] = gld(reinterpret_cast<const f32x4*>(p.ng + i));
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        hv[b][j] = gld(reinterpret_cast<const f32x4*>(p.nh + (int64_t)b * K + i));
+        const f32x4 v = hv[b][j];
+        ss[b] += in ? v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w : 0.f;
+      }
+    }
+  } else {
+    for (int i = tid * 4; i < K; i += NT * 4) {
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        const f32x4 v = gld(reinterpret_cast<const f32x4*>(p.nh + (int64_t)b * K + i));
+        ss[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
     }
   }
   EpiInputs<EPI, BT> ein;
@@ -206,14 +226,25 @@ __global__ __launch_bounds__(WAVE * IPW) void k_gemv_norm(MatmulParams p, int n_
     for (int ww = 0; ww < IPW; ++ww) t += red[ww][b];
     r[b] = 1.0f / sqrtf(t / (float)K + p.eps);
   }
-  for (int i = tid * 4; i < K; i += NT * 4) {
-    const f32x4 g = gld(reinterpret_cast<const f32x4*>(p.ng + i));
+  auto put_x = [&](int i, int b, const f32x4& v, const f32x4& g) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(v.x * r[b] * g.x) | ((uint32_t)f32_to_bf16(v.y * r[b] * g.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(v.z * r[b] * g.z) | ((uint32_t)f32_to_bf16(v.w * r[b] * g.w) << 16);
+    *reinterpret_cast<u32x2*>(xs + b * K + i) = u32x2{lo, hi};
+  };
+  if (held) {
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      const f32x4 v = gld(reinterpret_cast<const f32x4*>(p.nh + (int64_t)b * K + i));
-      const uint32_t lo = (uint32_t)f32_to_bf16(v.x * r[b] * g.x) | ((uint32_t)f32_to_bf16(v.y * r[b] * g.y) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16(v.z * r[b] * g.z) | ((uint32_t)f32_to_bf16(v.w * r[b] * g.w) << 16);
-      *reinterpret_cast<u32x2*>(xs + b * K + i) = u32x2{lo, hi};
+    for (int j = 0; j < NHR; ++j) {
+      const int i = (j * NT + tid) * 4;
+      if (i < K) {
+#pragma unroll
+        for (int b = 0; b < BT; ++b) put_x(i, b, hv[b][j], gv[j]);
+      }
+    }
+  } else {
+    for (int i = tid * 4; i < K; i += NT * 4) {
+      const f32x4 g = gld(reinterpret_cast<const f32x4*>(p.ng + i));
+#pragma unroll
+      for (int b = 0; b < BT; ++b) put_x(i, b, gld(reinterpret_cast<const f32x4*>(p.nh + (int64_t)b * K + i)), g);
     }
   }
   __syncthreads();
