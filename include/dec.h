@@ -185,6 +185,16 @@ typedef enum {
  * Needs a previous dec_step; DEC_E_INVALID for a bad `which` or `layer`. */
 int dec_launch_matmul(dec_ctx* ctx, int which, int layer);
 
+/* Greedy sampling after the last step: token_ids[s] = the index of the largest logit of
+ * sequence s (the first one on ties; NaN never wins), for s < n_seqs of that step,
+ * enqueued on the context's stream.  token_ids: device memory, int32 [n_seqs], 4-byte
+ * aligned, owned by the caller.  The sampling kernel that turns the logits into token
+ * ids on the GPU, so that only the ids need to be copied back ("Kernels, Fusion & CUDA
+ * Graphs", Fix 1 table: sampling; "The serving engine's kernel stack").  Needs a
+ * previous dec_step (DEC_E_STATE otherwise); DEC_E_INVALID for a NULL or misaligned
+ * token_ids. */
+int dec_sample_greedy(dec_ctx* ctx, int32_t* token_ids);
+
 /* Describe the last step (kernels, bucket, path). */
 int dec_get_info(const dec_ctx* ctx, dec_info* out);
 

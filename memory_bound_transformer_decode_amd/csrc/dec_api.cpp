@@ -226,6 +226,7 @@ struct dec_ctx {
   Layout L{};
   bool loaded = false;
   bool failed = false;
+  int last_n = 0;  // sequences of the last enqueued step (0: none yet)
   // weights
   dec_mat embed{}, lm{};
   std::vector<dec_mat> qkv, o, gu, down;
@@ -819,6 +820,7 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   const int per_layer = unfused ? 11 : fused_norm(g, Bp) ? 5 : 7;
   c->info.kernels_per_step = persist ? 1 : 2 + per_layer * L + (slices - 1) * (4 * L + 1);
   c->info.bucket = Bp;
+  c->last_n = n;
   c->info.attn_splits = persist ? n_split_persistent(g, Bp) : n_split_for(g, Bp);
   c->info.used_mfma = mfma ? 1 : 0;
   c->info.persistent = persist ? 1 : 0;
@@ -842,6 +844,16 @@ int dec_launch_matmul(dec_ctx* c, int which, int layer) {
     if (which == DEC_MAT_LM_HEAD) ng = c->final_norm;
   }
   hipError_t e = run_matmul(c, which, which == DEC_MAT_LM_HEAD ? 0 : layer, c->info.bucket, c->stream, ng);
+  if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
+  return DEC_OK;
+}
+
+int dec_sample_greedy(dec_ctx* c, int32_t* token_ids) {
+  if (!c || !token_ids) return fail(DEC_E_INVALID, "ctx or token_ids is NULL");
+  if (((uintptr_t)token_ids & 3u) != 0) return fail(DEC_E_INVALID, "token_ids is not 4-byte aligned");
+  if (c->failed) return fail(DEC_E_STATE, "context has failed; destroy it");
+  if (!c->loaded || c->last_n <= 0) return fail(DEC_E_STATE, "dec_sample_greedy needs a previous dec_step");
+  hipError_t e = dec::launch_argmax(c->logits, c->cfg.vocab, c->cfg.vocab, c->last_n, token_ids, c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
   return DEC_OK;
 }

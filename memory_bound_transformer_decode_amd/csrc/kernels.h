@@ -131,6 +131,9 @@ hipError_t launch_rope_kv(const MatmulParams& p, const float* qkv, bool kv_fp8, 
 hipError_t launch_silu_mul(const float* gu, int d_ff, int Bp, uint16_t* a, int lda, hipStream_t s);
 hipError_t launch_add(float* h, const float* delta, int n, hipStream_t s);
 
+// out[r] = argmax over v < V of logits[r][v] (first index of the largest value), r < n
+hipError_t launch_argmax(const float* logits, int ldl, int V, int n, int32_t* out, hipStream_t s);
+
 // (cos, sin)(p * theta^(-2i/dh)) for p < max_seq, i < dh/2, evaluated in double
 hipError_t launch_rope_table(float2* rope, int max_seq, int dh, double theta, hipStream_t s);
 

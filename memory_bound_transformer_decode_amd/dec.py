@@ -62,7 +62,8 @@ class DecError(RuntimeError):
 
 
 EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_load_weights", "dec_step", "dec_set_flags",
-           "dec_get_info", "dec_destroy", "dec_last_error", "dec_bw_probe", "dec_launch_matmul")
+           "dec_get_info", "dec_destroy", "dec_last_error", "dec_bw_probe", "dec_launch_matmul",
+           "dec_sample_greedy")
 MAT_QKV, MAT_O, MAT_GATE_UP, MAT_DOWN, MAT_LM_HEAD = 0, 1, 2, 3, 4
 
 _lib = None
@@ -97,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dec_last_error.restype = ctypes.c_char_p
     lib.dec_bw_probe.argtypes = [c_void_p, c_size_t, c_int, c_void_p, POINTER(c_double)]
     lib.dec_bw_probe.restype = c_int
+    lib.dec_sample_greedy.argtypes = [c_void_p, c_void_p]
+    lib.dec_sample_greedy.restype = c_int
     lib.dec_launch_matmul.argtypes = [c_void_p, c_int, c_int]
     lib.dec_launch_matmul.restype = c_int
     _lib = lib
@@ -171,6 +174,7 @@ class Decoder:
         self.workspace = torch.empty(ws_n, dtype=torch.uint8, device=self.device)
         self.logits = torch.empty(max_batch, model.vocab, dtype=torch.float32, device=self.device)
         self.stream = torch.cuda.current_stream(self.device)
+        self._last_n = 0
         ctx = c_void_p()
         _check(self.lib.dec_create(ctypes.byref(self.cfg), c_void_p(self.stream.cuda_stream),
                                    c_void_p(kv_pool.data_ptr()), c_void_p(self.workspace.data_ptr()),
@@ -200,7 +204,15 @@ class Decoder:
         P = POINTER(c_int32)
         args = DecStepArgs(n, ids.ctypes.data_as(P), lens.ctypes.data_as(P), bt.ctypes.data_as(P))
         _check(self.lib.dec_step(self.ctx, ctypes.byref(args)))
+        self._last_n = n
         return self.logits[:n]
+
+    def sample_greedy(self) -> torch.Tensor:
+        """Enqueue greedy sampling of the last step: int32 [n] token ids on the device."""
+        n = self._last_n
+        out = torch.empty(n, dtype=torch.int32, device=self.device)
+        _check(self.lib.dec_sample_greedy(self.ctx, c_void_p(out.data_ptr())))
+        return out
 
     def launch_matmul(self, which: int, layer: int = 0) -> None:
         """Enqueue one matrix kernel of the step alone (for timing; clobbers intermediates)."""

@@ -106,6 +106,7 @@ def test_null_context_calls():
     assert lib.dec_load_weights(None, None) == dec.DEC_E_INVALID
     assert lib.dec_get_info(None, None) == dec.DEC_E_INVALID
     assert lib.dec_set_flags(None, 0) == dec.DEC_E_INVALID
+    assert lib.dec_sample_greedy(None, None) == dec.DEC_E_INVALID
     assert lib.dec_destroy(None) == dec.DEC_OK
     out = ctypes.c_double()
     assert lib.dec_bw_probe(None, 16, 1, None, ctypes.byref(out)) == dec.DEC_E_INVALID

@@ -13,7 +13,7 @@ import torch
 
 from memory_bound_transformer_decode_amd import synth
 
-from harness import Case, assert_ok, log, make_case, require_gpu, run_parity
+from harness import Case, assert_ok, log, make_case, require_gpu, run_parity, tol_of
 
 pytestmark = pytest.mark.gpu
 
@@ -143,6 +143,55 @@ def test_mini_model_persistent_plan(dec, w, kv, B):
     ids = synth.make_token_ids(cfg, 3, B, seed=12)
     log(f"mini persistent {w}/{kv} B={B}")
     assert_ok(run_parity(case, ids, flags=dec.FLAG_PERSISTENT), cfg)
+
+
+@pytest.mark.parametrize("B", [1, 5, 24])
+def test_greedy_sampling(dec, B):
+    """Greedy sampling on the device: bit-exact against the argmax (first index) of the
+    same logits, and equal to the oracle's argmax where the oracle's top-2 margin is
+    above the logit tolerance."""
+    from oracle import decoder as OD
+    from oracle import inputs as OI
+    cfg = fmt(MINI, "bf16", "bf16")
+    rng = np.random.default_rng(90 + B)
+    case = make_case(cfg, ctx_mix(B, rng), 128, seed=16)
+    ids = synth.make_token_ids(cfg, 1, B, seed=16)[0]
+    d = dec.Decoder(case.cfg, case.weights, num_blocks=case.num_blocks, max_batch=dec.ladder_bucket(B),
+                    max_seq_len=case.max_seq_len, kv_pool=case.pool.clone())
+    z = d.step(ids, case.ctx_lens, case.block_tables[:B]).clone()
+    tok = d.sample_greedy().cpu().numpy()
+    zc = z.cpu().numpy()
+    d.close()
+    assert tok.dtype == np.int32 and tok.shape == (B,)
+    assert np.array_equal(tok, np.argmax(zc, axis=1).astype(np.int32))
+    m = OI.model(case.weights)
+    cache = OI.cache(cfg, synth.kv_codes_numpy(case.pool))
+    zo = OD.decode_step(m, cache, ids, case.ctx_lens, case.block_tables[:B])
+    tol = tol_of(cfg)
+    for r in range(B):
+        top = np.argsort(zo[r])[-2:]
+        if zo[r][top[1]] - zo[r][top[0]] > tol * (zo[r].max() - zo[r].min()):
+            assert tok[r] == top[1]
+
+
+def test_greedy_sampling_ties_and_errors(dec):
+    """First index on ties, NaN never wins; sampling before any step is refused."""
+    cfg = fmt(MINI, "bf16", "bf16")
+    case = make_case(cfg, [5], 128, seed=17)
+    d = dec.Decoder(case.cfg, case.weights, num_blocks=case.num_blocks, max_batch=1,
+                    max_seq_len=case.max_seq_len, kv_pool=case.pool.clone())
+    with pytest.raises(dec.DecError):
+        d.sample_greedy()
+    d.step([1], [5], case.block_tables[:1])
+    torch.cuda.synchronize()
+    V = cfg.vocab
+    row = torch.full((V,), -3.0, dtype=torch.float32)
+    row[7] = 2.0
+    row[V - 3] = 2.0  # tie: the first one wins
+    row[11] = float("nan")
+    d.logits[0].copy_(row.cuda())
+    assert int(d.sample_greedy().cpu()[0]) == 7
+    d.close()
 
 
 @pytest.mark.parametrize("w,kv", [("bf16", "bf16"), ("fp8", "fp8")])
