@@ -153,6 +153,7 @@ def run_batch(wl, B: int, steps: int, warmup: int, seed: int, want_eager: bool, 
         plans = {}
         for name, flags in (("persistent_graph", dec.FLAG_PERSISTENT),
                             ("multi_kernel_eager", dec.FLAG_EAGER),
+                            ("fused_qkv_attention_graph", dec.FLAG_FUSED_QKV_ATTN),
                             ("unfused_graph", dec.FLAG_UNFUSED),
                             ("unfused_eager", dec.FLAG_UNFUSED | dec.FLAG_EAGER)):
             w2, _ = timed(flags)

@@ -72,9 +72,13 @@ enum {
                                 KV write, SiLU x mul and residual adds as kernels of their own */
   DEC_FLAG_NO_MFMA = 4u,     /* matrix-vector kernels at every batch size (no MFMA tiles) */
   DEC_FLAG_CAPTURE_ALL = 8u, /* capture every batch bucket at the first step instead of lazily */
-  DEC_FLAG_PERSISTENT = 16u  /* a padded batch of <= 8 whose layer input fits in LDS runs the
+  DEC_FLAG_PERSISTENT = 16u, /* a padded batch of <= 8 whose layer input fits in LDS runs the
                                 whole step as one persistent kernel with grid barriers; without
                                 it (the default) every batch runs one kernel per fused op */
+  DEC_FLAG_FUSED_QKV_ATTN = 32u /* batches of <= 8 with <= 4 query heads per kv head: QKV
+                                projection and attention in one kernel, its attention work groups
+                                waiting (bounded) for their kv head's q/k/v rows; measured slower
+                                than the two kernels of the default plan */
 };
 
 typedef struct dec_config {

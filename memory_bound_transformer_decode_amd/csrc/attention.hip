@@ -31,7 +31,8 @@ namespace dec {
 
 template <int DH, bool FP8, int G, int NW>
 __global__ __launch_bounds__(WAVE * NW) void k_attn_split(AttnParams p) {
-  attn_unit<DH, FP8, G, NW>(p, blockIdx.x, blockIdx.y, blockIdx.z);
+  __shared__ AttnSmem<DH, G, NW> S;
+  attn_unit<DH, FP8, G, NW>(p, blockIdx.x, blockIdx.y, blockIdx.z, S);
 }
 
 namespace {

@@ -1,6 +1,8 @@
 // Split-K paged GQA decode attention: the work of one work group (shared by the
-// attention kernel and the fused attention + O-projection kernel).
+// attention kernel and the QKV + attention kernel).
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -14,25 +16,72 @@ constexpr int MAX_SPLIT = 64;  // splits per (sequence, kv head); the host keeps
 #endif
 constexpr int ATTN_WAVES = DEC_ATTN_WAVES;  // waves per work group
 
+// LDS of one attention work group
+template <int DH, int G, int NW>
+struct AttnSmem {
+  float q[G][DH];              // the group's scaled queries (QKV + attention kernel)
+  float sm[NW][G], sl[NW][G];  // per-wave running max and sum
+  float so[NW][G][DH];         // per-wave output
+  float cm[G][MAX_SPLIT], cl[G][MAX_SPLIT], cM[G];  // the combine's partial max and sum
+  int last;
+};
+
 // K and V of one block of one kv head for this lane: NPASS 16-byte loads each
-// (a lane holds 8 cache elements of a row: 16 bytes of bf16 or 8 bytes of E4M3, in .x .y)
+// (a lane holds 8 cache elements of a row: 16 bytes of bf16 or 8 bytes of E4M3, in .x .y).
+// coh: device-coherent loads (the block holds a slot written earlier in the same kernel).
 template <int DH, bool FP8, int NPASS, int PPP>
 __device__ __forceinline__ void attn_load(const uint8_t* pool, int64_t kbase, int64_t vbase, int prow, int eoff,
-                                          u32x4 (&kr)[NPASS], u32x4 (&vr)[NPASS]) {
+                                          u32x4 (&kr)[NPASS], u32x4 (&vr)[NPASS], bool coh = false) {
   constexpr int ESZ = FP8 ? 1 : 2;
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int64_t off = (int64_t)(ps * PPP + prow) * DH + eoff;
     if (FP8) {
-      const u32x2 k2 = gld(reinterpret_cast<const u32x2*>(pool + (kbase + off)));
-      const u32x2 v2 = gld(reinterpret_cast<const u32x2*>(pool + (vbase + off)));
+      const u32x2* kp = reinterpret_cast<const u32x2*>(pool + (kbase + off));
+      const u32x2* vp = reinterpret_cast<const u32x2*>(pool + (vbase + off));
+      u32x2 k2, v2;
+      if (coh) {
+        const uint64_t a = cld(reinterpret_cast<const uint64_t*>(kp)), b = cld(reinterpret_cast<const uint64_t*>(vp));
+        k2 = u32x2{(uint32_t)a, (uint32_t)(a >> 32)};
+        v2 = u32x2{(uint32_t)b, (uint32_t)(b >> 32)};
+      } else {
+        k2 = gld(kp);
+        v2 = gld(vp);
+      }
       kr[ps] = u32x4{k2.x, k2.y, 0u, 0u};
       vr[ps] = u32x4{v2.x, v2.y, 0u, 0u};
+    } else if (coh) {
+      kr[ps] = cld16(pool + (kbase + off) * ESZ);
+      vr[ps] = cld16(pool + (vbase + off) * ESZ);
     } else {
       kr[ps] = gld16(pool + (kbase + off) * ESZ);
       vr[ps] = gld16(pool + (vbase + off) * ESZ);
     }
   }
+}
+
+// Wait (thread 0, bounded) until the work groups that write kv head c's q, k and v in the
+// same kernel have all counted themselves in ready[c] (which the next kernel of the step
+// clears).  A wait past the time bound sets the error flags and lets the work group go on
+// (its results are then not used).
+__device__ __forceinline__ void attn_wait_ready(const AttnParams& p, int c) {
+  if (threadIdx.x == 0) {
+    const unsigned* ready = p.ready + (int64_t)c * COUNTER_STRIDE;
+    if (cld(ready) < p.ready_target) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      // the shared error flag is polled only now and then (every poll of a shared line
+      // queues behind the others)
+      for (unsigned it = 1; cld(ready) < p.ready_target; ++it) {
+        __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > p.timeout_ticks || ((it & 1023u) == 0 && cld(p.err_dev) != 0u)) {
+          cst(p.err_dev, 1u);
+          __hip_atomic_store(p.err_host, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // the 8 cache elements a lane holds, as fp32
@@ -49,9 +98,10 @@ __device__ __forceinline__ void attn_widen(const u32x4& r, float (&f)[8]) {
   }
 }
 
-// online-softmax update of the G heads' (m, l, o) with one block (positions blk*16 ..)
-template <int DH, bool FP8, int G, int NPASS, int PPP, int LPP, int EPL>
-__device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const float (&qv)[G][EPL],
+// online-softmax update of the G heads' (m, l, o) with one block (positions blk*16 ..);
+// qf(h, e): element e of the lane's 8 scaled query elements of head h
+template <int DH, bool FP8, int G, int NPASS, int PPP, int LPP, int EPL, typename QF>
+__device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const QF& qf,
                                             const u32x4 (&kr)[NPASS], const u32x4 (&vr)[NPASS], float (&m)[G],
                                             float (&l)[G], float (&o)[G][EPL]) {
   float sc[NPASS][G];
@@ -66,7 +116,7 @@ __device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const f
     for (int h = 0; h < G; ++h) {
       float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s = fmaf(qv[h][e], kf[e], s);
+      for (int e = 0; e < EPL; ++e) s = fmaf(qf(h, e), kf[e], s);
 #pragma unroll
       for (int off = 1; off < LPP; off <<= 1) s += __shfl_xor(s, off);
       sc[ps][h] = valid ? s : -INFINITY;
@@ -87,21 +137,32 @@ __device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const f
     for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      const float pr = exp2f(sc[ps][h] - mn);
-      l[h] += pr;
-      float vf[EPL];
-      attn_widen<FP8>(vr[ps], vf);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pr, vld[ps] ? vf[e] : 0.f, o[h][e]);
+      sc[ps][h] = exp2f(sc[ps][h] - mn);  // the probability, in place of the score
+      l[h] += sc[ps][h];
     }
+  }
+  // each V row is widened once and serves every head (one row's elements live at a time)
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    float vf[EPL];
+    attn_widen<FP8>(vr[ps], vf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) vf[e] = vld[ps] ? vf[e] : 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(sc[ps][h], vf[e], o[h][e]);
   }
 }
 
 // One work group computes one (split, kv head c, sequence b) unit of attention.  With
 // one split it writes o; otherwise it writes its partial, and the last split of the
 // group to arrive combines.  o is written device-coherently.
-template <int DH, bool FP8, int G, int NW>
-__device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c, int b) {
+// FUSED: q and the new token's K/V are written by other work groups of the same kernel.
+// The block ids and the first block (unless it holds the new token) are loaded before
+// waiting for them; q and the new token's block are then read device-coherently.
+template <int DH, bool FP8, int G, int NW, bool FUSED = false>
+__device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c, int b, AttnSmem<DH, G, NW>& S) {
   constexpr int EPL = 8;             // cache elements per lane per row
   constexpr int LPP = DH / EPL;      // lanes per position row
   constexpr int PPP = WAVE / LPP;    // positions per pass
@@ -120,84 +181,129 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
   const int my_blk = blk0 + wave + lane * NW;
   const int my_phys = lane < nb ? gld(p.bt + (int64_t)b * p.bps + my_blk) : 0;
 
-  const float qscale = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
-  float qv[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float* qh = p.q + ((int64_t)b * p.Hq + c * G + h) * DH + eoff;
-#pragma unroll
-    for (int e = 0; e < EPL; e += 4) {
-      const f32x4 t = gld(reinterpret_cast<const f32x4*>(qh + e));
-      qv[h][e] = t.x * qscale;
-      qv[h][e + 1] = t.y * qscale;
-      qv[h][e + 2] = t.z * qscale;
-      qv[h][e + 3] = t.w * qscale;
-    }
-  }
-
-  float m[G], l[G], o[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
-  }
-
   const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
-  auto bases = [&](int i, int64_t& kb, int64_t& vb) {
+  // loads of the wave's i-th block (coherent for the block of the new token when FUSED)
+  auto load_blk = [&](int i, u32x4 (&kr)[NPASS], u32x4 (&vr)[NPASS]) {
     const int phys = __shfl(my_phys, i);
-    kb = kv_offset(p.layer, 0, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
-    vb = kv_offset(p.layer, 1, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
+    const int64_t kb = kv_offset(p.layer, 0, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
+    const int64_t vb = kv_offset(p.layer, 1, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
+    const bool coh = FUSED && blk0 + wave + i * NW == nblk - 1;
+    attn_load<DH, FP8, NPASS, PPP>(pool, kb, vb, prow, eoff, kr, vr, coh);
   };
-  if (nb > 0 && G > 6) {
-    // wide groups: the per-head state leaves no room for a second block in registers
-    u32x4 ka[NPASS], va[NPASS];
-    int64_t kbase, vbase;
-    for (int i = 0; i < nb; ++i) {
-      bases(i, kbase, vbase);
-      attn_load<DH, FP8, NPASS, PPP>(pool, kbase, vbase, prow, eoff, ka, va);
-      attn_update<DH, FP8, G, NPASS, PPP, LPP, EPL>(blk0 + wave + i * NW, ntok, prow, qv, ka, va, m, l, o);
+  u32x4 ka[NPASS], va[NPASS];
+  bool first = false;  // block 0 already in ka/va
+  if (FUSED) {
+    if (nb > 0 && blk0 + wave != nblk - 1) {
+      load_blk(0, ka, va);
+      first = true;
     }
-  } else if (nb > 0) {
-    // two blocks in flight: the next block's loads are issued before this one's math
-    u32x4 ka[NPASS], va[NPASS], kb2[NPASS], vb2[NPASS];
-    int64_t kbase, vbase;
-    bases(0, kbase, vbase);
-    attn_load<DH, FP8, NPASS, PPP>(pool, kbase, vbase, prow, eoff, ka, va);
-    for (int i = 0; i < nb; i += 2) {
-      bases(min(i + 1, nb - 1), kbase, vbase);
-      attn_load<DH, FP8, NPASS, PPP>(pool, kbase, vbase, prow, eoff, kb2, vb2);
-      attn_update<DH, FP8, G, NPASS, PPP, LPP, EPL>(blk0 + wave + i * NW, ntok, prow, qv, ka, va, m, l, o);
-      if (i + 1 >= nb) break;
-      bases(min(i + 2, nb - 1), kbase, vbase);
-      attn_load<DH, FP8, NPASS, PPP>(pool, kbase, vbase, prow, eoff, ka, va);
-      attn_update<DH, FP8, G, NPASS, PPP, LPP, EPL>(blk0 + wave + (i + 1) * NW, ntok, prow, qv, kb2, vb2, m, l, o);
+    attn_wait_ready(p, c);
+    // the block of the new token: its loads go out together with q's
+    if (nb > 0 && !first) {
+      load_blk(0, ka, va);
+      first = true;
     }
   }
 
-  // sum l and o over the position rows of the wave (lanes with the same eoff)
+  const float qscale = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
+  // the queries: in registers, or (FUSED, where registers are scarcer than in the
+  // attention kernel: the kernel's register budget is shared with the product) in LDS
+  float qv[FUSED ? 1 : G][EPL];
+  if (FUSED) {
+    const float* qg = p.q + ((int64_t)b * p.Hq + c * G) * DH;
+    for (int i = threadIdx.x * 4; i < G * DH; i += NW * WAVE * 4) {
+      const f32x4 t = cld_f4(qg + i);
+      float* d = &S.q[0][0] + i;
+      d[0] = t.x * qscale;
+      d[1] = t.y * qscale;
+      d[2] = t.z * qscale;
+      d[3] = t.w * qscale;
+    }
+    __syncthreads();
+  } else {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < G; ++h) {
+      const float* qh = p.q + ((int64_t)b * p.Hq + c * G + h) * DH + eoff;
 #pragma unroll
-    for (int off = LPP; off < WAVE; off <<= 1) {
-      l[h] += __shfl_xor(l[h], off);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], off);
+      for (int e = 0; e < EPL; e += 4) {
+        const f32x4 t = gld(reinterpret_cast<const f32x4*>(qh + e));
+        qv[h][e] = t.x * qscale;
+        qv[h][e + 1] = t.y * qscale;
+        qv[h][e + 2] = t.z * qscale;
+        qv[h][e + 3] = t.w * qscale;
+      }
     }
   }
+  auto qf = [&](int h, int e) -> float { return FUSED ? S.q[h][eoff + e] : qv[FUSED ? 0 : h][e]; };
 
-  __shared__ float sm[NW][G], sl[NW][G];
-  __shared__ float so[NW][G][DH];
-  if (lane == 0) {
+  auto& sm = S.sm;
+  auto& sl = S.sl;
+  auto& so = S.so;
+  // The heads [H0, H0 + GH): running state, blocks, then the wave's partial into LDS.
+  // FUSED with g = 4 takes the heads two at a time, which keeps the attention state within
+  // the register budget the product part leaves; a wave with one block keeps it in ka/va
+  // for the second pair.
+  constexpr int GH = (FUSED && G == 4) ? 2 : G;
+  static_assert(GH == G || G == 2 * GH, "one or two chunks of heads");
+  auto chunk = [&](auto h0c) {
+    constexpr int H0 = decltype(h0c)::value;
+    float m[GH], l[GH], o[GH][EPL];
 #pragma unroll
-    for (int h = 0; h < G; ++h) { sm[wave][h] = m[h]; sl[wave][h] = l[h]; }
-  }
-  if (prow == 0) {
+    for (int h = 0; h < GH; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+    }
+    auto qc = [&](int h, int e) -> float { return qf(H0 + h, e); };
+
+    if (nb > 0 && (G > 6 || FUSED)) {
+      // wide groups, or the QKV + attention kernel: no room for a second block in registers
+      for (int i = 0; i < nb; ++i) {
+        // ka/va hold block 0 only before the first chunk moves on, or when it is the only one
+        const bool held = H0 == 0 ? i == 0 && first : nb == 1;
+        if (!held) load_blk(i, ka, va);
+        attn_update<DH, FP8, GH, NPASS, PPP, LPP, EPL>(blk0 + wave + i * NW, ntok, prow, qc, ka, va, m, l, o);
+      }
+    } else if (nb > 0) {
+      // two blocks in flight: the next block's loads are issued before this one's math
+      u32x4 kb2[NPASS], vb2[NPASS];
+      if (!first) load_blk(0, ka, va);
+      for (int i = 0; i < nb; i += 2) {
+        load_blk(min(i + 1, nb - 1), kb2, vb2);
+        attn_update<DH, FP8, GH, NPASS, PPP, LPP, EPL>(blk0 + wave + i * NW, ntok, prow, qc, ka, va, m, l, o);
+        if (i + 1 >= nb) break;
+        load_blk(min(i + 2, nb - 1), ka, va);
+        attn_update<DH, FP8, GH, NPASS, PPP, LPP, EPL>(blk0 + wave + (i + 1) * NW, ntok, prow, qc, kb2, vb2, m, l,
+                                                       o);
+      }
+    }
+
+    // sum l and o over the position rows of the wave (lanes with the same eoff)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) so[wave][h][eoff + e] = o[h][e];
+    for (int h = 0; h < GH; ++h) {
+#pragma unroll
+      for (int off = LPP; off < WAVE; off <<= 1) {
+        l[h] += __shfl_xor(l[h], off);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], off);
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < GH; ++h) { sm[wave][H0 + h] = m[h]; sl[wave][H0 + h] = l[h]; }
+    }
+    if (prow == 0) {
+#pragma unroll
+      for (int h = 0; h < GH; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) so[wave][H0 + h][eoff + e] = o[h][e];
+    }
+  };
+  chunk(std::integral_constant<int, 0>{});
+  if constexpr (GH < G) {
+    __builtin_amdgcn_sched_barrier(0);
+    chunk(std::integral_constant<int, GH>{});
   }
   __syncthreads();
   const bool single = p.n_split == 1;
@@ -228,7 +334,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
 
   // arrival: the partial stores of every wave complete before this work group counts
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __shared__ int last;
+  int& last = S.last;
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned* cnt = p.cnt + (int64_t)b * p.Hkv + c;
@@ -240,7 +346,9 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
   if (!last) return;
 
   // combine the n_split partials of the group's G heads
-  __shared__ float cm[G][MAX_SPLIT], cl[G][MAX_SPLIT], cM[G];
+  auto& cm = S.cm;
+  auto& cl = S.cl;
+  auto& cM = S.cM;
   for (int idx = threadIdx.x; idx < G * p.n_split; idx += NW * WAVE) {
     const int h = idx / p.n_split, sp = idx % p.n_split;
     const int64_t row = ((int64_t)b * p.Hq + c * G + h) * p.n_split + sp;

@@ -47,9 +47,9 @@ constexpr int ATTN_TARGET_GROUPS = DEC_ATTN_GROUPS;  // work groups per attentio
 constexpr int ATTN_BLOCKS_PER_SPLIT = 8;  // context blocks one attention work group takes alone
 constexpr int ATTN_WAVES_ = 8;            // waves per attention work group (attention.hip)
 constexpr int WAVE_ = 64;
-constexpr uint32_t KNOWN_FLAGS =
-    DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL | DEC_FLAG_PERSISTENT;
-constexpr int N_MODES = 8;  // plan-changing flag combinations (UNFUSED, NO_MFMA, PERSISTENT)
+constexpr uint32_t KNOWN_FLAGS = DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL |
+                                 DEC_FLAG_PERSISTENT | DEC_FLAG_FUSED_QKV_ATTN;
+constexpr int N_MODES = 16;  // plan-changing flag combinations (UNFUSED, NO_MFMA, PERSISTENT, FUSED_QKV_ATTN)
 constexpr int PERSIST_MAX_BATCH = 8;
 constexpr size_t PERSIST_XS_BUDGET = 128 * 1024;  // LDS for one layer input block
 constexpr int PERSIST_ASSUMED_WAVES = 256 * 8;    // sizes the attention split count
@@ -57,7 +57,7 @@ constexpr double BARRIER_TIMEOUT_S = 0.25;
 
 int mode_of(uint32_t flags) {
   return (int)(((flags & DEC_FLAG_UNFUSED) ? 1 : 0) | ((flags & DEC_FLAG_NO_MFMA) ? 2 : 0) |
-               ((flags & DEC_FLAG_PERSISTENT) ? 4 : 0));
+               ((flags & DEC_FLAG_PERSISTENT) ? 4 : 0) | ((flags & DEC_FLAG_FUSED_QKV_ATTN) ? 8 : 0));
 }
 
 int bucket_index(int n) {
@@ -108,6 +108,7 @@ struct Layout {
   size_t h, x, q, part_o, part_ml, o, a, rope;
   size_t uf;                           // unfused step: fp32 product rows [MB][max(N)]
   size_t mats, bar, attn_cnt, err;     // persistent-step state
+  size_t ready;                        // QKV + attention kernel: [n_kv_heads] counters, 256 B apart
   size_t total;
 };
 
@@ -162,6 +163,8 @@ Layout layout_of(const dec_config& c) {
   off = align256(off + MB * c.n_q_heads * 4);
   L.err = off;
   off = align256(off + 4);
+  L.ready = off;
+  off = align256(off + (size_t)c.n_kv_heads * dec::COUNTER_STRIDE * 4);
   L.total = off;
   return L;
 }
@@ -305,6 +308,9 @@ dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) 
       p.ldx = Hq * dh;
       p.out = h;
       p.ldo = d;
+      // clears the wait counters of the QKV + attention kernel that precedes it
+      p.rearm = ws_ptr<unsigned>(c, c->L.ready);
+      p.n_rearm = Hkv;
       *epi = dec::EPI_RESID;
       break;
     case DEC_MAT_GATE_UP:  // a = silu(W_gate x) * (W_up x)
@@ -361,6 +367,17 @@ hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const
 // Batches of <= 8 rows run matrix-vector kernels that normalize their own input in
 // LDS ([Bp][d] bf16 must fit in 128 KB)
 bool fused_norm(const dec_config& g, int Bp) { return Bp <= 8 && (size_t)Bp * g.d_model * 2 <= 128 * 1024; }
+
+// QKV projection and attention in one kernel (opt-in): the norm-fused batches, for head
+// sizes whose QKV work groups each lie in one head, groups of up to QKV_ATTN_MAX_GROUP
+// query heads, and while the product's activations or the attention state fit the LDS
+// of a work group
+bool fuse_qkv_attn(const dec_ctx* c, int Bp) {
+  const dec_config& g = c->cfg;
+  return fused_norm(g, Bp) && (g.flags & DEC_FLAG_FUSED_QKV_ATTN) && g.d_head % (2 * dec::QKV_ATTN_IPW) == 0 &&
+         (g.d_head == 64 || g.d_head == 128) && g.n_q_heads / g.n_kv_heads <= dec::QKV_ATTN_MAX_GROUP &&
+         dec::qkv_attn_lds_bytes(Bp, g.d_model, g.n_q_heads, g.n_kv_heads, g.d_head) <= 160 * 1024 - 1024;
+}
 
 bool use_persistent(const dec_ctx* c, int Bp) {
   return (c->cfg.flags & DEC_FLAG_PERSISTENT) && !(c->cfg.flags & DEC_FLAG_UNFUSED) && persistent_fits(c->cfg, Bp);
@@ -545,16 +562,36 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
 
   // the matrix-vector kernels normalize their own input (no RMSNorm kernels)
   const bool fn = fused_norm(g, Bp);
+  const bool fqa = fuse_qkv_attn(c, Bp);
+  if (fqa) {
+    unsigned* ready = ws_ptr<unsigned>(c, c->L.ready);
+    ap.ready = ready;
+    ap.ready_target = dec::qkv_attn_ready_target(Hq, Hkv, dh);
+    ap.err_dev = ws_ptr<unsigned>(c, c->L.err);
+    ap.err_host = c->err_host_dev;
+    ap.timeout_ticks = c->timeout_ticks;
+  }
   for (int l = 0; l < g.n_layers; ++l) {
     const float* an = c->attn_norm + (size_t)l * d;
     if (l > 0 && !fn) {
       np.gain = an;
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
-    if ((e = run_matmul(c, DEC_MAT_QKV, l, Bp, s, fn ? an : nullptr)) != hipSuccess) return e;
-    // attention over positions 0..p
     ap.layer = l;
-    if ((e = dec::launch_attention(ap, kvfp8, s)) != hipSuccess) return e;
+    if (fqa) {
+      // [q; k; v] = W_qkv RMSNorm(h) g_attn with RoPE and the cache write, and attention
+      // over positions 0..p, in one kernel
+      int epi = 0;
+      dec::MatmulParams mp = matmul_params(c, DEC_MAT_QKV, l, Bp, &epi);
+      mp.nh = h;
+      mp.ng = an;
+      mp.eps = g.rms_eps;
+      if ((e = dec::launch_qkv_attn(mp, ap, wfp8, kvfp8, s)) != hipSuccess) return e;
+    } else {
+      if ((e = run_matmul(c, DEC_MAT_QKV, l, Bp, s, fn ? an : nullptr)) != hipSuccess) return e;
+      // attention over positions 0..p
+      if ((e = dec::launch_attention(ap, kvfp8, s)) != hipSuccess) return e;
+    }
     if ((e = run_matmul(c, DEC_MAT_O, l, Bp, s)) != hipSuccess) return e;
     // x = RMSNorm(h) g_mlp
     const float* mn = c->mlp_norm + (size_t)l * d;
@@ -743,7 +780,8 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   if (!c->loaded) return fail(DEC_E_STATE, "dec_step before dec_load_weights");
   if (*reinterpret_cast<volatile unsigned*>(c->err_host) != 0u) {
     c->failed = true;
-    return fail(DEC_E_HIP, "a grid-wide barrier of an earlier step timed out; the context is unusable");
+    return fail(DEC_E_HIP, "a bounded wait of an earlier step (grid barrier or attention wait) timed out; "
+                            "the context is unusable");
   }
   const dec_config& g = c->cfg;
   const int n = a->n_seqs;
@@ -814,10 +852,10 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   const int slices = (!mfma && Bp > 8) ? Bp / 8 : 1;
   const int L = g.n_layers;
   // per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the
-  // matrix-vector kernels fuse them; unfused: also RoPE + KV write, SiLU x mul and two
-  // residual adds
+  // matrix-vector kernels fuse them (and QKV + attention as one kernel where
+  // fuse_qkv_attn holds); unfused: also RoPE + KV write, SiLU x mul and two residual adds
   const bool unfused = (g.flags & DEC_FLAG_UNFUSED) != 0;
-  const int per_layer = unfused ? 11 : fused_norm(g, Bp) ? 5 : 7;
+  const int per_layer = unfused ? 11 : fuse_qkv_attn(c, Bp) ? 4 : fused_norm(g, Bp) ? 5 : 7;
   c->info.kernels_per_step = persist ? 1 : 2 + per_layer * L + (slices - 1) * (4 * L + 1);
   c->info.bucket = Bp;
   c->last_n = n;

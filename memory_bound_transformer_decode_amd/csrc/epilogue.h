@@ -104,8 +104,9 @@ __device__ __forceinline__ void epi_fetch(const MatmulParams& p, int r0, int r1,
   }
 }
 
-// pair_epilogue with the inputs fetched by epi_fetch (per-op kernels only: plain stores)
-template <int EPI, int BT>
+// pair_epilogue with the inputs fetched by epi_fetch; plain stores, or device-coherent
+// ones (COH) where a later work group of the same kernel reads the result
+template <int EPI, int BT, bool COH = false>
 __device__ __forceinline__ void pair_epilogue_pre(const MatmulParams& p, bool kv_fp8, const EpiInputs<EPI, BT>& in,
                                                   int b, int item, int r0, int r1, float a0, float a1) {
   float y0 = a0 * in.s0, y1 = a1 * in.s1;
@@ -130,7 +131,11 @@ __device__ __forceinline__ void pair_epilogue_pre(const MatmulParams& p, bool kv
     }
     if (r0 < qrows) {
       const int j = r0 / dh, e = r0 % dh;
-      gst(reinterpret_cast<f32x2*>(p.q + ((int64_t)b * p.Hq + j) * dh + e), f32x2{y0, y1});
+      float* qp = p.q + ((int64_t)b * p.Hq + j) * dh + e;
+      if (COH)
+        cst_f2(qp, y0, y1);
+      else
+        gst(reinterpret_cast<f32x2*>(qp), f32x2{y0, y1});
       return;
     }
     const int pos = in.pos[b];
@@ -141,10 +146,18 @@ __device__ __forceinline__ void pair_epilogue_pre(const MatmulParams& p, bool kv
     const int64_t off = kv_offset(p.layer, kv, in.blk[b], c, pos % KV_BLOCK, e, p.num_blocks, p.Hkv, dh);
     if (kv_fp8) {
       const uint32_t c0 = f32_to_e4m3(y0), c1 = f32_to_e4m3(y1);
-      gst(reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.pool) + off), (uint16_t)(c0 | (c1 << 8)));
+      uint16_t* kp = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.pool) + off);
+      if (COH)
+        cst(kp, (uint16_t)(c0 | (c1 << 8)));
+      else
+        gst(kp, (uint16_t)(c0 | (c1 << 8)));
     } else {
       const uint32_t w = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
-      gst(reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.pool) + off), w);
+      uint32_t* kp = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.pool) + off);
+      if (COH)
+        cst(kp, w);
+      else
+        gst(kp, w);
     }
   }
 }

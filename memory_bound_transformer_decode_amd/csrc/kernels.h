@@ -6,6 +6,10 @@
 
 namespace dec {
 
+// Counters that many work groups update or poll sit 256 bytes apart: accesses to one
+// address, or to one line, are served one after another.
+constexpr int COUNTER_STRIDE = 64;
+
 // What the matrix kernels do with the fp32 row sums y[b][n] = scale[n] * sum_k W[n][k] x[b][k].
 enum Epilogue : int {
   EPI_LOGITS = 0,  // out[b][n] = y                                   (LM head)
@@ -39,6 +43,10 @@ struct MatmulParams {
   const float* nh;        // [Bp][K] fp32 residual stream
   const float* ng;        // [K] gain
   float eps;
+  // matrix-vector kernels (k_gemv): work group 0 zeroes rearm[i COUNTER_STRIDE], i <
+  // n_rearm, at its start (the counters of the QKV + attention kernel before it)
+  unsigned* rearm;
+  int n_rearm;
 };
 
 // y = matrix x for one of the epilogues; gemv kernels for Bp <= 8, MFMA tiles for
@@ -73,11 +81,34 @@ struct AttnParams {
   uint16_t* o;            // [Bp][Hq * dh] bf16 out
   unsigned* cnt;          // [Bp][Hkv] split arrival counters, zero between launches
   int Bp, Hq, Hkv, dh, num_blocks, bps, n_split;
+  // QKV + attention kernel only: per kv head c, work groups that wrote its q/k/v rows
+  // (ready[c COUNTER_STRIDE], complete at ready_target); zero at the launch (the
+  // O-projection kernel that follows clears them: MatmulParams::rearm)
+  unsigned* ready;
+  unsigned ready_target;
+  unsigned* err_dev;      // wait timeout flag, device copy
+  unsigned* err_host;     // wait timeout flag, pinned host copy
+  uint64_t timeout_ticks; // bound on one wait, in s_memrealtime ticks
 };
 
 // split-K paged GQA decode attention; the last split of each (sequence, kv head)
 // combines (one kernel)
 hipError_t launch_attention(const AttnParams& p, bool kv_fp8, hipStream_t s);
+
+// The norm-fused QKV product (mp, Bp <= 8) and attention (ap) in one kernel: the
+// attention work groups follow the product's and start once the product work groups of
+// their kv head are done.  Needs d_head % (2 QKV_ATTN_IPW) == 0 and
+// qkv_attn_lds_bytes(...) <= 160 KB; returns hipErrorInvalidValue otherwise.
+constexpr int QKV_ATTN_IPW = 8;  // row pairs (waves) per product work group
+// Query heads per kv head up to which the kernel is built: the attention state of wider
+// groups does not fit the 128 registers per lane that keep two product work groups per
+// CU (one work group's 8 waves at up to 4 waves per SIMD).
+constexpr int QKV_ATTN_MAX_GROUP = 4;
+hipError_t launch_qkv_attn(const MatmulParams& mp, const AttnParams& ap, bool w_fp8, bool kv_fp8, hipStream_t s);
+// work groups of the product part; the attention part's ready_target
+int qkv_attn_groups(const MatmulParams& mp);
+unsigned qkv_attn_ready_target(int Hq, int Hkv, int dh);
+size_t qkv_attn_lds_bytes(int Bp, int K, int Hq, int Hkv, int dh);
 
 // ---------------------------------------------------------------- persistent step (Bp <= 8)
 

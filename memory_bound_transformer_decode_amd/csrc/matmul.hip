@@ -22,6 +22,7 @@
 
 #include "common.h"
 #include "epilogue.h"
+#include "gemv_norm.h"
 #include "kernels.h"
 
 namespace dec {
@@ -37,6 +38,8 @@ __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
   const int lane = threadIdx.x % WAVE;
   const int w = S == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int it = blockIdx.x;
+  if (it == 0)
+    for (int i = threadIdx.x; i < p.n_rearm; i += WAVE * S) cst(p.rearm + (int64_t)i * COUNTER_STRIDE, 0u);
   const int KV = p.K / EPV;  // 16-byte vectors per weight row (K % EPV == 0)
   const int kb = (int)((int64_t)KV * w / S), ke = (int)((int64_t)KV * (w + 1) / S);
   const u32x4* W = static_cast<const u32x4*>(p.W);
@@ -117,152 +120,15 @@ __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
 
 // The same products with the activations x = bf16(h g / sqrt(mean(h^2) + eps)) computed
 // by the work group itself from the fp32 residual stream h into LDS, so that the
-// RMSNorm of the layer input costs no kernel of its own (h is a few KB per row and
-// L2-resident; the kernel-fusion study's section 8 on intermediates round-tripping
-// through HBM).  IPW waves per work group, one row pair per wave.  The first pass's
-// weight loads are issued before the norm, so the norm runs under the weight stream.
-template <int BT, bool FP8, int EPI, bool KVFP8, int U, int IPW>
-__global__ __launch_bounds__(WAVE * IPW) void k_gemv_norm(MatmulParams p, int n_items) {
+// RMSNorm fused into the matrix-vector product (the work of a group: gemv_norm.h), ipw
+// <= NORM_IPW_MAX waves per work group.
+constexpr int NORM_IPW_MAX = 10;
+
+template <int BT, bool FP8, int EPI, bool KVFP8, int U>
+__global__ __launch_bounds__(WAVE * NORM_IPW_MAX) void k_gemv_norm(MatmulParams p, int n_items, int ipw) {
   extern __shared__ __align__(16) uint8_t gemv_smem[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(gemv_smem);  // [BT][K] bf16
-  __shared__ float red[IPW][BT];
-  constexpr int EPV = FP8 ? 16 : 8;
-  constexpr int NT = WAVE * IPW;
-  const int tid = threadIdx.x, lane = tid % WAVE;
-  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
-  const int K = p.K, KV = K / EPV;
-  const int it = blockIdx.x * IPW + w;
-  const bool have = it < n_items;
-  int r0, r1;
-  item_rows<EPI>(p, have ? it : n_items - 1, r0, r1);  // a wave without an item loads a valid row
-  const u32x4* W = static_cast<const u32x4*>(p.W);
-  const u32x4* w0p = W + (int64_t)r0 * KV;
-  const u32x4* w1p = W + (int64_t)r1 * KV;
-
-  // sum of squares of this thread's elements of each row (issued first: L2 hits that
-  // complete ahead of the weight loads).  For small batches the thread keeps its h and
-  // gain values in registers, so that x can be written without a second read, which
-  // would queue behind the weight loads.
-  constexpr int NHR = BT <= 2 ? 2 : 1;  // float4 of h per row held per thread (K <= 4096)
-  const bool held = BT <= 2 && K <= NHR * NT * 4;
-  f32x4 hv[BT][NHR], gv[NHR];
-  float ss[BT];
-#pragma unroll
-  for (int b = 0; b < BT; ++b) ss[b] = 0.f;
-  if (held) {
-#pragma unroll
-    for (int j = 0; j < NHR; ++j) {
-      const int i = min((j * NT + tid) * 4, K - 4);  // past K: a re-read that is not counted
-      const bool in = (j * NT + tid) * 4 < K;
-      gv[j] = gld(reinterpret_cast<const f32x4*>(p.ng + i));
-#pragma unroll
-      for (int b = 0; b < BT; ++b) {
-        hv[b][j] = gld(reinterpret_cast<const f32x4*>(p.nh + (int64_t)b * K + i));
-        const f32x4 v = hv[b][j];
-        ss[b] += in ? v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w : 0.f;
-      }
-    }
-  } else {
-    for (int i = tid * 4; i < K; i += NT * 4) {
-#pragma unroll
-      for (int b = 0; b < BT; ++b) {
-        const f32x4 v = gld(reinterpret_cast<const f32x4*>(p.nh + (int64_t)b * K + i));
-        ss[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-      }
-    }
-  }
-  EpiInputs<EPI, BT> ein;
-  if (lane == 0) epi_fetch<EPI, BT>(p, r0, r1, ein);
-
-  u32x4 w0[U], w1[U];
-  auto load_pass = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = k0 + WAVE * u;
-      if (kk < KV) {
-        w0[u] = ld_stream(w0p + kk);
-        w1[u] = ld_stream(w1p + kk);
-      }
-    }
-  };
-  float acc0[BT], acc1[BT];
-#pragma unroll
-  for (int b = 0; b < BT; ++b) acc0[b] = acc1[b] = 0.0f;
-  auto compute_pass = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = k0 + WAVE * u;
-      if (kk < KV) {
-#pragma unroll
-        for (int b = 0; b < BT; ++b) {
-          const uint16_t* xb = xs + b * K + kk * EPV;
-          if (FP8) {
-            const u32x4 xa = *reinterpret_cast<const u32x4*>(xb), xc = *reinterpret_cast<const u32x4*>(xb + 8);
-            acc0[b] = dot16_e4m3(w0[u], xa, xc, acc0[b]);
-            acc1[b] = dot16_e4m3(w1[u], xa, xc, acc1[b]);
-          } else {
-            const u32x4 xa = *reinterpret_cast<const u32x4*>(xb);
-            acc0[b] = dot8_bf16(w0[u], xa, acc0[b]);
-            acc1[b] = dot8_bf16(w1[u], xa, acc1[b]);
-          }
-        }
-      }
-    }
-  };
-  load_pass(lane);
-
-  // the norm: reduce the sums over the work group, then write x into LDS
-#pragma unroll
-  for (int b = 0; b < BT; ++b) {
-    const float t = wave_sum(ss[b]);
-    if (lane == 0) red[w][b] = t;
-  }
-  __syncthreads();
-  float r[BT];
-#pragma unroll
-  for (int b = 0; b < BT; ++b) {
-    float t = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < IPW; ++ww) t += red[ww][b];
-    r[b] = 1.0f / sqrtf(t / (float)K + p.eps);
-  }
-  auto put_x = [&](int i, int b, const f32x4& v, const f32x4& g) {
-    const uint32_t lo = (uint32_t)f32_to_bf16(v.x * r[b] * g.x) | ((uint32_t)f32_to_bf16(v.y * r[b] * g.y) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(v.z * r[b] * g.z) | ((uint32_t)f32_to_bf16(v.w * r[b] * g.w) << 16);
-    *reinterpret_cast<u32x2*>(xs + b * K + i) = u32x2{lo, hi};
-  };
-  if (held) {
-#pragma unroll
-    for (int j = 0; j < NHR; ++j) {
-      const int i = (j * NT + tid) * 4;
-      if (i < K) {
-#pragma unroll
-        for (int b = 0; b < BT; ++b) put_x(i, b, hv[b][j], gv[j]);
-      }
-    }
-  } else {
-    for (int i = tid * 4; i < K; i += NT * 4) {
-      const f32x4 g = gld(reinterpret_cast<const f32x4*>(p.ng + i));
-#pragma unroll
-      for (int b = 0; b < BT; ++b) put_x(i, b, gld(reinterpret_cast<const f32x4*>(p.nh + (int64_t)b * K + i)), g);
-    }
-  }
-  __syncthreads();
-
-  compute_pass(lane);
-  for (int k0 = lane + WAVE * U; k0 < KV; k0 += WAVE * U) {
-    load_pass(k0);
-    compute_pass(k0);
-  }
-#pragma unroll
-  for (int b = 0; b < BT; ++b) {
-    acc0[b] = wave_sum(acc0[b]);
-    acc1[b] = wave_sum(acc1[b]);
-  }
-  if (lane == 0 && have) {
-#pragma unroll
-    for (int b = 0; b < BT; ++b) pair_epilogue_pre<EPI, BT>(p, KVFP8, ein, b, it, r0, r1, acc0[b], acc1[b]);
-  }
+  gemv_norm_group<BT, FP8, EPI, KVFP8, U, NORM_IPW_MAX, false>(p, n_items, blockIdx.x,
+                                                               reinterpret_cast<uint16_t*>(gemv_smem), ipw);
 }
 
 // ---------------------------------------------------------------- MFMA tiles (Bp >= 16)
@@ -446,14 +312,35 @@ hipError_t gemv_s(const MatmulParams& p, int n_items, int kv, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Waves (row pairs) per work group of the norm-fused kernel: 8, so that one
-// normalization serves 8 row pairs (smaller work groups measured slower: the
-// normalization's L2 reads grow with the number of work groups).
+// Waves (row pairs) per work group of the norm-fused kernel.  Where every work group
+// fits on the chip at once (two per CU), the waves per group are chosen so that the
+// groups split evenly over the CUs: 384 groups of 8 would leave half of the 256 CUs with
+// twice the rows of the other half, and the kernel ends with the slowest CU.  Otherwise
+// 8, so that one normalization serves 8 row pairs (smaller work groups measured slower
+// there: the normalization's L2 reads grow with the number of work groups), and the
+// hardware dispatcher balances the rounds.
 constexpr int NORM_IPW = 8;
 
-template <int BT, bool FP8, int EPI, bool KVFP8, int U, int IPW>
-hipError_t gemv_norm_ipw(const MatmulParams& p, int n_items, hipStream_t s) {
-  auto kern = k_gemv_norm<BT, FP8, EPI, KVFP8, U, IPW>;
+int norm_ipw(const void* kern, int n_items, size_t lds) {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      v = 256;
+    n_cu = v > 0 ? v : 256;
+  }
+  const int ipw = (n_items + 2 * n_cu - 1) / (2 * n_cu);
+  if (ipw > NORM_IPW_MAX) return NORM_IPW;
+  const int w = ipw < 1 ? 1 : ipw;
+  int occ = 0;  // two groups per CU must be resident together
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, WAVE * w, lds) != hipSuccess || occ < 2)
+    return w <= NORM_IPW ? w : NORM_IPW;
+  return w;
+}
+
+template <int BT, bool FP8, int EPI, bool KVFP8, int U>
+hipError_t gemv_norm_go(const MatmulParams& p, int n_items, hipStream_t s) {
+  auto kern = k_gemv_norm<BT, FP8, EPI, KVFP8, U>;
   const size_t lds = (size_t)BT * p.K * 2;
   static size_t allowed = 64 * 1024;  // per instance: the dynamic LDS size enabled so far
   if (lds > allowed) {
@@ -462,14 +349,20 @@ hipError_t gemv_norm_ipw(const MatmulParams& p, int n_items, hipStream_t s) {
     if (e != hipSuccess) return e;
     allowed = lds;
   }
-  const int grid = (n_items + IPW - 1) / IPW;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVE * IPW), lds, s, p, n_items);
+  // one choice per (instance, rows, LDS): launches are captured into graphs once per shape
+  struct Pick { int n; size_t lds; int ipw; };
+  static Pick cache[8];
+  static int n_cache = 0;
+  int ipw = 0;
+  for (int i = 0; i < n_cache; ++i)
+    if (cache[i].n == n_items && cache[i].lds == lds) ipw = cache[i].ipw;
+  if (ipw == 0) {
+    ipw = norm_ipw(reinterpret_cast<const void*>(kern), n_items, lds);
+    if (n_cache < 8) cache[n_cache++] = Pick{n_items, lds, ipw};
+  }
+  const int grid = (n_items + ipw - 1) / ipw;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVE * ipw), lds, s, p, n_items, ipw);
   return hipGetLastError();
-}
-
-template <int BT, bool FP8, int EPI, bool KVFP8, int U>
-hipError_t gemv_norm_go(const MatmulParams& p, int n_items, hipStream_t s) {
-  return gemv_norm_ipw<BT, FP8, EPI, KVFP8, U, NORM_IPW>(p, n_items, s);
 }
 
 template <int BT, bool FP8, int EPI, bool KVFP8>

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdec.so")
 
 DEC_OK, DEC_E_INVALID, DEC_E_STATE, DEC_E_CAPACITY, DEC_E_UNSUPPORTED, DEC_E_HIP = 0, -1, -2, -3, -4, -5
 DEC_BF16, DEC_FP8_E4M3 = 0, 1
-FLAG_EAGER, FLAG_UNFUSED, FLAG_NO_MFMA, FLAG_CAPTURE_ALL, FLAG_PERSISTENT = 1, 2, 4, 8, 16
+FLAG_EAGER, FLAG_UNFUSED, FLAG_NO_MFMA, FLAG_CAPTURE_ALL, FLAG_PERSISTENT, FLAG_FUSED_QKV_ATTN = 1, 2, 4, 8, 16, 32
 LADDER = (1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64)
 BLOCK = 16
 

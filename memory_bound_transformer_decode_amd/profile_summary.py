@@ -29,7 +29,7 @@ import sys
 from typing import Dict, List
 
 # sources of the matrix-vector kernels (the benchmark's dominant kernel)
-KERNEL_SOURCES = ("csrc/matmul.hip", "csrc/epilogue.h", "csrc/common.h", "csrc/kernels.h")
+KERNEL_SOURCES = ("csrc/matmul.hip", "csrc/gemv_norm.h", "csrc/epilogue.h", "csrc/common.h", "csrc/kernels.h")
 
 
 def kernel_source_sha256() -> str:

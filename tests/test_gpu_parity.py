@@ -24,6 +24,24 @@ MINI = synth.ModelConfig("mini", 7, n_layers=2, d_model=320, n_q_heads=10, n_kv_
                          d_head=64, d_ff=1040, vocab=1000)
 MINI128 = synth.ModelConfig("mini128", 8, n_layers=2, d_model=256, n_q_heads=8, n_kv_heads=1,
                             d_head=128, d_ff=512, vocab=512)
+# g = 4 query heads per KV head: batches <= 8 run QKV and attention as one kernel
+MINI4 = synth.ModelConfig("mini4", 9, n_layers=2, d_model=320, n_q_heads=8, n_kv_heads=2,
+                          d_head=64, d_ff=1040, vocab=1000)
+MINI4_128 = synth.ModelConfig("mini4x128", 10, n_layers=2, d_model=256, n_q_heads=8, n_kv_heads=2,
+                              d_head=128, d_ff=512, vocab=512)
+
+
+def fused_qkv_attn(cfg, B):
+    """Whether the library runs QKV and attention as one kernel for this batch."""
+    return B <= 8 and cfg.n_q_heads // cfg.n_kv_heads <= 4 and cfg.d_head % 16 == 0
+
+
+def kernels_per_step(cfg, B, flags=0):
+    if B <= 8:
+        per_layer = 4 if fused_qkv_attn(cfg, B) and flags & 32 else 5
+    else:
+        per_layer = 7
+    return per_layer * cfg.n_layers + 2
 
 
 def fmt(cfg, w, kv):
@@ -129,7 +147,7 @@ def test_graph_replay_equals_eager_bitwise(dec, B, persist):
     assert ie.persistent == ig.persistent == int(persistent)
     # per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the
     # matrix-vector kernels (batch <= 8) normalize their own input
-    expect = 1 if persistent else (5 if B <= 8 else 7) * cfg.n_layers + 2
+    expect = 1 if persistent else kernels_per_step(cfg, B)
     assert ie.kernels_per_step == ig.kernels_per_step == expect
 
 
@@ -143,6 +161,79 @@ def test_mini_model_persistent_plan(dec, w, kv, B):
     ids = synth.make_token_ids(cfg, 3, B, seed=12)
     log(f"mini persistent {w}/{kv} B={B}")
     assert_ok(run_parity(case, ids, flags=dec.FLAG_PERSISTENT), cfg)
+
+
+@pytest.mark.parametrize("w,kv", [("bf16", "bf16"), ("fp8", "fp8"), ("bf16", "fp8")])
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_fused_qkv_attention(dec, w, kv, B):
+    """QKV projection and attention as one kernel (g = 4), against the oracle."""
+    cfg = fmt(MINI4, w, kv)
+    rng = np.random.default_rng(100 + B)
+    case = make_case(cfg, ctx_mix(B, rng), 128, seed=18, gains="random")
+    ids = synth.make_token_ids(cfg, 3, B, seed=18)
+    log(f"mini4 fused qkv+attention {w}/{kv} B={B}")
+    assert_ok(run_parity(case, ids, flags=dec.FLAG_FUSED_QKV_ATTN), cfg)
+
+
+@pytest.mark.parametrize("cfg0", [MINI4, MINI4_128])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("B", [1, 5, 8])
+def test_fused_qkv_attention_matches_separate(dec, cfg0, kv, B):
+    """One kernel or two for QKV + attention: the same arithmetic up to the order of the
+    RMSNorm sum (the two kernels give its work groups different widths), the same cache
+    slots; one kernel fewer per layer."""
+    cfg = fmt(cfg0, "bf16", kv)
+    rng = np.random.default_rng(110 + B)
+    # contexts long enough that the attention splits (several work groups per kv head
+    # wait, and the last one combines)
+    lens = [int(x) for x in rng.integers(0, 500, size=B)]
+    lens[0] = 499
+    case = make_case(cfg, lens, 512, seed=19, gains="random")
+    ids = synth.make_token_ids(cfg, 1, B, seed=19)[0]
+    log(f"{cfg.name} fused vs separate B={B}")
+    zf, pf, inf_ = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_FUSED_QKV_ATTN)
+    zs, ps, ins = _one_step(dec, case, ids, case.ctx_lens, 0)
+    assert inf_.kernels_per_step == kernels_per_step(cfg, B, dec.FLAG_FUSED_QKV_ATTN) == 4 * cfg.n_layers + 2
+    assert ins.kernels_per_step == kernels_per_step(cfg, B) == 5 * cfg.n_layers + 2
+    a, b = zf.double().cpu().numpy(), zs.double().cpu().numpy()
+    R = a.max(axis=1) - a.min(axis=1)
+    assert np.max(np.abs(a - b) / R[:, None]) < 5e-3
+    canary = synth.KV_CANARY_BF16 if kv == "bf16" else synth.KV_CANARY_FP8
+    assert np.array_equal(synth.kv_codes_numpy(pf) != canary, synth.kv_codes_numpy(ps) != canary)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_fused_qkv_attention_several_blocks_per_wave(dec, kv):
+    """Long contexts at batch 8: each attention wave takes two or more KV blocks, so the
+    second pair of heads of a group re-reads the wave's first block."""
+    cfg = fmt(MINI4, "bf16", kv)
+    B = 8
+    rng = np.random.default_rng(120)
+    lens = [int(x) for x in rng.integers(2600, 4000, size=B)]
+    case = make_case(cfg, lens, 4096, seed=21)
+    ids = synth.make_token_ids(cfg, 2, B, seed=21)
+    log(f"{cfg.name} long contexts B={B}")
+    assert_ok(run_parity(case, ids, flags=dec.FLAG_FUSED_QKV_ATTN), cfg)
+
+
+def test_fused_qkv_attention_repeated_steps(dec):
+    """The kernel's wait counters are cleared by the O projection after it: many launches
+    in a row (graph replays, every layer) keep giving the eager result."""
+    cfg = fmt(MINI4, "fp8", "fp8")
+    B = 3
+    case = make_case(cfg, [40, 7, 100], 128, seed=20)
+    ids = synth.make_token_ids(cfg, 1, B, seed=20)[0]
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=4,
+                    max_seq_len=128, kv_pool=case.pool.clone(), flags=dec.FLAG_FUSED_QKV_ATTN)
+    outs = [d.step(ids, case.ctx_lens, case.block_tables).clone() for _ in range(6)]
+    d.set_flags(dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_EAGER)
+    ref = d.step(ids, case.ctx_lens, case.block_tables).clone()
+    d.set_flags(dec.FLAG_FUSED_QKV_ATTN)
+    outs.append(d.step(ids, case.ctx_lens, case.block_tables).clone())
+    torch.cuda.synchronize()
+    d.close()
+    for z in outs:
+        assert torch.equal(z.view(torch.int32), ref.view(torch.int32))
 
 
 @pytest.mark.parametrize("B", [1, 5, 24])
