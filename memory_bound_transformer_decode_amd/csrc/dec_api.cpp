@@ -109,6 +109,8 @@ struct Layout {
   size_t uf;                           // unfused step: fp32 product rows [MB][max(N)]
   size_t mats, bar, attn_cnt, err;     // persistent-step state
   size_t ready;                        // QKV + attention kernel: [n_kv_heads] counters, 256 B apart
+  size_t gpart, gcnt;                  // MFMA products split over K: partial tiles, row-block counters
+  size_t gpart_floats, gcnt_n;
   size_t total;
 };
 
@@ -155,6 +157,27 @@ Layout layout_of(const dec_config& c) {
     if ((size_t)c.d_model > n) n = c.d_model;
     off = align256(off + MB * n * 4);
   }
+  // MFMA products (buckets of 16 rows and more): the largest partial-tile buffer and
+  // row-block count over the step's matrices (gate+up also as one plain matrix, as the
+  // unfused step runs it)
+  size_t part_floats = 0, n_rb = 0;
+  for (int i = 0; i < N_BUCKETS && LADDER[i] <= c.max_batch; ++i) {
+    const int Bp = LADDER[i];
+    if (Bp < 16) continue;
+    const int qkv_rows = (c.n_q_heads + 2 * c.n_kv_heads) * c.d_head;
+    const int shapes[6][3] = {{qkv_rows, 1, c.d_model}, {c.d_model, 1, c.n_q_heads * c.d_head},
+                              {c.d_ff, 2, c.d_model},   {2 * c.d_ff, 1, c.d_model},
+                              {c.d_model, 1, c.d_ff},   {c.vocab, 1, c.d_model}};
+    for (const auto& sh : shapes) {
+      const dec::GemmPlan gp = dec::gemm_plan(sh[0], sh[1], sh[2], Bp);
+      if (gp.part_floats > part_floats) part_floats = gp.part_floats;
+      if (gp.ks > 1 && (size_t)gp.n_rb > n_rb) n_rb = gp.n_rb;
+    }
+  }
+  L.gpart = off;
+  L.gpart_floats = part_floats;
+  L.gcnt_n = n_rb;
+  off = align256(off + part_floats * 4);
   L.mats = off;  // device copies of the per-layer weight pointers: 4 arrays of n_layers
   off = align256(off + (size_t)4 * (c.n_layers > 0 ? c.n_layers : 1) * sizeof(dec::DevMat));
   L.bar = off;
@@ -165,6 +188,8 @@ Layout layout_of(const dec_config& c) {
   off = align256(off + 4);
   L.ready = off;
   off = align256(off + (size_t)c.n_kv_heads * dec::COUNTER_STRIDE * 4);
+  L.gcnt = off;
+  off = align256(off + n_rb * dec::COUNTER_STRIDE * 4);
   L.total = off;
   return L;
 }
@@ -287,6 +312,10 @@ dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) 
   p.bps = blocks_per_seq(g);
   p.d_ff = g.d_ff;
   p.layer = l;
+  p.gpart = ws_ptr<float>(c, c->L.gpart);
+  p.gcnt = ws_ptr<unsigned>(c, c->L.gcnt);
+  p.gpart_floats = c->L.gpart_floats;
+  p.gcnt_n = (int)c->L.gcnt_n;
   uint16_t* x = ws_ptr<uint16_t>(c, c->L.x);
   float* h = ws_ptr<float>(c, c->L.h);
   switch (which) {

@@ -1,0 +1,326 @@
+// Weight-streaming products for batches of 16 to 64 rows on the matrix cores.
+//
+// At these batches y = s (.) (W x) is a real (if skinny) contraction: 2 Bp FLOP per
+// weight element, more than the vector ALUs issue at HBM rate, so the products run on
+// v_mfma_f32_16x16x32_bf16 tiles.  The kernel is still bound by HBM ("GPU Inference
+// Internals", Roofline: Why Decode Is Memory-Bound: the intensity 2 Bp / b_w stays
+// far below the chip's balance), so its design is about bytes, not FLOPs:
+//
+//  * Every weight byte is read once, with 16-byte non-temporal loads in which 16
+//    lanes read 256 contiguous bytes of one row (a load instruction covers 4 rows).
+//    The MFMA operand layout would have each instruction touch 16 rows with 64 bytes
+//    each, which streams measurably slower from HBM; each wave instead passes its
+//    loads through a small private LDS tile that hands every lane its operand.
+//  * E4M3 codes are widened to bf16 in registers (exact), and the per-row scale is
+//    applied once in the epilogue (dequantization fused into the matmul: kernel-fusion
+//    architecture study, section 11).
+//  * The activations x [Bp][K] are the other operand of every tile.  A work group owns
+//    W 16-row tiles (one per wave) and stages x through LDS in chunks of KC k-values
+//    shared by all of its waves, so its L2 reads of x are Bp / 16 W of the weight bytes
+//    instead of Bp / 16 of them for a work group of one tile.
+//  * Matrices with too few row blocks to fill the chip also split K over KS work
+//    groups.  Each writes its partial tiles; the last one of a row block to arrive sums
+//    the KS partials in split order (so the result does not depend on arrival order)
+//    and applies the epilogue.
+//
+// Fused epilogues as in the matrix-vector kernels: QKV + RoPE + paged KV-cache write,
+// gate+up + SiLU x mul (a tile holds 8 gate rows and the 8 up rows of the same
+// intermediate indices), residual add (O, down), fp32 logits (LM head).
+
+#include "common.h"
+#include "epilogue.h"
+#include "kernels.h"
+
+namespace dec {
+
+namespace {
+
+constexpr int KC = 256;          // k-values per staged chunk of x
+constexpr int XROW = KC + 8;     // LDS row of a staged x chunk, in bf16: 16 bytes of padding
+                                 // move consecutive batch rows to different LDS banks
+constexpr int TROW = 256 + 16;   // LDS row of a wave's weight tile, in bytes (padded alike)
+
+// v_mfma_f32_16x16x32_bf16: lane l supplies A[l % 16][8 k-values] and B[8 k-values][l % 16],
+// the four lane groups l / 16 four disjoint sets of 8 k-values; lane l receives
+// D[4 (l / 16) + j][l % 16], j = 0..3.  Which k-values a lane group covers is free as long
+// as A and B agree: in k-step s of a group of GK k-values, lane group g takes the 8
+// k-values s 32 + 8 g + [0, 8).
+template <int NT, bool FP8, int EPI, bool KVFP8, int W>
+__global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n) {
+  extern __shared__ __align__(16) uint8_t lds[];  // x: [2][NT 16][XROW] bf16; tiles: [W][16][TROW]
+  constexpr bool SILU = EPI == EPI_SILU;
+  constexpr int GK = FP8 ? 256 : 128;              // k-values per group: 256 bytes of a row
+  constexpr int NGRP = KC / GK;                    // groups per chunk (2 bf16, 1 fp8)
+  constexpr int NS = GK / 32;                      // MFMA k-steps per group
+  constexpr int COLS = NT * 16;
+  constexpr int XSEG = KC / 8;                     // 16-byte pieces per staged x row
+  constexpr int XL = (COLS * XSEG + W * WAVE - 1) / (W * WAVE);  // x staging loads per thread
+  constexpr int XBUF = COLS * XROW;                // bf16 per x buffer
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int lane = tid % WAVE, m = lane % 16, kg = lane / 16;
+  uint8_t* tile = lds + (size_t)2 * XBUF * 2 + (size_t)wave * 16 * TROW;
+  // rows: output rows of the product (d_ff intermediate indices for gate+up); a tile
+  // covers TR of them
+  constexpr int TR = SILU ? 8 : 16;
+  const int rows = SILU ? p.d_ff : p.N;
+  const int rb = blockIdx.x / ks_n, ks = blockIdx.x % ks_n;
+  const int nch = (p.K + KC - 1) / KC;
+  const int c0 = (int)((int64_t)nch * ks / ks_n), c1 = (int)((int64_t)nch * (ks + 1) / ks_n);
+  const int row0 = (rb * W + wave) * TR;  // first output row of this wave's tile
+
+  // weight row of tile row i (rows past the matrix are clamped: their results are dropped)
+  auto wrow = [&](int i) -> int {
+    if (SILU) return (i < 8 ? 0 : p.d_ff) + min(row0 + (i & 7), rows - 1);
+    return min(row0 + i, rows - 1);
+  };
+  const size_t rowbytes = FP8 ? (size_t)p.K : (size_t)p.K * 2;
+  // load q of a group: lane (r = kg, j = m) reads 16 bytes at byte 16 j of the group's 256
+  // bytes of tile row 4 q + r
+  const uint8_t* wp[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) wp[q] = static_cast<const uint8_t*>(p.W) + (size_t)wrow(4 * q + kg) * rowbytes;
+  const int lastv = (int)rowbytes - 16;  // last 16-byte piece of a row
+
+  // weight loads of chunk c, unconditional: pieces past K are read at the row's last
+  // piece (x is zero there, so they add nothing)
+  auto load_w = [&](int c, u32x4 (&wr)[NGRP][4]) {
+#pragma unroll
+    for (int gi = 0; gi < NGRP; ++gi) {
+      const int off = min(c * KC * (FP8 ? 1 : 2) + gi * 256 + m * 16, lastv);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wr[gi][q] = ld_stream(reinterpret_cast<const u32x4*>(wp[q] + off));
+    }
+  };
+  // x loads of chunk c into registers (rows past Bp read row Bp - 1; k past K is zero)
+  auto load_x = [&](int c, u32x4 (&xr)[XL]) {
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int i = tid + j * W * WAVE;
+      const int b = min(i / XSEG, p.Bp - 1), k = c * KC + (i % XSEG) * 8;
+      const u32x4 v = gld16(p.x + (int64_t)b * p.ldx + min(k, p.K - 8));
+      xr[j] = k < p.K ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_x = [&](int buf, const u32x4 (&xr)[XL]) {
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int i = tid + j * W * WAVE;
+      if (XL * W * WAVE == COLS * XSEG || i < COLS * XSEG)
+        *reinterpret_cast<u32x4*>(xs + buf * XBUF + (i / XSEG) * XROW + (i % XSEG) * 8) = xr[j];
+    }
+  };
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mma_chunk = [&](int buf, const u32x4 (&wr)[NGRP][4]) {
+    const uint16_t* xb = xs + buf * XBUF;
+#pragma unroll
+    for (int gi = 0; gi < NGRP; ++gi) {
+      // this wave's 16 x 256-byte tile of the group, then each lane's operands from it
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(tile + (4 * q + kg) * TROW + m * 16) = wr[gi][q];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        bf16x8 av;
+        if (FP8) {
+          const u32x2 c8 = *reinterpret_cast<const u32x2*>(tile + m * TROW + s * 32 + kg * 8);
+          const bf16x2 q0 = e4m3x2_to_bf16x2<false>(c8.x), q1 = e4m3x2_to_bf16x2<true>(c8.x);
+          const bf16x2 q2 = e4m3x2_to_bf16x2<false>(c8.y), q3 = e4m3x2_to_bf16x2<true>(c8.y);
+          av = bf16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+        } else {
+          av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + m * TROW + s * 64 + kg * 16));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, ld16(xb + (t * 16 + m) * XROW + gi * GK + s * 32 + kg * 8));
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[t], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // chunk c's weights and the next chunk's loads are in flight while chunk c's tiles
+  // are multiplied; one barrier per chunk hands the staged x over (each wave's weight
+  // tile is its own: LDS operations of one wave complete in order)
+  {
+    u32x4 wa[NGRP][4], wb[NGRP][4], xr[XL];
+    load_x(c0, xr);
+    load_w(c0, wa);
+    store_x(0, xr);
+    __syncthreads();
+    for (int c = c0; c < c1; c += 2) {
+      if (c + 1 < c1) {
+        load_x(c + 1, xr);
+        load_w(c + 1, wb);
+      }
+      mma_chunk(0, wa);
+      if (c + 1 >= c1) break;
+      store_x(1, xr);
+      __syncthreads();
+      if (c + 2 < c1) {
+        load_x(c + 2, xr);
+        load_w(c + 2, wa);
+      }
+      mma_chunk(1, wb);
+      if (c + 2 >= c1) break;
+      store_x(0, xr);
+      __syncthreads();
+    }
+  }
+
+  if (ks_n > 1) {
+    // partial tiles of this split: part[blockIdx.x][wave][t][lane] (f32x4), written
+    // device-coherently for the work group that combines them
+    float* part = p.gpart + ((int64_t)blockIdx.x * W + wave) * NT * (WAVE * 4);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 v = acc[t];
+      cst_f4(part + (t * WAVE + lane) * 4, v.x, v.y, v.z, v.w);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial stores have completed
+    __shared__ int last;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned* cnt = p.gcnt + (int64_t)rb * COUNTER_STRIDE;
+      const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = prev == (unsigned)ks_n - 1;
+      if (last) cst(cnt, 0u);  // ready for the next launch
+    }
+    __syncthreads();
+    if (!last) return;
+    // sum the splits in order 0..ks_n-1 (this work group's own from registers)
+    f32x4 tot[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ks_n; ++s) {
+      const float* ps = p.gpart + ((int64_t)(rb * ks_n + s) * W + wave) * NT * (WAVE * 4);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) tot[t] += s == ks ? acc[t] : cld_f4(ps + (t * WAVE + lane) * 4);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = tot[t];
+  }
+
+  // epilogue: lane holds tile rows 4 kg + j (j = 0..3) of batch column t 16 + m
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = t * 16 + m;
+    if (SILU) {
+      // gate rows are tile rows 0..7 (lane groups 0, 1), up rows 8..15 (lane groups 2, 3):
+      // lane l pairs with lane l + 32
+      f32x4 up;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) up[j] = __shfl_xor(acc[t][j], 32);
+      if (kg >= 2 || col >= p.Bp) continue;
+      uint16_t* o = p.act + (int64_t)col * p.ldact;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = row0 + 4 * kg + j;
+        if (r >= rows) break;
+        const float sg = p.scale ? gld(p.scale + r) : 1.f, su = p.scale ? gld(p.scale + p.d_ff + r) : 1.f;
+        gst(o + r, f32_to_bf16(silu_f(acc[t][j] * sg) * (up[j] * su)));
+      }
+      continue;
+    }
+    if (col >= p.Bp) continue;
+    const int r0 = row0 + 4 * kg;
+    if (EPI == EPI_QKV) {
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const int r = r0 + j;  // even; rows is a multiple of d_head
+        if (r >= rows) break;
+        const float s0 = p.scale ? gld(p.scale + r) : 1.f, s1 = p.scale ? gld(p.scale + r + 1) : 1.f;
+        qkv_pair_out(p, KVFP8, col, r, acc[t][j] * s0, acc[t][j + 1] * s1);
+      }
+    } else {
+      float* o = p.out + (int64_t)col * p.ldo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = r0 + j;
+        if (r >= rows) break;
+        const float y = acc[t][j] * (p.scale ? gld(p.scale + r) : 1.f);
+        if (EPI == EPI_RESID)
+          gst(o + r, gld(o + r) + y);
+        else
+          gst(o + r, y);
+      }
+    }
+  }
+}
+
+constexpr size_t lds_bytes(int NT, int W) { return (size_t)2 * NT * 16 * XROW * 2 + (size_t)W * 16 * TROW; }
+
+template <int NT, bool FP8, int EPI, bool KVFP8, int W>
+hipError_t go(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
+  auto kern = k_gemm_lds<NT, FP8, EPI, KVFP8, W>;
+  constexpr size_t lds = lds_bytes(NT, W);
+  static_assert(lds <= 160 * 1024, "LDS of one work group");
+  static bool attr = false;
+  if (!attr && lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(g.n_rb * g.ks), dim3(WAVE * W), lds, s, p, g.ks);
+  return hipGetLastError();
+}
+
+template <bool FP8, int EPI, bool KVFP8>
+hipError_t go_nt(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
+  if (p.Bp <= 16) return go<1, FP8, EPI, KVFP8, GEMM_WAVES>(p, g, s);
+  if (p.Bp <= 32) return go<2, FP8, EPI, KVFP8, GEMM_WAVES>(p, g, s);
+  if (p.Bp <= 48) return go<3, FP8, EPI, KVFP8, GEMM_WAVES>(p, g, s);
+  return go<4, FP8, EPI, KVFP8, GEMM_WAVES>(p, g, s);
+}
+
+}  // namespace
+
+// Row blocks of GEMM_WAVES tiles and the K split: where the row blocks alone would leave
+// the chip under-filled (fewer than GEMM_TARGET_GROUPS work groups for MI355X's 256
+// CUs), K is split so that about that many work groups run, with at least two chunks
+// each.  A pure function of the shape: the workspace is sized with it.
+GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp) {
+  GemmPlan g{};
+  const int tile_rows = n_groups == 2 ? 8 : 16;  // gate+up tiles hold 8 of each
+  g.n_rb = (rows + tile_rows * GEMM_WAVES - 1) / (tile_rows * GEMM_WAVES);
+  const int nch = (K + KC - 1) / KC;
+  int ks = 1;
+  if (g.n_rb < GEMM_TARGET_GROUPS) {
+    ks = (GEMM_TARGET_GROUPS + g.n_rb - 1) / g.n_rb;
+    const int cap = nch / 2 > 1 ? nch / 2 : 1;
+    if (ks > cap) ks = cap;
+    if (ks > GEMM_MAX_SPLIT) ks = GEMM_MAX_SPLIT;
+  }
+  g.ks = ks;
+  const int NT = (Bp + 15) / 16;
+  g.part_floats = ks > 1 ? (size_t)g.n_rb * ks * GEMM_WAVES * NT * WAVE * 4 : 0;
+  return g;
+}
+
+hipError_t launch_gemm_mfma(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, hipStream_t s) {
+  const int rows = epi == EPI_SILU ? p.d_ff : p.N;
+  if (rows <= 0 || p.Bp <= 0) return hipSuccess;
+  if (p.Bp > 64 || p.K < 16 || p.K % 16) return hipErrorInvalidValue;
+  const GemmPlan g = gemm_plan(rows, epi == EPI_SILU ? 2 : 1, p.K, p.Bp);
+  if (g.ks > 1 && (!p.gpart || !p.gcnt || g.part_floats > p.gpart_floats || g.n_rb > p.gcnt_n))
+    return hipErrorInvalidValue;
+  switch (epi) {
+    case EPI_LOGITS:
+      return w_fp8 ? go_nt<true, EPI_LOGITS, false>(p, g, s) : go_nt<false, EPI_LOGITS, false>(p, g, s);
+    case EPI_RESID:
+      return w_fp8 ? go_nt<true, EPI_RESID, false>(p, g, s) : go_nt<false, EPI_RESID, false>(p, g, s);
+    case EPI_SILU:
+      return w_fp8 ? go_nt<true, EPI_SILU, false>(p, g, s) : go_nt<false, EPI_SILU, false>(p, g, s);
+    default:
+      if (w_fp8)
+        return kv_fp8 ? go_nt<true, EPI_QKV, true>(p, g, s) : go_nt<true, EPI_QKV, false>(p, g, s);
+      return kv_fp8 ? go_nt<false, EPI_QKV, true>(p, g, s) : go_nt<false, EPI_QKV, false>(p, g, s);
+  }
+}
+
+}  // namespace dec

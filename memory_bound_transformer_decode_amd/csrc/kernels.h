@@ -47,7 +47,27 @@ struct MatmulParams {
   // n_rearm, at its start (the counters of the QKV + attention kernel before it)
   unsigned* rearm;
   int n_rearm;
+  // MFMA products that split K over work groups: partial tiles and per-row-block
+  // arrival counters (COUNTER_STRIDE apart, zero between launches)
+  float* gpart;
+  unsigned* gcnt;
+  size_t gpart_floats;   // capacity of gpart
+  int gcnt_n;            // counters at gcnt
 };
+
+// MFMA products (Bp 16..64): row blocks of GEMM_WAVES 16-row tiles, K split over
+// ks work groups where the row blocks alone leave the chip under-filled.
+constexpr int GEMM_WAVES = 4;
+constexpr int GEMM_MAX_SPLIT = 16;
+constexpr int GEMM_TARGET_GROUPS = 256;  // one per CU of MI355X
+struct GemmPlan {
+  int n_rb;            // row blocks
+  int ks;              // work groups per row block (K split)
+  size_t part_floats;  // partial-tile floats the launch needs (0 when ks == 1)
+};
+// rows: per group (d_ff for gate+up, whose groups are 2); K; padded batch
+GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp);
+hipError_t launch_gemm_mfma(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, hipStream_t s);
 
 // y = matrix x for one of the epilogues; gemv kernels for Bp <= 8, MFMA tiles for
 // Bp >= 16 unless no_mfma.  Returns the number of kernels launched through *n.

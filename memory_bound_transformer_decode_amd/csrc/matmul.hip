@@ -12,9 +12,8 @@
 //    registers (exact) and the per-row scale is applied once in the epilogue
 //    ("dequantization fused into the matmul ... converted in-register",
 //    kernel-fusion architecture study, section 11).
-//  * k_gemm_mfma (Bp >= 16): the batch is wide enough to make this a dense
-//    contraction, so 16x16x32 bf16 MFMA tiles do the products.  A work group owns
-//    a 16-row tile; its waves split K and reduce through LDS.
+//  * Bp >= 16: the batch is wide enough to make this a dense contraction, so MFMA
+//    tiles do the products (gemm_mfma.hip).
 //
 // Fused epilogues (fused-kernel table of "Kernels, Fusion & CUDA Graphs", Fix 1):
 // QKV + RoPE + paged KV-cache write, gate+up + SiLU x mul, residual add (O, down),
@@ -131,163 +130,6 @@ __global__ __launch_bounds__(WAVE * NORM_IPW_MAX) void k_gemv_norm(MatmulParams 
                                                                reinterpret_cast<uint16_t*>(gemv_smem), ipw);
 }
 
-// ---------------------------------------------------------------- MFMA tiles (Bp >= 16)
-//
-// v_mfma_f32_16x16x32_bf16: lane l supplies A[l % 16][8 k-values] and B[8 k-values][l % 16];
-// the four lane groups l / 16 cover four disjoint sets of 8 k-values; lane l receives
-// D[4 (l / 16) + j][l % 16], j = 0..3.  Which k-values a lane group covers is free as long
-// as A and B agree, so each lane takes a contiguous run (32 bytes of a weight row: 16 bf16
-// or 32 E4M3 codes) and 4 lanes cover a whole 128-byte line of each of the tile's rows.
-
-constexpr int MFMA_WAVES = 8;  // waves per work group; they split K
-
-template <int NT, bool FP8, int EPI, bool KVFP8, int RT>
-__global__ __launch_bounds__(WAVE * MFMA_WAVES) void k_gemm_mfma(MatmulParams p) {
-  extern __shared__ __align__(16) float mfma_red[];   // [waves][NA][NT][64][4]
-  constexpr int NG = EPI == EPI_SILU ? 2 : 1;  // row groups (gate, up)
-  constexpr int NA = NG * RT;                  // A tiles per work group: RT 16-row tiles per group
-  constexpr int EPL = FP8 ? 32 : 16;           // weight elements per lane per step
-  constexpr int KSTEP = 4 * EPL;               // k per step (4 lane groups)
-  constexpr int NM = EPL / 8;                  // MFMAs per step per (A tile, column tile)
-  const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-  const int m = lane % 16, kg = lane / 16;
-  const int tile = blockIdx.x;  // RT * 16 rows (per group)
-
-  // rows of this lane's A operands: tile a = (group a / RT, 16-row tile a % RT); rows past
-  // the matrix are clamped (their results are dropped by the epilogue)
-  int arow[NA];
-#pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    const int gidx = a / RT;
-    const int r = (EPI == EPI_SILU ? gidx * p.d_ff : 0) + (tile * RT + a % RT) * 16 + m;
-    const int lim = EPI == EPI_SILU ? (gidx + 1) * p.d_ff : p.N;
-    arow[a] = min(r, lim - 1);
-  }
-  // k range of this wave
-  const int nsteps = (p.K + KSTEP - 1) / KSTEP;
-  const int per = (nsteps + MFMA_WAVES - 1) / MFMA_WAVES;
-  const int s0 = wave * per, s1 = min(nsteps, s0 + per);
-
-  f32x4 acc[NA][NT];
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const size_t wrow_bytes = FP8 ? (size_t)p.K : (size_t)p.K * 2;
-  const uint8_t* Wb = static_cast<const uint8_t*>(p.W);
-
-  // One step: 32 bytes of each A row per lane (two 16-byte halves) and EPL activations
-  // per lane per column tile.  Every load is unconditional at a clamped address: rows
-  // past the matrix feed columns the epilogue drops, activations past the batch feed
-  // batch columns it drops, and activations past K are replaced by zeros, so that the
-  // re-read weights there contribute nothing.
-  auto load_step = [&](int st, u32x4 (&wa)[NA][2], u32x4 (&xb)[NT][EPL / 8]) {
-    const int k0 = st * KSTEP + kg * EPL;  // first k of this lane's run
-#pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int kh = min(k0 + hh * (EPL / 2), p.K - EPL / 2);
-        wa[a][hh] = ld_stream(reinterpret_cast<const u32x4*>(Wb + (size_t)arow[a] * wrow_bytes +
-                                                             (size_t)kh * (FP8 ? 1 : 2)));
-      }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int col = min(t * 16 + m, p.Bp - 1);
-#pragma unroll
-      for (int v = 0; v < EPL / 8; ++v) {
-        const int kv = k0 + v * 8;
-        const u32x4 xv = gld16(p.x + (int64_t)col * p.ldx + min(kv, p.K - 8));
-        xb[t][v] = kv < p.K ? xv : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto mma_step = [&](const u32x4 (&wa)[NA][2], const u32x4 (&xb)[NT][EPL / 8]) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int a = 0; a < NA; ++a) {
-#pragma unroll
-        for (int mm = 0; mm < NM; ++mm) {
-          bf16x8 av;
-          if (FP8) {
-            // 8 codes: bytes [8 mm, 8 mm + 8) of the lane's 32-byte run
-            const u32x4& h = wa[a][mm / 2];
-            const uint32_t c0 = (mm & 1) ? h.z : h.x, c1 = (mm & 1) ? h.w : h.y;
-            const bf16x2 p0 = e4m3x2_to_bf16x2<false>(c0), p1 = e4m3x2_to_bf16x2<true>(c0);
-            const bf16x2 p2 = e4m3x2_to_bf16x2<false>(c1), p3 = e4m3x2_to_bf16x2<true>(c1);
-            av = bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-          } else {
-            av = __builtin_bit_cast(bf16x8, wa[a][mm]);
-          }
-          const bf16x8 bv = __builtin_bit_cast(bf16x8, xb[t][mm]);
-          acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[a][t], 0, 0, 0);
-        }
-      }
-    }
-  };
-  // two steps in flight: the next step's loads are issued before this step's products
-  if (s0 < s1) {
-    u32x4 wa0[NA][2], wa1[NA][2], xb0[NT][EPL / 8], xb1[NT][EPL / 8];
-    load_step(s0, wa0, xb0);
-    for (int st = s0; st < s1; st += 2) {
-      if (st + 1 < s1) load_step(st + 1, wa1, xb1);
-      mma_step(wa0, xb0);
-      if (st + 1 >= s1) break;
-      if (st + 2 < s1) load_step(st + 2, wa0, xb0);
-      mma_step(wa1, xb1);
-    }
-  }
-
-  // reduce the waves' partial tiles through LDS: red[wave][a][t][lane][j]
-  float* red = mfma_red;
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) red[(((wave * NA + a) * NT + t) * 64 + lane) * 4 + j] = acc[a][t][j];
-  __syncthreads();
-
-  auto total = [&](int a, int t, int l, int j) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < MFMA_WAVES; ++w) s += red[(((w * NA + a) * NT + t) * 64 + l) * 4 + j];
-    return s;
-  };
-  if (EPI == EPI_QKV) {
-    // pairs (j, j + 1) are rows (2i, 2i + 1) of the same lane
-    for (int idx = tid; idx < RT * NT * 64 * 2; idx += WAVE * MFMA_WAVES) {
-      const int rt = idx / (NT * 128), t = (idx / 128) % NT, l = (idx / 2) % 64, jp = (idx % 2) * 2;
-      const int col = t * 16 + l % 16, row = (tile * RT + rt) * 16 + 4 * (l / 16) + jp;
-      if (col >= p.Bp || row >= p.N) continue;
-      const float s0 = p.scale ? p.scale[row] : 1.f, s1 = p.scale ? p.scale[row + 1] : 1.f;
-      qkv_pair_out(p, KVFP8, col, row, total(rt, t, l, jp) * s0, total(rt, t, l, jp + 1) * s1);
-    }
-  } else {
-    for (int idx = tid; idx < RT * NT * 64 * 4; idx += WAVE * MFMA_WAVES) {
-      const int rt = idx / (NT * 256), t = (idx / 256) % NT, l = (idx / 4) % 64, j = idx % 4;
-      const int col = t * 16 + l % 16, r = (tile * RT + rt) * 16 + 4 * (l / 16) + j;
-      if (col >= p.Bp) continue;
-      if (EPI == EPI_SILU) {
-        if (r >= p.d_ff) continue;
-        const float sg = p.scale ? p.scale[r] : 1.f, su = p.scale ? p.scale[p.d_ff + r] : 1.f;
-        const float g = total(rt, t, l, j) * sg, u = total(RT + rt, t, l, j) * su;
-        p.act[(int64_t)col * p.ldact + r] = f32_to_bf16(silu_f(g) * u);
-      } else {
-        if (r >= p.N) continue;
-        const float y = total(rt, t, l, j) * (p.scale ? p.scale[r] : 1.f);
-        float* o = p.out + (int64_t)col * p.ldo + r;
-        if (EPI == EPI_RESID)
-          *o += y;
-        else
-          *o = y;
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- dispatch
 
 namespace {
@@ -381,33 +223,6 @@ hipError_t gemv_go(const MatmulParams& p, hipStream_t s) {
   return gemv_s<BT, FP8, EPI, KVFP8, 2>(p, n_items, kv, s);
 }
 
-// RT 16-row tiles per work group: the activations each wave loads serve RT times the
-// rows (their L2 reads fall from Bp/16 to Bp/(16 RT) of the weight bytes)
-template <int NT, bool FP8, int EPI, bool KVFP8, int RT>
-hipError_t mfma_rt(const MatmulParams& p, hipStream_t s) {
-  constexpr int NA = (EPI == EPI_SILU ? 2 : 1) * RT;
-  const size_t lds = (size_t)MFMA_WAVES * NA * NT * 64 * 4 * sizeof(float);
-  auto kern = k_gemm_mfma<NT, FP8, EPI, KVFP8, RT>;
-  static bool attr = false;
-  if (!attr && lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  const int rows = EPI == EPI_SILU ? p.d_ff : p.N;
-  const int grid = (rows + 16 * RT - 1) / (16 * RT);
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVE * MFMA_WAVES), lds, s, p);
-  return hipGetLastError();
-}
-
-// one 16-row tile per work group (two measured no faster at batch 32)
-template <int NT, bool FP8, int EPI, bool KVFP8>
-hipError_t mfma_go(const MatmulParams& p, hipStream_t s) {
-  return mfma_rt<NT, FP8, EPI, KVFP8, 1>(p, s);
-}
-
 template <bool FP8, int EPI, bool KVFP8>
 hipError_t dispatch_bt(const MatmulParams& p, bool mfma, hipStream_t s) {
   if (p.Bp <= 8 || !mfma) {
@@ -435,10 +250,7 @@ hipError_t dispatch_bt(const MatmulParams& p, bool mfma, hipStream_t s) {
     }
     return hipSuccess;
   }
-  if (p.Bp <= 16) return mfma_go<1, FP8, EPI, KVFP8>(p, s);
-  if (p.Bp <= 32) return mfma_go<2, FP8, EPI, KVFP8>(p, s);
-  if (p.Bp <= 48) return mfma_go<3, FP8, EPI, KVFP8>(p, s);
-  return mfma_go<4, FP8, EPI, KVFP8>(p, s);
+  return launch_gemm_mfma(p, EPI, FP8, KVFP8, s);
 }
 
 template <bool FP8, bool KVFP8>
