@@ -49,14 +49,14 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def gate_up_bytes(cfg, B: int) -> int:
+def gate_up_bytes(cfg, B: int, mfma: bool) -> int:
     """Algorithmic bytes of one gate+up launch: the weights once (+ fp8 row scales),
-    the input read once -- the fp32 residual rows and the norm gain where the kernel
-    normalizes its own input (batch <= 8), else the bf16 activations -- and the bf16
-    SiLU x mul output written."""
+    the input read once -- the fp32 residual rows and the norm gain where the
+    matrix-vector kernel normalizes its own input, else (MFMA tiles) the bf16
+    activations -- and the bf16 SiLU x mul output written."""
     b = 1 if cfg.weight_dtype == "fp8" else 2
     w = 2 * cfg.d_ff * cfg.d_model * b + (2 * cfg.d_ff * 4 if cfg.weight_dtype == "fp8" else 0)
-    x = B * cfg.d_model * 4 + cfg.d_model * 4 if B <= 8 else B * cfg.d_model * 2
+    x = B * cfg.d_model * 2 if mfma else B * cfg.d_model * 4 + cfg.d_model * 4
     return w + x + B * cfg.d_ff * 2
 
 
@@ -178,8 +178,8 @@ def run_batch(wl, B: int, steps: int, warmup: int, seed: int, want_eager: bool, 
             if rep > 0:
                 durs.append(e0.elapsed_time(e1) / 1e3 / L)
         avg = float(np.mean(durs))
-        nbytes = gate_up_bytes(cfg, B)
-        res["kernel"] = {"name": ("k_gemm_mfma" if B >= 16 else "k_gemv_norm") + " gate+up + SiLU x mul",
+        nbytes = gate_up_bytes(cfg, B, bool(info.used_mfma))
+        res["kernel"] = {"name": ("k_gemm_lds" if info.used_mfma else "k_gemv_norm") + " gate+up + SiLU x mul",
                          "avg_s": avg, "bytes": nbytes, "gbps": nbytes / avg / 1e9, "launches": len(durs) * L}
     d.close()
     del pool

@@ -157,13 +157,12 @@ Layout layout_of(const dec_config& c) {
     if ((size_t)c.d_model > n) n = c.d_model;
     off = align256(off + MB * n * 4);
   }
-  // MFMA products (buckets of 16 rows and more): the largest partial-tile buffer and
-  // row-block count over the step's matrices (gate+up also as one plain matrix, as the
-  // unfused step runs it)
+  // MFMA products: the largest partial-tile buffer and row-block count over the step's
+  // matrices (gate+up also as one plain matrix, as the unfused step runs it) and the
+  // buckets (every bucket, so that the size does not depend on which run on MFMA)
   size_t part_floats = 0, n_rb = 0;
   for (int i = 0; i < N_BUCKETS && LADDER[i] <= c.max_batch; ++i) {
     const int Bp = LADDER[i];
-    if (Bp < 16) continue;
     const int qkv_rows = (c.n_q_heads + 2 * c.n_kv_heads) * c.d_head;
     const int shapes[6][3] = {{qkv_rows, 1, c.d_model}, {c.d_model, 1, c.n_q_heads * c.d_head},
                               {c.d_ff, 2, c.d_model},   {2 * c.d_ff, 1, c.d_model},
@@ -379,6 +378,19 @@ dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) 
   return p;
 }
 
+// Buckets from 8 rows (bf16 weights) or 4 rows (E4M3 weights) up run the products on
+// the matrix cores (unless DEC_FLAG_NO_MFMA); smaller ones run the matrix-vector
+// kernels.  Measured on the 8B and 32B shapes: the vector kernels' activation reads from
+// LDS (Bp per weight vector) and, for E4M3, the widening of every weight once per batch
+// row make them slower than the MFMA tiles from these batches on; the MFMA tiles pad the
+// batch to 16 columns at no extra HBM traffic.
+constexpr int MFMA_MIN_BATCH_BF16 = 8;
+constexpr int MFMA_MIN_BATCH_FP8 = 4;
+bool use_mfma(const dec_config& g, int Bp) {
+  return !(g.flags & DEC_FLAG_NO_MFMA) &&
+         Bp >= (g.weight_dtype == DEC_FP8_E4M3 ? MFMA_MIN_BATCH_FP8 : MFMA_MIN_BATCH_BF16);
+}
+
 // norm_gain: when set, the kernel computes x = RMSNorm(h) norm_gain itself (fused_norm)
 hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const float* norm_gain = nullptr) {
   const dec_config& g = c->cfg;
@@ -389,13 +401,14 @@ hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const
     p.ng = norm_gain;
     p.eps = g.rms_eps;
   }
-  const bool mfma = !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
-  return dec::launch_matmul(p, epi, g.weight_dtype == DEC_FP8_E4M3, g.kv_dtype == DEC_FP8_E4M3, mfma, s);
+  return dec::launch_matmul(p, epi, g.weight_dtype == DEC_FP8_E4M3, g.kv_dtype == DEC_FP8_E4M3, use_mfma(g, Bp), s);
 }
 
-// Batches of <= 8 rows run matrix-vector kernels that normalize their own input in
-// LDS ([Bp][d] bf16 must fit in 128 KB)
-bool fused_norm(const dec_config& g, int Bp) { return Bp <= 8 && (size_t)Bp * g.d_model * 2 <= 128 * 1024; }
+// Batches of <= 8 rows on the matrix-vector kernels normalize their own input in LDS
+// ([Bp][d] bf16 must fit in 128 KB)
+bool fused_norm(const dec_config& g, int Bp) {
+  return !use_mfma(g, Bp) && Bp <= 8 && (size_t)Bp * g.d_model * 2 <= 128 * 1024;
+}
 
 // QKV projection and attention in one kernel (opt-in): the norm-fused batches, for head
 // sizes whose QKV work groups each lie in one head, groups of up to QKV_ATTN_MAX_GROUP
@@ -475,7 +488,7 @@ hipError_t enqueue_persistent(dec_ctx* c, int Bp, hipStream_t s) {
 hipError_t enqueue_unfused(dec_ctx* c, int Bp, hipStream_t s) {
   const dec_config& g = c->cfg;
   const bool wfp8 = g.weight_dtype == DEC_FP8_E4M3, kvfp8 = g.kv_dtype == DEC_FP8_E4M3;
-  const bool mfma = !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
+  const bool mfma = use_mfma(g, Bp);
   const int d = g.d_model;
   float* h = ws_ptr<float>(c, c->L.h);
   float* uf = ws_ptr<float>(c, c->L.uf);
@@ -877,7 +890,7 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   for (auto& row : c->graphs)
     for (auto& ge : row) ncap += ge != nullptr;
   const bool persist = use_persistent(c, Bp);
-  const bool mfma = !persist && !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= 16;
+  const bool mfma = !persist && use_mfma(g, Bp);
   const int slices = (!mfma && Bp > 8) ? Bp / 8 : 1;
   const int L = g.n_layers;
   // per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the

@@ -1,4 +1,4 @@
-// Weight-streaming products for batches of 16 to 64 rows on the matrix cores.
+// Weight-streaming products for batches of 4 to 64 rows on the matrix cores.
 //
 // At these batches y = s (.) (W x) is a real (if skinny) contraction: 2 Bp FLOP per
 // weight element, more than the vector ALUs issue at HBM rate, so the products run on
@@ -39,6 +39,9 @@ constexpr int KC = 256;          // k-values per staged chunk of x
 constexpr int XROW = KC + 8;     // LDS row of a staged x chunk, in bf16: 16 bytes of padding
                                  // move consecutive batch rows to different LDS banks
 constexpr int TROW = 256 + 16;   // LDS row of a wave's weight tile, in bytes (padded alike)
+// x chunk buffers: two (the next chunk is staged while this one is read) up to 32 batch
+// columns; one beyond, where two would hold the LDS to one work group per CU
+constexpr int x_buffers(int NT) { return NT >= 3 ? 1 : 2; }
 
 // v_mfma_f32_16x16x32_bf16: lane l supplies A[l % 16][8 k-values] and B[8 k-values][l % 16],
 // the four lane groups l / 16 four disjoint sets of 8 k-values; lane l receives
@@ -47,7 +50,7 @@ constexpr int TROW = 256 + 16;   // LDS row of a wave's weight tile, in bytes (p
 // k-values s 32 + 8 g + [0, 8).
 template <int NT, bool FP8, int EPI, bool KVFP8, int W>
 __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n) {
-  extern __shared__ __align__(16) uint8_t lds[];  // x: [2][NT 16][XROW] bf16; tiles: [W][16][TROW]
+  extern __shared__ __align__(16) uint8_t lds[];  // x: [XBUFS][NT 16][XROW] bf16; tiles: [W][16][TROW]
   constexpr bool SILU = EPI == EPI_SILU;
   constexpr int GK = FP8 ? 256 : 128;              // k-values per group: 256 bytes of a row
   constexpr int NGRP = KC / GK;                    // groups per chunk (2 bf16, 1 fp8)
@@ -56,11 +59,12 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   constexpr int XSEG = KC / 8;                     // 16-byte pieces per staged x row
   constexpr int XL = (COLS * XSEG + W * WAVE - 1) / (W * WAVE);  // x staging loads per thread
   constexpr int XBUF = COLS * XROW;                // bf16 per x buffer
+  constexpr int XBUFS = x_buffers(NT);
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int lane = tid % WAVE, m = lane % 16, kg = lane / 16;
-  uint8_t* tile = lds + (size_t)2 * XBUF * 2 + (size_t)wave * 16 * TROW;
+  uint8_t* tile = lds + (size_t)XBUFS * XBUF * 2 + (size_t)wave * 16 * TROW;
   // rows: output rows of the product (d_ff intermediate indices for gate+up); a tile
   // covers TR of them
   constexpr int TR = SILU ? 8 : 16;
@@ -144,9 +148,11 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   };
 
   // chunk c's weights and the next chunk's loads are in flight while chunk c's tiles
-  // are multiplied; one barrier per chunk hands the staged x over (each wave's weight
-  // tile is its own: LDS operations of one wave complete in order)
+  // are multiplied; a barrier hands the staged x over (two buffers: one barrier per
+  // chunk; one buffer: a second barrier before it is overwritten).  Each wave's weight
+  // tile is its own: LDS operations of one wave complete in order.
   {
+    constexpr int B1 = XBUFS == 2 ? 1 : 0;
     u32x4 wa[NGRP][4], wb[NGRP][4], xr[XL];
     load_x(c0, xr);
     load_w(c0, wa);
@@ -159,14 +165,16 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
       }
       mma_chunk(0, wa);
       if (c + 1 >= c1) break;
-      store_x(1, xr);
+      if (XBUFS == 1) __syncthreads();
+      store_x(B1, xr);
       __syncthreads();
       if (c + 2 < c1) {
         load_x(c + 2, xr);
         load_w(c + 2, wa);
       }
-      mma_chunk(1, wb);
+      mma_chunk(B1, wb);
       if (c + 2 >= c1) break;
+      if (XBUFS == 1) __syncthreads();
       store_x(0, xr);
       __syncthreads();
     }
@@ -252,7 +260,9 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   }
 }
 
-constexpr size_t lds_bytes(int NT, int W) { return (size_t)2 * NT * 16 * XROW * 2 + (size_t)W * 16 * TROW; }
+constexpr size_t lds_bytes(int NT, int W) {
+  return (size_t)x_buffers(NT) * NT * 16 * XROW * 2 + (size_t)W * 16 * TROW;
+}
 
 template <int NT, bool FP8, int EPI, bool KVFP8, int W>
 hipError_t go(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {

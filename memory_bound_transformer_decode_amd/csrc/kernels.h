@@ -69,8 +69,8 @@ struct GemmPlan {
 GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp);
 hipError_t launch_gemm_mfma(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, hipStream_t s);
 
-// y = matrix x for one of the epilogues; gemv kernels for Bp <= 8, MFMA tiles for
-// Bp >= 16 unless no_mfma.  Returns the number of kernels launched through *n.
+// y = matrix x for one of the epilogues: MFMA tiles when mfma, else the matrix-vector
+// kernels (batches above 8 rows in slices of 8).
 hipError_t launch_matmul(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, bool mfma,
                          hipStream_t s);
 

@@ -225,7 +225,7 @@ hipError_t gemv_go(const MatmulParams& p, hipStream_t s) {
 
 template <bool FP8, int EPI, bool KVFP8>
 hipError_t dispatch_bt(const MatmulParams& p, bool mfma, hipStream_t s) {
-  if (p.Bp <= 8 || !mfma) {
+  if (!mfma) {
     if (p.Bp <= 1) return gemv_go<1, FP8, EPI, KVFP8>(p, s);
     if (p.Bp <= 2) return gemv_go<2, FP8, EPI, KVFP8>(p, s);
     if (p.Bp <= 4) return gemv_go<4, FP8, EPI, KVFP8>(p, s);

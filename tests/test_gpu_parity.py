@@ -24,21 +24,38 @@ MINI = synth.ModelConfig("mini", 7, n_layers=2, d_model=320, n_q_heads=10, n_kv_
                          d_head=64, d_ff=1040, vocab=1000)
 MINI128 = synth.ModelConfig("mini128", 8, n_layers=2, d_model=256, n_q_heads=8, n_kv_heads=1,
                             d_head=128, d_ff=512, vocab=512)
-# g = 4 query heads per KV head: batches <= 8 run QKV and attention as one kernel
+# g = 4 query heads per KV head: with FLAG_FUSED_QKV_ATTN, the matrix-vector path runs
+# QKV and attention as one kernel
 MINI4 = synth.ModelConfig("mini4", 9, n_layers=2, d_model=320, n_q_heads=8, n_kv_heads=2,
                           d_head=64, d_ff=1040, vocab=1000)
 MINI4_128 = synth.ModelConfig("mini4x128", 10, n_layers=2, d_model=256, n_q_heads=8, n_kv_heads=2,
                               d_head=128, d_ff=512, vocab=512)
 
 
-def fused_qkv_attn(cfg, B):
-    """Whether the library runs QKV and attention as one kernel for this batch."""
-    return B <= 8 and cfg.n_q_heads // cfg.n_kv_heads <= 4 and cfg.d_head % 16 == 0
+LADDER = (1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64)
+FLAG_NO_MFMA, FLAG_FUSED = 4, 32  # dec.FLAG_NO_MFMA, dec.FLAG_FUSED_QKV_ATTN
+
+
+def bucket(B):
+    return next(b for b in LADDER if b >= B)
+
+
+def uses_mfma(cfg, B, flags=0):
+    """Whether the library runs the products on MFMA tiles: from the bucket of 8 rows
+    with bf16 weights, of 4 with E4M3 weights, unless FLAG_NO_MFMA."""
+    return not flags & FLAG_NO_MFMA and bucket(B) >= (4 if cfg.weight_dtype == "fp8" else 8)
+
+
+def fused_qkv_attn(cfg, B, flags=0):
+    """Whether the library runs QKV and attention as one kernel for this batch (the
+    matrix-vector path of buckets <= 8, g <= 4)."""
+    return (bool(flags & FLAG_FUSED) and not uses_mfma(cfg, B, flags) and bucket(B) <= 8
+            and cfg.n_q_heads // cfg.n_kv_heads <= 4 and cfg.d_head % 16 == 0)
 
 
 def kernels_per_step(cfg, B, flags=0):
-    if B <= 8:
-        per_layer = 4 if fused_qkv_attn(cfg, B) and flags & 32 else 5
+    if not uses_mfma(cfg, B, flags) and bucket(B) <= 8:
+        per_layer = 4 if fused_qkv_attn(cfg, B, flags) else 5
     else:
         per_layer = 7
     return per_layer * cfg.n_layers + 2
@@ -146,7 +163,7 @@ def test_graph_replay_equals_eager_bitwise(dec, B, persist):
     persistent = B <= 8 and persist
     assert ie.persistent == ig.persistent == int(persistent)
     # per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the
-    # matrix-vector kernels (batch <= 8) normalize their own input
+    # matrix-vector kernels (buckets below the MFMA threshold) normalize their own input
     expect = 1 if persistent else kernels_per_step(cfg, B)
     assert ie.kernels_per_step == ig.kernels_per_step == expect
 
@@ -172,7 +189,7 @@ def test_fused_qkv_attention(dec, w, kv, B):
     case = make_case(cfg, ctx_mix(B, rng), 128, seed=18, gains="random")
     ids = synth.make_token_ids(cfg, 3, B, seed=18)
     log(f"mini4 fused qkv+attention {w}/{kv} B={B}")
-    assert_ok(run_parity(case, ids, flags=dec.FLAG_FUSED_QKV_ATTN), cfg)
+    assert_ok(run_parity(case, ids, flags=dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_NO_MFMA), cfg)
 
 
 @pytest.mark.parametrize("cfg0", [MINI4, MINI4_128])
@@ -191,10 +208,11 @@ def test_fused_qkv_attention_matches_separate(dec, cfg0, kv, B):
     case = make_case(cfg, lens, 512, seed=19, gains="random")
     ids = synth.make_token_ids(cfg, 1, B, seed=19)[0]
     log(f"{cfg.name} fused vs separate B={B}")
-    zf, pf, inf_ = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_FUSED_QKV_ATTN)
-    zs, ps, ins = _one_step(dec, case, ids, case.ctx_lens, 0)
-    assert inf_.kernels_per_step == kernels_per_step(cfg, B, dec.FLAG_FUSED_QKV_ATTN) == 4 * cfg.n_layers + 2
-    assert ins.kernels_per_step == kernels_per_step(cfg, B) == 5 * cfg.n_layers + 2
+    mv = dec.FLAG_NO_MFMA  # the matrix-vector path, where the fused kernel applies
+    zf, pf, inf_ = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_FUSED_QKV_ATTN | mv)
+    zs, ps, ins = _one_step(dec, case, ids, case.ctx_lens, mv)
+    assert inf_.kernels_per_step == kernels_per_step(cfg, B, dec.FLAG_FUSED_QKV_ATTN | mv) == 4 * cfg.n_layers + 2
+    assert ins.kernels_per_step == kernels_per_step(cfg, B, mv) == 5 * cfg.n_layers + 2
     a, b = zf.double().cpu().numpy(), zs.double().cpu().numpy()
     R = a.max(axis=1) - a.min(axis=1)
     assert np.max(np.abs(a - b) / R[:, None]) < 5e-3
@@ -213,7 +231,7 @@ def test_fused_qkv_attention_several_blocks_per_wave(dec, kv):
     case = make_case(cfg, lens, 4096, seed=21)
     ids = synth.make_token_ids(cfg, 2, B, seed=21)
     log(f"{cfg.name} long contexts B={B}")
-    assert_ok(run_parity(case, ids, flags=dec.FLAG_FUSED_QKV_ATTN), cfg)
+    assert_ok(run_parity(case, ids, flags=dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_NO_MFMA), cfg)
 
 
 def test_fused_qkv_attention_repeated_steps(dec):
@@ -224,11 +242,11 @@ def test_fused_qkv_attention_repeated_steps(dec):
     case = make_case(cfg, [40, 7, 100], 128, seed=20)
     ids = synth.make_token_ids(cfg, 1, B, seed=20)[0]
     d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=4,
-                    max_seq_len=128, kv_pool=case.pool.clone(), flags=dec.FLAG_FUSED_QKV_ATTN)
+                    max_seq_len=128, kv_pool=case.pool.clone(), flags=dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_NO_MFMA)
     outs = [d.step(ids, case.ctx_lens, case.block_tables).clone() for _ in range(6)]
-    d.set_flags(dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_EAGER)
+    d.set_flags(dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_NO_MFMA | dec.FLAG_EAGER)
     ref = d.step(ids, case.ctx_lens, case.block_tables).clone()
-    d.set_flags(dec.FLAG_FUSED_QKV_ATTN)
+    d.set_flags(dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_NO_MFMA)
     outs.append(d.step(ids, case.ctx_lens, case.block_tables).clone())
     torch.cuda.synchronize()
     d.close()
@@ -362,11 +380,12 @@ def test_padding_rows_are_inert(dec, b_small, b_big):
     assert torch.equal(zs.view(torch.int32), zb[:b_small].view(torch.int32))
 
 
-def test_gemv_path_matches_mfma_path(dec):
+@pytest.mark.parametrize("B", [5, 24])
+def test_gemv_path_matches_mfma_path(dec, B):
     cfg = fmt(MINI, "bf16", "bf16")
     rng = np.random.default_rng(40)
-    case = make_case(cfg, ctx_mix(24, rng), 128, seed=8, gains="random")
-    ids = synth.make_token_ids(cfg, 2, 24, seed=8)
+    case = make_case(cfg, ctx_mix(B, rng), 128, seed=8, gains="random")
+    ids = synth.make_token_ids(cfg, 2, B, seed=8)
     assert_ok(run_parity(case, ids, flags=dec.FLAG_NO_MFMA), cfg)
     za, _, ia = _one_step(dec, case, ids[0], case.ctx_lens, 0)
     zb, _, ib = _one_step(dec, case, ids[0], case.ctx_lens, dec.FLAG_NO_MFMA)
