@@ -117,8 +117,7 @@ __device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const Q
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) s = fmaf(qf(h, e), kf[e], s);
-#pragma unroll
-      for (int off = 1; off < LPP; off <<= 1) s += __shfl_xor(s, off);
+      s = group_sum<LPP>(s);  // over the LPP lanes of the position row
       sc[ps][h] = valid ? s : -INFINITY;
     }
   }
@@ -267,6 +266,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
       }
     } else if (nb > 0) {
       // two blocks in flight: the next block's loads are issued before this one's math
+      // (four in flight measured slower: the registers they take)
       u32x4 kb2[NPASS], vb2[NPASS];
       if (!first) load_blk(0, ka, va);
       for (int i = 0; i < nb; i += 2) {

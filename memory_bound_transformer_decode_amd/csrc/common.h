@@ -149,6 +149,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over aligned groups of N = 8 or 16 lanes, every lane of a group receiving the
+// group's sum, with DPP lane moves inside a 16-lane row (no trip through the LDS
+// crossbar that __shfl_xor takes): swap neighbours, swap pairs, mirror each half-row
+// (lane i <-> 7 - i, which pairs the two quads of a half), and for 16 mirror the row
+// (lane i <-> 15 - i, which pairs its two halves).  Each step adds a value that covers
+// a disjoint set of lanes, and fp addition is commutative, so all lanes of a group end
+// with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16, "8- or 16-lane groups");
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  if (N == 16) v += dpp_mov<0x140>(v);  // row_mirror
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
