@@ -109,6 +109,7 @@ struct Layout {
   size_t uf;                           // unfused step: fp32 product rows [MB][max(N)]
   size_t mats, bar, attn_cnt, err;     // persistent-step state
   size_t ready;                        // QKV + attention kernel: [n_kv_heads] counters, 256 B apart
+  size_t ssq;                          // folded RMSNorm: row-block sums of squares
   size_t gpart, gcnt;                  // MFMA products split over K: partial tiles, row-block counters
   size_t gpart_floats, gcnt_n;
   size_t total;
@@ -187,6 +188,8 @@ Layout layout_of(const dec_config& c) {
   off = align256(off + 4);
   L.ready = off;
   off = align256(off + (size_t)c.n_kv_heads * dec::COUNTER_STRIDE * 4);
+  L.ssq = off;
+  off = align256(off + (size_t)dec::GEMM_SSQ_MAX * dec::GEMM_SSQ_STRIDE * 4);
   L.gcnt = off;
   off = align256(off + n_rb * dec::COUNTER_STRIDE * 4);
   L.total = off;
@@ -391,6 +394,39 @@ bool use_mfma(const dec_config& g, int Bp) {
          Bp >= (g.weight_dtype == DEC_FP8_E4M3 ? MFMA_MIN_BATCH_FP8 : MFMA_MIN_BATCH_BF16);
 }
 
+// Row blocks of the residual products (O, down) on the MFMA tiles: the number of
+// row-block sums of squares a folded RMSNorm adds up.
+int residual_row_blocks(const dec_config& g, int Bp) {
+  return dec::gemm_plan(g.d_model, 1, g.d_model, Bp).n_rb;
+}
+
+// The MFMA plan folds the two RMSNorms of a layer and the final one into the products:
+// O and down write the next norm's input times its gain (x) and their row blocks' sums of
+// squares of h; QKV (past layer 0, whose x the embedding kernel normalizes), gate+up and
+// the LM head scale their sums by 1 / rms.  Up to GEMM_SSQ_MAX row blocks; not in the
+// unfused step, which runs the norms as kernels of their own.
+bool fold_norm(const dec_config& g, int Bp) {
+  return use_mfma(g, Bp) && !(g.flags & DEC_FLAG_UNFUSED) && residual_row_blocks(g, Bp) <= dec::GEMM_SSQ_MAX;
+}
+
+void set_fold_norm(dec_ctx* c, int which, int l, int Bp, dec::MatmulParams& p) {
+  const dec_config& g = c->cfg;
+  const int d = g.d_model;
+  float* ssq = ws_ptr<float>(c, c->L.ssq);
+  p.eps = g.rms_eps;
+  if (which == DEC_MAT_O || which == DEC_MAT_DOWN) {
+    p.xout = ws_ptr<uint16_t>(c, c->L.x);
+    p.ldxo = d;
+    p.xg = which == DEC_MAT_O ? c->mlp_norm + (size_t)l * d
+           : l + 1 < g.n_layers ? c->attn_norm + (size_t)(l + 1) * d : c->final_norm;
+    p.ssq_out = ssq;
+  } else if (which == DEC_MAT_GATE_UP || (which == DEC_MAT_QKV && l > 0) ||
+             (which == DEC_MAT_LM_HEAD && g.n_layers > 0)) {
+    p.ssq_in = ssq;
+    p.ssq_n = residual_row_blocks(g, Bp);
+  }
+}
+
 // norm_gain: when set, the kernel computes x = RMSNorm(h) norm_gain itself (fused_norm)
 hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const float* norm_gain = nullptr) {
   const dec_config& g = c->cfg;
@@ -401,6 +437,7 @@ hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const
     p.ng = norm_gain;
     p.eps = g.rms_eps;
   }
+  if (fold_norm(g, Bp)) set_fold_norm(c, which, l, Bp, p);
   return dec::launch_matmul(p, epi, g.weight_dtype == DEC_FP8_E4M3, g.kv_dtype == DEC_FP8_E4M3, use_mfma(g, Bp), s);
 }
 
@@ -613,9 +650,12 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
     ap.err_host = c->err_host_dev;
     ap.timeout_ticks = c->timeout_ticks;
   }
+  // no RMSNorm kernels: the matrix-vector kernels normalize their own input (fn), or the
+  // MFMA products fold the norms (fold)
+  const bool nk = !fn && !fold_norm(g, Bp);
   for (int l = 0; l < g.n_layers; ++l) {
     const float* an = c->attn_norm + (size_t)l * d;
-    if (l > 0 && !fn) {
+    if (l > 0 && nk) {
       np.gain = an;
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
@@ -637,14 +677,14 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
     if ((e = run_matmul(c, DEC_MAT_O, l, Bp, s)) != hipSuccess) return e;
     // x = RMSNorm(h) g_mlp
     const float* mn = c->mlp_norm + (size_t)l * d;
-    if (!fn) {
+    if (nk) {
       np.gain = mn;
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
     if ((e = run_matmul(c, DEC_MAT_GATE_UP, l, Bp, s, fn ? mn : nullptr)) != hipSuccess) return e;
     if ((e = run_matmul(c, DEC_MAT_DOWN, l, Bp, s)) != hipSuccess) return e;
   }
-  if (g.n_layers > 0 && !fn) {
+  if (g.n_layers > 0 && nk) {
     np.gain = c->final_norm;
     if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
   }
@@ -894,10 +934,11 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
   const int slices = (!mfma && Bp > 8) ? Bp / 8 : 1;
   const int L = g.n_layers;
   // per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the
-  // matrix-vector kernels fuse them (and QKV + attention as one kernel where
-  // fuse_qkv_attn holds); unfused: also RoPE + KV write, SiLU x mul and two residual adds
+  // matrix-vector kernels fuse them or the MFMA products fold them (and QKV + attention
+  // as one kernel where fuse_qkv_attn holds); unfused: also RoPE + KV write, SiLU x mul
+  // and two residual adds
   const bool unfused = (g.flags & DEC_FLAG_UNFUSED) != 0;
-  const int per_layer = unfused ? 11 : fuse_qkv_attn(c, Bp) ? 4 : fused_norm(g, Bp) ? 5 : 7;
+  const int per_layer = unfused ? 11 : fuse_qkv_attn(c, Bp) ? 4 : fused_norm(g, Bp) || fold_norm(g, Bp) ? 5 : 7;
   c->info.kernels_per_step = persist ? 1 : 2 + per_layer * L + (slices - 1) * (4 * L + 1);
   c->info.bucket = Bp;
   c->last_n = n;

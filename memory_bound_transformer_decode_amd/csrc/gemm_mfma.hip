@@ -151,11 +151,29 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   // are multiplied; a barrier hands the staged x over (two buffers: one barrier per
   // chunk; one buffer: a second barrier before it is overwritten).  Each wave's weight
   // tile is its own: LDS operations of one wave complete in order.
+  // folded RMSNorm (ssq_n > 0): thread (part, column) adds the producer's row-block sums
+  // of squares i = part, part + W, ... of its batch column; loaded ahead of the first
+  // chunk, added once those loads are out; combined per column in the epilogue
+  __shared__ float ssq_s[W][GEMM_SSQ_STRIDE];
+  constexpr int SPER = (GEMM_SSQ_MAX + W - 1) / W;
   {
     constexpr int B1 = XBUFS == 2 ? 1 : 0;
     u32x4 wa[NGRP][4], wb[NGRP][4], xr[XL];
+    const int scol = tid % GEMM_SSQ_STRIDE, spart = tid / GEMM_SSQ_STRIDE;
+    float sv[SPER];
+    if (p.ssq_n > 0) {
+      const float* sp = p.ssq_in + min(scol, p.Bp - 1);
+#pragma unroll
+      for (int j = 0; j < SPER; ++j) sv[j] = gld(sp + (size_t)min(spart + j * W, p.ssq_n - 1) * GEMM_SSQ_STRIDE);
+    }
     load_x(c0, xr);
     load_w(c0, wa);
+    if (p.ssq_n > 0) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < SPER; ++j) ss += spart + j * W < p.ssq_n ? sv[j] : 0.f;
+      ssq_s[spart][scol] = ss;
+    }
     store_x(0, xr);
     __syncthreads();
     for (int c = c0; c < c1; c += 2) {
@@ -214,8 +232,21 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   }
 
   // epilogue: lane holds tile rows 4 kg + j (j = 0..3) of batch column t 16 + m
+  if (p.ssq_n > 0) {
+    // the folded RMSNorm's 1 / rms of each batch column, on the sums
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int col = t * 16 + m;
+      float ss = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) ss += ssq_s[w][col];
+      acc[t] *= 1.0f / sqrtf(ss / (float)p.K + p.eps);
+    }
+  }
+  float sq[NT];  // residual products that fold the next norm: this lane's sum of h^2
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
+    sq[t] = 0.f;
     const int col = t * 16 + m;
     if (SILU) {
       // gate rows are tile rows 0..7 (lane groups 0, 1), up rows 8..15 (lane groups 2, 3):
@@ -251,11 +282,34 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
         const int r = r0 + j;
         if (r >= rows) break;
         const float y = acc[t][j] * (p.scale ? gld(p.scale + r) : 1.f);
-        if (EPI == EPI_RESID)
-          gst(o + r, gld(o + r) + y);
-        else
+        if (EPI == EPI_RESID) {
+          const float hn = gld(o + r) + y;
+          gst(o + r, hn);
+          if (p.xout) {
+            gst(p.xout + (int64_t)col * p.ldxo + r, f32_to_bf16(hn * gld(p.xg + r)));
+            sq[t] += hn * hn;
+          }
+        } else {
           gst(o + r, y);
+        }
       }
+    }
+  }
+  if (EPI == EPI_RESID && p.xout) {
+    // the row block's sum of h^2 per batch column: over the lane's rows (above), the four
+    // lane groups, then the waves in order
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      sq[t] += __shfl_xor(sq[t], 16);
+      sq[t] += __shfl_xor(sq[t], 32);
+      if (kg == 0) ssq_s[wave][t * 16 + m] = sq[t];
+    }
+    __syncthreads();
+    if (tid < p.Bp) {
+      float ss = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) ss += ssq_s[w][tid];
+      gst(p.ssq_out + (int64_t)rb * GEMM_SSQ_STRIDE + tid, ss);
     }
   }
 }
@@ -318,6 +372,10 @@ hipError_t launch_gemm_mfma(const MatmulParams& p, int epi, bool w_fp8, bool kv_
   if (p.Bp > 64 || p.K < 16 || p.K % 16) return hipErrorInvalidValue;
   const GemmPlan g = gemm_plan(rows, epi == EPI_SILU ? 2 : 1, p.K, p.Bp);
   if (g.ks > 1 && (!p.gpart || !p.gcnt || g.part_floats > p.gpart_floats || g.n_rb > p.gcnt_n))
+    return hipErrorInvalidValue;
+  // the folded RMSNorm: row-block sums within GEMM_SSQ_MAX x GEMM_SSQ_STRIDE
+  if (p.ssq_n > GEMM_SSQ_MAX || (p.ssq_n > 0 && !p.ssq_in) ||
+      (p.xout && (epi != EPI_RESID || !p.xg || !p.ssq_out || g.n_rb > GEMM_SSQ_MAX)))
     return hipErrorInvalidValue;
   switch (epi) {
     case EPI_LOGITS:

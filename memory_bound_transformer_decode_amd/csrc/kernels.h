@@ -53,6 +53,19 @@ struct MatmulParams {
   unsigned* gcnt;
   size_t gpart_floats;   // capacity of gpart
   int gcnt_n;            // counters at gcnt
+  // RMSNorm folded into the MFMA products (the norm's 1 / rms is one factor per batch
+  // row, so it can be applied to the products' sums).  A residual-add product (O, down)
+  // with xout set also writes xout[b][r] = bf16(h_new[b][r] xg[r]) -- the next norm's
+  // input times its gain -- and, for its row block rb, ssq_out[rb GEMM_SSQ_STRIDE + b] =
+  // the sum of h_new[b][r]^2 over the block's rows.  A product with ssq_n > 0 multiplies
+  // its sums for batch row b by 1 / sqrt(sum_{i < ssq_n} ssq_in[i GEMM_SSQ_STRIDE + b] / K
+  // + eps).
+  uint16_t* xout;
+  int ldxo;
+  const float* xg;
+  float* ssq_out;
+  const float* ssq_in;
+  int ssq_n;
 };
 
 // MFMA products (Bp 16..64): row blocks of GEMM_WAVES 16-row tiles, K split over
@@ -67,6 +80,10 @@ struct GemmPlan {
 };
 // rows: per group (d_ff for gate+up, whose groups are 2); K; padded batch
 GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp);
+// row-block sums of squares of the folded RMSNorm: at most GEMM_SSQ_MAX row blocks of
+// the residual products (d_model <= 8192), GEMM_SSQ_STRIDE batch rows apart
+constexpr int GEMM_SSQ_MAX = 128;
+constexpr int GEMM_SSQ_STRIDE = 64;
 hipError_t launch_gemm_mfma(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, hipStream_t s);
 
 // y = matrix x for one of the epilogues: MFMA tiles when mfma, else the matrix-vector

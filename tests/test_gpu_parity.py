@@ -54,7 +54,12 @@ def fused_qkv_attn(cfg, B, flags=0):
 
 
 def kernels_per_step(cfg, B, flags=0):
-    if not uses_mfma(cfg, B, flags) and bucket(B) <= 8:
+    """Kernels of one step: per layer QKV, attention, O, gate+up, down, plus two RMSNorm
+    kernels unless the matrix-vector kernels normalize their own input or the MFMA
+    products fold the norms (d_model <= 8192); embedding and LM head."""
+    if uses_mfma(cfg, B, flags):
+        per_layer = 5 if cfg.d_model <= 8192 else 7
+    elif bucket(B) <= 8:
         per_layer = 4 if fused_qkv_attn(cfg, B, flags) else 5
     else:
         per_layer = 7
