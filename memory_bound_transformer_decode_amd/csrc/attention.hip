@@ -35,11 +35,23 @@ __global__ __launch_bounds__(WAVE * NW) void k_attn_split(AttnParams p) {
   attn_unit<DH, FP8, G, NW>(p, blockIdx.x, blockIdx.y, blockIdx.z, S);
 }
 
+// The same work with each wave's blocks on the matrix cores (attn_wave_mfma): for batches
+// where the per-position arithmetic of the vector form is what the kernel waits on.
+template <int DH, bool FP8, int G, int NW>
+__global__ __launch_bounds__(WAVE * NW) void k_attn_mfma(AttnParams p) {
+  __shared__ AttnSmem<DH, G, NW> S;
+  __shared__ __align__(16) uint8_t vt[NW * 16 * attn_vt_row<DH>()];
+  attn_unit<DH, FP8, G, NW, false, true>(p, blockIdx.x, blockIdx.y, blockIdx.z, S, vt);
+}
+
 namespace {
 template <int DH, bool FP8, int G>
 hipError_t attn_g(const AttnParams& p, hipStream_t s) {
   const dim3 grid(p.n_split, p.Hkv, p.Bp);
-  hipLaunchKernelGGL((k_attn_split<DH, FP8, G, ATTN_WAVES>), grid, dim3(WAVE * ATTN_WAVES), 0, s, p);
+  if (p.mfma)
+    hipLaunchKernelGGL((k_attn_mfma<DH, FP8, G, ATTN_WAVES>), grid, dim3(WAVE * ATTN_WAVES), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_attn_split<DH, FP8, G, ATTN_WAVES>), grid, dim3(WAVE * ATTN_WAVES), 0, s, p);
   return hipGetLastError();
 }
 

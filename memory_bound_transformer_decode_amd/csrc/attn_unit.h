@@ -154,14 +154,181 @@ __device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const Q
   }
 }
 
+// V tile of one wave for the MFMA form: 16 position rows of DH bf16, padded by 16 bytes
+template <int DH>
+constexpr int attn_vt_row() { return DH * 2 + 16; }
+
+// The MFMA form of one wave's blocks (batches where attention's arithmetic, not its
+// memory latency, sets the pace: the scores and the P V products on the matrix cores).
+// Per block of 16 positions:
+//   S^T = K q^T     v_mfma_f32_16x16x32_bf16, A = K rows (the 16 positions), B = the
+//                   group's queries as 16 columns (heads >= G are zero); lane l ends with
+//                   S[position 4 (l / 16) + j][head l % 16], j < 4;
+//   online softmax per head (column): the block's max over the lane's 4 positions and the
+//                   four lane groups; running max, this lane's share of the sum, and the
+//                   output rescaled in the lane's registers;
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16, A = V^T (16 dims x 16 positions, from the
+//                   wave's LDS tile), B = the probabilities exactly as the lane holds them.
+// q and P enter as bf16 high and low parts (two products each), so the scores and the
+// weighted sum keep about 16 bits of their fp32 operands.  Writes the wave's running max,
+// sum and output of each head h < G to sm, sl and so.
+template <int DH, bool FP8, int G, int NW>
+__device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c, int lane, int nb, int bfirst,
+                                               int ntok, int my_phys, uint8_t* vt, float* sm, float* sl,
+                                               float (*so)[DH]) {
+  constexpr int NS = DH / 32;   // score k-steps
+  constexpr int NC = DH / 16;   // output dim chunks
+  constexpr int TR = attn_vt_row<DH>();
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const int m = lane % 16, g = lane / 16;
+  const bool hv = m < G;
+  const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
+
+  // q^T operands of head m: elements s 32 + 8 g + [0, 8), scaled, as bf16 high + low
+  const float qscale = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
+  bf16x8 qh[NS], ql[NS];
+  {
+    const float* qp = p.q + ((int64_t)b * p.Hq + c * G + (hv ? m : 0)) * DH;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const f32x4 a0 = gld(reinterpret_cast<const f32x4*>(qp + s * 32 + g * 8));
+      const f32x4 a1 = gld(reinterpret_cast<const f32x4*>(qp + s * 32 + g * 8 + 4));
+      const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = hv ? x[e] * qscale : 0.f;
+        const uint16_t hi = f32_to_bf16(v);
+        qh[s][e] = __builtin_bit_cast(__bf16, hi);
+        ql[s][e] = __builtin_bit_cast(__bf16, f32_to_bf16(v - bf16_to_f32(hi)));
+      }
+    }
+  }
+
+  // the lane's 8 elements of K and V row m per k-step: bf16 (16 bytes) or E4M3 (8 bytes)
+  typedef u32x4 KVReg[2][NS];
+  auto load = [&](int i, KVReg& r) {
+    const int phys = __shfl(my_phys, i);
+    const int64_t kb = kv_offset(p.layer, 0, phys, c, 0, 0, p.num_blocks, p.Hkv, DH) + (int64_t)m * DH;
+    const int64_t vb = kv_offset(p.layer, 1, phys, c, 0, 0, p.num_blocks, p.Hkv, DH) + (int64_t)m * DH;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int e = s * 32 + g * 8;
+      if (FP8) {
+        const u32x2 k2 = gld(reinterpret_cast<const u32x2*>(pool + kb + e));
+        const u32x2 v2 = gld(reinterpret_cast<const u32x2*>(pool + vb + e));
+        r[0][s] = u32x4{k2.x, k2.y, 0u, 0u};
+        r[1][s] = u32x4{v2.x, v2.y, 0u, 0u};
+      } else {
+        r[0][s] = gld16(pool + (kb + e) * 2);
+        r[1][s] = gld16(pool + (vb + e) * 2);
+      }
+    }
+  };
+  auto as_bf16x8 = [&](const u32x4& w) -> bf16x8 {
+    if (FP8) {
+      const bf16x2 a = e4m3x2_to_bf16x2<false>(w.x), bb = e4m3x2_to_bf16x2<true>(w.x);
+      const bf16x2 cc = e4m3x2_to_bf16x2<false>(w.y), d = e4m3x2_to_bf16x2<true>(w.y);
+      return bf16x8{a.x, a.y, bb.x, bb.y, cc.x, cc.y, d.x, d.y};
+    }
+    return __builtin_bit_cast(bf16x8, w);
+  };
+
+  float mrun = -INFINITY, lrun = 0.f;  // head m; lrun: this lane's positions only
+  f32x4 o[NC];
+#pragma unroll
+  for (int t = 0; t < NC; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto block = [&](int i, const KVReg& r) {
+    const int pos0 = (bfirst + i * NW) * KV_BLOCK;
+    // V row m into the tile; zeros past the last position (those slots may hold
+    // anything, even NaN, which a zero probability would not cancel in the product)
+    const bool rv = pos0 + m < ntok;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 v = as_bf16x8(r[1][s]);
+      *reinterpret_cast<u32x4*>(vt + m * TR + (s * 32 + g * 8) * 2) =
+          rv ? __builtin_bit_cast(u32x4, v) : u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 kv = as_bf16x8(r[0][s]);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[s], sa, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[s], sa, 0, 0, 0);
+    }
+    float sc[4], bm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = pos0 + 4 * g + j < ntok ? sa[j] : -INFINITY;
+      bm = fmaxf(bm, sc[j]);
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(mrun, bm);  // finite: the block's first position is valid
+    const float alpha = exp2f(mrun - mn);
+    mrun = mn;
+    bf16x4 ph, pl;
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float pj = exp2f(sc[j] - mn);
+      ps += pj;
+      const uint16_t hi = f32_to_bf16(pj);
+      ph[j] = __builtin_bit_cast(__bf16, hi);
+      pl[j] = __builtin_bit_cast(__bf16, f32_to_bf16(pj - bf16_to_f32(hi)));
+    }
+    lrun = lrun * alpha + ps;
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      o[t] *= alpha;
+      // V^T[dim 16 t + m][positions 4 g .. 4 g + 3] from the tile
+      bf16x4 va;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) va[j] = *reinterpret_cast<const __bf16*>(vt + (4 * g + j) * TR + (16 * t + m) * 2);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, o[t], 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, o[t], 0, 0, 0);
+    }
+  };
+
+  // two blocks in flight: the next block's loads are issued before this one's math
+  if (nb > 0) {
+    KVReg ra, rb;
+    load(0, ra);
+    for (int i = 0; i < nb; i += 2) {
+      if (i + 1 < nb) load(i + 1, rb);
+      block(i, ra);
+      if (i + 1 >= nb) break;
+      if (i + 2 < nb) load(i + 2, ra);
+      block(i + 1, rb);
+    }
+  }
+  // the sum over the four lane groups' positions
+  lrun += __shfl_xor(lrun, 16);
+  lrun += __shfl_xor(lrun, 32);
+  if (hv) {
+    // o[t][j] = O[head m][dim 16 t + 4 g + j]
+#pragma unroll
+    for (int t = 0; t < NC; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) so[m][16 * t + 4 * g + j] = o[t][j];
+    if (g == 0) {
+      sm[m] = mrun;
+      sl[m] = lrun;
+    }
+  }
+}
+
 // One work group computes one (split, kv head c, sequence b) unit of attention.  With
 // one split it writes o; otherwise it writes its partial, and the last split of the
 // group to arrive combines.  o is written device-coherently.
 // FUSED: q and the new token's K/V are written by other work groups of the same kernel.
 // The block ids and the first block (unless it holds the new token) are loaded before
 // waiting for them; q and the new token's block are then read device-coherently.
-template <int DH, bool FP8, int G, int NW, bool FUSED = false>
-__device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c, int b, AttnSmem<DH, G, NW>& S) {
+// MF: the wave's blocks in the MFMA form (attn_wave_mfma), with the wave's V tile at
+// vtile + wave 16 attn_vt_row<DH>() bytes of LDS.
+template <int DH, bool FP8, int G, int NW, bool FUSED = false, bool MF = false>
+__device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c, int b, AttnSmem<DH, G, NW>& S,
+                                          uint8_t* vtile = nullptr) {
   constexpr int EPL = 8;             // cache elements per lane per row
   constexpr int LPP = DH / EPL;      // lanes per position row
   constexpr int PPP = WAVE / LPP;    // positions per pass
@@ -189,6 +356,11 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
     const bool coh = FUSED && blk0 + wave + i * NW == nblk - 1;
     attn_load<DH, FP8, NPASS, PPP>(pool, kb, vb, prow, eoff, kr, vr, coh);
   };
+  if constexpr (MF) {
+    static_assert(!FUSED, "the MFMA form is the attention kernel's");
+    attn_wave_mfma<DH, FP8, G, NW>(p, b, c, lane, nb, blk0 + wave, ntok, my_phys,
+                                   vtile + wave * 16 * attn_vt_row<DH>(), S.sm[wave], S.sl[wave], S.so[wave]);
+  } else {
   u32x4 ka[NPASS], va[NPASS];
   bool first = false;  // block 0 already in ka/va
   if (FUSED) {
@@ -305,7 +477,11 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
     __builtin_amdgcn_sched_barrier(0);
     chunk(std::integral_constant<int, GH>{});
   }
+  }
   __syncthreads();
+  auto& sm = S.sm;
+  auto& sl = S.sl;
+  auto& so = S.so;
   const bool single = p.n_split == 1;
   for (int idx = threadIdx.x; idx < G * DH; idx += NW * WAVE) {
     const int h = idx / DH, e = idx % DH;

@@ -427,6 +427,16 @@ void set_fold_norm(dec_ctx* c, int which, int l, int Bp, dec::MatmulParams& p) {
   }
 }
 
+// Attention's arithmetic on the matrix cores (k_attn_mfma) from buckets of
+// ATTN_MFMA_MIN_BATCH rows (unless DEC_FLAG_NO_MFMA): there many (sequence, kv head)
+// work groups share the chip and the vector form's per-position arithmetic sets the pace;
+// below, a wave has about one block and waits on memory either way.
+#ifndef DEC_ATTN_MFMA_MIN_BATCH
+#define DEC_ATTN_MFMA_MIN_BATCH 16
+#endif
+constexpr int ATTN_MFMA_MIN_BATCH = DEC_ATTN_MFMA_MIN_BATCH;
+bool attn_mfma(const dec_config& g, int Bp) { return !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= ATTN_MFMA_MIN_BATCH; }
+
 // norm_gain: when set, the kernel computes x = RMSNorm(h) norm_gain itself (fused_norm)
 hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const float* norm_gain = nullptr) {
   const dec_config& g = c->cfg;
@@ -567,6 +577,7 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, hipStream_t s) {
   ap.num_blocks = g.num_blocks;
   ap.bps = blocks_per_seq(g);
   ap.n_split = n_split_for(g, Bp);
+  ap.mfma = attn_mfma(g, Bp) ? 1 : 0;
   for (int l = 0; l < g.n_layers; ++l) {
     if (l > 0) {
       np.gain = c->attn_norm + (size_t)l * d;
@@ -637,6 +648,7 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
   ap.num_blocks = g.num_blocks;
   ap.bps = bps;
   ap.n_split = n_split_for(g, Bp);
+  ap.mfma = attn_mfma(g, Bp) ? 1 : 0;
   ap.cnt = ws_ptr<unsigned>(c, c->L.attn_cnt);
 
   // the matrix-vector kernels normalize their own input (no RMSNorm kernels)

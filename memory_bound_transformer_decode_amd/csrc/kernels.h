@@ -118,6 +118,7 @@ struct AttnParams {
   uint16_t* o;            // [Bp][Hq * dh] bf16 out
   unsigned* cnt;          // [Bp][Hkv] split arrival counters, zero between launches
   int Bp, Hq, Hkv, dh, num_blocks, bps, n_split;
+  int mfma;               // the MFMA form of the blocks' arithmetic (k_attn_mfma)
   // QKV + attention kernel only: per kv head c, work groups that wrote its q/k/v rows
   // (ready[c COUNTER_STRIDE], complete at ready_target); zero at the launch (the
   // O-projection kernel that follows clears them: MatmulParams::rearm)
