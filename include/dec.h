@@ -70,7 +70,7 @@ enum {
   DEC_FLAG_UNFUSED = 2u,     /* one kernel per op, intermediates through HBM (measurement only):
                                 RMSNorm kernels, the matrix kernels with fp32 outputs, then RoPE +
                                 KV write, SiLU x mul and residual adds as kernels of their own */
-  DEC_FLAG_NO_MFMA = 4u,     /* matrix-vector kernels at every batch size (no MFMA tiles) */
+  DEC_FLAG_NO_MFMA = 4u,     /* matrix-vector kernels and vector attention at every batch size (no MFMA) */
   DEC_FLAG_CAPTURE_ALL = 8u, /* capture every batch bucket at the first step instead of lazily */
   DEC_FLAG_PERSISTENT = 16u, /* a padded batch of <= 8 whose layer input fits in LDS runs the
                                 whole step as one persistent kernel with grid barriers; without
