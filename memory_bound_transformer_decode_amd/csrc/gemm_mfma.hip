@@ -151,6 +151,43 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   // are multiplied; a barrier hands the staged x over (two buffers: one barrier per
   // chunk; one buffer: a second barrier before it is overwritten).  Each wave's weight
   // tile is its own: LDS operations of one wave complete in order.
+  // What the epilogue reads besides the sums, fetched at kernel start so that these loads
+  // overlap the weight stream: for the lane's four rows r0 .. r0 + 3 (in range: full)
+  // and each of its batch columns, the row scales, the residual rows (O, down), and for
+  // QKV the token's position, the RoPE angles of the lane's two row pairs (adjacent in
+  // the table: r0 is a multiple of 4, d_head of 64) and the cache block.
+  const int er0 = row0 + 4 * kg;
+  const bool full = er0 + 4 <= rows;
+  f32x4 e_sc = f32x4{1.f, 1.f, 1.f, 1.f}, e_su = f32x4{1.f, 1.f, 1.f, 1.f};
+  f32x4 e_h[EPI == EPI_RESID ? NT : 1];
+  int e_pos[EPI == EPI_QKV ? NT : 1], e_blk[EPI == EPI_QKV ? NT : 1];
+  f32x4 e_cs[EPI == EPI_QKV ? NT : 1];
+  auto epi_prefetch = [&]() {
+    if (!full) return;
+    if (p.scale) {
+      e_sc = gld(reinterpret_cast<const f32x4*>(p.scale + er0));
+      if (SILU) e_su = gld(reinterpret_cast<const f32x4*>(p.scale + p.d_ff + er0));
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int col = min(t * 16 + m, p.Bp - 1);
+      if (EPI == EPI_RESID) e_h[t] = gld(reinterpret_cast<const f32x4*>(p.out + (int64_t)col * p.ldo + er0));
+      if (EPI == EPI_QKV) e_pos[t] = gld(p.seq_lens + col);
+    }
+    if (EPI == EPI_QKV) {
+      const int qrows = p.Hq * p.dh, krows = p.Hkv * p.dh;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int col = min(t * 16 + m, p.Bp - 1);
+        const int pr = e_pos[t] < 0 ? 0 : e_pos[t];
+        e_cs[t] = er0 < qrows + krows
+                      ? gld(reinterpret_cast<const f32x4*>(p.rope + (int64_t)pr * (p.dh / 2) + ((er0 % p.dh) >> 1)))
+                      : f32x4{1.f, 0.f, 1.f, 0.f};
+        e_blk[t] = er0 >= qrows && e_pos[t] >= 0 ? gld(p.bt + (int64_t)col * p.bps + e_pos[t] / KV_BLOCK) : 0;
+      }
+    }
+  };
+
   // folded RMSNorm (ssq_n > 0): thread (part, column) adds the producer's row-block sums
   // of squares i = part, part + W, ... of its batch column; loaded ahead of the first
   // chunk, added once those loads are out; combined per column in the epilogue
@@ -168,6 +205,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
     }
     load_x(c0, xr);
     load_w(c0, wa);
+    epi_prefetch();
     if (p.ssq_n > 0) {
       float ss = 0.f;
 #pragma unroll
@@ -260,7 +298,8 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
       for (int j = 0; j < 4; ++j) {
         const int r = row0 + 4 * kg + j;
         if (r >= rows) break;
-        const float sg = p.scale ? gld(p.scale + r) : 1.f, su = p.scale ? gld(p.scale + p.d_ff + r) : 1.f;
+        const float sg = full ? e_sc[j] : p.scale ? gld(p.scale + r) : 1.f;
+        const float su = full ? e_su[j] : p.scale ? gld(p.scale + p.d_ff + r) : 1.f;
         gst(o + r, f32_to_bf16(silu_f(acc[t][j] * sg) * (up[j] * su)));
       }
       continue;
@@ -268,6 +307,39 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
     if (col >= p.Bp) continue;
     const int r0 = row0 + 4 * kg;
     if (EPI == EPI_QKV) {
+      if (full) {
+        // rows r0 .. r0 + 3 lie in one head (r0 % 4 == 0, d_head % 4 == 0)
+        const int qrows = p.Hq * p.dh, krows = p.Hkv * p.dh, dh = p.dh;
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = acc[t][j] * e_sc[j];
+        if (r0 < qrows + krows) {  // q or k: rotate the adjacent pairs
+          const f32x4 cs = e_cs[t];
+          const float a0 = y[0] * cs.x - y[1] * cs.y, a1 = y[0] * cs.y + y[1] * cs.x;
+          const float b0 = y[2] * cs.z - y[3] * cs.w, b1 = y[2] * cs.w + y[3] * cs.z;
+          y[0] = a0; y[1] = a1; y[2] = b0; y[3] = b1;
+        }
+        if (r0 < qrows) {
+          float* qp = p.q + ((int64_t)col * p.Hq + r0 / dh) * dh + r0 % dh;
+          cst_f2(qp, y[0], y[1]);
+          cst_f2(qp + 2, y[2], y[3]);
+        } else if (e_pos[t] >= 0) {  // padded rows write no cache slot
+          const int kv = r0 < qrows + krows ? 0 : 1;
+          const int rr = r0 - qrows - kv * krows;
+          const int64_t off = kv_offset(p.layer, kv, e_blk[t], rr / dh, e_pos[t] % KV_BLOCK, rr % dh, p.num_blocks,
+                                        p.Hkv, dh);
+          if (KVFP8) {
+            const uint32_t w = f32_to_e4m3(y[0]) | (f32_to_e4m3(y[1]) << 8) | (f32_to_e4m3(y[2]) << 16) |
+                               (f32_to_e4m3(y[3]) << 24);
+            cst(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p.pool) + off), w);
+          } else {
+            const uint64_t w = (uint64_t)f32_to_bf16(y[0]) | ((uint64_t)f32_to_bf16(y[1]) << 16) |
+                               ((uint64_t)f32_to_bf16(y[2]) << 32) | ((uint64_t)f32_to_bf16(y[3]) << 48);
+            cst(reinterpret_cast<uint64_t*>(static_cast<uint16_t*>(p.pool) + off), w);
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
         const int r = r0 + j;  // even; rows is a multiple of d_head
@@ -281,9 +353,9 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
       for (int j = 0; j < 4; ++j) {
         const int r = r0 + j;
         if (r >= rows) break;
-        const float y = acc[t][j] * (p.scale ? gld(p.scale + r) : 1.f);
+        const float y = acc[t][j] * (full ? e_sc[j] : p.scale ? gld(p.scale + r) : 1.f);
         if (EPI == EPI_RESID) {
-          const float hn = gld(o + r) + y;
+          const float hn = (full ? e_h[t][j] : gld(o + r)) + y;
           gst(o + r, hn);
           if (p.xout) {
             gst(p.xout + (int64_t)col * p.ldxo + r, f32_to_bf16(hn * gld(p.xg + r)));
