@@ -154,6 +154,11 @@ __device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const Q
   }
 }
 
+#ifndef DEC_ATTN_MFMA_DEPTH
+#define DEC_ATTN_MFMA_DEPTH 2
+#endif
+constexpr int ATTN_MFMA_DEPTH = DEC_ATTN_MFMA_DEPTH;  // KV blocks in flight per wave (MFMA form)
+
 // V tile of one wave for the MFMA form: 16 position rows of DH bf16, padded by 16 bytes
 template <int DH>
 constexpr int attn_vt_row() { return DH * 2 + 16; }
@@ -290,16 +295,21 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
     }
   };
 
-  // two blocks in flight: the next block's loads are issued before this one's math
+  // MFA_DEPTH blocks in flight: block i + D is loaded into the registers block i leaves
+  constexpr int D = ATTN_MFMA_DEPTH;
   if (nb > 0) {
-    KVReg ra, rb;
-    load(0, ra);
-    for (int i = 0; i < nb; i += 2) {
-      if (i + 1 < nb) load(i + 1, rb);
-      block(i, ra);
-      if (i + 1 >= nb) break;
-      if (i + 2 < nb) load(i + 2, ra);
-      block(i + 1, rb);
+    KVReg r[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < nb) load(j, r[j]);
+    for (int i = 0; i < nb; i += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        if (i + j < nb) {
+          block(i + j, r[j]);
+          if (i + j + D < nb) load(i + j + D, r[j]);
+        }
+      }
     }
   }
   // the sum over the four lane groups' positions

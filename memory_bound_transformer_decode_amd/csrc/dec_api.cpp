@@ -169,7 +169,7 @@ Layout layout_of(const dec_config& c) {
                               {c.d_ff, 2, c.d_model},   {2 * c.d_ff, 1, c.d_model},
                               {c.d_model, 1, c.d_ff},   {c.vocab, 1, c.d_model}};
     for (const auto& sh : shapes) {
-      const dec::GemmPlan gp = dec::gemm_plan(sh[0], sh[1], sh[2], Bp);
+      const dec::GemmPlan gp = dec::gemm_plan(sh[0], sh[1], sh[2], Bp, c.weight_dtype == DEC_FP8_E4M3);
       if (gp.part_floats > part_floats) part_floats = gp.part_floats;
       if (gp.ks > 1 && (size_t)gp.n_rb > n_rb) n_rb = gp.n_rb;
     }
@@ -394,10 +394,12 @@ bool use_mfma(const dec_config& g, int Bp) {
          Bp >= (g.weight_dtype == DEC_FP8_E4M3 ? MFMA_MIN_BATCH_FP8 : MFMA_MIN_BATCH_BF16);
 }
 
-// Row blocks of the residual products (O, down) on the MFMA tiles: the number of
-// row-block sums of squares a folded RMSNorm adds up.
-int residual_row_blocks(const dec_config& g, int Bp) {
-  return dec::gemm_plan(g.d_model, 1, g.d_model, Bp).n_rb;
+// Row blocks of a residual product on the MFMA tiles -- O (K = Hq dh) or down (K = d_ff)
+// -- : the number of row-block sums of squares it writes for the folded RMSNorm that
+// follows it.
+int residual_row_blocks(const dec_config& g, int Bp, int which) {
+  const int K = which == DEC_MAT_O ? g.n_q_heads * g.d_head : g.d_ff;
+  return dec::gemm_plan(g.d_model, 1, K, Bp, g.weight_dtype == DEC_FP8_E4M3).n_rb;
 }
 
 // The MFMA plan folds the two RMSNorms of a layer and the final one into the products:
@@ -406,7 +408,9 @@ int residual_row_blocks(const dec_config& g, int Bp) {
 // the LM head scale their sums by 1 / rms.  Up to GEMM_SSQ_MAX row blocks; not in the
 // unfused step, which runs the norms as kernels of their own.
 bool fold_norm(const dec_config& g, int Bp) {
-  return use_mfma(g, Bp) && !(g.flags & DEC_FLAG_UNFUSED) && residual_row_blocks(g, Bp) <= dec::GEMM_SSQ_MAX;
+  return use_mfma(g, Bp) && !(g.flags & DEC_FLAG_UNFUSED) &&
+         residual_row_blocks(g, Bp, DEC_MAT_O) <= dec::GEMM_SSQ_MAX &&
+         residual_row_blocks(g, Bp, DEC_MAT_DOWN) <= dec::GEMM_SSQ_MAX;
 }
 
 void set_fold_norm(dec_ctx* c, int which, int l, int Bp, dec::MatmulParams& p) {
@@ -422,8 +426,10 @@ void set_fold_norm(dec_ctx* c, int which, int l, int Bp, dec::MatmulParams& p) {
     p.ssq_out = ssq;
   } else if (which == DEC_MAT_GATE_UP || (which == DEC_MAT_QKV && l > 0) ||
              (which == DEC_MAT_LM_HEAD && g.n_layers > 0)) {
+    // the sums of the residual product before it: O before gate+up, down before the
+    // next layer's QKV and before the LM head
     p.ssq_in = ssq;
-    p.ssq_n = residual_row_blocks(g, Bp);
+    p.ssq_n = residual_row_blocks(g, Bp, which == DEC_MAT_GATE_UP ? DEC_MAT_O : DEC_MAT_DOWN);
   }
 }
 

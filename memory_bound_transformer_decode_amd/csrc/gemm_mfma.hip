@@ -38,21 +38,44 @@ namespace {
 constexpr int KC = 256;          // k-values per staged chunk of x
 constexpr int XROW = KC + 8;     // LDS row of a staged x chunk, in bf16: 16 bytes of padding
                                  // move consecutive batch rows to different LDS banks
-constexpr int TROW = 256 + 16;   // LDS row of a wave's weight tile, in bytes (padded alike)
+#ifndef DEC_MFMA_ROWS_PER_LOAD
+#define DEC_MFMA_ROWS_PER_LOAD 4
+#endif
+// Weight rows one load instruction covers (bf16; E4M3 always 4): each row gets 64 / R
+// lanes of 16 bytes, i.e. 4 rows x 256 bytes or 2 rows x 512 bytes per instruction
+constexpr int RPL_BF16 = DEC_MFMA_ROWS_PER_LOAD;
+template <bool FP8>
+constexpr int tile_bytes() { return FP8 ? 256 : 16 * (64 / RPL_BF16); }  // of a row per group
+template <bool FP8>
+constexpr int tile_row() { return tile_bytes<FP8>() + 16; }  // LDS row of a wave's weight tile (padded)
 // x chunk buffers: two (the next chunk is staged while this one is read) up to 32 batch
 // columns; one beyond, where two would hold the LDS to one work group per CU
 constexpr int x_buffers(int NT) { return NT >= 3 ? 1 : 2; }
+// 16-row tiles per wave (measured on the 8B, 32B and 70B shapes at 48-64 rows): with E4M3
+// weights each x operand read from LDS (NT per k-step) costs the LDS more than the
+// weights do, so from 48 columns a wave takes two tiles that share those reads -- on
+// matrices of at least TPW2_MIN_WEIGHTS weights; smaller ones would need twice the K
+// split, which costs more than it saves.  bf16 weights: one tile (two take 256 registers
+// per lane, one wave per SIMD).
+constexpr size_t TPW2_MIN_WEIGHTS = (size_t)200 << 20;
+int tiles_per_wave(int NT, bool fp8, int n_rows_total, int K) {
+  return fp8 && NT >= 3 && (size_t)n_rows_total * (size_t)K >= TPW2_MIN_WEIGHTS ? 2 : 1;
+}
 
 // v_mfma_f32_16x16x32_bf16: lane l supplies A[l % 16][8 k-values] and B[8 k-values][l % 16],
 // the four lane groups l / 16 four disjoint sets of 8 k-values; lane l receives
 // D[4 (l / 16) + j][l % 16], j = 0..3.  Which k-values a lane group covers is free as long
 // as A and B agree: in k-step s of a group of GK k-values, lane group g takes the 8
 // k-values s 32 + 8 g + [0, 8).
-template <int NT, bool FP8, int EPI, bool KVFP8, int W>
+template <int NT, bool FP8, int EPI, bool KVFP8, int W, int TPW>
 __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n) {
-  extern __shared__ __align__(16) uint8_t lds[];  // x: [XBUFS][NT 16][XROW] bf16; tiles: [W][16][TROW]
+  extern __shared__ __align__(16) uint8_t lds[];  // x: [XBUFS][NT 16][XROW] bf16; tiles: [W][TPW][16][TROW]
   constexpr bool SILU = EPI == EPI_SILU;
-  constexpr int GK = FP8 ? 256 : 128;              // k-values per group: 256 bytes of a row
+  constexpr int RPL = FP8 ? 4 : RPL_BF16;          // rows per weight load instruction
+  constexpr int LPR = WAVE / RPL;                  // lanes per row of a load
+  constexpr int TB = tile_bytes<FP8>();            // bytes of a row per group
+  constexpr int TROW = tile_row<FP8>();
+  constexpr int GK = FP8 ? TB : TB / 2;            // k-values per group
   constexpr int NGRP = KC / GK;                    // groups per chunk (2 bf16, 1 fp8)
   constexpr int NS = GK / 32;                      // MFMA k-steps per group
   constexpr int COLS = NT * 16;
@@ -64,37 +87,47 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int lane = tid % WAVE, m = lane % 16, kg = lane / 16;
-  uint8_t* tile = lds + (size_t)XBUFS * XBUF * 2 + (size_t)wave * 16 * TROW;
+  uint8_t* tile = lds + (size_t)XBUFS * XBUF * 2 + (size_t)wave * TPW * 16 * tile_row<FP8>();
   // rows: output rows of the product (d_ff intermediate indices for gate+up); a tile
-  // covers TR of them
+  // covers TR of them, a wave TPW tiles (TPW > 1: each x operand read from LDS feeds
+  // TPW tiles' products)
   constexpr int TR = SILU ? 8 : 16;
   const int rows = SILU ? p.d_ff : p.N;
   const int rb = blockIdx.x / ks_n, ks = blockIdx.x % ks_n;
   const int nch = (p.K + KC - 1) / KC;
   const int c0 = (int)((int64_t)nch * ks / ks_n), c1 = (int)((int64_t)nch * (ks + 1) / ks_n);
-  const int row0 = (rb * W + wave) * TR;  // first output row of this wave's tile
+  const int row0 = (rb * W + wave) * TR * TPW;  // first output row of this wave's tiles
 
-  // weight row of tile row i (rows past the matrix are clamped: their results are dropped)
-  auto wrow = [&](int i) -> int {
-    if (SILU) return (i < 8 ? 0 : p.d_ff) + min(row0 + (i & 7), rows - 1);
-    return min(row0 + i, rows - 1);
+  // weight row of row i of tile tt (rows past the matrix are clamped: their results are
+  // dropped)
+  auto wrow = [&](int tt, int i) -> int {
+    const int r0 = row0 + tt * TR;
+    if (SILU) return (i < 8 ? 0 : p.d_ff) + min(r0 + (i & 7), rows - 1);
+    return min(r0 + i, rows - 1);
   };
   const size_t rowbytes = FP8 ? (size_t)p.K : (size_t)p.K * 2;
-  // load q of a group: lane (r = kg, j = m) reads 16 bytes at byte 16 j of the group's 256
-  // bytes of tile row 4 q + r
-  const uint8_t* wp[4];
+  // load q of a group: lane (r = lane / LPR, j = lane % LPR) reads 16 bytes at byte 16 j
+  // of the group's TB bytes of tile row RPL q + r
+  constexpr int NQ = 16 / RPL;
+  const int lr = lane / LPR, lj = lane % LPR;
+  const uint8_t* wp[TPW][NQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) wp[q] = static_cast<const uint8_t*>(p.W) + (size_t)wrow(4 * q + kg) * rowbytes;
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      wp[tt][q] = static_cast<const uint8_t*>(p.W) + (size_t)wrow(tt, RPL * q + lr) * rowbytes;
   const int lastv = (int)rowbytes - 16;  // last 16-byte piece of a row
 
   // weight loads of chunk c, unconditional: pieces past K are read at the row's last
   // piece (x is zero there, so they add nothing)
-  auto load_w = [&](int c, u32x4 (&wr)[NGRP][4]) {
+  auto load_w = [&](int c, u32x4 (&wr)[TPW][NGRP][NQ]) {
 #pragma unroll
     for (int gi = 0; gi < NGRP; ++gi) {
-      const int off = min(c * KC * (FP8 ? 1 : 2) + gi * 256 + m * 16, lastv);
+      const int off = min(c * KC * (FP8 ? 1 : 2) + gi * TB + lj * 16, lastv);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wr[gi][q] = ld_stream(reinterpret_cast<const u32x4*>(wp[q] + off));
+      for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) wr[tt][gi][q] = ld_stream(reinterpret_cast<const u32x4*>(wp[tt][q] + off));
     }
   };
   // x loads of chunk c into registers (rows past Bp read row Bp - 1; k past K is zero)
@@ -116,63 +149,82 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
     }
   };
 
-  f32x4 acc[NT];
+  f32x4 acc[TPW][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto mma_chunk = [&](int buf, const u32x4 (&wr)[NGRP][4]) {
+  auto mma_chunk = [&](int buf, const u32x4 (&wr)[TPW][NGRP][NQ]) {
     const uint16_t* xb = xs + buf * XBUF;
 #pragma unroll
     for (int gi = 0; gi < NGRP; ++gi) {
-      // this wave's 16 x 256-byte tile of the group, then each lane's operands from it
+      // this wave's TPW 16 x TB-byte tiles of the group, then each lane's operands from them
 #pragma unroll
-      for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(tile + (4 * q + kg) * TROW + m * 16) = wr[gi][q];
+      for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          *reinterpret_cast<u32x4*>(tile + (tt * 16 + RPL * q + lr) * TROW + lj * 16) = wr[tt][gi][q];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        bf16x8 av;
-        if (FP8) {
-          const u32x2 c8 = *reinterpret_cast<const u32x2*>(tile + m * TROW + s * 32 + kg * 8);
-          const bf16x2 q0 = e4m3x2_to_bf16x2<false>(c8.x), q1 = e4m3x2_to_bf16x2<true>(c8.x);
-          const bf16x2 q2 = e4m3x2_to_bf16x2<false>(c8.y), q3 = e4m3x2_to_bf16x2<true>(c8.y);
-          av = bf16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
-        } else {
-          av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + m * TROW + s * 64 + kg * 16));
+        bf16x8 av[TPW];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+          const uint8_t* tr = tile + (tt * 16 + m) * TROW;
+          if (FP8) {
+            const u32x2 c8 = *reinterpret_cast<const u32x2*>(tr + s * 32 + kg * 8);
+            const bf16x2 q0 = e4m3x2_to_bf16x2<false>(c8.x), q1 = e4m3x2_to_bf16x2<true>(c8.x);
+            const bf16x2 q2 = e4m3x2_to_bf16x2<false>(c8.y), q3 = e4m3x2_to_bf16x2<true>(c8.y);
+            av[tt] = bf16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+          } else {
+            av[tt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tr + s * 64 + kg * 16));
+          }
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const bf16x8 bv = __builtin_bit_cast(bf16x8, ld16(xb + (t * 16 + m) * XROW + gi * GK + s * 32 + kg * 8));
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[t], 0, 0, 0);
+#pragma unroll
+          for (int tt = 0; tt < TPW; ++tt)
+            acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bv, acc[tt][t], 0, 0, 0);
         }
       }
     }
   };
 
-  // chunk c's weights and the next chunk's loads are in flight while chunk c's tiles
-  // are multiplied; a barrier hands the staged x over (two buffers: one barrier per
-  // chunk; one buffer: a second barrier before it is overwritten).  Each wave's weight
-  // tile is its own: LDS operations of one wave complete in order.
   // What the epilogue reads besides the sums, fetched at kernel start so that these loads
-  // overlap the weight stream: for the lane's four rows r0 .. r0 + 3 (in range: full)
-  // and each of its batch columns, the row scales, the residual rows (O, down), and for
-  // QKV the token's position, the RoPE angles of the lane's two row pairs (adjacent in
-  // the table: r0 is a multiple of 4, d_head of 64) and the cache block.
-  const int er0 = row0 + 4 * kg;
-  const bool full = er0 + 4 <= rows;
-  f32x4 e_sc = f32x4{1.f, 1.f, 1.f, 1.f}, e_su = f32x4{1.f, 1.f, 1.f, 1.f};
-  f32x4 e_h[EPI == EPI_RESID ? NT : 1];
+  // overlap the weight stream: for the lane's four rows er0 .. er0 + 3 of each tile (in
+  // range: full) and each of its batch columns, the row scales, the residual rows (O,
+  // down), and for QKV the token's position and cache block and the RoPE angles of the
+  // lane's two row pairs (adjacent in the table: er0 is a multiple of 4, d_head of 64).
+  int er0[TPW];
+  bool full[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    er0[tt] = row0 + tt * TR + 4 * kg;
+    full[tt] = er0[tt] + 4 <= rows;
+  }
+  f32x4 e_sc[TPW], e_su[TPW];
+  f32x4 e_h[TPW][EPI == EPI_RESID ? NT : 1];
+  f32x4 e_cs[TPW][EPI == EPI_QKV ? NT : 1];
   int e_pos[EPI == EPI_QKV ? NT : 1], e_blk[EPI == EPI_QKV ? NT : 1];
-  f32x4 e_cs[EPI == EPI_QKV ? NT : 1];
   auto epi_prefetch = [&]() {
-    if (!full) return;
-    if (p.scale) {
-      e_sc = gld(reinterpret_cast<const f32x4*>(p.scale + er0));
-      if (SILU) e_su = gld(reinterpret_cast<const f32x4*>(p.scale + p.d_ff + er0));
+    if (EPI == EPI_QKV) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) e_pos[t] = gld(p.seq_lens + min(t * 16 + m, p.Bp - 1));
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int col = min(t * 16 + m, p.Bp - 1);
-      if (EPI == EPI_RESID) e_h[t] = gld(reinterpret_cast<const f32x4*>(p.out + (int64_t)col * p.ldo + er0));
-      if (EPI == EPI_QKV) e_pos[t] = gld(p.seq_lens + col);
+    for (int tt = 0; tt < TPW; ++tt) {
+      e_sc[tt] = e_su[tt] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if (!full[tt]) continue;
+      if (p.scale) {
+        e_sc[tt] = gld(reinterpret_cast<const f32x4*>(p.scale + er0[tt]));
+        if (SILU) e_su[tt] = gld(reinterpret_cast<const f32x4*>(p.scale + p.d_ff + er0[tt]));
+      }
+      if (EPI == EPI_RESID) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          e_h[tt][t] = gld(reinterpret_cast<const f32x4*>(p.out + (int64_t)min(t * 16 + m, p.Bp - 1) * p.ldo + er0[tt]));
+      }
     }
     if (EPI == EPI_QKV) {
       const int qrows = p.Hq * p.dh, krows = p.Hkv * p.dh;
@@ -180,10 +232,12 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
       for (int t = 0; t < NT; ++t) {
         const int col = min(t * 16 + m, p.Bp - 1);
         const int pr = e_pos[t] < 0 ? 0 : e_pos[t];
-        e_cs[t] = er0 < qrows + krows
-                      ? gld(reinterpret_cast<const f32x4*>(p.rope + (int64_t)pr * (p.dh / 2) + ((er0 % p.dh) >> 1)))
-                      : f32x4{1.f, 0.f, 1.f, 0.f};
-        e_blk[t] = er0 >= qrows && e_pos[t] >= 0 ? gld(p.bt + (int64_t)col * p.bps + e_pos[t] / KV_BLOCK) : 0;
+        e_blk[t] = e_pos[t] >= 0 ? gld(p.bt + (int64_t)col * p.bps + e_pos[t] / KV_BLOCK) : 0;
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+          e_cs[tt][t] = full[tt] && er0[tt] < qrows + krows
+                            ? gld(reinterpret_cast<const f32x4*>(p.rope + (int64_t)pr * (p.dh / 2) + ((er0[tt] % p.dh) >> 1)))
+                            : f32x4{1.f, 0.f, 1.f, 0.f};
       }
     }
   };
@@ -195,7 +249,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   constexpr int SPER = (GEMM_SSQ_MAX + W - 1) / W;
   {
     constexpr int B1 = XBUFS == 2 ? 1 : 0;
-    u32x4 wa[NGRP][4], wb[NGRP][4], xr[XL];
+    u32x4 wa[TPW][NGRP][NQ], wb[TPW][NGRP][NQ], xr[XL];
     const int scol = tid % GEMM_SSQ_STRIDE, spart = tid / GEMM_SSQ_STRIDE;
     float sv[SPER];
     if (p.ssq_n > 0) {
@@ -237,14 +291,17 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   }
 
   if (ks_n > 1) {
-    // partial tiles of this split: part[blockIdx.x][wave][t][lane] (f32x4), written
+    // partial tiles of this split: part[blockIdx.x][wave][tt][t][lane] (f32x4), written
     // device-coherently for the work group that combines them
-    float* part = p.gpart + ((int64_t)blockIdx.x * W + wave) * NT * (WAVE * 4);
+    constexpr int PT = TPW * NT;
+    float* part = p.gpart + ((int64_t)blockIdx.x * W + wave) * PT * (WAVE * 4);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const f32x4 v = acc[t];
-      cst_f4(part + (t * WAVE + lane) * 4, v.x, v.y, v.z, v.w);
-    }
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const f32x4 v = acc[tt][t];
+        cst_f4(part + ((tt * NT + t) * WAVE + lane) * 4, v.x, v.y, v.z, v.w);
+      }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial stores have completed
     __shared__ int last;
     __syncthreads();
@@ -257,19 +314,26 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
     __syncthreads();
     if (!last) return;
     // sum the splits in order 0..ks_n-1 (this work group's own from registers)
-    f32x4 tot[NT];
+    f32x4 tot[TPW][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) tot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ks_n; ++s) {
-      const float* ps = p.gpart + ((int64_t)(rb * ks_n + s) * W + wave) * NT * (WAVE * 4);
+    for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) tot[t] += s == ks ? acc[t] : cld_f4(ps + (t * WAVE + lane) * 4);
+      for (int t = 0; t < NT; ++t) tot[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < ks_n; ++sp) {
+      const float* ps = p.gpart + ((int64_t)(rb * ks_n + sp) * W + wave) * PT * (WAVE * 4);
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          tot[tt][t] += sp == ks ? acc[tt][t] : cld_f4(ps + ((tt * NT + t) * WAVE + lane) * 4);
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = tot[t];
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[tt][t] = tot[tt][t];
   }
 
-  // epilogue: lane holds tile rows 4 kg + j (j = 0..3) of batch column t 16 + m
+  // epilogue: lane holds rows 4 kg + j (j = 0..3) of each tile, batch column t 16 + m
   if (p.ssq_n > 0) {
     // the folded RMSNorm's 1 / rms of each batch column, on the sums
 #pragma unroll
@@ -278,91 +342,97 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
       float ss = 0.f;
 #pragma unroll
       for (int w = 0; w < W; ++w) ss += ssq_s[w][col];
-      acc[t] *= 1.0f / sqrtf(ss / (float)p.K + p.eps);
+      const float rinv = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) acc[tt][t] *= rinv;
     }
   }
   float sq[NT];  // residual products that fold the next norm: this lane's sum of h^2
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    sq[t] = 0.f;
-    const int col = t * 16 + m;
-    if (SILU) {
-      // gate rows are tile rows 0..7 (lane groups 0, 1), up rows 8..15 (lane groups 2, 3):
-      // lane l pairs with lane l + 32
-      f32x4 up;
+  for (int t = 0; t < NT; ++t) sq[t] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) up[j] = __shfl_xor(acc[t][j], 32);
-      if (kg >= 2 || col >= p.Bp) continue;
-      uint16_t* o = p.act + (int64_t)col * p.ldact;
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int r0 = er0[tt];  // the lane's first row in tile tt (for gate+up: lane groups 0, 1)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = row0 + 4 * kg + j;
-        if (r >= rows) break;
-        const float sg = full ? e_sc[j] : p.scale ? gld(p.scale + r) : 1.f;
-        const float su = full ? e_su[j] : p.scale ? gld(p.scale + p.d_ff + r) : 1.f;
-        gst(o + r, f32_to_bf16(silu_f(acc[t][j] * sg) * (up[j] * su)));
-      }
-      continue;
-    }
-    if (col >= p.Bp) continue;
-    const int r0 = row0 + 4 * kg;
-    if (EPI == EPI_QKV) {
-      if (full) {
-        // rows r0 .. r0 + 3 lie in one head (r0 % 4 == 0, d_head % 4 == 0)
-        const int qrows = p.Hq * p.dh, krows = p.Hkv * p.dh, dh = p.dh;
-        float y[4];
+    for (int t = 0; t < NT; ++t) {
+      const int col = t * 16 + m;
+      if (SILU) {
+        // gate rows are tile rows 0..7 (lane groups 0, 1), up rows 8..15 (lane groups 2,
+        // 3): lane l pairs with lane l + 32
+        f32x4 up;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] = acc[t][j] * e_sc[j];
-        if (r0 < qrows + krows) {  // q or k: rotate the adjacent pairs
-          const f32x4 cs = e_cs[t];
-          const float a0 = y[0] * cs.x - y[1] * cs.y, a1 = y[0] * cs.y + y[1] * cs.x;
-          const float b0 = y[2] * cs.z - y[3] * cs.w, b1 = y[2] * cs.w + y[3] * cs.z;
-          y[0] = a0; y[1] = a1; y[2] = b0; y[3] = b1;
-        }
-        if (r0 < qrows) {
-          float* qp = p.q + ((int64_t)col * p.Hq + r0 / dh) * dh + r0 % dh;
-          cst_f2(qp, y[0], y[1]);
-          cst_f2(qp + 2, y[2], y[3]);
-        } else if (e_pos[t] >= 0) {  // padded rows write no cache slot
-          const int kv = r0 < qrows + krows ? 0 : 1;
-          const int rr = r0 - qrows - kv * krows;
-          const int64_t off = kv_offset(p.layer, kv, e_blk[t], rr / dh, e_pos[t] % KV_BLOCK, rr % dh, p.num_blocks,
-                                        p.Hkv, dh);
-          if (KVFP8) {
-            const uint32_t w = f32_to_e4m3(y[0]) | (f32_to_e4m3(y[1]) << 8) | (f32_to_e4m3(y[2]) << 16) |
-                               (f32_to_e4m3(y[3]) << 24);
-            cst(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p.pool) + off), w);
-          } else {
-            const uint64_t w = (uint64_t)f32_to_bf16(y[0]) | ((uint64_t)f32_to_bf16(y[1]) << 16) |
-                               ((uint64_t)f32_to_bf16(y[2]) << 32) | ((uint64_t)f32_to_bf16(y[3]) << 48);
-            cst(reinterpret_cast<uint64_t*>(static_cast<uint16_t*>(p.pool) + off), w);
-          }
+        for (int j = 0; j < 4; ++j) up[j] = __shfl_xor(acc[tt][t][j], 32);
+        if (kg >= 2 || col >= p.Bp) continue;
+        uint16_t* o = p.act + (int64_t)col * p.ldact;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = r0 + j;
+          if (r >= rows) break;
+          const float sg = full[tt] ? e_sc[tt][j] : p.scale ? gld(p.scale + r) : 1.f;
+          const float su = full[tt] ? e_su[tt][j] : p.scale ? gld(p.scale + p.d_ff + r) : 1.f;
+          gst(o + r, f32_to_bf16(silu_f(acc[tt][t][j] * sg) * (up[j] * su)));
         }
         continue;
       }
+      if (col >= p.Bp) continue;
+      if (EPI == EPI_QKV) {
+        if (full[tt]) {
+          // rows r0 .. r0 + 3 lie in one head (r0 % 4 == 0, d_head % 4 == 0)
+          const int qrows = p.Hq * p.dh, krows = p.Hkv * p.dh, dh = p.dh;
+          float y[4];
 #pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        const int r = r0 + j;  // even; rows is a multiple of d_head
-        if (r >= rows) break;
-        const float s0 = p.scale ? gld(p.scale + r) : 1.f, s1 = p.scale ? gld(p.scale + r + 1) : 1.f;
-        qkv_pair_out(p, KVFP8, col, r, acc[t][j] * s0, acc[t][j + 1] * s1);
-      }
-    } else {
-      float* o = p.out + (int64_t)col * p.ldo;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = r0 + j;
-        if (r >= rows) break;
-        const float y = acc[t][j] * (full ? e_sc[j] : p.scale ? gld(p.scale + r) : 1.f);
-        if (EPI == EPI_RESID) {
-          const float hn = (full ? e_h[t][j] : gld(o + r)) + y;
-          gst(o + r, hn);
-          if (p.xout) {
-            gst(p.xout + (int64_t)col * p.ldxo + r, f32_to_bf16(hn * gld(p.xg + r)));
-            sq[t] += hn * hn;
+          for (int j = 0; j < 4; ++j) y[j] = acc[tt][t][j] * e_sc[tt][j];
+          if (r0 < qrows + krows) {  // q or k: rotate the adjacent pairs
+            const f32x4 cs = e_cs[tt][t];
+            const float a0 = y[0] * cs.x - y[1] * cs.y, a1 = y[0] * cs.y + y[1] * cs.x;
+            const float b0 = y[2] * cs.z - y[3] * cs.w, b1 = y[2] * cs.w + y[3] * cs.z;
+            y[0] = a0; y[1] = a1; y[2] = b0; y[3] = b1;
           }
-        } else {
-          gst(o + r, y);
+          if (r0 < qrows) {
+            float* qp = p.q + ((int64_t)col * p.Hq + r0 / dh) * dh + r0 % dh;
+            cst_f2(qp, y[0], y[1]);
+            cst_f2(qp + 2, y[2], y[3]);
+          } else if (e_pos[t] >= 0) {  // padded rows write no cache slot
+            const int kv = r0 < qrows + krows ? 0 : 1;
+            const int rr = r0 - qrows - kv * krows;
+            const int64_t off = kv_offset(p.layer, kv, e_blk[t], rr / dh, e_pos[t] % KV_BLOCK, rr % dh, p.num_blocks,
+                                          p.Hkv, dh);
+            if (KVFP8) {
+              const uint32_t w = f32_to_e4m3(y[0]) | (f32_to_e4m3(y[1]) << 8) | (f32_to_e4m3(y[2]) << 16) |
+                                 (f32_to_e4m3(y[3]) << 24);
+              cst(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p.pool) + off), w);
+            } else {
+              const uint64_t w = (uint64_t)f32_to_bf16(y[0]) | ((uint64_t)f32_to_bf16(y[1]) << 16) |
+                                 ((uint64_t)f32_to_bf16(y[2]) << 32) | ((uint64_t)f32_to_bf16(y[3]) << 48);
+              cst(reinterpret_cast<uint64_t*>(static_cast<uint16_t*>(p.pool) + off), w);
+            }
+          }
+          continue;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          const int r = r0 + j;  // even; rows is a multiple of d_head
+          if (r >= rows) break;
+          const float s0 = p.scale ? gld(p.scale + r) : 1.f, s1 = p.scale ? gld(p.scale + r + 1) : 1.f;
+          qkv_pair_out(p, KVFP8, col, r, acc[tt][t][j] * s0, acc[tt][t][j + 1] * s1);
+        }
+      } else {
+        float* o = p.out + (int64_t)col * p.ldo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = r0 + j;
+          if (r >= rows) break;
+          const float y = acc[tt][t][j] * (full[tt] ? e_sc[tt][j] : p.scale ? gld(p.scale + r) : 1.f);
+          if (EPI == EPI_RESID) {
+            const float hn = (full[tt] ? e_h[tt][t][j] : gld(o + r)) + y;
+            gst(o + r, hn);
+            if (p.xout) {
+              gst(p.xout + (int64_t)col * p.ldxo + r, f32_to_bf16(hn * gld(p.xg + r)));
+              sq[t] += hn * hn;
+            }
+          } else {
+            gst(o + r, y);
+          }
         }
       }
     }
@@ -386,14 +456,15 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   }
 }
 
-constexpr size_t lds_bytes(int NT, int W) {
-  return (size_t)x_buffers(NT) * NT * 16 * XROW * 2 + (size_t)W * 16 * TROW;
+template <bool FP8>
+constexpr size_t lds_bytes(int NT, int W, int TPW) {
+  return (size_t)x_buffers(NT) * NT * 16 * XROW * 2 + (size_t)W * TPW * 16 * tile_row<FP8>();
 }
 
-template <int NT, bool FP8, int EPI, bool KVFP8, int W>
-hipError_t go(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
-  auto kern = k_gemm_lds<NT, FP8, EPI, KVFP8, W>;
-  constexpr size_t lds = lds_bytes(NT, W);
+template <int NT, bool FP8, int EPI, bool KVFP8, int W, int TPW>
+hipError_t go_tpw(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
+  auto kern = k_gemm_lds<NT, FP8, EPI, KVFP8, W, TPW>;
+  constexpr size_t lds = lds_bytes<FP8>(NT, W, TPW);
   static_assert(lds <= 160 * 1024, "LDS of one work group");
   static bool attr = false;
   if (!attr && lds > 64 * 1024) {
@@ -404,6 +475,13 @@ hipError_t go(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
   }
   hipLaunchKernelGGL(kern, dim3(g.n_rb * g.ks), dim3(WAVE * W), lds, s, p, g.ks);
   return hipGetLastError();
+}
+
+template <int NT, bool FP8, int EPI, bool KVFP8, int W>
+hipError_t go(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
+  if constexpr (FP8 && NT >= 3)
+    if (g.tpw == 2) return go_tpw<NT, FP8, EPI, KVFP8, W, 2>(p, g, s);
+  return go_tpw<NT, FP8, EPI, KVFP8, W, 1>(p, g, s);
 }
 
 template <bool FP8, int EPI, bool KVFP8>
@@ -420,9 +498,11 @@ hipError_t go_nt(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
 // the chip under-filled (fewer than GEMM_TARGET_GROUPS work groups for MI355X's 256
 // CUs), K is split so that about that many work groups run, with at least two chunks
 // each.  A pure function of the shape: the workspace is sized with it.
-GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp) {
+GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool fp8) {
   GemmPlan g{};
-  const int tile_rows = n_groups == 2 ? 8 : 16;  // gate+up tiles hold 8 of each
+  const int NT = (Bp + 15) / 16;
+  const int tpw = tiles_per_wave(NT, fp8, rows * n_groups, K);
+  const int tile_rows = (n_groups == 2 ? 8 : 16) * tpw;  // gate+up tiles hold 8 of each
   g.n_rb = (rows + tile_rows * GEMM_WAVES - 1) / (tile_rows * GEMM_WAVES);
   const int nch = (K + KC - 1) / KC;
   int ks = 1;
@@ -433,8 +513,8 @@ GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp) {
     if (ks > GEMM_MAX_SPLIT) ks = GEMM_MAX_SPLIT;
   }
   g.ks = ks;
-  const int NT = (Bp + 15) / 16;
-  g.part_floats = ks > 1 ? (size_t)g.n_rb * ks * GEMM_WAVES * NT * WAVE * 4 : 0;
+  g.tpw = tpw;
+  g.part_floats = ks > 1 ? (size_t)g.n_rb * ks * GEMM_WAVES * tpw * NT * WAVE * 4 : 0;
   return g;
 }
 
@@ -442,7 +522,7 @@ hipError_t launch_gemm_mfma(const MatmulParams& p, int epi, bool w_fp8, bool kv_
   const int rows = epi == EPI_SILU ? p.d_ff : p.N;
   if (rows <= 0 || p.Bp <= 0) return hipSuccess;
   if (p.Bp > 64 || p.K < 16 || p.K % 16) return hipErrorInvalidValue;
-  const GemmPlan g = gemm_plan(rows, epi == EPI_SILU ? 2 : 1, p.K, p.Bp);
+  const GemmPlan g = gemm_plan(rows, epi == EPI_SILU ? 2 : 1, p.K, p.Bp, w_fp8);
   if (g.ks > 1 && (!p.gpart || !p.gcnt || g.part_floats > p.gpart_floats || g.n_rb > p.gcnt_n))
     return hipErrorInvalidValue;
   // the folded RMSNorm: row-block sums within GEMM_SSQ_MAX x GEMM_SSQ_STRIDE

@@ -68,7 +68,7 @@ struct MatmulParams {
   int ssq_n;
 };
 
-// MFMA products (Bp 16..64): row blocks of GEMM_WAVES 16-row tiles, K split over
+// MFMA products (Bp up to 64): row blocks of GEMM_WAVES waves of 16-row tiles, K split over
 // ks work groups where the row blocks alone leave the chip under-filled.
 constexpr int GEMM_WAVES = 4;
 constexpr int GEMM_MAX_SPLIT = 16;
@@ -76,10 +76,11 @@ constexpr int GEMM_TARGET_GROUPS = 256;  // one per CU of MI355X
 struct GemmPlan {
   int n_rb;            // row blocks
   int ks;              // work groups per row block (K split)
+  int tpw;             // 16-row tiles per wave
   size_t part_floats;  // partial-tile floats the launch needs (0 when ks == 1)
 };
-// rows: per group (d_ff for gate+up, whose groups are 2); K; padded batch
-GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp);
+// rows: per group (d_ff for gate+up, whose groups are 2); K; padded batch; E4M3 weights
+GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool fp8);
 // row-block sums of squares of the folded RMSNorm: at most GEMM_SSQ_MAX row blocks of
 // the residual products (d_model <= 8192), GEMM_SSQ_STRIDE batch rows apart
 constexpr int GEMM_SSQ_MAX = 128;
