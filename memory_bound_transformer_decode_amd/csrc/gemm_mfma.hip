@@ -203,7 +203,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
     er0[tt] = row0 + tt * TR + 4 * kg;
     full[tt] = er0[tt] + 4 <= rows;
   }
-  f32x4 e_sc[TPW], e_su[TPW];
+  f32x4 e_sc[TPW], e_su[TPW], e_g[TPW];  // e_g: the folded next norm's gain (O, down)
   f32x4 e_h[TPW][EPI == EPI_RESID ? NT : 1];
   f32x4 e_cs[TPW][EPI == EPI_QKV ? NT : 1];
   int e_pos[EPI == EPI_QKV ? NT : 1], e_blk[EPI == EPI_QKV ? NT : 1];
@@ -221,6 +221,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
         if (SILU) e_su[tt] = gld(reinterpret_cast<const f32x4*>(p.scale + p.d_ff + er0[tt]));
       }
       if (EPI == EPI_RESID) {
+        if (p.xout) e_g[tt] = gld(reinterpret_cast<const f32x4*>(p.xg + er0[tt]));
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           e_h[tt][t] = gld(reinterpret_cast<const f32x4*>(p.out + (int64_t)min(t * 16 + m, p.Bp - 1) * p.ldo + er0[tt]));
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
             const float hn = (full[tt] ? e_h[tt][t][j] : gld(o + r)) + y;
             gst(o + r, hn);
             if (p.xout) {
-              gst(p.xout + (int64_t)col * p.ldxo + r, f32_to_bf16(hn * gld(p.xg + r)));
+              gst(p.xout + (int64_t)col * p.ldxo + r, f32_to_bf16(hn * (full[tt] ? e_g[tt][j] : gld(p.xg + r))));
               sq[t] += hn * hn;
             }
           } else {
