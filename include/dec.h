@@ -199,6 +199,21 @@ int dec_launch_matmul(dec_ctx* ctx, int which, int layer);
  * token_ids. */
 int dec_sample_greedy(dec_ctx* ctx, int32_t* token_ids);
 
+/* Top-k / top-p sampling after the last step, enqueued on the context's stream: for each
+ * sequence s < n_seqs of that step, the candidates are its top_k largest logits (the
+ * lower index first on equal logits; NaN ranks as -inf), weighted exp((z - z_max) /
+ * temperature) in that order; the nucleus is the shortest prefix of them whose weight
+ * reaches top_p of the candidates' total; token_ids[s] = the first nucleus candidate
+ * whose running weight exceeds uniforms[s] times the nucleus weight.  The random draws
+ * are inputs: uniforms, device float32 [n_seqs] in [0, 1), 4-byte aligned, owned by the
+ * caller; token_ids: device int32 [n_seqs], 4-byte aligned, owned by the caller.  The
+ * sampling step after the LM head, on the GPU ("Kernels, Fusion & CUDA Graphs", Fix 1
+ * table: sampling; "The serving engine's kernel stack").  1 <= top_k <= 64, temperature
+ * > 0, 0 < top_p <= 1 (DEC_E_INVALID otherwise, and for NULL or misaligned pointers);
+ * needs a previous dec_step (DEC_E_STATE otherwise).  top_k = 1 is greedy sampling. */
+int dec_sample(dec_ctx* ctx, const float* uniforms, float temperature, int32_t top_k, float top_p,
+               int32_t* token_ids);
+
 /* Describe the last step (kernels, bucket, path). */
 int dec_get_info(const dec_ctx* ctx, dec_info* out);
 

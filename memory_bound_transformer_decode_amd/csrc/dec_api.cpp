@@ -997,6 +997,24 @@ int dec_sample_greedy(dec_ctx* c, int32_t* token_ids) {
   return DEC_OK;
 }
 
+int dec_sample(dec_ctx* c, const float* uniforms, float temperature, int32_t top_k, float top_p,
+               int32_t* token_ids) {
+  if (!c || !token_ids || !uniforms) return fail(DEC_E_INVALID, "ctx, uniforms or token_ids is NULL");
+  if (((uintptr_t)token_ids & 3u) != 0 || ((uintptr_t)uniforms & 3u) != 0)
+    return fail(DEC_E_INVALID, "token_ids or uniforms is not 4-byte aligned");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(DEC_E_INVALID, "temperature must be positive and finite");
+  if (top_k < 1 || top_k > dec::SAMPLE_MAX_K)
+    return fail(DEC_E_INVALID, "top_k must be in [1, %d] (got %d)", dec::SAMPLE_MAX_K, top_k);
+  if (!(top_p > 0.f) || top_p > 1.f) return fail(DEC_E_INVALID, "top_p must be in (0, 1]");
+  if (c->failed) return fail(DEC_E_STATE, "context has failed; destroy it");
+  if (!c->loaded || c->last_n <= 0) return fail(DEC_E_STATE, "dec_sample needs a previous dec_step");
+  hipError_t e = dec::launch_sample_topkp(c->logits, c->cfg.vocab, c->cfg.vocab, c->last_n, uniforms, temperature,
+                                          top_k, top_p, token_ids, c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
+  return DEC_OK;
+}
+
 int dec_get_info(const dec_ctx* c, dec_info* out) {
   if (!c || !out) return fail(DEC_E_INVALID, "ctx or out is NULL");
   *out = c->info;

@@ -201,6 +201,12 @@ hipError_t launch_rope_kv(const MatmulParams& p, const float* qkv, bool kv_fp8, 
 hipError_t launch_silu_mul(const float* gu, int d_ff, int Bp, uint16_t* a, int lda, hipStream_t s);
 hipError_t launch_add(float* h, const float* delta, int n, hipStream_t s);
 
+// top-k / top-p sampling of rows r < n with the draws uniforms[r] in [0, 1) (see
+// sample.hip); 1 <= top_k <= SAMPLE_MAX_K, temperature > 0, 0 < top_p <= 1
+constexpr int SAMPLE_MAX_K = 64;
+hipError_t launch_sample_topkp(const float* logits, int ldl, int V, int n, const float* uniforms, float temperature,
+                               int top_k, float top_p, int32_t* out, hipStream_t s);
+
 // out[r] = argmax over v < V of logits[r][v] (first index of the largest value), r < n
 hipError_t launch_argmax(const float* logits, int ldl, int V, int n, int32_t* out, hipStream_t s);
 

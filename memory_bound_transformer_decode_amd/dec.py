@@ -63,7 +63,7 @@ class DecError(RuntimeError):
 
 EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_load_weights", "dec_step", "dec_set_flags",
            "dec_get_info", "dec_destroy", "dec_last_error", "dec_bw_probe", "dec_launch_matmul",
-           "dec_sample_greedy")
+           "dec_sample_greedy", "dec_sample")
 MAT_QKV, MAT_O, MAT_GATE_UP, MAT_DOWN, MAT_LM_HEAD = 0, 1, 2, 3, 4
 
 _lib = None
@@ -100,6 +100,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dec_bw_probe.restype = c_int
     lib.dec_sample_greedy.argtypes = [c_void_p, c_void_p]
     lib.dec_sample_greedy.restype = c_int
+    lib.dec_sample.argtypes = [c_void_p, c_void_p, c_float, c_int, c_float, c_void_p]
+    lib.dec_sample.restype = c_int
     lib.dec_launch_matmul.argtypes = [c_void_p, c_int, c_int]
     lib.dec_launch_matmul.restype = c_int
     _lib = lib
@@ -212,6 +214,15 @@ class Decoder:
         n = self._last_n
         out = torch.empty(n, dtype=torch.int32, device=self.device)
         _check(self.lib.dec_sample_greedy(self.ctx, c_void_p(out.data_ptr())))
+        return out
+
+    def sample(self, uniforms: torch.Tensor, temperature: float, top_k: int, top_p: float) -> torch.Tensor:
+        """Enqueue top-k / top-p sampling of the last step with the draws `uniforms`
+        (float32 [n] on the device, in [0, 1)): int32 [n] token ids on the device."""
+        n = self._last_n
+        out = torch.empty(n, dtype=torch.int32, device=self.device)
+        _check(self.lib.dec_sample(self.ctx, c_void_p(uniforms.data_ptr()), float(temperature), int(top_k),
+                                   float(top_p), c_void_p(out.data_ptr())))
         return out
 
     def launch_matmul(self, which: int, layer: int = 0) -> None:

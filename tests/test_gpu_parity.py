@@ -308,6 +308,80 @@ def test_greedy_sampling_ties_and_errors(dec):
     d.close()
 
 
+SAMPLE_SETTINGS = [(1.0, 1, 1.0), (0.7, 8, 0.9), (1.3, 64, 0.5), (0.5, 40, 1.0), (2.0, 64, 0.95)]
+
+
+@pytest.mark.parametrize("B", [1, 5, 24])
+def test_topk_topp_sampling(dec, B):
+    """Top-k / top-p sampling on the device against the oracle's rule on the same logits:
+    the same token wherever the oracle's deciding comparisons are clear of rounding
+    (relative margin 1e-4), else a rank neighbour of it; top_k = 1 equals greedy."""
+    from oracle import sampling as OS
+    cfg = fmt(MINI, "bf16", "bf16")
+    rng = np.random.default_rng(130 + B)
+    case = make_case(cfg, ctx_mix(B, rng), 128, seed=22)
+    ids = synth.make_token_ids(cfg, 1, B, seed=22)[0]
+    d = dec.Decoder(case.cfg, case.weights, num_blocks=case.num_blocks, max_batch=dec.ladder_bucket(B),
+                    max_seq_len=case.max_seq_len, kv_pool=case.pool.clone())
+    d.step(ids, case.ctx_lens, case.block_tables[:B])
+    # sharper rows than the random model's, so that the nucleus and the draw both matter
+    zc = (d.logits[:B].cpu().numpy() * 40.0).astype(np.float32)
+    d.logits[:B].copy_(torch.from_numpy(zc).cuda())
+    greedy = d.sample_greedy().cpu().numpy()
+    checked = 0
+    for si, (T, k, p) in enumerate(SAMPLE_SETTINGS):
+        u = np.random.default_rng(1000 * B + si).random(B).astype(np.float32)
+        tok = d.sample(torch.from_numpy(u).cuda(), T, k, p).cpu().numpy()
+        assert tok.dtype == np.int32 and tok.shape == (B,)
+        if k == 1:
+            assert np.array_equal(tok, greedy)
+        for r in range(B):
+            ref = OS.sample(zc[r], T, k, p, float(u[r]))
+            if ref.margin > 1e-4:
+                assert tok[r] == ref.token, (T, k, p, r, ref.margin)
+                checked += 1
+            else:
+                j = int(np.nonzero(ref.order == ref.token)[0][0])
+                assert tok[r] in ref.order[max(0, j - 1): j + 2]
+    d.close()
+    assert checked >= 2 * B  # most of the 5 B decisions are clear of rounding
+
+
+def test_topk_topp_sampling_crafted_rows_and_errors(dec):
+    """Lower index first on equal logits, equal logits split the draw in index order,
+    NaN carries no weight; bad arguments and sampling before a step are refused."""
+    cfg = fmt(MINI, "bf16", "bf16")
+    case = make_case(cfg, [5, 9, 3], 128, seed=23)
+    d = dec.Decoder(case.cfg, case.weights, num_blocks=case.num_blocks, max_batch=4,
+                    max_seq_len=case.max_seq_len, kv_pool=case.pool.clone())
+    u3 = torch.tensor([0.5, 0.5, 0.5], dtype=torch.float32, device="cuda")
+    with pytest.raises(dec.DecError):
+        d.sample(u3, 1.0, 4, 1.0)
+    d.step([1, 2, 3], [5, 9, 3], case.block_tables[:3])
+    torch.cuda.synchronize()
+    V = cfg.vocab
+    rows = torch.full((3, V), -5.0, dtype=torch.float32)
+    rows[0, 11] = rows[0, V - 2] = rows[0, 500] = 4.0       # three-way tie at the top
+    rows[1, :] = 0.0                                         # all equal
+    rows[2, 3] = float("nan")
+    rows[2, 4] = 1.0
+    rows[2, 9] = 1.0
+    d.logits[:3].copy_(rows.cuda())
+    assert d.sample(u3, 1.0, 1, 1.0).cpu().tolist()[0] == 11
+    u = torch.tensor([0.0, 0.26, 0.99], dtype=torch.float32, device="cuda")
+    tok = d.sample(u, 1.0, 4, 1.0).cpu().tolist()
+    assert tok[0] == 11                      # ranked 11, 500, V - 2, then a -5 row
+    assert tok[1] == 1                       # equal weights: floor(0.26 * 4)
+    assert tok[2] in (4, 9) or tok[2] == 0   # NaN (index 3) never drawn
+    assert tok[2] != 3
+    tok = d.sample(u, 1.0, 2, 1.0).cpu().tolist()
+    assert tok[2] == 9                       # u = 0.99 over the two equal candidates 4, 9
+    for bad in ((0.0, 4, 1.0), (1.0, 0, 1.0), (1.0, 65, 1.0), (1.0, 4, 0.0), (1.0, 4, 1.5)):
+        with pytest.raises(dec.DecError):
+            d.sample(u, *bad)
+    d.close()
+
+
 @pytest.mark.parametrize("w,kv", [("bf16", "bf16"), ("fp8", "fp8")])
 @pytest.mark.parametrize("B", [1, 3, 16])
 def test_mini_model_unfused_plan(dec, w, kv, B):
