@@ -346,16 +346,19 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), lane = threadIdx.x % WAVE;
   const int prow = lane / LPP, eoff = (lane % LPP) * EPL;
 
+  // The splits divide the longest context the block table holds (bps blocks), so that a
+  // wave's block ids are fetched together with the sequence length rather than after it.
+  const int per = (p.bps + p.n_split - 1) / p.n_split;
+  const int blk0 = split * per;
+  // lane i holds the physical id of the wave's i-th block, blk0 + wave + i NW (read for
+  // every block the table holds; used for the i < nb that the context reaches)
+  const int my_blk = blk0 + wave + lane * NW;
   const int pos = gld(p.seq_lens + b);
+  const int my_phys = my_blk < p.bps ? gld(p.bt + (int64_t)b * p.bps + my_blk) : 0;
   const int ntok = pos + 1;  // 0 for a padded row
   const int nblk = pos >= 0 ? pos / KV_BLOCK + 1 : 0;
-  const int per = (nblk + p.n_split - 1) / p.n_split;
-  const int blk0 = split * per;
   const int blk1 = min(nblk, blk0 + per);
-  // this wave's blocks: blk0 + wave + i NW, i < nb; lane i holds the physical id of the i-th
   const int nb = blk0 + wave < blk1 ? (blk1 - blk0 - wave + NW - 1) / NW : 0;
-  const int my_blk = blk0 + wave + lane * NW;
-  const int my_phys = lane < nb ? gld(p.bt + (int64_t)b * p.bps + my_blk) : 0;
 
   const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
   // loads of the wave's i-th block (coherent for the block of the new token when FUSED)
