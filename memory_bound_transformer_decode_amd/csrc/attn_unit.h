@@ -11,6 +11,11 @@ namespace dec {
 
 
 constexpr int MAX_SPLIT = 64;  // splits per (sequence, kv head); the host keeps n_split within it
+#ifndef DEC_ATTN_COMBINE_PRE
+#define DEC_ATTN_COMBINE_PRE 4
+#endif
+// most splits whose partial outputs the combine loads ahead of their max and sum
+constexpr int ATTN_COMBINE_PRE = DEC_ATTN_COMBINE_PRE;
 #ifndef DEC_ATTN_WAVES
 #define DEC_ATTN_WAVES 8
 #endif
@@ -534,14 +539,34 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
   __syncthreads();
   if (!last) return;
 
-  // combine the n_split partials of the group's G heads
+  // combine the n_split partials of the group's G heads.  The partial max and sum of
+  // (head, split) pair threadIdx.x are loaded first; with at most ATTN_COMBINE_PRE
+  // splits each thread's partial outputs follow at once, before the max and sum reach
+  // LDS, so that their round trip overlaps that of the max and sum (measured: a gain
+  // with 3 splits, a loss with 8 or more held in registers).
+  constexpr int PRE = ATTN_COMBINE_PRE;
+  constexpr int NI = (G * DH + NW * WAVE - 1) / (NW * WAVE);  // outputs per thread
   auto& cm = S.cm;
   auto& cl = S.cl;
   auto& cM = S.cM;
-  for (int idx = threadIdx.x; idx < G * p.n_split; idx += NW * WAVE) {
+  const int nml = G * p.n_split;
+  const int64_t row_g = ((int64_t)b * p.Hq + c * G) * p.n_split;  // (head c G, split 0)
+  uint64_t ml0 = 0;
+  if (threadIdx.x < nml) ml0 = cld(reinterpret_cast<const uint64_t*>(p.part_ml + (row_g + threadIdx.x) * 2));
+  const bool pre = p.n_split <= PRE;
+  float po[NI][PRE];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = threadIdx.x + i * NW * WAVE;
+    const int64_t row0 = row_g + (int64_t)(idx / DH) * p.n_split;
+#pragma unroll
+    for (int sp = 0; sp < PRE; ++sp)
+      if (pre && idx < G * DH && sp < p.n_split) po[i][sp] = cld(p.part_o + (row0 + sp) * DH + idx % DH);
+  }
+  for (int idx = threadIdx.x; idx < nml; idx += NW * WAVE) {
     const int h = idx / p.n_split, sp = idx % p.n_split;
-    const int64_t row = ((int64_t)b * p.Hq + c * G + h) * p.n_split + sp;
-    const uint64_t ml = cld(reinterpret_cast<const uint64_t*>(p.part_ml + row * 2));
+    const uint64_t ml =
+        idx == (int)threadIdx.x ? ml0 : cld(reinterpret_cast<const uint64_t*>(p.part_ml + (row_g + idx) * 2));
     cm[h][sp] = __uint_as_float((uint32_t)ml);
     cl[h][sp] = __uint_as_float((uint32_t)(ml >> 32));
   }
@@ -552,18 +577,32 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
     cM[threadIdx.x] = M;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * DH; idx += NW * WAVE) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = threadIdx.x + i * NW * WAVE;
+    if (idx >= G * DH) break;
     const int h = idx / DH, e = idx % DH;
     const float M = cM[h];
     const int64_t row0 = ((int64_t)b * p.Hq + c * G + h) * p.n_split;
     float out = 0.f;
     if (M != -INFINITY) {
       float O = 0.f, L = 0.f;
+      if (pre) {
+#pragma unroll
+        for (int sp = 0; sp < PRE; ++sp) {
+          if (sp < p.n_split) {
+            const float f = exp2f(cm[h][sp] - M);
+            O = fmaf(f, po[i][sp], O);
+            L = fmaf(f, cl[h][sp], L);
+          }
+        }
+      } else {
 #pragma unroll 8
-      for (int sp = 0; sp < p.n_split; ++sp) {
-        const float f = exp2f(cm[h][sp] - M);
-        O = fmaf(f, cld(p.part_o + (row0 + sp) * DH + e), O);
-        L = fmaf(f, cl[h][sp], L);
+        for (int sp = 0; sp < p.n_split; ++sp) {
+          const float f = exp2f(cm[h][sp] - M);
+          O = fmaf(f, cld(p.part_o + (row0 + sp) * DH + e), O);
+          L = fmaf(f, cl[h][sp], L);
+        }
       }
       out = O / L;
     }

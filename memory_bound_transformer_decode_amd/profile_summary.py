@@ -3,7 +3,12 @@
 Kernel durations (from ``rocprofv3 --kernel-trace --stats --output-format csv``)::
 
     python -m memory_bound_transformer_decode_amd.profile_summary stats DIR \
-        --command "<the rocprofv3 command>" [--top 12] > profiles/<kernel>_<workload>.md
+        --command "<the rocprofv3 command>" [--top 12] [--match dec::] > profiles/<...>.md
+
+Counters of any --pmc run, as the mean per dispatch for each kernel::
+
+    python -m memory_bound_transformer_decode_amd.profile_summary counters DIR \
+        --command "<the rocprofv3 command>" [--match dec::] > profiles/<...>.md
 
 HBM traffic of one kernel per dispatch, from two counter runs of the benchmark
 (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``) and two of a device-to-device copy of
@@ -59,6 +64,9 @@ def _col(row: Dict[str, str], *names: str) -> str:
 def stats(args) -> None:
     path = _find(args.dir, "kernel_stats.csv")
     rows = list(csv.DictReader(open(path)))
+    if args.match:
+        # the share column stays a share of all GPU time, set-up kernels included
+        rows = [r for r in rows if args.match in _col(r, "Name", "KernelName")]
     rows.sort(key=lambda r: -float(_col(r, "TotalDurationNs")))
     print("# Kernel durations (rocprofv3 --kernel-trace --stats)\n")
     print(f"Command: `{args.command}`\n")
@@ -82,6 +90,28 @@ def _counter(d: str, counter: str, kernel: str) -> List[float]:
     if not vals:
         raise SystemExit(f"no {counter} rows for kernels matching {kernel!r} in {path}")
     return vals
+
+
+def counters(args) -> None:
+    """Mean per dispatch of every counter of a --pmc run, per kernel."""
+    path = _find(args.dir, "counter_collection.csv")
+    acc: Dict[tuple, List[float]] = {}
+    for r in csv.DictReader(open(path)):
+        name = _col(r, "Kernel_Name", "KernelName")
+        if args.match not in name:
+            continue
+        key = (name, _col(r, "Counter_Name", "CounterName"))
+        acc.setdefault(key, []).append(float(_col(r, "Counter_Value", "CounterValue")))
+    names = sorted({k for k, _ in acc})
+    ctrs = sorted({c for _, c in acc})
+    print("# Counters per dispatch (rocprofv3 --pmc), mean over dispatches\n")
+    print(f"Command: `{args.command}`\n")
+    print("| kernel | dispatches | " + " | ".join(ctrs) + " |")
+    print("|---|---|" + "---|" * len(ctrs))
+    for n in names:
+        vals = [acc.get((n, c), []) for c in ctrs]
+        print(f"| `{n[:90]}` | {max(len(v) for v in vals)} | " +
+              " | ".join(f"{sum(v) / len(v):.4g}" if v else "" for v in vals) + " |")
 
 
 def traffic(args) -> None:
@@ -130,13 +160,18 @@ def main(argv=None) -> int:
     s.add_argument("dir")
     s.add_argument("--command", required=True)
     s.add_argument("--top", type=int, default=12)
+    s.add_argument("--match", default="", help="keep only kernels whose name contains this text")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--command", required=True)
+    c.add_argument("--match", default="", help="keep only kernels whose name contains this text")
     t = sub.add_parser("traffic")
     for name in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--commands"):
         t.add_argument(name, required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--copy-kernel", default="copyBuffer")
     args = ap.parse_args(argv)
-    (stats if args.cmd == "stats" else traffic)(args)
+    {"stats": stats, "counters": counters, "traffic": traffic}[args.cmd](args)
     return 0
 
 
