@@ -207,9 +207,8 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = hv ? x[e] * qscale : 0.f;
-        const uint16_t hi = f32_to_bf16(v);
-        qh[s][e] = __builtin_bit_cast(__bf16, hi);
-        ql[s][e] = __builtin_bit_cast(__bf16, f32_to_bf16(v - bf16_to_f32(hi)));
+        qh[s][e] = (__bf16)v;  // v_cvt_pk_bf16_f32: round to nearest even
+        ql[s][e] = (__bf16)(v - (float)qh[s][e]);
       }
     }
   }
@@ -283,9 +282,8 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
     for (int j = 0; j < 4; ++j) {
       const float pj = exp2f(sc[j] - mn);
       ps += pj;
-      const uint16_t hi = f32_to_bf16(pj);
-      ph[j] = __builtin_bit_cast(__bf16, hi);
-      pl[j] = __builtin_bit_cast(__bf16, f32_to_bf16(pj - bf16_to_f32(hi)));
+      ph[j] = (__bf16)pj;  // the hardware conversion (round to nearest even), two per instruction
+      pl[j] = (__bf16)(pj - (float)ph[j]);
     }
     lrun = lrun * alpha + ps;
 #pragma unroll
