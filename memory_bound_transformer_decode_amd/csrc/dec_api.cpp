@@ -434,11 +434,12 @@ void set_fold_norm(dec_ctx* c, int which, int l, int Bp, dec::MatmulParams& p) {
 }
 
 // Attention's arithmetic on the matrix cores (k_attn_mfma) from buckets of
-// ATTN_MFMA_MIN_BATCH rows (unless DEC_FLAG_NO_MFMA): there many (sequence, kv head)
-// work groups share the chip and the vector form's per-position arithmetic sets the pace;
-// below, a wave has about one block and waits on memory either way.
+// ATTN_MFMA_MIN_BATCH rows (unless DEC_FLAG_NO_MFMA): there several (sequence, kv head)
+// work groups share the chip and the vector form's per-position arithmetic sets the pace
+// (measured from 4 rows: 8B and 70B at batch 4 and 8 as fast or faster); below, a wave
+// has about one block and waits on memory either way.
 #ifndef DEC_ATTN_MFMA_MIN_BATCH
-#define DEC_ATTN_MFMA_MIN_BATCH 16
+#define DEC_ATTN_MFMA_MIN_BATCH 4
 #endif
 constexpr int ATTN_MFMA_MIN_BATCH = DEC_ATTN_MFMA_MIN_BATCH;
 bool attn_mfma(const dec_config& g, int Bp) { return !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= ATTN_MFMA_MIN_BATCH; }
