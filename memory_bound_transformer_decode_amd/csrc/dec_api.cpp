@@ -434,12 +434,12 @@ void set_fold_norm(dec_ctx* c, int which, int l, int Bp, dec::MatmulParams& p) {
 }
 
 // Attention's arithmetic on the matrix cores (k_attn_mfma) from buckets of
-// ATTN_MFMA_MIN_BATCH rows (unless DEC_FLAG_NO_MFMA): there several (sequence, kv head)
-// work groups share the chip and the vector form's per-position arithmetic sets the pace
-// (measured from 4 rows: 8B and 70B at batch 4 and 8 as fast or faster); below, a wave
-// has about one block and waits on memory either way.
+// ATTN_MFMA_MIN_BATCH rows (unless DEC_FLAG_NO_MFMA).  Measured, with q and P split into
+// bf16 parts by the hardware conversion: as fast or faster than the vector form from
+// one row (8B batch 1 2.82 against 2.86 ms per step, 32B 6.38 against 6.50), as the
+// vector form's per-position arithmetic sits on each wave's chain of blocks.
 #ifndef DEC_ATTN_MFMA_MIN_BATCH
-#define DEC_ATTN_MFMA_MIN_BATCH 4
+#define DEC_ATTN_MFMA_MIN_BATCH 1
 #endif
 constexpr int ATTN_MFMA_MIN_BATCH = DEC_ATTN_MFMA_MIN_BATCH;
 bool attn_mfma(const dec_config& g, int Bp) { return !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= ATTN_MFMA_MIN_BATCH; }
