@@ -41,10 +41,21 @@ template <int DH, bool FP8, int G, int NW>
 __global__ __launch_bounds__(WAVE * NW) void k_attn_mfma(AttnParams p) {
   __shared__ AttnSmem<DH, G, NW> S;
   __shared__ __align__(16) uint8_t vt[NW * 16 * attn_vt_row<DH>()];
-  attn_unit<DH, FP8, G, NW, false, true>(p, blockIdx.x, blockIdx.y, blockIdx.z, S, vt);
+  attn_unit<DH, FP8, G, NW, true>(p, blockIdx.x, blockIdx.y, blockIdx.z, S, vt);
 }
 
 namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Work groups per attention launch to aim for (one per CU of MI355X), and the context
+// blocks one work group takes before the context is split further.  A split costs a
+// round of partial stores, an arrival counter and a combine; a longer split costs more
+// blocks per wave in sequence (splits of 16 or 24 blocks, and target grids of 512 or
+// 1024 work groups, measured slower).
+constexpr int ATTN_TARGET_GROUPS = 256;
+constexpr int ATTN_BLOCKS_PER_SPLIT = 8;
+
 template <int DH, bool FP8, int G>
 hipError_t attn_g(const AttnParams& p, hipStream_t s) {
   const dim3 grid(p.n_split, p.Hkv, p.Bp);
@@ -71,10 +82,54 @@ hipError_t attn_go(const AttnParams& p, hipStream_t s) {
 }
 }  // namespace
 
+// Split only past ATTN_BLOCKS_PER_SPLIT blocks (of the longest context the block table
+// holds), and only while there are few (sequence, kv head) groups; every wave holds the
+// ids of its blocks in its 64 lanes, which sets the fewest splits.
+int attn_splits(const AttnShape& c, int Bp) {
+  int ns = (ATTN_TARGET_GROUPS + Bp * c.Hkv - 1) / (Bp * c.Hkv);
+  const int by_len = (c.bps + ATTN_BLOCKS_PER_SPLIT - 1) / ATTN_BLOCKS_PER_SPLIT;
+  if (ns > by_len) ns = by_len;
+  const int min_ns = (c.bps + WAVE * ATTN_WAVES - 1) / (WAVE * ATTN_WAVES);
+  if (ns < min_ns) ns = min_ns;
+  if (ns > ATTN_MAX_SPLIT) ns = ATTN_MAX_SPLIT;
+  return ns < 1 ? 1 : ns;
+}
+
+AttnScratch attn_scratch(const AttnShape& c, int Bp) {
+  const size_t rows = (size_t)Bp * attn_splits(c, Bp);
+  AttnScratch a{};
+  size_t off = 0;
+  a.part_o = off;
+  off = align256(off + rows * c.Hq * c.dh * 4);
+  a.part_ml = off;
+  off = align256(off + rows * c.Hq * 2 * 4);
+  a.cnt = off;
+  off = align256(off + (size_t)Bp * c.Hkv * 4);
+  a.total = off;
+  return a;
+}
+
 hipError_t launch_attention(const AttnParams& p, bool kv_fp8, hipStream_t s) {
+  if (p.n_split < 1 || p.n_split > ATTN_MAX_SPLIT || p.bps > p.n_split * WAVE * ATTN_WAVES) return hipErrorInvalidValue;
   if (p.dh == 64) return kv_fp8 ? attn_go<64, true>(p, s) : attn_go<64, false>(p, s);
   if (p.dh == 128) return kv_fp8 ? attn_go<128, true>(p, s) : attn_go<128, false>(p, s);
   return hipErrorInvalidValue;
+}
+
+}  // namespace dec
+
+namespace dec {
+
+// zero n counters (a kernel rather than a memset, so that a captured graph replays it)
+__global__ void k_zero_u32(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_u32, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
 }
 
 }  // namespace dec

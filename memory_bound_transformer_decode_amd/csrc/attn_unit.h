@@ -1,5 +1,4 @@
-// Split-K paged GQA decode attention: the work of one work group (shared by the
-// attention kernel and the QKV + attention kernel).
+// Split-K paged GQA decode attention: the work of one work group.
 #pragma once
 
 #include <type_traits>
@@ -10,83 +9,38 @@
 namespace dec {
 
 
-constexpr int MAX_SPLIT = 64;  // splits per (sequence, kv head); the host keeps n_split within it
-#ifndef DEC_ATTN_COMBINE_PRE
-#define DEC_ATTN_COMBINE_PRE 4
-#endif
 // most splits whose partial outputs the combine loads ahead of their max and sum
-constexpr int ATTN_COMBINE_PRE = DEC_ATTN_COMBINE_PRE;
-#ifndef DEC_ATTN_WAVES
-#define DEC_ATTN_WAVES 8
-#endif
-constexpr int ATTN_WAVES = DEC_ATTN_WAVES;  // waves per work group
+// (measured: a gain with 3 splits, a loss with 8 or more held in registers)
+constexpr int ATTN_COMBINE_PRE = 4;
 
 // LDS of one attention work group
 template <int DH, int G, int NW>
 struct AttnSmem {
-  float q[G][DH];              // the group's scaled queries (QKV + attention kernel)
   float sm[NW][G], sl[NW][G];  // per-wave running max and sum
   float so[NW][G][DH];         // per-wave output
-  float cm[G][MAX_SPLIT], cl[G][MAX_SPLIT], cM[G];  // the combine's partial max and sum
+  float cm[G][ATTN_MAX_SPLIT], cl[G][ATTN_MAX_SPLIT], cM[G];  // the combine's partial max and sum
   int last;
 };
 
 // K and V of one block of one kv head for this lane: NPASS 16-byte loads each
 // (a lane holds 8 cache elements of a row: 16 bytes of bf16 or 8 bytes of E4M3, in .x .y).
-// coh: device-coherent loads (the block holds a slot written earlier in the same kernel).
 template <int DH, bool FP8, int NPASS, int PPP>
 __device__ __forceinline__ void attn_load(const uint8_t* pool, int64_t kbase, int64_t vbase, int prow, int eoff,
-                                          u32x4 (&kr)[NPASS], u32x4 (&vr)[NPASS], bool coh = false) {
+                                          u32x4 (&kr)[NPASS], u32x4 (&vr)[NPASS]) {
   constexpr int ESZ = FP8 ? 1 : 2;
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int64_t off = (int64_t)(ps * PPP + prow) * DH + eoff;
     if (FP8) {
-      const u32x2* kp = reinterpret_cast<const u32x2*>(pool + (kbase + off));
-      const u32x2* vp = reinterpret_cast<const u32x2*>(pool + (vbase + off));
-      u32x2 k2, v2;
-      if (coh) {
-        const uint64_t a = cld(reinterpret_cast<const uint64_t*>(kp)), b = cld(reinterpret_cast<const uint64_t*>(vp));
-        k2 = u32x2{(uint32_t)a, (uint32_t)(a >> 32)};
-        v2 = u32x2{(uint32_t)b, (uint32_t)(b >> 32)};
-      } else {
-        k2 = gld(kp);
-        v2 = gld(vp);
-      }
+      const u32x2 k2 = gld(reinterpret_cast<const u32x2*>(pool + (kbase + off)));
+      const u32x2 v2 = gld(reinterpret_cast<const u32x2*>(pool + (vbase + off)));
       kr[ps] = u32x4{k2.x, k2.y, 0u, 0u};
       vr[ps] = u32x4{v2.x, v2.y, 0u, 0u};
-    } else if (coh) {
-      kr[ps] = cld16(pool + (kbase + off) * ESZ);
-      vr[ps] = cld16(pool + (vbase + off) * ESZ);
     } else {
       kr[ps] = gld16(pool + (kbase + off) * ESZ);
       vr[ps] = gld16(pool + (vbase + off) * ESZ);
     }
   }
-}
-
-// Wait (thread 0, bounded) until the work groups that write kv head c's q, k and v in the
-// same kernel have all counted themselves in ready[c] (which the next kernel of the step
-// clears).  A wait past the time bound sets the error flags and lets the work group go on
-// (its results are then not used).
-__device__ __forceinline__ void attn_wait_ready(const AttnParams& p, int c) {
-  if (threadIdx.x == 0) {
-    const unsigned* ready = p.ready + (int64_t)c * COUNTER_STRIDE;
-    if (cld(ready) < p.ready_target) {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      // the shared error flag is polled only now and then (every poll of a shared line
-      // queues behind the others)
-      for (unsigned it = 1; cld(ready) < p.ready_target; ++it) {
-        __builtin_amdgcn_s_sleep(1);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > p.timeout_ticks || ((it & 1023u) == 0 && cld(p.err_dev) != 0u)) {
-          cst(p.err_dev, 1u);
-          __hip_atomic_store(p.err_host, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-          break;
-        }
-      }
-    }
-  }
-  __syncthreads();
 }
 
 // the 8 cache elements a lane holds, as fp32
@@ -159,10 +113,9 @@ __device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const Q
   }
 }
 
-#ifndef DEC_ATTN_MFMA_DEPTH
-#define DEC_ATTN_MFMA_DEPTH 2
-#endif
-constexpr int ATTN_MFMA_DEPTH = DEC_ATTN_MFMA_DEPTH;  // KV blocks in flight per wave (MFMA form)
+// KV blocks in flight per wave in the MFMA form (three or four measured slower at batch
+// 32 and 64: the registers they take)
+constexpr int ATTN_MFMA_DEPTH = 2;
 
 // V tile of one wave for the MFMA form: 16 position rows of DH bf16, padded by 16 bytes
 template <int DH>
@@ -252,12 +205,17 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
     // V row m into the tile; zeros past the last position (those slots may hold
     // anything, even NaN, which a zero probability would not cancel in the product)
     const bool rv = pos0 + m < ntok;
+    // the previous block's reads of the tile come before these writes (LDS serves one
+    // wave's accesses in order; the wave barrier keeps the compiler from reordering them)
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const bf16x8 v = as_bf16x8(r[1][s]);
       *reinterpret_cast<u32x4*>(vt + m * TR + (s * 32 + g * 8) * 2) =
           rv ? __builtin_bit_cast(u32x4, v) : u32x4{0u, 0u, 0u, 0u};
     }
+    // ... and these writes before this block's transposed reads below
+    __builtin_amdgcn_wave_barrier();
     f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -334,12 +292,9 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
 // One work group computes one (split, kv head c, sequence b) unit of attention.  With
 // one split it writes o; otherwise it writes its partial, and the last split of the
 // group to arrive combines.  o is written device-coherently.
-// FUSED: q and the new token's K/V are written by other work groups of the same kernel.
-// The block ids and the first block (unless it holds the new token) are loaded before
-// waiting for them; q and the new token's block are then read device-coherently.
 // MF: the wave's blocks in the MFMA form (attn_wave_mfma), with the wave's V tile at
 // vtile + wave 16 attn_vt_row<DH>() bytes of LDS.
-template <int DH, bool FP8, int G, int NW, bool FUSED = false, bool MF = false>
+template <int DH, bool FP8, int G, int NW, bool MF = false>
 __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c, int b, AttnSmem<DH, G, NW>& S,
                                           uint8_t* vtile = nullptr) {
   constexpr int EPL = 8;             // cache elements per lane per row
@@ -356,58 +311,29 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
   // lane i holds the physical id of the wave's i-th block, blk0 + wave + i NW (read for
   // every block the table holds; used for the i < nb that the context reaches)
   const int my_blk = blk0 + wave + lane * NW;
-  const int pos = gld(p.seq_lens + b);
-  const int my_phys = my_blk < p.bps ? gld(p.bt + (int64_t)b * p.bps + my_blk) : 0;
+  // positions and block ids are clamped into the table and the pool, so that no
+  // metadata, whatever its source, makes a read leave them
+  const int pos = min(gld(p.seq_lens + b), p.bps * KV_BLOCK - 1);
+  const int my_phys = my_blk < p.bps ? min(max(gld(p.bt + (int64_t)b * p.bps + my_blk), 0), p.num_blocks - 1) : 0;
   const int ntok = pos + 1;  // 0 for a padded row
   const int nblk = pos >= 0 ? pos / KV_BLOCK + 1 : 0;
   const int blk1 = min(nblk, blk0 + per);
   const int nb = blk0 + wave < blk1 ? (blk1 - blk0 - wave + NW - 1) / NW : 0;
 
   const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
-  // loads of the wave's i-th block (coherent for the block of the new token when FUSED)
+  // loads of the wave's i-th block
   auto load_blk = [&](int i, u32x4 (&kr)[NPASS], u32x4 (&vr)[NPASS]) {
     const int phys = __shfl(my_phys, i);
     const int64_t kb = kv_offset(p.layer, 0, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
     const int64_t vb = kv_offset(p.layer, 1, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
-    const bool coh = FUSED && blk0 + wave + i * NW == nblk - 1;
-    attn_load<DH, FP8, NPASS, PPP>(pool, kb, vb, prow, eoff, kr, vr, coh);
+    attn_load<DH, FP8, NPASS, PPP>(pool, kb, vb, prow, eoff, kr, vr);
   };
   if constexpr (MF) {
-    static_assert(!FUSED, "the MFMA form is the attention kernel's");
     attn_wave_mfma<DH, FP8, G, NW>(p, b, c, lane, nb, blk0 + wave, ntok, my_phys,
                                    vtile + wave * 16 * attn_vt_row<DH>(), S.sm[wave], S.sl[wave], S.so[wave]);
   } else {
-  u32x4 ka[NPASS], va[NPASS];
-  bool first = false;  // block 0 already in ka/va
-  if (FUSED) {
-    if (nb > 0 && blk0 + wave != nblk - 1) {
-      load_blk(0, ka, va);
-      first = true;
-    }
-    attn_wait_ready(p, c);
-    // the block of the new token: its loads go out together with q's
-    if (nb > 0 && !first) {
-      load_blk(0, ka, va);
-      first = true;
-    }
-  }
-
-  const float qscale = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
-  // the queries: in registers, or (FUSED, where registers are scarcer than in the
-  // attention kernel: the kernel's register budget is shared with the product) in LDS
-  float qv[FUSED ? 1 : G][EPL];
-  if (FUSED) {
-    const float* qg = p.q + ((int64_t)b * p.Hq + c * G) * DH;
-    for (int i = threadIdx.x * 4; i < G * DH; i += NW * WAVE * 4) {
-      const f32x4 t = cld_f4(qg + i);
-      float* d = &S.q[0][0] + i;
-      d[0] = t.x * qscale;
-      d[1] = t.y * qscale;
-      d[2] = t.z * qscale;
-      d[3] = t.w * qscale;
-    }
-    __syncthreads();
-  } else {
+    const float qscale = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
+    float qv[G][EPL];  // the lane's 8 elements of each head's query, scaled
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float* qh = p.q + ((int64_t)b * p.Hq + c * G + h) * DH + eoff;
@@ -420,56 +346,41 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
         qv[h][e + 3] = t.w * qscale;
       }
     }
-  }
-  auto qf = [&](int h, int e) -> float { return FUSED ? S.q[h][eoff + e] : qv[FUSED ? 0 : h][e]; };
+    auto qf = [&](int h, int e) -> float { return qv[h][e]; };
 
-  auto& sm = S.sm;
-  auto& sl = S.sl;
-  auto& so = S.so;
-  // The heads [H0, H0 + GH): running state, blocks, then the wave's partial into LDS.
-  // FUSED with g = 4 takes the heads two at a time, which keeps the attention state within
-  // the register budget the product part leaves; a wave with one block keeps it in ka/va
-  // for the second pair.
-  constexpr int GH = (FUSED && G == 4) ? 2 : G;
-  static_assert(GH == G || G == 2 * GH, "one or two chunks of heads");
-  auto chunk = [&](auto h0c) {
-    constexpr int H0 = decltype(h0c)::value;
-    float m[GH], l[GH], o[GH][EPL];
+    float m[G], l[G], o[G][EPL];
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
+    for (int h = 0; h < G; ++h) {
       m[h] = -INFINITY;
       l[h] = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
     }
-    auto qc = [&](int h, int e) -> float { return qf(H0 + h, e); };
-
-    if (nb > 0 && (G > 6 || FUSED)) {
-      // wide groups, or the QKV + attention kernel: no room for a second block in registers
+    u32x4 ka[NPASS], va[NPASS];
+    if (nb > 0 && G > 6) {
+      // wide groups: no room for a second block in registers
       for (int i = 0; i < nb; ++i) {
-        // ka/va hold block 0 only before the first chunk moves on, or when it is the only one
-        const bool held = H0 == 0 ? i == 0 && first : nb == 1;
-        if (!held) load_blk(i, ka, va);
-        attn_update<DH, FP8, GH, NPASS, PPP, LPP, EPL>(blk0 + wave + i * NW, ntok, prow, qc, ka, va, m, l, o);
+        load_blk(i, ka, va);
+        attn_update<DH, FP8, G, NPASS, PPP, LPP, EPL>(blk0 + wave + i * NW, ntok, prow, qf, ka, va, m, l, o);
       }
     } else if (nb > 0) {
       // two blocks in flight: the next block's loads are issued before this one's math
       // (four in flight measured slower: the registers they take)
       u32x4 kb2[NPASS], vb2[NPASS];
-      if (!first) load_blk(0, ka, va);
+      load_blk(0, ka, va);
       for (int i = 0; i < nb; i += 2) {
         load_blk(min(i + 1, nb - 1), kb2, vb2);
-        attn_update<DH, FP8, GH, NPASS, PPP, LPP, EPL>(blk0 + wave + i * NW, ntok, prow, qc, ka, va, m, l, o);
+        attn_update<DH, FP8, G, NPASS, PPP, LPP, EPL>(blk0 + wave + i * NW, ntok, prow, qf, ka, va, m, l, o);
         if (i + 1 >= nb) break;
         load_blk(min(i + 2, nb - 1), ka, va);
-        attn_update<DH, FP8, GH, NPASS, PPP, LPP, EPL>(blk0 + wave + (i + 1) * NW, ntok, prow, qc, kb2, vb2, m, l,
-                                                       o);
+        attn_update<DH, FP8, G, NPASS, PPP, LPP, EPL>(blk0 + wave + (i + 1) * NW, ntok, prow, qf, kb2, vb2, m, l,
+                                                      o);
       }
     }
 
     // sum l and o over the position rows of the wave (lanes with the same eoff)
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
+    for (int h = 0; h < G; ++h) {
 #pragma unroll
       for (int off = LPP; off < WAVE; off <<= 1) {
         l[h] += __shfl_xor(l[h], off);
@@ -479,20 +390,14 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
     }
     if (lane == 0) {
 #pragma unroll
-      for (int h = 0; h < GH; ++h) { sm[wave][H0 + h] = m[h]; sl[wave][H0 + h] = l[h]; }
+      for (int h = 0; h < G; ++h) { S.sm[wave][h] = m[h]; S.sl[wave][h] = l[h]; }
     }
     if (prow == 0) {
 #pragma unroll
-      for (int h = 0; h < GH; ++h)
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) so[wave][H0 + h][eoff + e] = o[h][e];
+        for (int e = 0; e < EPL; ++e) S.so[wave][h][eoff + e] = o[h][e];
     }
-  };
-  chunk(std::integral_constant<int, 0>{});
-  if constexpr (GH < G) {
-    __builtin_amdgcn_sched_barrier(0);
-    chunk(std::integral_constant<int, GH>{});
-  }
   }
   __syncthreads();
   auto& sm = S.sm;
@@ -525,23 +430,12 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
   if (single) return;
 
   // arrival: the partial stores of every wave complete before this work group counts
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  int& last = S.last;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned* cnt = p.cnt + (int64_t)b * p.Hkv + c;
-    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last = prev == (unsigned)p.n_split - 1;
-    if (last) cst(cnt, 0u);  // ready for the next launch
-  }
-  __syncthreads();
-  if (!last) return;
+  if (!arrive_after_stores(p.cnt + (int64_t)b * p.Hkv + c, (unsigned)p.n_split, &S.last)) return;
 
   // combine the n_split partials of the group's G heads.  The partial max and sum of
   // (head, split) pair threadIdx.x are loaded first; with at most ATTN_COMBINE_PRE
   // splits each thread's partial outputs follow at once, before the max and sum reach
-  // LDS, so that their round trip overlaps that of the max and sum (measured: a gain
-  // with 3 splits, a loss with 8 or more held in registers).
+  // LDS, so that their round trip overlaps that of the max and sum.
   constexpr int PRE = ATTN_COMBINE_PRE;
   constexpr int NI = (G * DH + NW * WAVE - 1) / (NW * WAVE);  // outputs per thread
   auto& cm = S.cm;

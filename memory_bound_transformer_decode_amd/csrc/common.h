@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace dec {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -36,12 +38,11 @@ __device__ __forceinline__ u32x4 gld16(const void* p) { return gld(reinterpret_c
 // 16 bytes from LDS or global memory (the caller's pointer decides)
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Data one work group writes and another work group of the same kernel reads (the
-// persistent step's residual stream, q, attention partials, activations, the new
-// token's K/V) goes through device-coherent accesses: each L2 (one per XCD) is not
-// coherent with the others, so these stores write through it and these loads bypass
-// it.  No cache flush or invalidate is then needed at a grid barrier, only that the
-// stores have completed (see the barrier in the persistent step).
+// Data one work group writes and another work group of the same kernel reads (attention
+// partials, the split products' partial tiles) goes through device-coherent accesses:
+// each L2 (one per XCD) is not coherent with the others, so these stores write through
+// it and these loads bypass it.  The reader learns that the data is there from an
+// arrival counter (see arrive_after_stores).
 template <typename T>
 __device__ __forceinline__ T cld(const T* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 template <typename T>
@@ -61,6 +62,37 @@ __device__ __forceinline__ void cst_f4(float* p, float x, float y, float z, floa
 __device__ __forceinline__ f32x4 cld_f4(const float* p) {
   const u32x4 v = cld16(p);
   return f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+}
+
+// Count this work group's arrival at *cnt once every thread's device-coherent stores
+// have completed.  Returns, in every thread, whether this work group is the last of n
+// to arrive; the last one resets the counter to zero for the next launch.
+//
+// Why the last arriver sees every other work group's stores:
+//  1. each thread waits until its own stores are acknowledged (vmcnt(0): on this family
+//     the vector-memory counter also counts stores, and a device-coherent store is
+//     acknowledged once it has reached the memory side that every XCD shares).  The
+//     compiler-only fences on both sides of the wait keep the compiler from moving the
+//     atomic stores below it or the counter update above it;
+//  2. the work-group barrier orders every thread's wait before thread 0's update;
+//  3. the update is one agent-scope atomic add, so the work group that reads n - 1 has
+//     seen the n - 1 earlier updates, each made after its work group's stores completed;
+//  4. the last arriver then reads with device-coherent loads, which bypass the
+//     non-coherent L2 and cannot return a stale line.
+// `flag`: one int of LDS.
+__device__ __forceinline__ bool arrive_after_stores(unsigned* cnt, unsigned n, int* flag) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited on
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == n - 1;
+    *flag = last;
+    if (last) cst(cnt, 0u);  // ready for the next launch
+  }
+  __syncthreads();
+  return *flag != 0;
 }
 
 // ---------------------------------------------------------------- number formats
@@ -106,6 +138,32 @@ __device__ __forceinline__ f32x2 e4m3x2_to_f32x2(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
 }
 
+// two int8 codes (bytes 0,1 or bytes 2,3 of w) -> two fp32 / two bf16 (exact: |v| <= 128
+// has at most 8 significant bits).  Each byte is sign-extended and converted by one
+// instruction (a byte-select on the conversion's source), the pair packed by another.
+template <bool HI>
+__device__ __forceinline__ f32x2 i8x2_to_f32x2(uint32_t w) {
+  const uint32_t v = HI ? w >> 16 : w;
+  return f32x2{(float)(int8_t)v, (float)(int8_t)(v >> 8)};
+}
+template <bool HI>
+__device__ __forceinline__ bf16x2 i8x2_to_bf16x2(uint32_t w) {
+  const f32x2 f = i8x2_to_f32x2<HI>(w);
+  return bf16x2{(__bf16)f.x, (__bf16)f.y};
+}
+
+// two one-byte codes of format WQ -> two bf16 / two fp32
+template <int WQ, bool HI>
+__device__ __forceinline__ bf16x2 b8x2_to_bf16x2(uint32_t w) {
+  if constexpr (WQ == W_I8) return i8x2_to_bf16x2<HI>(w);
+  else return e4m3x2_to_bf16x2<HI>(w);
+}
+template <int WQ, bool HI>
+__device__ __forceinline__ f32x2 b8x2_to_f32x2(uint32_t w) {
+  if constexpr (WQ == W_I8) return i8x2_to_f32x2<HI>(w);
+  else return e4m3x2_to_f32x2<HI>(w);
+}
+
 // ---------------------------------------------------------------- dot products
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
@@ -125,19 +183,21 @@ __device__ __forceinline__ float dot8_bf16(const u32x4& w, const u32x4& x, float
   return acc;
 }
 
-// 4 E4M3 weights (one u32) . 4 bf16 activations (two u32)
-__device__ __forceinline__ float dot4_e4m3(uint32_t w, uint32_t x01, uint32_t x23, float acc) {
-  acc = dot2_bf16v(e4m3x2_to_bf16x2<false>(w), x01, acc);
-  acc = dot2_bf16v(e4m3x2_to_bf16x2<true>(w), x23, acc);
+// 4 one-byte weights (one u32) . 4 bf16 activations (two u32)
+template <int WQ>
+__device__ __forceinline__ float dot4_b8(uint32_t w, uint32_t x01, uint32_t x23, float acc) {
+  acc = dot2_bf16v(b8x2_to_bf16x2<WQ, false>(w), x01, acc);
+  acc = dot2_bf16v(b8x2_to_bf16x2<WQ, true>(w), x23, acc);
   return acc;
 }
 
-// 16 E4M3 weights . 16 bf16 activations (xa: elements 0..7, xb: 8..15)
-__device__ __forceinline__ float dot16_e4m3(const u32x4& w, const u32x4& xa, const u32x4& xb, float acc) {
-  acc = dot4_e4m3(w.x, xa.x, xa.y, acc);
-  acc = dot4_e4m3(w.y, xa.z, xa.w, acc);
-  acc = dot4_e4m3(w.z, xb.x, xb.y, acc);
-  acc = dot4_e4m3(w.w, xb.z, xb.w, acc);
+// 16 one-byte weights . 16 bf16 activations (xa: elements 0..7, xb: 8..15)
+template <int WQ>
+__device__ __forceinline__ float dot16_b8(const u32x4& w, const u32x4& xa, const u32x4& xb, float acc) {
+  acc = dot4_b8<WQ>(w.x, xa.x, xa.y, acc);
+  acc = dot4_b8<WQ>(w.y, xa.z, xa.w, acc);
+  acc = dot4_b8<WQ>(w.z, xb.x, xb.y, acc);
+  acc = dot4_b8<WQ>(w.w, xb.z, xb.w, acc);
   return acc;
 }
 

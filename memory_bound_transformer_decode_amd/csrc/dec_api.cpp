@@ -10,6 +10,14 @@
 // engine's kernel stack; "CUDA graphs & kernel fusion", Direct answer and Deep
 // dive).  Everything that varies per step is read by the kernels from device
 // buffers, so one graph per bucket serves every step.
+//
+// A plan runs over rows.  A row is one token of one sequence: its id, its 0-based
+// position and its sequence's block table.  A decode step has one row per sequence;
+// the k-token verify step has k rows per sequence at consecutive positions; a prefill
+// chunk has one row per prompt token.  The QKV kernel writes the K/V of every row
+// before the attention kernel starts, so a row at position p attends to the rows of
+// its own sequence at positions below p in the same launch: the causal mask of a
+// multi-token step comes from the per-row positions alone.
 
 #include <hip/hip_runtime.h>
 
@@ -39,25 +47,15 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int LADDER[] = {1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64};
 constexpr int N_BUCKETS = sizeof(LADDER) / sizeof(LADDER[0]);
-constexpr int MAX_SPLIT = 64;
-#ifndef DEC_ATTN_GROUPS
-#define DEC_ATTN_GROUPS 256
-#endif
-constexpr int ATTN_TARGET_GROUPS = DEC_ATTN_GROUPS;  // work groups per attention launch to aim for
-constexpr int ATTN_BLOCKS_PER_SPLIT = 8;  // context blocks one attention work group takes alone
-constexpr int ATTN_WAVES_ = 8;            // waves per attention work group (attention.hip)
-constexpr int WAVE_ = 64;
-constexpr uint32_t KNOWN_FLAGS = DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL |
-                                 DEC_FLAG_PERSISTENT | DEC_FLAG_FUSED_QKV_ATTN;
-constexpr int N_MODES = 16;  // plan-changing flag combinations (UNFUSED, NO_MFMA, PERSISTENT, FUSED_QKV_ATTN)
-constexpr int PERSIST_MAX_BATCH = 8;
-constexpr size_t PERSIST_XS_BUDGET = 128 * 1024;  // LDS for one layer input block
-constexpr int PERSIST_ASSUMED_WAVES = 256 * 8;    // sizes the attention split count
-constexpr double BARRIER_TIMEOUT_S = 0.25;
+constexpr uint32_t KNOWN_FLAGS = DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL;
+// Plans: the flags that change the kernels (UNFUSED, NO_MFMA) and whether the LM head
+// runs (prefill chunks before the last skip it).
+constexpr int MODE_SKIP_LM = 4;
+constexpr int N_MODES = 8;
+constexpr int MAX_VERIFY_K = 8;
 
-int mode_of(uint32_t flags) {
-  return (int)(((flags & DEC_FLAG_UNFUSED) ? 1 : 0) | ((flags & DEC_FLAG_NO_MFMA) ? 2 : 0) |
-               ((flags & DEC_FLAG_PERSISTENT) ? 4 : 0) | ((flags & DEC_FLAG_FUSED_QKV_ATTN) ? 8 : 0));
+int mode_of(uint32_t flags, bool skip_lm) {
+  return ((flags & DEC_FLAG_UNFUSED) ? 1 : 0) | ((flags & DEC_FLAG_NO_MFMA) ? 2 : 0) | (skip_lm ? MODE_SKIP_LM : 0);
 }
 
 int bucket_index(int n) {
@@ -70,45 +68,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int blocks_per_seq(const dec_config& c) { return (c.max_seq_len + 15) / 16; }
 
-// Context splits per (sequence, kv head) of the attention kernel.  A split costs a
-// round of partial stores, an arrival counter and a combine; a longer split costs
-// more blocks per wave in sequence.  Split only past ATTN_BLOCKS_PER_SPLIT blocks
-// (at the longest context), and only while there are few (sequence, head) groups.
-int n_split_for(const dec_config& c, int Bp) {
-  int ns = (ATTN_TARGET_GROUPS + Bp * c.n_kv_heads - 1) / (Bp * c.n_kv_heads);
-  const int bps = blocks_per_seq(c), by_len = (bps + ATTN_BLOCKS_PER_SPLIT - 1) / ATTN_BLOCKS_PER_SPLIT;
-  if (ns > by_len) ns = by_len;
-  // a wave holds the block ids of its share in its 64 lanes
-  const int min_ns = (bps + WAVE_ * ATTN_WAVES_ - 1) / (WAVE_ * ATTN_WAVES_);
-  if (ns < min_ns) ns = min_ns;
-  if (ns > MAX_SPLIT) ns = MAX_SPLIT;
-  return ns < 1 ? 1 : ns;
-}
-
-// context splits of the persistent step's attention: about two (sequence, head, split)
-// units per wave
-int n_split_persistent(const dec_config& c, int Bp) {
-  int ns = (2 * PERSIST_ASSUMED_WAVES + Bp * c.n_q_heads - 1) / (Bp * c.n_q_heads);
-  const int bps = blocks_per_seq(c);
-  if (ns > bps) ns = bps;
-  if (ns > MAX_SPLIT) ns = MAX_SPLIT;
-  return ns < 1 ? 1 : ns;
-}
-
-// the persistent step holds one layer input block [Bp][K] of bf16 in LDS
-bool persistent_fits(const dec_config& c, int Bp) {
-  size_t k = (size_t)c.d_model;
-  if ((size_t)c.n_q_heads * c.d_head > k) k = (size_t)c.n_q_heads * c.d_head;
-  if ((size_t)c.d_ff > k) k = (size_t)c.d_ff;
-  return Bp <= PERSIST_MAX_BATCH && (size_t)Bp * k * 2 <= PERSIST_XS_BUDGET;
+dec::AttnShape attn_shape(const dec_config& c) {
+  return dec::AttnShape{c.n_q_heads, c.n_kv_heads, c.d_head, blocks_per_seq(c)};
 }
 
 struct Layout {
   size_t ids, lens, bt, static_bytes;  // static region: ids | lens | block tables
   size_t h, x, q, part_o, part_ml, o, a, rope;
   size_t uf;                           // unfused step: fp32 product rows [MB][max(N)]
-  size_t mats, bar, attn_cnt, err;     // persistent-step state
-  size_t ready;                        // QKV + attention kernel: [n_kv_heads] counters, 256 B apart
+  size_t us;                           // unfused step: attention scores [MB][Hq][max_seq_len]
+  size_t attn_cnt;                     // attention split arrival counters
   size_t ssq;                          // folded RMSNorm: row-block sums of squares
   size_t gpart, gcnt;                  // MFMA products split over K: partial tiles, row-block counters
   size_t gpart_floats, gcnt_n;
@@ -136,10 +105,8 @@ Layout layout_of(const dec_config& c) {
   off = align256(off + MB * c.n_q_heads * c.d_head * 4);
   size_t rows_split = 0;  // max over buckets of Bp * n_split
   for (int i = 0; i < N_BUCKETS && LADDER[i] <= c.max_batch; ++i) {
-    size_t r = (size_t)LADDER[i] * n_split_for(c, LADDER[i]);
+    const size_t r = (size_t)LADDER[i] * dec::attn_splits(attn_shape(c), LADDER[i]);
     if (r > rows_split) rows_split = r;
-    r = (size_t)LADDER[i] * n_split_persistent(c, LADDER[i]);
-    if (persistent_fits(c, LADDER[i]) && r > rows_split) rows_split = r;
   }
   L.part_o = off;
   off = align256(off + rows_split * c.n_q_heads * c.d_head * 4);
@@ -158,6 +125,8 @@ Layout layout_of(const dec_config& c) {
     if ((size_t)c.d_model > n) n = c.d_model;
     off = align256(off + MB * n * 4);
   }
+  L.us = off;
+  off = align256(off + MB * c.n_q_heads * (size_t)c.max_seq_len * 4);
   // MFMA products: the largest partial-tile buffer and row-block count over the step's
   // matrices (gate+up also as one plain matrix, as the unfused step runs it) and the
   // buckets (every bucket, so that the size does not depend on which run on MFMA)
@@ -169,7 +138,7 @@ Layout layout_of(const dec_config& c) {
                               {c.d_ff, 2, c.d_model},   {2 * c.d_ff, 1, c.d_model},
                               {c.d_model, 1, c.d_ff},   {c.vocab, 1, c.d_model}};
     for (const auto& sh : shapes) {
-      const dec::GemmPlan gp = dec::gemm_plan(sh[0], sh[1], sh[2], Bp, c.weight_dtype == DEC_FP8_E4M3);
+      const dec::GemmPlan gp = dec::gemm_plan(sh[0], sh[1], sh[2], Bp, c.weight_dtype != DEC_BF16);
       if (gp.part_floats > part_floats) part_floats = gp.part_floats;
       if (gp.ks > 1 && (size_t)gp.n_rb > n_rb) n_rb = gp.n_rb;
     }
@@ -178,16 +147,8 @@ Layout layout_of(const dec_config& c) {
   L.gpart_floats = part_floats;
   L.gcnt_n = n_rb;
   off = align256(off + part_floats * 4);
-  L.mats = off;  // device copies of the per-layer weight pointers: 4 arrays of n_layers
-  off = align256(off + (size_t)4 * (c.n_layers > 0 ? c.n_layers : 1) * sizeof(dec::DevMat));
-  L.bar = off;
-  off = align256(off + 2 * 4);
   L.attn_cnt = off;
-  off = align256(off + MB * c.n_q_heads * 4);
-  L.err = off;
-  off = align256(off + 4);
-  L.ready = off;
-  off = align256(off + (size_t)c.n_kv_heads * dec::COUNTER_STRIDE * 4);
+  off = align256(off + MB * c.n_kv_heads * 4);
   L.ssq = off;
   off = align256(off + (size_t)dec::GEMM_SSQ_MAX * dec::GEMM_SSQ_STRIDE * 4);
   L.gcnt = off;
@@ -209,41 +170,34 @@ int validate_config(const dec_config* c) {
   if (c->vocab <= 0 || c->vocab % 2) return fail(DEC_E_INVALID, "vocab must be positive and even (got %d)", c->vocab);
   if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(DEC_E_INVALID, "rms_eps must be a positive finite number");
   if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta)) return fail(DEC_E_INVALID, "rope_theta must be finite and > 1");
-  if ((c->weight_dtype != DEC_BF16 && c->weight_dtype != DEC_FP8_E4M3) || (c->kv_dtype != DEC_BF16 && c->kv_dtype != DEC_FP8_E4M3))
-    return fail(DEC_E_INVALID, "weight_dtype / kv_dtype must be DEC_BF16 or DEC_FP8_E4M3");
+  if ((c->weight_dtype != DEC_BF16 && c->weight_dtype != DEC_FP8_E4M3 && c->weight_dtype != DEC_INT8) ||
+      (c->kv_dtype != DEC_BF16 && c->kv_dtype != DEC_FP8_E4M3))
+    return fail(DEC_E_INVALID, "weight_dtype must be DEC_BF16, DEC_FP8_E4M3 or DEC_INT8; kv_dtype DEC_BF16 or DEC_FP8_E4M3");
   if (c->block_size != 16) return fail(DEC_E_UNSUPPORTED, "block_size must be 16 (got %d)", c->block_size);
   if (c->num_blocks <= 0) return fail(DEC_E_INVALID, "num_blocks must be positive (got %d)", c->num_blocks);
   if (bucket_index(c->max_batch) < 0 || LADDER[bucket_index(c->max_batch)] != c->max_batch)
     return fail(DEC_E_INVALID, "max_batch must be one of 1, 2, 4, 8, 16, 24, ..., 64 (got %d)", c->max_batch);
   if (c->max_seq_len <= 0) return fail(DEC_E_INVALID, "max_seq_len must be positive (got %d)", c->max_seq_len);
+  // attention keeps a wave's block ids in its 64 lanes: at most 64 splits x 8 waves x 64
+  // blocks of 16 positions
+  if (c->max_seq_len > dec::ATTN_MAX_SPLIT * dec::ATTN_WAVES * 64 * 16)
+    return fail(DEC_E_UNSUPPORTED, "max_seq_len must be <= %d (got %d)", dec::ATTN_MAX_SPLIT * dec::ATTN_WAVES * 64 * 16,
+                c->max_seq_len);
   if (c->flags & ~KNOWN_FLAGS) return fail(DEC_E_INVALID, "unknown flag bits 0x%x", c->flags & ~KNOWN_FLAGS);
   return DEC_OK;
 }
 
-// waves of one work group that share a row pair's K range in a persistent product
-// phase: the smallest S in {1, 2, 4, 8} that spreads the rows evenly over the waves
-int choose_split(int items, int groups) {
-  const int pw = dec::step_waves_per_group();
-  int best = 1;
-  double best_eff = 0.0;
-  for (int S = 1; S <= pw; S *= 2) {
-    const int wg_items = (items + groups - 1) / groups;
-    const int slots = pw / S;
-    const int per_slot = (wg_items + slots - 1) / slots;
-    if (S > 1 && per_slot > dec::step_max_rounds()) continue;
-    const double work = (double)per_slot / S;
-    const double eff = ((double)items / ((double)groups * pw)) / work;
-    if (eff > best_eff + 1e-9) {
-      best_eff = eff;
-      best = S;
-    }
-  }
-  return best;
-}
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+dec::WFmt wfmt_of(int weight_dtype) {
+  return weight_dtype == DEC_FP8_E4M3 ? dec::W_E4M3 : weight_dtype == DEC_INT8 ? dec::W_I8 : dec::W_BF16;
+}
+
 }  // namespace
+
+namespace dec {
+void set_last_error(const char* msg) { g_err = msg; }
+}  // namespace dec
 
 struct dec_ctx {
   dec_config cfg{};
@@ -256,7 +210,7 @@ struct dec_ctx {
   Layout L{};
   bool loaded = false;
   bool failed = false;
-  int last_n = 0;  // sequences of the last enqueued step (0: none yet)
+  int last_n = 0;  // rows with logits after the last call (0: none yet)
   // weights
   dec_mat embed{}, lm{};
   std::vector<dec_mat> qkv, o, gu, down;
@@ -268,14 +222,9 @@ struct dec_ctx {
   hipEvent_t slot_ev[2] = {nullptr, nullptr};
   bool slot_pending[2] = {false, false};
   int slot = 0;
-  // graphs per (bucket, plan flags)
+  // graphs per (bucket, plan)
   hipGraphExec_t graphs[N_BUCKETS][N_MODES] = {};
   dec_info info{};
-  // persistent step
-  int n_cu = 0;
-  uint64_t timeout_ticks = 0;
-  unsigned* err_host = nullptr;      // pinned, written by the device on a barrier timeout
-  unsigned* err_host_dev = nullptr;  // its device address
 };
 
 namespace {
@@ -339,9 +288,6 @@ dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) 
       p.ldx = Hq * dh;
       p.out = h;
       p.ldo = d;
-      // clears the wait counters of the QKV + attention kernel that precedes it
-      p.rearm = ws_ptr<unsigned>(c, c->L.ready);
-      p.n_rearm = Hkv;
       *epi = dec::EPI_RESID;
       break;
     case DEC_MAT_GATE_UP:  // a = silu(W_gate x) * (W_up x)
@@ -381,17 +327,17 @@ dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) 
   return p;
 }
 
-// Buckets from 8 rows (bf16 weights) or 4 rows (E4M3 weights) up run the products on
+// Buckets from 8 rows (bf16 weights) or 4 rows (one-byte weights) up run the products on
 // the matrix cores (unless DEC_FLAG_NO_MFMA); smaller ones run the matrix-vector
 // kernels.  Measured on the 8B and 32B shapes: the vector kernels' activation reads from
 // LDS (Bp per weight vector) and, for E4M3, the widening of every weight once per batch
 // row make them slower than the MFMA tiles from these batches on; the MFMA tiles pad the
 // batch to 16 columns at no extra HBM traffic.
 constexpr int MFMA_MIN_BATCH_BF16 = 8;
-constexpr int MFMA_MIN_BATCH_FP8 = 4;
+constexpr int MFMA_MIN_BATCH_BYTE = 4;
 bool use_mfma(const dec_config& g, int Bp) {
   return !(g.flags & DEC_FLAG_NO_MFMA) &&
-         Bp >= (g.weight_dtype == DEC_FP8_E4M3 ? MFMA_MIN_BATCH_FP8 : MFMA_MIN_BATCH_BF16);
+         Bp >= (g.weight_dtype != DEC_BF16 ? MFMA_MIN_BATCH_BYTE : MFMA_MIN_BATCH_BF16);
 }
 
 // Row blocks of a residual product on the MFMA tiles -- O (K = Hq dh) or down (K = d_ff)
@@ -399,7 +345,7 @@ bool use_mfma(const dec_config& g, int Bp) {
 // follows it.
 int residual_row_blocks(const dec_config& g, int Bp, int which) {
   const int K = which == DEC_MAT_O ? g.n_q_heads * g.d_head : g.d_ff;
-  return dec::gemm_plan(g.d_model, 1, K, Bp, g.weight_dtype == DEC_FP8_E4M3).n_rb;
+  return dec::gemm_plan(g.d_model, 1, K, Bp, g.weight_dtype != DEC_BF16).n_rb;
 }
 
 // The MFMA plan folds the two RMSNorms of a layer and the final one into the products:
@@ -433,16 +379,12 @@ void set_fold_norm(dec_ctx* c, int which, int l, int Bp, dec::MatmulParams& p) {
   }
 }
 
-// Attention's arithmetic on the matrix cores (k_attn_mfma) from buckets of
-// ATTN_MFMA_MIN_BATCH rows (unless DEC_FLAG_NO_MFMA).  Measured, with q and P split into
-// bf16 parts by the hardware conversion: as fast or faster than the vector form from
-// one row (8B batch 1 2.82 against 2.86 ms per step, 32B 6.38 against 6.50), as the
-// vector form's per-position arithmetic sits on each wave's chain of blocks.
-#ifndef DEC_ATTN_MFMA_MIN_BATCH
-#define DEC_ATTN_MFMA_MIN_BATCH 1
-#endif
-constexpr int ATTN_MFMA_MIN_BATCH = DEC_ATTN_MFMA_MIN_BATCH;
-bool attn_mfma(const dec_config& g, int Bp) { return !(g.flags & DEC_FLAG_NO_MFMA) && Bp >= ATTN_MFMA_MIN_BATCH; }
+// Attention's arithmetic on the matrix cores (k_attn_mfma) at every batch unless
+// DEC_FLAG_NO_MFMA.  Measured, with q and P split into bf16 parts by the hardware
+// conversion: as fast or faster than the vector form from one row (8B batch 1 2.82
+// against 2.86 ms per step, 32B 6.38 against 6.50), as the vector form's per-position
+// arithmetic sits on each wave's chain of blocks.
+bool attn_mfma(const dec_config& g) { return !(g.flags & DEC_FLAG_NO_MFMA); }
 
 // norm_gain: when set, the kernel computes x = RMSNorm(h) norm_gain itself (fused_norm)
 hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const float* norm_gain = nullptr) {
@@ -455,7 +397,7 @@ hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const
     p.eps = g.rms_eps;
   }
   if (fold_norm(g, Bp)) set_fold_norm(c, which, l, Bp, p);
-  return dec::launch_matmul(p, epi, g.weight_dtype == DEC_FP8_E4M3, g.kv_dtype == DEC_FP8_E4M3, use_mfma(g, Bp), s);
+  return dec::launch_matmul(p, epi, wfmt_of(g.weight_dtype), g.kv_dtype == DEC_FP8_E4M3, use_mfma(g, Bp), s);
 }
 
 // Batches of <= 8 rows on the matrix-vector kernels normalize their own input in LDS
@@ -464,84 +406,36 @@ bool fused_norm(const dec_config& g, int Bp) {
   return !use_mfma(g, Bp) && Bp <= 8 && (size_t)Bp * g.d_model * 2 <= 128 * 1024;
 }
 
-// QKV projection and attention in one kernel (opt-in): the norm-fused batches, for head
-// sizes whose QKV work groups each lie in one head, groups of up to QKV_ATTN_MAX_GROUP
-// query heads, and while the product's activations or the attention state fit the LDS
-// of a work group
-bool fuse_qkv_attn(const dec_ctx* c, int Bp) {
+dec::AttnParams attn_params(dec_ctx* c, int Bp, int layer) {
   const dec_config& g = c->cfg;
-  return fused_norm(g, Bp) && (g.flags & DEC_FLAG_FUSED_QKV_ATTN) && g.d_head % (2 * dec::QKV_ATTN_IPW) == 0 &&
-         (g.d_head == 64 || g.d_head == 128) && g.n_q_heads / g.n_kv_heads <= dec::QKV_ATTN_MAX_GROUP &&
-         dec::qkv_attn_lds_bytes(Bp, g.d_model, g.n_q_heads, g.n_kv_heads, g.d_head) <= 160 * 1024 - 1024;
+  dec::AttnParams ap{};
+  ap.q = ws_ptr<float>(c, c->L.q);
+  ap.pool = c->pool;
+  ap.seq_lens = ws_ptr<int32_t>(c, c->L.lens);
+  ap.bt = ws_ptr<int32_t>(c, c->L.bt);
+  ap.part_o = ws_ptr<float>(c, c->L.part_o);
+  ap.part_ml = ws_ptr<float>(c, c->L.part_ml);
+  ap.o = ws_ptr<uint16_t>(c, c->L.o);
+  ap.cnt = ws_ptr<unsigned>(c, c->L.attn_cnt);
+  ap.Bp = Bp;
+  ap.Hq = g.n_q_heads;
+  ap.Hkv = g.n_kv_heads;
+  ap.dh = g.d_head;
+  ap.num_blocks = g.num_blocks;
+  ap.bps = blocks_per_seq(g);
+  ap.n_split = dec::attn_splits(attn_shape(g), Bp);
+  ap.mfma = attn_mfma(g) ? 1 : 0;
+  ap.layer = layer;
+  return ap;
 }
 
-bool use_persistent(const dec_ctx* c, int Bp) {
-  return (c->cfg.flags & DEC_FLAG_PERSISTENT) && !(c->cfg.flags & DEC_FLAG_UNFUSED) && persistent_fits(c->cfg, Bp);
-}
-
-// The whole step as one persistent kernel (Bp <= 8).
-hipError_t enqueue_persistent(dec_ctx* c, int Bp, hipStream_t s) {
-  const dec_config& g = c->cfg;
-  dec::StepParams p{};
-  p.L = g.n_layers;
-  p.d = g.d_model;
-  p.Hq = g.n_q_heads;
-  p.Hkv = g.n_kv_heads;
-  p.dh = g.d_head;
-  p.dff = g.d_ff;
-  p.V = g.vocab;
-  p.Bp = Bp;
-  p.num_blocks = g.num_blocks;
-  p.bps = blocks_per_seq(g);
-  p.n_split = n_split_persistent(g, Bp);
-  p.eps = g.rms_eps;
-  const int G = c->n_cu;
-  p.split[0] = choose_split((g.n_q_heads + 2 * g.n_kv_heads) * g.d_head / 2, G);
-  p.split[1] = choose_split(g.d_model / 2, G);
-  p.split[2] = choose_split(g.d_ff, G);
-  p.split[3] = choose_split(g.d_model / 2, G);
-  p.split[4] = choose_split(g.vocab / 2, G);
-  size_t k = (size_t)g.d_model;
-  if ((size_t)g.n_q_heads * g.d_head > k) k = (size_t)g.n_q_heads * g.d_head;
-  if ((size_t)g.d_ff > k) k = (size_t)g.d_ff;
-  p.xs_bytes = (int)(((size_t)Bp * k * 2 + 15) & ~(size_t)15);
-  const dec::DevMat* mats = ws_ptr<dec::DevMat>(c, c->L.mats);
-  const int Ls = g.n_layers > 0 ? g.n_layers : 1;
-  p.w_qkv = mats;
-  p.w_o = mats + Ls;
-  p.w_gu = mats + 2 * Ls;
-  p.w_down = mats + 3 * Ls;
-  p.embed = dec::DevMat{c->embed.w, c->embed.scale};
-  p.lm = dec::DevMat{c->lm.w, c->lm.scale};
-  p.attn_norm = c->attn_norm;
-  p.mlp_norm = c->mlp_norm;
-  p.final_norm = c->final_norm;
-  p.ids = ws_ptr<int32_t>(c, c->L.ids);
-  p.lens = ws_ptr<int32_t>(c, c->L.lens);
-  p.bt = ws_ptr<int32_t>(c, c->L.bt);
-  p.h = ws_ptr<float>(c, c->L.h);
-  p.q = ws_ptr<float>(c, c->L.q);
-  p.part_o = ws_ptr<float>(c, c->L.part_o);
-  p.part_ml = ws_ptr<float>(c, c->L.part_ml);
-  p.o = ws_ptr<uint16_t>(c, c->L.o);
-  p.a = ws_ptr<uint16_t>(c, c->L.a);
-  p.rope = ws_ptr<float2>(c, c->L.rope);
-  p.pool = c->pool;
-  p.logits = c->logits;
-  p.bar = ws_ptr<unsigned>(c, c->L.bar);
-  p.attn_cnt = ws_ptr<unsigned>(c, c->L.attn_cnt);
-  p.err_dev = ws_ptr<unsigned>(c, c->L.err);
-  p.err_host = c->err_host_dev;
-  p.timeout_ticks = c->timeout_ticks;
-  return dec::launch_step(p, g.weight_dtype == DEC_FP8_E4M3, g.kv_dtype == DEC_FP8_E4M3, G, s);
-}
-
-// Enqueue the plan of one step for a padded batch of Bp rows on stream s.
 // The unfused step (DEC_FLAG_UNFUSED, measurement only): RMSNorm kernels, the matrix
-// kernels with a plain fp32 output, and the elementwise work as kernels of its own.
-hipError_t enqueue_unfused(dec_ctx* c, int Bp, hipStream_t s) {
+// kernels with a plain fp32 output, attention as scores -> softmax -> P V through HBM,
+// and the elementwise work as kernels of its own.
+hipError_t enqueue_unfused(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   const dec_config& g = c->cfg;
-  const bool wfp8 = g.weight_dtype == DEC_FP8_E4M3, kvfp8 = g.kv_dtype == DEC_FP8_E4M3;
+  const dec::WFmt wq = wfmt_of(g.weight_dtype);
+  const bool kvfp8 = g.kv_dtype == DEC_FP8_E4M3;
   const bool mfma = use_mfma(g, Bp);
   const int d = g.d_model;
   float* h = ws_ptr<float>(c, c->L.h);
@@ -558,7 +452,7 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, hipStream_t s) {
   np.E_scale = c->embed.scale;
   np.ids = ws_ptr<int32_t>(c, c->L.ids);
   np.gain = g.n_layers > 0 ? c->attn_norm : c->final_norm;
-  if ((e = dec::launch_embed_norm(np, wfp8, s)) != hipSuccess) return e;
+  if ((e = dec::launch_embed_norm(np, wq, s)) != hipSuccess) return e;
   // the product of `which` with its rows written plainly to uf [Bp][N]
   auto plain = [&](int which, int l, dec::MatmulParams* keep) -> hipError_t {
     int epi = 0;
@@ -566,25 +460,8 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, hipStream_t s) {
     if (keep) *keep = p;
     p.out = uf;
     p.ldo = p.N;
-    return dec::launch_matmul(p, dec::EPI_LOGITS, wfp8, kvfp8, mfma, s);
+    return dec::launch_matmul(p, dec::EPI_LOGITS, wq, kvfp8, mfma, s);
   };
-  dec::AttnParams ap{};
-  ap.q = ws_ptr<float>(c, c->L.q);
-  ap.pool = c->pool;
-  ap.seq_lens = ws_ptr<int32_t>(c, c->L.lens);
-  ap.bt = ws_ptr<int32_t>(c, c->L.bt);
-  ap.part_o = ws_ptr<float>(c, c->L.part_o);
-  ap.part_ml = ws_ptr<float>(c, c->L.part_ml);
-  ap.o = ws_ptr<uint16_t>(c, c->L.o);
-  ap.cnt = ws_ptr<unsigned>(c, c->L.attn_cnt);
-  ap.Bp = Bp;
-  ap.Hq = g.n_q_heads;
-  ap.Hkv = g.n_kv_heads;
-  ap.dh = g.d_head;
-  ap.num_blocks = g.num_blocks;
-  ap.bps = blocks_per_seq(g);
-  ap.n_split = n_split_for(g, Bp);
-  ap.mfma = attn_mfma(g, Bp) ? 1 : 0;
   for (int l = 0; l < g.n_layers; ++l) {
     if (l > 0) {
       np.gain = c->attn_norm + (size_t)l * d;
@@ -593,8 +470,9 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, hipStream_t s) {
     dec::MatmulParams qp{};
     if ((e = plain(DEC_MAT_QKV, l, &qp)) != hipSuccess) return e;
     if ((e = dec::launch_rope_kv(qp, uf, kvfp8, s)) != hipSuccess) return e;
-    ap.layer = l;
-    if ((e = dec::launch_attention(ap, kvfp8, s)) != hipSuccess) return e;
+    dec::AttnParams ap = attn_params(c, Bp, l);
+    if ((e = dec::launch_attention_unfused(ap, ws_ptr<float>(c, c->L.us), g.max_seq_len, kvfp8, s)) != hipSuccess)
+      return e;
     if ((e = plain(DEC_MAT_O, l, nullptr)) != hipSuccess) return e;
     if ((e = dec::launch_add(h, uf, Bp * d, s)) != hipSuccess) return e;
     np.gain = c->mlp_norm + (size_t)l * d;
@@ -604,6 +482,7 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, hipStream_t s) {
     if ((e = plain(DEC_MAT_DOWN, l, nullptr)) != hipSuccess) return e;
     if ((e = dec::launch_add(h, uf, Bp * d, s)) != hipSuccess) return e;
   }
+  if (skip_lm) return hipSuccess;
   if (g.n_layers > 0) {
     np.gain = c->final_norm;
     if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
@@ -611,20 +490,16 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, hipStream_t s) {
   return run_matmul(c, DEC_MAT_LM_HEAD, 0, Bp, s);
 }
 
-hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
-  if (use_persistent(c, Bp)) return enqueue_persistent(c, Bp, s);
-  if (c->cfg.flags & DEC_FLAG_UNFUSED) return enqueue_unfused(c, Bp, s);
+// Enqueue the plan of one step for a padded batch of Bp rows on stream s (without the
+// LM head when skip_lm).
+hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
+  if (c->cfg.flags & DEC_FLAG_UNFUSED) return enqueue_unfused(c, Bp, skip_lm, s);
   const dec_config& g = c->cfg;
-  const bool wfp8 = g.weight_dtype == DEC_FP8_E4M3, kvfp8 = g.kv_dtype == DEC_FP8_E4M3;
-  const int bps = blocks_per_seq(g);
-  int32_t* ids = ws_ptr<int32_t>(c, c->L.ids);
-  int32_t* lens = ws_ptr<int32_t>(c, c->L.lens);
-  int32_t* bt = ws_ptr<int32_t>(c, c->L.bt);
+  const dec::WFmt wq = wfmt_of(g.weight_dtype);
+  const bool kvfp8 = g.kv_dtype == DEC_FP8_E4M3;
   float* h = ws_ptr<float>(c, c->L.h);
   uint16_t* x = ws_ptr<uint16_t>(c, c->L.x);
-  float* q = ws_ptr<float>(c, c->L.q);
-  uint16_t* o = ws_ptr<uint16_t>(c, c->L.o);
-  const int d = g.d_model, dh = g.d_head, Hq = g.n_q_heads, Hkv = g.n_kv_heads;
+  const int d = g.d_model;
   hipError_t e;
 
   dec::NormParams np{};
@@ -636,41 +511,13 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
   np.eps = g.rms_eps;
   np.E = c->embed.w;
   np.E_scale = c->embed.scale;
-  np.ids = ids;
+  np.ids = ws_ptr<int32_t>(c, c->L.ids);
   np.gain = g.n_layers > 0 ? c->attn_norm : c->final_norm;
-  if ((e = dec::launch_embed_norm(np, wfp8, s)) != hipSuccess) return e;
+  if ((e = dec::launch_embed_norm(np, wq, s)) != hipSuccess) return e;
 
-  dec::AttnParams ap{};
-  ap.q = q;
-  ap.pool = c->pool;
-  ap.seq_lens = lens;
-  ap.bt = bt;
-  ap.part_o = ws_ptr<float>(c, c->L.part_o);
-  ap.part_ml = ws_ptr<float>(c, c->L.part_ml);
-  ap.o = o;
-  ap.Bp = Bp;
-  ap.Hq = Hq;
-  ap.Hkv = Hkv;
-  ap.dh = dh;
-  ap.num_blocks = g.num_blocks;
-  ap.bps = bps;
-  ap.n_split = n_split_for(g, Bp);
-  ap.mfma = attn_mfma(g, Bp) ? 1 : 0;
-  ap.cnt = ws_ptr<unsigned>(c, c->L.attn_cnt);
-
-  // the matrix-vector kernels normalize their own input (no RMSNorm kernels)
-  const bool fn = fused_norm(g, Bp);
-  const bool fqa = fuse_qkv_attn(c, Bp);
-  if (fqa) {
-    unsigned* ready = ws_ptr<unsigned>(c, c->L.ready);
-    ap.ready = ready;
-    ap.ready_target = dec::qkv_attn_ready_target(Hq, Hkv, dh);
-    ap.err_dev = ws_ptr<unsigned>(c, c->L.err);
-    ap.err_host = c->err_host_dev;
-    ap.timeout_ticks = c->timeout_ticks;
-  }
   // no RMSNorm kernels: the matrix-vector kernels normalize their own input (fn), or the
-  // MFMA products fold the norms (fold)
+  // MFMA products fold the norms
+  const bool fn = fused_norm(g, Bp);
   const bool nk = !fn && !fold_norm(g, Bp);
   for (int l = 0; l < g.n_layers; ++l) {
     const float* an = c->attn_norm + (size_t)l * d;
@@ -678,21 +525,9 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
       np.gain = an;
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
-    ap.layer = l;
-    if (fqa) {
-      // [q; k; v] = W_qkv RMSNorm(h) g_attn with RoPE and the cache write, and attention
-      // over positions 0..p, in one kernel
-      int epi = 0;
-      dec::MatmulParams mp = matmul_params(c, DEC_MAT_QKV, l, Bp, &epi);
-      mp.nh = h;
-      mp.ng = an;
-      mp.eps = g.rms_eps;
-      if ((e = dec::launch_qkv_attn(mp, ap, wfp8, kvfp8, s)) != hipSuccess) return e;
-    } else {
-      if ((e = run_matmul(c, DEC_MAT_QKV, l, Bp, s, fn ? an : nullptr)) != hipSuccess) return e;
-      // attention over positions 0..p
-      if ((e = dec::launch_attention(ap, kvfp8, s)) != hipSuccess) return e;
-    }
+    if ((e = run_matmul(c, DEC_MAT_QKV, l, Bp, s, fn ? an : nullptr)) != hipSuccess) return e;
+    // attention over positions 0..p
+    if ((e = dec::launch_attention(attn_params(c, Bp, l), kvfp8, s)) != hipSuccess) return e;
     if ((e = run_matmul(c, DEC_MAT_O, l, Bp, s)) != hipSuccess) return e;
     // x = RMSNorm(h) g_mlp
     const float* mn = c->mlp_norm + (size_t)l * d;
@@ -703,12 +538,34 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, hipStream_t s) {
     if ((e = run_matmul(c, DEC_MAT_GATE_UP, l, Bp, s, fn ? mn : nullptr)) != hipSuccess) return e;
     if ((e = run_matmul(c, DEC_MAT_DOWN, l, Bp, s)) != hipSuccess) return e;
   }
+  if (skip_lm) return hipSuccess;
   if (g.n_layers > 0 && nk) {
     np.gain = c->final_norm;
     if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
   }
   if ((e = run_matmul(c, DEC_MAT_LM_HEAD, 0, Bp, s, fn ? c->final_norm : nullptr)) != hipSuccess) return e;
   return hipSuccess;
+}
+
+// Kernels one plan launches (graph nodes when replayed).
+int kernels_of_plan(const dec_config& g, int Bp, bool skip_lm) {
+  const bool mfma = use_mfma(g, Bp);
+  const int slices = (!mfma && Bp > 8) ? Bp / 8 : 1;  // the matrix-vector kernels take 8 rows
+  const int L = g.n_layers;
+  if (g.flags & DEC_FLAG_UNFUSED) {
+    // embedding; per layer two norms (one in layer 0), QKV, RoPE + KV write, scores,
+    // softmax, P V, O, add, gate+up, SiLU x mul, down, add; final norm and LM head
+    const int per_layer = 13 + 4 * (slices - 1);
+    int n = 1 + per_layer * L - (L > 0 ? 1 : 0);
+    if (!skip_lm) n += (L > 0 ? 1 : 0) + slices;
+    return n;
+  }
+  // per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the
+  // matrix-vector kernels fuse them or the MFMA products fold them
+  const bool norms = !fused_norm(g, Bp) && !fold_norm(g, Bp);
+  int n = 1 + (5 + (norms ? 2 : 0) + 4 * (slices - 1)) * L - (norms && L > 0 ? 1 : 0);
+  if (!skip_lm) n += slices + (norms && L > 0 ? 1 : 0);
+  return n;
 }
 
 void drop_graphs(dec_ctx* c) {
@@ -723,7 +580,7 @@ void drop_graphs(dec_ctx* c) {
 int capture(dec_ctx* c, int bi, int mode) {
   hipGraph_t graph = nullptr;
   HIPCHK(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
-  hipError_t e = enqueue_step(c, LADDER[bi], c->cap_stream);
+  hipError_t e = enqueue_step(c, LADDER[bi], (mode & MODE_SKIP_LM) != 0, c->cap_stream);
   hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
   if (e != hipSuccess) {
     if (graph) (void)hipGraphDestroy(graph);
@@ -738,11 +595,99 @@ int capture(dec_ctx* c, int bi, int mode) {
   return DEC_OK;
 }
 
-int check_mat(const dec_mat& m, bool fp8, const char* name, int layer) {
+int check_mat(const dec_mat& m, bool scaled, const char* name, int layer) {
   if (!m.w) return fail(DEC_E_INVALID, "%s[%d].w is NULL", name, layer);
   if (!aligned16(m.w)) return fail(DEC_E_INVALID, "%s[%d].w is not 16-byte aligned", name, layer);
-  if (fp8 && !m.scale) return fail(DEC_E_INVALID, "%s[%d].scale is NULL for E4M3 weights", name, layer);
-  if (!fp8 && m.scale) return fail(DEC_E_INVALID, "%s[%d].scale must be NULL for bf16 weights", name, layer);
+  if (scaled && !m.scale) return fail(DEC_E_INVALID, "%s[%d].scale is NULL for one-byte weights", name, layer);
+  if (!scaled && m.scale) return fail(DEC_E_INVALID, "%s[%d].scale must be NULL for bf16 weights", name, layer);
+  return DEC_OK;
+}
+
+// The checks every call that runs the plan makes before anything is enqueued.
+int check_ready(dec_ctx* c) {
+  if (c->failed) return fail(DEC_E_STATE, "context has failed; destroy it");
+  if (!c->loaded) return fail(DEC_E_STATE, "no weights loaded (dec_load_weights)");
+  return DEC_OK;
+}
+
+// Token id, positions [p0, p1] and the block-table entries they need, for one sequence.
+int check_tokens(const dec_config& g, const char* what, int s, const int32_t* ids, int n_ids, int p0, int p1,
+                 const int32_t* bt_row) {
+  for (int j = 0; j < n_ids; ++j)
+    if (ids[j] < 0 || ids[j] >= g.vocab)
+      return fail(DEC_E_INVALID, "%s: token id %d of sequence %d is %d, outside [0, %d)", what, j, s, ids[j], g.vocab);
+  if (p0 < 0) return fail(DEC_E_INVALID, "%s: seq_lens[%d] = %d is negative", what, s, p0);
+  if (p1 >= g.max_seq_len)
+    return fail(DEC_E_CAPACITY, "%s: sequence %d reaches position %d; positions must be < max_seq_len %d", what, s,
+                p1, g.max_seq_len);
+  for (int k = 0; k <= p1 / 16; ++k) {
+    const int blk = bt_row[k];
+    if (blk < 0 || blk >= g.num_blocks)
+      return fail(DEC_E_CAPACITY, "%s: block_tables[%d][%d] = %d outside [0, %d)", what, s, k, blk, g.num_blocks);
+  }
+  return DEC_OK;
+}
+
+// Staging of `rows` rows padded to Bp: fill(ids, lens, bt) writes the live rows into the
+// pinned slot, the padded rows get token 0 and position -1 (no cache write, no
+// attention), and one copy moves the static region to the device.
+template <typename Fill>
+int stage(dec_ctx* c, int rows, int Bp, const Fill& fill) {
+  const int bps = blocks_per_seq(c->cfg);
+  const int s = c->slot;
+  c->slot ^= 1;
+  // wait until the copy that last used this slot has finished
+  if (c->slot_pending[s]) HIPCHK(c, hipEventSynchronize(c->slot_ev[s]), "waiting for a staging slot");
+  uint8_t* st = c->pinned[s];
+  int32_t* ids = reinterpret_cast<int32_t*>(st + c->L.ids);
+  int32_t* lens = reinterpret_cast<int32_t*>(st + c->L.lens);
+  int32_t* bt = reinterpret_cast<int32_t*>(st + c->L.bt);
+  fill(ids, lens, bt);
+  for (int b = rows; b < Bp; ++b) {
+    ids[b] = 0;
+    lens[b] = -1;
+    std::memset(bt + (size_t)b * bps, 0, (size_t)bps * 4);
+  }
+  HIPCHK(c, hipMemcpyAsync(c->ws, st, c->L.static_bytes, hipMemcpyHostToDevice, c->stream), "staging copy");
+  HIPCHK(c, hipEventRecord(c->slot_ev[s], c->stream), "hipEventRecord");
+  c->slot_pending[s] = true;
+  return DEC_OK;
+}
+
+// Run the plan for Bp padded rows already staged: replay the bucket's graph (captured
+// on first use) or launch eagerly.
+int run_plan(dec_ctx* c, int Bp, bool skip_lm) {
+  const dec_config& g = c->cfg;
+  const int bi = bucket_index(Bp);
+  const int mode = mode_of(g.flags, skip_lm);
+  if (g.flags & DEC_FLAG_EAGER) {
+    hipError_t e = enqueue_step(c, Bp, skip_lm, c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
+    c->info.used_graph = 0;
+  } else {
+    if (g.flags & DEC_FLAG_CAPTURE_ALL) {
+      for (int i = 0; i < N_BUCKETS && LADDER[i] <= g.max_batch; ++i)
+        if (!c->graphs[i][mode]) {
+          int rc = capture(c, i, mode);
+          if (rc != DEC_OK) return rc;
+        }
+    }
+    if (!c->graphs[bi][mode]) {
+      int rc = capture(c, bi, mode);
+      if (rc != DEC_OK) return rc;
+    }
+    HIPCHK(c, hipGraphLaunch(c->graphs[bi][mode], c->stream), "hipGraphLaunch");
+    c->info.used_graph = 1;
+  }
+  int ncap = 0;
+  for (auto& row : c->graphs)
+    for (auto& ge : row) ncap += ge != nullptr;
+  c->info.kernels_per_step = kernels_of_plan(g, Bp, skip_lm);
+  c->info.bucket = Bp;
+  c->info.attn_splits = dec::attn_splits(attn_shape(g), Bp);
+  c->info.used_mfma = use_mfma(g, Bp) ? 1 : 0;
+  c->info.graphs_captured = ncap;
+  c->info.flags = g.flags;
   return DEC_OK;
 }
 
@@ -783,18 +728,6 @@ int dec_create(const dec_config* cfg, void* hip_stream, void* kv_pool, void* wor
     delete c;
     return rc;
   }
-  int wall_khz = 0;
-  if ((e = hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device)) != hipSuccess ||
-      (e = hipHostMalloc(reinterpret_cast<void**>(&c->err_host), 64, hipHostMallocMapped)) != hipSuccess ||
-      (e = hipHostGetDevicePointer(reinterpret_cast<void**>(&c->err_host_dev), c->err_host, 0)) != hipSuccess) {
-    rc = hip_fail(nullptr, e, "dec_create: device attributes / error word");
-    dec_destroy(c);
-    return rc;
-  }
-  *reinterpret_cast<volatile unsigned*>(c->err_host) = 0u;
-  if (hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, c->device) != hipSuccess || wall_khz <= 0)
-    wall_khz = 100000;  // the s_memrealtime counter runs at 100 MHz on this family
-  c->timeout_ticks = (uint64_t)((double)wall_khz * 1e3 * BARRIER_TIMEOUT_S);
   for (int i = 0; i < 2; ++i) {
     if ((e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned[i]), L.static_bytes, hipHostMallocDefault)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&c->slot_ev[i], hipEventDisableTiming)) != hipSuccess) {
@@ -804,11 +737,12 @@ int dec_create(const dec_config* cfg, void* hip_stream, void* kv_pool, void* wor
     }
     std::memset(c->pinned[i], 0, L.static_bytes);
   }
-  // RoPE table once; static region starts zeroed (ids 0, every row padded until set)
+  // RoPE table once; the static region starts zeroed (ids 0, every row padded until
+  // set) and so do the arrival counters
   if ((e = dec::launch_rope_table(ws_ptr<float2>(c, L.rope), cfg->max_seq_len, cfg->d_head, (double)cfg->rope_theta,
                                   c->stream)) != hipSuccess ||
       (e = hipMemsetAsync(c->ws, 0, L.static_bytes, c->stream)) != hipSuccess ||
-      (e = hipMemsetAsync(c->ws + L.bar, 0, L.total - L.bar, c->stream)) != hipSuccess ||
+      (e = hipMemsetAsync(c->ws + L.attn_cnt, 0, L.total - L.attn_cnt, c->stream)) != hipSuccess ||
       (e = hipStreamSynchronize(c->stream)) != hipSuccess) {
     rc = hip_fail(nullptr, e, "dec_create: initialising the workspace");
     dec_destroy(c);
@@ -823,18 +757,18 @@ int dec_load_weights(dec_ctx* c, const dec_weights* w) {
   if (!c || !w) return fail(DEC_E_INVALID, "ctx or weights is NULL");
   if (c->failed) return fail(DEC_E_STATE, "context has failed; destroy it");
   const dec_config& g = c->cfg;
-  const bool fp8 = g.weight_dtype == DEC_FP8_E4M3;
+  const bool scaled = g.weight_dtype != DEC_BF16;
   int rc;
-  if ((rc = check_mat(w->embed, fp8, "embed", 0)) != DEC_OK) return rc;
-  if ((rc = check_mat(w->lm_head, fp8, "lm_head", 0)) != DEC_OK) return rc;
+  if ((rc = check_mat(w->embed, scaled, "embed", 0)) != DEC_OK) return rc;
+  if ((rc = check_mat(w->lm_head, scaled, "lm_head", 0)) != DEC_OK) return rc;
   if (!w->final_norm) return fail(DEC_E_INVALID, "final_norm is NULL");
   if (g.n_layers > 0) {
     if (!w->attn_norm || !w->mlp_norm || !w->qkv || !w->o || !w->gate_up || !w->down)
       return fail(DEC_E_INVALID, "per-layer weight arrays must be non-NULL");
     for (int l = 0; l < g.n_layers; ++l) {
-      if ((rc = check_mat(w->qkv[l], fp8, "qkv", l)) != DEC_OK || (rc = check_mat(w->o[l], fp8, "o", l)) != DEC_OK ||
-          (rc = check_mat(w->gate_up[l], fp8, "gate_up", l)) != DEC_OK ||
-          (rc = check_mat(w->down[l], fp8, "down", l)) != DEC_OK)
+      if ((rc = check_mat(w->qkv[l], scaled, "qkv", l)) != DEC_OK || (rc = check_mat(w->o[l], scaled, "o", l)) != DEC_OK ||
+          (rc = check_mat(w->gate_up[l], scaled, "gate_up", l)) != DEC_OK ||
+          (rc = check_mat(w->down[l], scaled, "down", l)) != DEC_OK)
         return rc;
     }
   }
@@ -848,20 +782,6 @@ int dec_load_weights(dec_ctx* c, const dec_weights* w) {
   c->o.assign(w->o, w->o + g.n_layers);
   c->gu.assign(w->gate_up, w->gate_up + g.n_layers);
   c->down.assign(w->down, w->down + g.n_layers);
-  // device copies of the per-layer pointers for the persistent step
-  if (g.n_layers > 0) {
-    std::vector<dec::DevMat> host(4 * (size_t)g.n_layers);
-    for (int l = 0; l < g.n_layers; ++l) {
-      host[l] = dec::DevMat{c->qkv[l].w, c->qkv[l].scale};
-      host[g.n_layers + l] = dec::DevMat{c->o[l].w, c->o[l].scale};
-      host[2 * g.n_layers + l] = dec::DevMat{c->gu[l].w, c->gu[l].scale};
-      host[3 * g.n_layers + l] = dec::DevMat{c->down[l].w, c->down[l].scale};
-    }
-    hipError_t e = hipMemcpyAsync(c->ws + c->L.mats, host.data(), host.size() * sizeof(dec::DevMat),
-                                  hipMemcpyHostToDevice, c->stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
-    if (e != hipSuccess) return hip_fail(c, e, "dec_load_weights: uploading layer pointers");
-  }
   c->loaded = true;
   c->info.graphs_captured = 0;
   return DEC_OK;
@@ -877,13 +797,8 @@ int dec_set_flags(dec_ctx* c, uint32_t flags) {
 
 int dec_step(dec_ctx* c, const dec_step_args* a) {
   if (!c || !a) return fail(DEC_E_INVALID, "ctx or args is NULL");
-  if (c->failed) return fail(DEC_E_STATE, "context has failed; destroy it");
-  if (!c->loaded) return fail(DEC_E_STATE, "dec_step before dec_load_weights");
-  if (*reinterpret_cast<volatile unsigned*>(c->err_host) != 0u) {
-    c->failed = true;
-    return fail(DEC_E_HIP, "a bounded wait of an earlier step (grid barrier or attention wait) timed out; "
-                            "the context is unusable");
-  }
+  int rc = check_ready(c);
+  if (rc != DEC_OK) return rc;
   const dec_config& g = c->cfg;
   const int n = a->n_seqs;
   if (n < 1) return fail(DEC_E_INVALID, "n_seqs must be >= 1 (got %d)", n);
@@ -892,80 +807,96 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
     return fail(DEC_E_INVALID, "token_ids, seq_lens and block_tables must be non-NULL");
   const int bps = blocks_per_seq(g);
   for (int b = 0; b < n; ++b) {
-    const int t = a->token_ids[b], p = a->seq_lens[b];
-    if (t < 0 || t >= g.vocab) return fail(DEC_E_INVALID, "token_ids[%d] = %d outside [0, %d)", b, t, g.vocab);
-    if (p < 0) return fail(DEC_E_INVALID, "seq_lens[%d] = %d is negative", b, p);
-    if (p >= g.max_seq_len) return fail(DEC_E_CAPACITY, "seq_lens[%d] = %d: position must be < max_seq_len %d", b, p, g.max_seq_len);
-    for (int k = 0; k <= p / 16; ++k) {
-      const int blk = a->block_tables[(size_t)b * bps + k];
-      if (blk < 0 || blk >= g.num_blocks)
-        return fail(DEC_E_CAPACITY, "block_tables[%d][%d] = %d outside [0, %d)", b, k, blk, g.num_blocks);
-    }
+    const int p = a->seq_lens[b];
+    if ((rc = check_tokens(g, "dec_step", b, a->token_ids + b, 1, p, p, a->block_tables + (size_t)b * bps)) != DEC_OK)
+      return rc;
   }
-  const int bi = bucket_index(n);
-  const int Bp = LADDER[bi];
-
-  // stage into the pinned slot (wait until the copy that last used it has finished)
-  const int s = c->slot;
-  c->slot ^= 1;
-  if (c->slot_pending[s]) HIPCHK(c, hipEventSynchronize(c->slot_ev[s]), "waiting for a staging slot");
-  uint8_t* st = c->pinned[s];
-  int32_t* ids = reinterpret_cast<int32_t*>(st + c->L.ids);
-  int32_t* lens = reinterpret_cast<int32_t*>(st + c->L.lens);
-  int32_t* bt = reinterpret_cast<int32_t*>(st + c->L.bt);
-  std::memcpy(ids, a->token_ids, (size_t)n * 4);
-  std::memcpy(lens, a->seq_lens, (size_t)n * 4);
-  std::memcpy(bt, a->block_tables, (size_t)n * bps * 4);
-  for (int b = n; b < Bp; ++b) {  // padded rows: token 0, position -1 (no cache write, no attention)
-    ids[b] = 0;
-    lens[b] = -1;
-    std::memset(bt + (size_t)b * bps, 0, (size_t)bps * 4);
-  }
-  HIPCHK(c, hipMemcpyAsync(c->ws, st, c->L.static_bytes, hipMemcpyHostToDevice, c->stream), "staging copy");
-  HIPCHK(c, hipEventRecord(c->slot_ev[s], c->stream), "hipEventRecord");
-  c->slot_pending[s] = true;
-
-  const int mode = mode_of(g.flags);
-  if (g.flags & DEC_FLAG_EAGER) {
-    hipError_t e = enqueue_step(c, Bp, c->stream);
-    if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
-    c->info.used_graph = 0;
-  } else {
-    if (g.flags & DEC_FLAG_CAPTURE_ALL) {
-      for (int i = 0; i < N_BUCKETS && LADDER[i] <= g.max_batch; ++i)
-        if (!c->graphs[i][mode]) {
-          int rc = capture(c, i, mode);
-          if (rc != DEC_OK) return rc;
-        }
-    }
-    if (!c->graphs[bi][mode]) {
-      int rc = capture(c, bi, mode);
-      if (rc != DEC_OK) return rc;
-    }
-    HIPCHK(c, hipGraphLaunch(c->graphs[bi][mode], c->stream), "hipGraphLaunch");
-    c->info.used_graph = 1;
-  }
-  int ncap = 0;
-  for (auto& row : c->graphs)
-    for (auto& ge : row) ncap += ge != nullptr;
-  const bool persist = use_persistent(c, Bp);
-  const bool mfma = !persist && use_mfma(g, Bp);
-  const int slices = (!mfma && Bp > 8) ? Bp / 8 : 1;
-  const int L = g.n_layers;
-  // per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the
-  // matrix-vector kernels fuse them or the MFMA products fold them (and QKV + attention
-  // as one kernel where fuse_qkv_attn holds); unfused: also RoPE + KV write, SiLU x mul
-  // and two residual adds
-  const bool unfused = (g.flags & DEC_FLAG_UNFUSED) != 0;
-  const int per_layer = unfused ? 11 : fuse_qkv_attn(c, Bp) ? 4 : fused_norm(g, Bp) || fold_norm(g, Bp) ? 5 : 7;
-  c->info.kernels_per_step = persist ? 1 : 2 + per_layer * L + (slices - 1) * (4 * L + 1);
-  c->info.bucket = Bp;
+  const int Bp = LADDER[bucket_index(n)];
+  rc = stage(c, n, Bp, [&](int32_t* ids, int32_t* lens, int32_t* bt) {
+    std::memcpy(ids, a->token_ids, (size_t)n * 4);
+    std::memcpy(lens, a->seq_lens, (size_t)n * 4);
+    std::memcpy(bt, a->block_tables, (size_t)n * bps * 4);
+  });
+  if (rc != DEC_OK) return rc;
+  if ((rc = run_plan(c, Bp, false)) != DEC_OK) return rc;
   c->last_n = n;
-  c->info.attn_splits = persist ? n_split_persistent(g, Bp) : n_split_for(g, Bp);
-  c->info.used_mfma = mfma ? 1 : 0;
-  c->info.persistent = persist ? 1 : 0;
-  c->info.graphs_captured = ncap;
-  c->info.flags = g.flags;
+  c->info.rows = n;
+  c->info.launches = 1;
+  return DEC_OK;
+}
+
+int dec_verify(dec_ctx* c, const dec_verify_args* a) {
+  if (!c || !a) return fail(DEC_E_INVALID, "ctx or args is NULL");
+  int rc = check_ready(c);
+  if (rc != DEC_OK) return rc;
+  const dec_config& g = c->cfg;
+  const int n = a->n_seqs, k = a->k;
+  if (n < 1) return fail(DEC_E_INVALID, "n_seqs must be >= 1 (got %d)", n);
+  if (k < 1 || k > MAX_VERIFY_K) return fail(DEC_E_INVALID, "k must be in [1, %d] (got %d)", MAX_VERIFY_K, k);
+  if ((int64_t)n * k > g.max_batch)
+    return fail(DEC_E_CAPACITY, "n_seqs x k = %d rows exceed max_batch %d", n * k, g.max_batch);
+  if (!a->token_ids || !a->seq_lens || !a->block_tables)
+    return fail(DEC_E_INVALID, "token_ids, seq_lens and block_tables must be non-NULL");
+  const int bps = blocks_per_seq(g);
+  for (int s = 0; s < n; ++s) {
+    const int p = a->seq_lens[s];
+    if ((rc = check_tokens(g, "dec_verify", s, a->token_ids + (size_t)s * k, k, p, p + k - 1,
+                           a->block_tables + (size_t)s * bps)) != DEC_OK)
+      return rc;
+  }
+  const int rows = n * k;
+  const int Bp = LADDER[bucket_index(rows)];
+  // row s k + j: token j of sequence s at position seq_lens[s] + j, with s's block table
+  rc = stage(c, rows, Bp, [&](int32_t* ids, int32_t* lens, int32_t* bt) {
+    std::memcpy(ids, a->token_ids, (size_t)rows * 4);
+    for (int s = 0; s < n; ++s)
+      for (int j = 0; j < k; ++j) {
+        lens[s * k + j] = a->seq_lens[s] + j;
+        std::memcpy(bt + (size_t)(s * k + j) * bps, a->block_tables + (size_t)s * bps, (size_t)bps * 4);
+      }
+  });
+  if (rc != DEC_OK) return rc;
+  if ((rc = run_plan(c, Bp, false)) != DEC_OK) return rc;
+  c->last_n = rows;
+  c->info.rows = rows;
+  c->info.launches = 1;
+  return DEC_OK;
+}
+
+int dec_prefill(dec_ctx* c, const dec_prefill_args* a, int32_t* logits_row) {
+  if (!c || !a || !logits_row) return fail(DEC_E_INVALID, "ctx, args or logits_row is NULL");
+  int rc = check_ready(c);
+  if (rc != DEC_OK) return rc;
+  const dec_config& g = c->cfg;
+  const int n = a->n_tokens, p0 = a->start_pos;
+  if (n < 1) return fail(DEC_E_INVALID, "n_tokens must be >= 1 (got %d)", n);
+  if (!a->token_ids || !a->block_table) return fail(DEC_E_INVALID, "token_ids and block_table must be non-NULL");
+  if ((int64_t)p0 + n - 1 > INT32_MAX) return fail(DEC_E_CAPACITY, "start_pos + n_tokens overflows");
+  if ((rc = check_tokens(g, "dec_prefill", 0, a->token_ids, n, p0, p0 + n - 1, a->block_table)) != DEC_OK) return rc;
+  const int bps = blocks_per_seq(g);
+  const int chunk = g.max_batch;
+  int launches = 0, last_rows = 0;
+  for (int t0 = 0; t0 < n; t0 += chunk) {
+    const int rows = n - t0 < chunk ? n - t0 : chunk;
+    const bool last = t0 + rows >= n;
+    const int Bp = LADDER[bucket_index(rows)];
+    rc = stage(c, rows, Bp, [&](int32_t* ids, int32_t* lens, int32_t* bt) {
+      std::memcpy(ids, a->token_ids + t0, (size_t)rows * 4);
+      for (int j = 0; j < rows; ++j) {
+        lens[j] = p0 + t0 + j;
+        std::memcpy(bt + (size_t)j * bps, a->block_table, (size_t)bps * 4);
+      }
+    });
+    if (rc != DEC_OK) return rc;
+    // only the chunk that holds the prompt's last token needs logits
+    if ((rc = run_plan(c, Bp, !last)) != DEC_OK) return rc;
+    ++launches;
+    last_rows = rows;
+  }
+  c->last_n = last_rows;
+  c->info.rows = n;
+  c->info.launches = launches;
+  *logits_row = last_rows - 1;
   return DEC_OK;
 }
 
@@ -1016,7 +947,21 @@ int dec_sample(dec_ctx* c, const float* uniforms, float temperature, int32_t top
   return DEC_OK;
 }
 
-int dec_get_info(const dec_ctx* c, dec_info* out) {
+int dec_get_info(const dec_ctx* c, int32_t* kernels_per_step, int32_t* path_flags) {
+  if (!c || !kernels_per_step || !path_flags) return fail(DEC_E_INVALID, "ctx, kernels_per_step or path_flags is NULL");
+  const dec_info& i = c->info;
+  *kernels_per_step = i.kernels_per_step;
+  int32_t f = 0;
+  if (i.used_graph) f |= DEC_PATH_GRAPH;
+  if (i.used_mfma) f |= DEC_PATH_MFMA_PRODUCTS;
+  if (i.bucket > 0 && !(i.flags & DEC_FLAG_NO_MFMA)) f |= DEC_PATH_MFMA_ATTENTION;
+  if (i.flags & DEC_FLAG_UNFUSED) f |= DEC_PATH_UNFUSED;
+  else if (i.bucket > 0 && fold_norm(c->cfg, i.bucket)) f |= DEC_PATH_FOLDED_NORM;
+  *path_flags = f;
+  return DEC_OK;
+}
+
+int dec_get_step_info(const dec_ctx* c, dec_info* out) {
   if (!c || !out) return fail(DEC_E_INVALID, "ctx or out is NULL");
   *out = c->info;
   return DEC_OK;
@@ -1035,7 +980,6 @@ int dec_destroy(dec_ctx* c) {
     if (c->pinned[i]) (void)hipHostFree(c->pinned[i]);
   }
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
-  if (c->err_host) (void)hipHostFree(c->err_host);
   delete c;
   return rc;
 }

@@ -1,6 +1,5 @@
-// Epilogues of the weight-streaming matrix kernels (shared by the per-op kernels and
-// the persistent step kernel).  Everything they write that a later phase of the
-// persistent step reads in another work group is written device-coherently.
+// Epilogues of the weight-streaming matrix kernels: what each fused kernel does with its
+// fp32 row sums ("Kernels, Fusion & CUDA Graphs", Fix 1 table of fused kernels).
 #pragma once
 
 #include "common.h"
@@ -104,9 +103,8 @@ __device__ __forceinline__ void epi_fetch(const MatmulParams& p, int r0, int r1,
   }
 }
 
-// pair_epilogue with the inputs fetched by epi_fetch; plain stores, or device-coherent
-// ones (COH) where a later work group of the same kernel reads the result
-template <int EPI, int BT, bool COH = false>
+// pair_epilogue with the inputs fetched by epi_fetch
+template <int EPI, int BT>
 __device__ __forceinline__ void pair_epilogue_pre(const MatmulParams& p, bool kv_fp8, const EpiInputs<EPI, BT>& in,
                                                   int b, int item, int r0, int r1, float a0, float a1) {
   float y0 = a0 * in.s0, y1 = a1 * in.s1;
@@ -132,10 +130,7 @@ __device__ __forceinline__ void pair_epilogue_pre(const MatmulParams& p, bool kv
     if (r0 < qrows) {
       const int j = r0 / dh, e = r0 % dh;
       float* qp = p.q + ((int64_t)b * p.Hq + j) * dh + e;
-      if (COH)
-        cst_f2(qp, y0, y1);
-      else
-        gst(reinterpret_cast<f32x2*>(qp), f32x2{y0, y1});
+      gst(reinterpret_cast<f32x2*>(qp), f32x2{y0, y1});
       return;
     }
     const int pos = in.pos[b];
@@ -147,17 +142,11 @@ __device__ __forceinline__ void pair_epilogue_pre(const MatmulParams& p, bool kv
     if (kv_fp8) {
       const uint32_t c0 = f32_to_e4m3(y0), c1 = f32_to_e4m3(y1);
       uint16_t* kp = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.pool) + off);
-      if (COH)
-        cst(kp, (uint16_t)(c0 | (c1 << 8)));
-      else
-        gst(kp, (uint16_t)(c0 | (c1 << 8)));
+      gst(kp, (uint16_t)(c0 | (c1 << 8)));
     } else {
       const uint32_t w = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
       uint32_t* kp = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.pool) + off);
-      if (COH)
-        cst(kp, w);
-      else
-        gst(kp, w);
+      gst(kp, w);
     }
   }
 }

@@ -11,9 +11,9 @@
 //    The MFMA operand layout would have each instruction touch 16 rows with 64 bytes
 //    each, which streams measurably slower from HBM; each wave instead passes its
 //    loads through a small private LDS tile that hands every lane its operand.
-//  * E4M3 codes are widened to bf16 in registers (exact), and the per-row scale is
-//    applied once in the epilogue (dequantization fused into the matmul: kernel-fusion
-//    architecture study, section 11).
+//  * One-byte codes (E4M3 or int8) are widened to bf16 in registers (exact), and the
+//    per-row scale is applied once in the epilogue (dequantization fused into the
+//    matmul: kernel-fusion architecture study, section 11).
 //  * The activations x [Bp][K] are the other operand of every tile.  A work group owns
 //    W 16-row tiles (one per wave) and stages x through LDS in chunks of KC k-values
 //    shared by all of its waves, so its L2 reads of x are Bp / 16 W of the weight bytes
@@ -38,28 +38,26 @@ namespace {
 constexpr int KC = 256;          // k-values per staged chunk of x
 constexpr int XROW = KC + 8;     // LDS row of a staged x chunk, in bf16: 16 bytes of padding
                                  // move consecutive batch rows to different LDS banks
-#ifndef DEC_MFMA_ROWS_PER_LOAD
-#define DEC_MFMA_ROWS_PER_LOAD 4
-#endif
-// Weight rows one load instruction covers (bf16; E4M3 always 4): each row gets 64 / R
-// lanes of 16 bytes, i.e. 4 rows x 256 bytes or 2 rows x 512 bytes per instruction
-constexpr int RPL_BF16 = DEC_MFMA_ROWS_PER_LOAD;
-template <bool FP8>
-constexpr int tile_bytes() { return FP8 ? 256 : 16 * (64 / RPL_BF16); }  // of a row per group
-template <bool FP8>
-constexpr int tile_row() { return tile_bytes<FP8>() + 16; }  // LDS row of a wave's weight tile (padded)
+// Weight rows one load instruction covers (bf16; one-byte weights always 4): each row
+// gets 64 / R lanes of 16 bytes, i.e. 4 rows x 256 bytes per instruction (2 rows x 512
+// bytes measured within 1 % at 8 and 32 rows, 5 % slower at 64)
+constexpr int RPL_BF16 = 4;
+template <bool B8>
+constexpr int tile_bytes() { return B8 ? 256 : 16 * (64 / RPL_BF16); }  // of a row per group
+template <bool B8>
+constexpr int tile_row() { return tile_bytes<B8>() + 16; }  // LDS row of a wave's weight tile (padded)
 // x chunk buffers: two (the next chunk is staged while this one is read) up to 32 batch
 // columns; one beyond, where two would hold the LDS to one work group per CU
 constexpr int x_buffers(int NT) { return NT >= 3 ? 1 : 2; }
-// 16-row tiles per wave (measured on the 8B, 32B and 70B shapes at 48-64 rows): with E4M3
-// weights each x operand read from LDS (NT per k-step) costs the LDS more than the
+// 16-row tiles per wave (measured on the 8B, 32B and 70B shapes at 48-64 rows): with
+// one-byte (E4M3) weights each x operand read from LDS (NT per k-step) costs the LDS more than the
 // weights do, so from 48 columns a wave takes two tiles that share those reads -- on
 // matrices of at least TPW2_MIN_WEIGHTS weights; smaller ones would need twice the K
 // split, which costs more than it saves.  bf16 weights: one tile (two take 256 registers
 // per lane, one wave per SIMD).
 constexpr size_t TPW2_MIN_WEIGHTS = (size_t)200 << 20;
-int tiles_per_wave(int NT, bool fp8, int n_rows_total, int K) {
-  return fp8 && NT >= 3 && (size_t)n_rows_total * (size_t)K >= TPW2_MIN_WEIGHTS ? 2 : 1;
+int tiles_per_wave(int NT, bool byte_weights, int n_rows_total, int K) {
+  return byte_weights && NT >= 3 && (size_t)n_rows_total * (size_t)K >= TPW2_MIN_WEIGHTS ? 2 : 1;
 }
 
 // v_mfma_f32_16x16x32_bf16: lane l supplies A[l % 16][8 k-values] and B[8 k-values][l % 16],
@@ -67,16 +65,17 @@ int tiles_per_wave(int NT, bool fp8, int n_rows_total, int K) {
 // D[4 (l / 16) + j][l % 16], j = 0..3.  Which k-values a lane group covers is free as long
 // as A and B agree: in k-step s of a group of GK k-values, lane group g takes the 8
 // k-values s 32 + 8 g + [0, 8).
-template <int NT, bool FP8, int EPI, bool KVFP8, int W, int TPW>
+template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW>
 __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n) {
   extern __shared__ __align__(16) uint8_t lds[];  // x: [XBUFS][NT 16][XROW] bf16; tiles: [W][TPW][16][TROW]
+  constexpr bool B8 = WQ != W_BF16;  // one-byte weights (E4M3 or int8 codes)
   constexpr bool SILU = EPI == EPI_SILU;
-  constexpr int RPL = FP8 ? 4 : RPL_BF16;          // rows per weight load instruction
+  constexpr int RPL = B8 ? 4 : RPL_BF16;          // rows per weight load instruction
   constexpr int LPR = WAVE / RPL;                  // lanes per row of a load
-  constexpr int TB = tile_bytes<FP8>();            // bytes of a row per group
-  constexpr int TROW = tile_row<FP8>();
-  constexpr int GK = FP8 ? TB : TB / 2;            // k-values per group
-  constexpr int NGRP = KC / GK;                    // groups per chunk (2 bf16, 1 fp8)
+  constexpr int TB = tile_bytes<B8>();            // bytes of a row per group
+  constexpr int TROW = tile_row<B8>();
+  constexpr int GK = B8 ? TB : TB / 2;            // k-values per group
+  constexpr int NGRP = KC / GK;                    // groups per chunk (2 bf16, 1 one-byte)
   constexpr int NS = GK / 32;                      // MFMA k-steps per group
   constexpr int COLS = NT * 16;
   constexpr int XSEG = KC / 8;                     // 16-byte pieces per staged x row
@@ -87,7 +86,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int lane = tid % WAVE, m = lane % 16, kg = lane / 16;
-  uint8_t* tile = lds + (size_t)XBUFS * XBUF * 2 + (size_t)wave * TPW * 16 * tile_row<FP8>();
+  uint8_t* tile = lds + (size_t)XBUFS * XBUF * 2 + (size_t)wave * TPW * 16 * tile_row<B8>();
   // rows: output rows of the product (d_ff intermediate indices for gate+up); a tile
   // covers TR of them, a wave TPW tiles (TPW > 1: each x operand read from LDS feeds
   // TPW tiles' products)
@@ -105,7 +104,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
     if (SILU) return (i < 8 ? 0 : p.d_ff) + min(r0 + (i & 7), rows - 1);
     return min(r0 + i, rows - 1);
   };
-  const size_t rowbytes = FP8 ? (size_t)p.K : (size_t)p.K * 2;
+  const size_t rowbytes = B8 ? (size_t)p.K : (size_t)p.K * 2;
   // load q of a group: lane (r = lane / LPR, j = lane % LPR) reads 16 bytes at byte 16 j
   // of the group's TB bytes of tile row RPL q + r
   constexpr int NQ = 16 / RPL;
@@ -123,7 +122,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   auto load_w = [&](int c, u32x4 (&wr)[TPW][NGRP][NQ]) {
 #pragma unroll
     for (int gi = 0; gi < NGRP; ++gi) {
-      const int off = min(c * KC * (FP8 ? 1 : 2) + gi * TB + lj * 16, lastv);
+      const int off = min(c * KC * (B8 ? 1 : 2) + gi * TB + lj * 16, lastv);
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
@@ -171,10 +170,10 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const uint8_t* tr = tile + (tt * 16 + m) * TROW;
-          if (FP8) {
+          if (B8) {
             const u32x2 c8 = *reinterpret_cast<const u32x2*>(tr + s * 32 + kg * 8);
-            const bf16x2 q0 = e4m3x2_to_bf16x2<false>(c8.x), q1 = e4m3x2_to_bf16x2<true>(c8.x);
-            const bf16x2 q2 = e4m3x2_to_bf16x2<false>(c8.y), q3 = e4m3x2_to_bf16x2<true>(c8.y);
+            const bf16x2 q0 = b8x2_to_bf16x2<WQ, false>(c8.x), q1 = b8x2_to_bf16x2<WQ, true>(c8.x);
+            const bf16x2 q2 = b8x2_to_bf16x2<WQ, false>(c8.y), q3 = b8x2_to_bf16x2<WQ, true>(c8.y);
             av[tt] = bf16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
           } else {
             av[tt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tr + s * 64 + kg * 16));
@@ -303,17 +302,8 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
         const f32x4 v = acc[tt][t];
         cst_f4(part + ((tt * NT + t) * WAVE + lane) * 4, v.x, v.y, v.z, v.w);
       }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial stores have completed
     __shared__ int last;
-    __syncthreads();
-    if (tid == 0) {
-      unsigned* cnt = p.gcnt + (int64_t)rb * COUNTER_STRIDE;
-      const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = prev == (unsigned)ks_n - 1;
-      if (last) cst(cnt, 0u);  // ready for the next launch
-    }
-    __syncthreads();
-    if (!last) return;
+    if (!arrive_after_stores(p.gcnt + (int64_t)rb * COUNTER_STRIDE, (unsigned)ks_n, &last)) return;
     // sum the splits in order 0..ks_n-1 (this work group's own from registers)
     f32x4 tot[TPW][NT];
 #pragma unroll
@@ -457,15 +447,15 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   }
 }
 
-template <bool FP8>
+template <bool B8>
 constexpr size_t lds_bytes(int NT, int W, int TPW) {
-  return (size_t)x_buffers(NT) * NT * 16 * XROW * 2 + (size_t)W * TPW * 16 * tile_row<FP8>();
+  return (size_t)x_buffers(NT) * NT * 16 * XROW * 2 + (size_t)W * TPW * 16 * tile_row<B8>();
 }
 
-template <int NT, bool FP8, int EPI, bool KVFP8, int W, int TPW>
+template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW>
 hipError_t go_tpw(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
-  auto kern = k_gemm_lds<NT, FP8, EPI, KVFP8, W, TPW>;
-  constexpr size_t lds = lds_bytes<FP8>(NT, W, TPW);
+  auto kern = k_gemm_lds<NT, WQ, EPI, KVFP8, W, TPW>;
+  constexpr size_t lds = lds_bytes<WQ != W_BF16>(NT, W, TPW);
   static_assert(lds <= 160 * 1024, "LDS of one work group");
   static bool attr = false;
   if (!attr && lds > 64 * 1024) {
@@ -478,19 +468,29 @@ hipError_t go_tpw(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int NT, bool FP8, int EPI, bool KVFP8, int W>
+template <int NT, int WQ, int EPI, bool KVFP8, int W>
 hipError_t go(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
-  if constexpr (FP8 && NT >= 3)
-    if (g.tpw == 2) return go_tpw<NT, FP8, EPI, KVFP8, W, 2>(p, g, s);
-  return go_tpw<NT, FP8, EPI, KVFP8, W, 1>(p, g, s);
+  if constexpr (WQ != W_BF16 && NT >= 3)
+    if (g.tpw == 2) return go_tpw<NT, WQ, EPI, KVFP8, W, 2>(p, g, s);
+  return go_tpw<NT, WQ, EPI, KVFP8, W, 1>(p, g, s);
 }
 
-template <bool FP8, int EPI, bool KVFP8>
+template <int WQ, int EPI, bool KVFP8>
 hipError_t go_nt(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
-  if (p.Bp <= 16) return go<1, FP8, EPI, KVFP8, GEMM_WAVES>(p, g, s);
-  if (p.Bp <= 32) return go<2, FP8, EPI, KVFP8, GEMM_WAVES>(p, g, s);
-  if (p.Bp <= 48) return go<3, FP8, EPI, KVFP8, GEMM_WAVES>(p, g, s);
-  return go<4, FP8, EPI, KVFP8, GEMM_WAVES>(p, g, s);
+  if (p.Bp <= 16) return go<1, WQ, EPI, KVFP8, GEMM_WAVES>(p, g, s);
+  if (p.Bp <= 32) return go<2, WQ, EPI, KVFP8, GEMM_WAVES>(p, g, s);
+  if (p.Bp <= 48) return go<3, WQ, EPI, KVFP8, GEMM_WAVES>(p, g, s);
+  return go<4, WQ, EPI, KVFP8, GEMM_WAVES>(p, g, s);
+}
+
+template <int WQ>
+hipError_t go_epi(const MatmulParams& p, const GemmPlan& g, int epi, bool kv_fp8, hipStream_t s) {
+  switch (epi) {
+    case EPI_LOGITS: return go_nt<WQ, EPI_LOGITS, false>(p, g, s);
+    case EPI_RESID: return go_nt<WQ, EPI_RESID, false>(p, g, s);
+    case EPI_SILU: return go_nt<WQ, EPI_SILU, false>(p, g, s);
+    default: return kv_fp8 ? go_nt<WQ, EPI_QKV, true>(p, g, s) : go_nt<WQ, EPI_QKV, false>(p, g, s);
+  }
 }
 
 }  // namespace
@@ -499,10 +499,10 @@ hipError_t go_nt(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
 // the chip under-filled (fewer than GEMM_TARGET_GROUPS work groups for MI355X's 256
 // CUs), K is split so that about that many work groups run, with at least two chunks
 // each.  A pure function of the shape: the workspace is sized with it.
-GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool fp8) {
+GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool byte_weights) {
   GemmPlan g{};
   const int NT = (Bp + 15) / 16;
-  const int tpw = tiles_per_wave(NT, fp8, rows * n_groups, K);
+  const int tpw = tiles_per_wave(NT, byte_weights, rows * n_groups, K);
   const int tile_rows = (n_groups == 2 ? 8 : 16) * tpw;  // gate+up tiles hold 8 of each
   g.n_rb = (rows + tile_rows * GEMM_WAVES - 1) / (tile_rows * GEMM_WAVES);
   const int nch = (K + KC - 1) / KC;
@@ -519,28 +519,21 @@ GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool fp8) {
   return g;
 }
 
-hipError_t launch_gemm_mfma(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, hipStream_t s) {
+hipError_t launch_gemm_mfma(const MatmulParams& p, int epi, WFmt wq, bool kv_fp8, hipStream_t s) {
   const int rows = epi == EPI_SILU ? p.d_ff : p.N;
   if (rows <= 0 || p.Bp <= 0) return hipSuccess;
   if (p.Bp > 64 || p.K < 16 || p.K % 16) return hipErrorInvalidValue;
-  const GemmPlan g = gemm_plan(rows, epi == EPI_SILU ? 2 : 1, p.K, p.Bp, w_fp8);
+  const GemmPlan g = gemm_plan(rows, epi == EPI_SILU ? 2 : 1, p.K, p.Bp, wq != W_BF16);
   if (g.ks > 1 && (!p.gpart || !p.gcnt || g.part_floats > p.gpart_floats || g.n_rb > p.gcnt_n))
     return hipErrorInvalidValue;
   // the folded RMSNorm: row-block sums within GEMM_SSQ_MAX x GEMM_SSQ_STRIDE
   if (p.ssq_n > GEMM_SSQ_MAX || (p.ssq_n > 0 && !p.ssq_in) ||
       (p.xout && (epi != EPI_RESID || !p.xg || !p.ssq_out || g.n_rb > GEMM_SSQ_MAX)))
     return hipErrorInvalidValue;
-  switch (epi) {
-    case EPI_LOGITS:
-      return w_fp8 ? go_nt<true, EPI_LOGITS, false>(p, g, s) : go_nt<false, EPI_LOGITS, false>(p, g, s);
-    case EPI_RESID:
-      return w_fp8 ? go_nt<true, EPI_RESID, false>(p, g, s) : go_nt<false, EPI_RESID, false>(p, g, s);
-    case EPI_SILU:
-      return w_fp8 ? go_nt<true, EPI_SILU, false>(p, g, s) : go_nt<false, EPI_SILU, false>(p, g, s);
-    default:
-      if (w_fp8)
-        return kv_fp8 ? go_nt<true, EPI_QKV, true>(p, g, s) : go_nt<true, EPI_QKV, false>(p, g, s);
-      return kv_fp8 ? go_nt<false, EPI_QKV, true>(p, g, s) : go_nt<false, EPI_QKV, false>(p, g, s);
+  switch (wq) {
+    case W_E4M3: return go_epi<W_E4M3>(p, g, epi, kv_fp8, s);
+    case W_I8: return go_epi<W_I8>(p, g, epi, kv_fp8, s);
+    default: return go_epi<W_BF16>(p, g, epi, kv_fp8, s);
   }
 }
 

@@ -1,5 +1,4 @@
-// The norm-fused matrix-vector product of one work group (shared by the per-op kernel
-// and the QKV + attention kernel).
+// The norm-fused matrix-vector product of one work group.
 #pragma once
 
 #include "common.h"
@@ -14,13 +13,12 @@ namespace dec {
 // weight loads are issued before the norm, so the norm runs under the weight stream.
 //
 // The work of work group `group`: ipw <= IPW_MAX waves, items group ipw .. group ipw +
-// ipw - 1; xs is LDS of BT K bf16.  COH: the epilogue's stores are device-coherent (for a
-// reader in another work group of the same kernel).
-template <int BT, bool FP8, int EPI, bool KVFP8, int U, int IPW_MAX, bool COH>
+// ipw - 1; xs is LDS of BT K bf16.
+template <int BT, int WQ, int EPI, bool KVFP8, int U, int IPW_MAX>
 __device__ __forceinline__ void gemv_norm_group(const MatmulParams& p, int n_items, int group, uint16_t* xs,
                                                 int ipw) {
   __shared__ float red[IPW_MAX][BT];
-  constexpr int EPV = FP8 ? 16 : 8;
+  constexpr int EPV = WQ != W_BF16 ? 16 : 8;
   const int NT = WAVE * ipw;
   const int tid = threadIdx.x, lane = tid % WAVE;
   const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
@@ -90,10 +88,10 @@ __device__ __forceinline__ void gemv_norm_group(const MatmulParams& p, int n_ite
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
           const uint16_t* xb = xs + b * K + kk * EPV;
-          if (FP8) {
+          if constexpr (WQ != W_BF16) {
             const u32x4 xa = *reinterpret_cast<const u32x4*>(xb), xc = *reinterpret_cast<const u32x4*>(xb + 8);
-            acc0[b] = dot16_e4m3(w0[u], xa, xc, acc0[b]);
-            acc1[b] = dot16_e4m3(w1[u], xa, xc, acc1[b]);
+            acc0[b] = dot16_b8<WQ>(w0[u], xa, xc, acc0[b]);
+            acc1[b] = dot16_b8<WQ>(w1[u], xa, xc, acc1[b]);
           } else {
             const u32x4 xa = *reinterpret_cast<const u32x4*>(xb);
             acc0[b] = dot8_bf16(w0[u], xa, acc0[b]);
@@ -155,7 +153,7 @@ __device__ __forceinline__ void gemv_norm_group(const MatmulParams& p, int n_ite
   }
   if (lane == 0 && have) {
 #pragma unroll
-    for (int b = 0; b < BT; ++b) pair_epilogue_pre<EPI, BT, COH>(p, KVFP8, ein, b, it, r0, r1, acc0[b], acc1[b]);
+    for (int b = 0; b < BT; ++b) pair_epilogue_pre<EPI, BT>(p, KVFP8, ein, b, it, r0, r1, acc0[b], acc1[b]);
   }
 }
 

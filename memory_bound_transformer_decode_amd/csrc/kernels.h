@@ -6,6 +6,13 @@
 
 namespace dec {
 
+// Record the message dec_last_error() returns on this thread.
+void set_last_error(const char* msg);
+
+// Weight storage formats of the matrix kernels: bf16, or one byte per weight with an
+// fp32 scale per row -- OCP E4M3 codes or two's-complement int8 codes.
+enum WFmt : int { W_BF16 = 0, W_E4M3 = 1, W_I8 = 2 };
+
 // Counters that many work groups update or poll sit 256 bytes apart: accesses to one
 // address, or to one line, are served one after another.
 constexpr int COUNTER_STRIDE = 64;
@@ -19,7 +26,7 @@ enum Epilogue : int {
 };
 
 struct MatmulParams {
-  const void* W;         // [N][K] bf16 or E4M3
+  const void* W;         // [N][K] bf16, E4M3 or int8
   const float* scale;    // [N] or nullptr (bf16)
   int N, K;              // weight rows, columns
   int d_ff;              // EPI_SILU: up rows start at d_ff (N = 2 d_ff)
@@ -43,10 +50,6 @@ struct MatmulParams {
   const float* nh;        // [Bp][K] fp32 residual stream
   const float* ng;        // [K] gain
   float eps;
-  // matrix-vector kernels (k_gemv): work group 0 zeroes rearm[i COUNTER_STRIDE], i <
-  // n_rearm, at its start (the counters of the QKV + attention kernel before it)
-  unsigned* rearm;
-  int n_rearm;
   // MFMA products that split K over work groups: partial tiles and per-row-block
   // arrival counters (COUNTER_STRIDE apart, zero between launches)
   float* gpart;
@@ -79,18 +82,17 @@ struct GemmPlan {
   int tpw;             // 16-row tiles per wave
   size_t part_floats;  // partial-tile floats the launch needs (0 when ks == 1)
 };
-// rows: per group (d_ff for gate+up, whose groups are 2); K; padded batch; E4M3 weights
-GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool fp8);
+// rows: per group (d_ff for gate+up, whose groups are 2); K; padded batch; one-byte weights
+GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool byte_weights);
 // row-block sums of squares of the folded RMSNorm: at most GEMM_SSQ_MAX row blocks of
 // the residual products (d_model <= 8192), GEMM_SSQ_STRIDE batch rows apart
 constexpr int GEMM_SSQ_MAX = 128;
 constexpr int GEMM_SSQ_STRIDE = 64;
-hipError_t launch_gemm_mfma(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, hipStream_t s);
+hipError_t launch_gemm_mfma(const MatmulParams& p, int epi, WFmt wq, bool kv_fp8, hipStream_t s);
 
 // y = matrix x for one of the epilogues: MFMA tiles when mfma, else the matrix-vector
 // kernels (batches above 8 rows in slices of 8).
-hipError_t launch_matmul(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, bool mfma,
-                         hipStream_t s);
+hipError_t launch_matmul(const MatmulParams& p, int epi, WFmt wq, bool kv_fp8, bool mfma, hipStream_t s);
 
 struct NormParams {
   const float* h;       // [Bp][d] fp32 (input, or output for the embedding kernel)
@@ -104,7 +106,7 @@ struct NormParams {
 };
 
 // h = E[ids[b]] (dequantized), x = RMSNorm(h) g
-hipError_t launch_embed_norm(const NormParams& p, bool w_fp8, hipStream_t s);
+hipError_t launch_embed_norm(const NormParams& p, WFmt wq, hipStream_t s);
 // x = RMSNorm(h) g
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
 
@@ -112,7 +114,7 @@ struct AttnParams {
   const float* q;         // [Bp][Hq][dh] fp32 (RoPE applied)
   const void* pool;
   int layer;
-  const int32_t* seq_lens;  // [Bp]
+  const int32_t* seq_lens;  // [Bp]; the row's position p (attends to 0..p); < 0: no positions
   const int32_t* bt;        // [Bp][bps]
   float* part_o;          // [Bp][Hq][n_split][dh]
   float* part_ml;         // [Bp][Hq][n_split][2]
@@ -120,79 +122,33 @@ struct AttnParams {
   unsigned* cnt;          // [Bp][Hkv] split arrival counters, zero between launches
   int Bp, Hq, Hkv, dh, num_blocks, bps, n_split;
   int mfma;               // the MFMA form of the blocks' arithmetic (k_attn_mfma)
-  // QKV + attention kernel only: per kv head c, work groups that wrote its q/k/v rows
-  // (ready[c COUNTER_STRIDE], complete at ready_target); zero at the launch (the
-  // O-projection kernel that follows clears them: MatmulParams::rearm)
-  unsigned* ready;
-  unsigned ready_target;
-  unsigned* err_dev;      // wait timeout flag, device copy
-  unsigned* err_host;     // wait timeout flag, pinned host copy
-  uint64_t timeout_ticks; // bound on one wait, in s_memrealtime ticks
 };
+
+// Context splits per (sequence, kv head) of the attention kernel: a function of the
+// shape and the padded batch only (workspaces are sized with it).
+constexpr int ATTN_MAX_SPLIT = 64;
+constexpr int ATTN_WAVES = 8;  // waves per attention work group
+struct AttnShape {
+  int Hq, Hkv, dh;
+  int bps;  // block-table entries per sequence
+};
+int attn_splits(const AttnShape& s, int Bp);
+// Workspace of one attention launch: partial outputs, partial max / sum, counters.
+struct AttnScratch {
+  size_t part_o, part_ml, cnt, total;  // byte offsets (256-byte aligned) and size
+};
+AttnScratch attn_scratch(const AttnShape& s, int Bp);
 
 // split-K paged GQA decode attention; the last split of each (sequence, kv head)
 // combines (one kernel)
 hipError_t launch_attention(const AttnParams& p, bool kv_fp8, hipStream_t s);
+// zero n 32-bit counters with a kernel (safe inside a captured graph)
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t s);
 
-// The norm-fused QKV product (mp, Bp <= 8) and attention (ap) in one kernel: the
-// attention work groups follow the product's and start once the product work groups of
-// their kv head are done.  Needs d_head % (2 QKV_ATTN_IPW) == 0 and
-// qkv_attn_lds_bytes(...) <= 160 KB; returns hipErrorInvalidValue otherwise.
-constexpr int QKV_ATTN_IPW = 8;  // row pairs (waves) per product work group
-// Query heads per kv head up to which the kernel is built: the attention state of wider
-// groups does not fit the 128 registers per lane that keep two product work groups per
-// CU (one work group's 8 waves at up to 4 waves per SIMD).
-constexpr int QKV_ATTN_MAX_GROUP = 4;
-hipError_t launch_qkv_attn(const MatmulParams& mp, const AttnParams& ap, bool w_fp8, bool kv_fp8, hipStream_t s);
-// work groups of the product part; the attention part's ready_target
-int qkv_attn_groups(const MatmulParams& mp);
-unsigned qkv_attn_ready_target(int Hq, int Hkv, int dh);
-size_t qkv_attn_lds_bytes(int Bp, int K, int Hq, int Hkv, int dh);
-
-// ---------------------------------------------------------------- persistent step (Bp <= 8)
-
-struct DevMat {
-  const void* w;
-  const float* scale;
-};
-
-struct StepParams {
-  int L, d, Hq, Hkv, dh, dff, V, Bp, num_blocks, bps, n_split;
-  float eps;
-  int split[5];           // waves sharing one row pair's K range: QKV, O, gate+up, down, LM head
-  int xs_bytes;           // LDS bytes for the activation block
-  const DevMat* w_qkv;    // device arrays [L]
-  const DevMat* w_o;
-  const DevMat* w_gu;
-  const DevMat* w_down;
-  DevMat embed, lm;
-  const float* attn_norm;
-  const float* mlp_norm;
-  const float* final_norm;
-  const int32_t* ids;
-  const int32_t* lens;
-  const int32_t* bt;
-  float* h;
-  float* q;
-  float* part_o;
-  float* part_ml;
-  uint16_t* o;
-  uint16_t* a;
-  const float2* rope;
-  void* pool;
-  float* logits;
-  unsigned* bar;          // [count, generation] of the grid barrier
-  unsigned* attn_cnt;     // [Bp][Hq] splits finished per head (self-resetting)
-  unsigned* err_dev;      // barrier timeout flag, device copy
-  unsigned* err_host;     // barrier timeout flag, pinned host copy
-  uint64_t timeout_ticks; // bound on one barrier wait, in s_memrealtime ticks
-};
-
-// One launch of the whole step: grid = one work group per CU, all resident.
-hipError_t launch_step(const StepParams& p, bool w_fp8, bool kv_fp8, int grid, hipStream_t s);
-size_t step_lds_bytes(const StepParams& p);
-int step_max_rounds();
-int step_waves_per_group();
+// The unfused form for the unfused step (measurement only): scores S = q K^T / sqrt(dh)
+// written to HBM (scores [Bp][Hq][ld_s] fp32, ld_s >= the longest context), a softmax
+// kernel over each row in place, then o = P V.
+hipError_t launch_attention_unfused(const AttnParams& p, float* scores, int ld_s, bool kv_fp8, hipStream_t s);
 
 // Elementwise kernels of the unfused step (measurement only): RoPE + KV-cache write of
 // the fp32 QKV rows qkv [Bp][N] (p: the QKV product's parameters), SiLU x mul of the

@@ -8,10 +8,10 @@
 //  * k_gemv (Bp <= 8): one wave per work group; a wave owns a contiguous range of
 //    row pairs and streams both rows with 16-byte non-temporal loads, U loads per
 //    row in flight; activations come from L2 (they are tiny and shared by every
-//    wave); bf16 products use v_dot2_f32_bf16, E4M3 weights are widened to bf16 in
-//    registers (exact) and the per-row scale is applied once in the epilogue
-//    ("dequantization fused into the matmul ... converted in-register",
-//    kernel-fusion architecture study, section 11).
+//    wave); bf16 products use v_dot2_f32_bf16, one-byte weights (E4M3 or int8 codes)
+//    are widened to bf16 in registers (exact) and the per-row scale is applied once in
+//    the epilogue, so that dequantization costs no pass of its own over the weights
+//    (kernel-fusion architecture study, section 11).
 //  * Bp >= 16: the batch is wide enough to make this a dense contraction, so MFMA
 //    tiles do the products (gemm_mfma.hip).
 //
@@ -31,14 +31,12 @@ namespace dec {
 // Work group = one row pair (item blockIdx.x), S waves; wave w takes the contiguous
 // slice [KV w / S, KV (w + 1) / S) of the 16-byte vectors of both rows, with U loads
 // per row per lane in flight; the slices' sums are added in LDS in wave order.
-template <int BT, bool FP8, int EPI, bool KVFP8, int U, int S>
+template <int BT, int WQ, int EPI, bool KVFP8, int U, int S>
 __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
-  constexpr int EPV = FP8 ? 16 : 8;  // weight elements per 16-byte vector
+  constexpr int EPV = WQ != W_BF16 ? 16 : 8;  // weight elements per 16-byte vector
   const int lane = threadIdx.x % WAVE;
   const int w = S == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int it = blockIdx.x;
-  if (it == 0)
-    for (int i = threadIdx.x; i < p.n_rearm; i += WAVE * S) cst(p.rearm + (int64_t)i * COUNTER_STRIDE, 0u);
   const int KV = p.K / EPV;  // 16-byte vectors per weight row (K % EPV == 0)
   const int kb = (int)((int64_t)KV * w / S), ke = (int)((int64_t)KV * (w + 1) / S);
   const u32x4* W = static_cast<const u32x4*>(p.W);
@@ -69,10 +67,10 @@ __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
           const uint16_t* xb = p.x + (int64_t)b * p.ldx + (int64_t)kk * EPV;
-          if (FP8) {
+          if constexpr (WQ != W_BF16) {
             const u32x4 xa = gld16(xb), xc = gld16(xb + 8);
-            acc0[b] = dot16_e4m3(w0[u], xa, xc, acc0[b]);
-            acc1[b] = dot16_e4m3(w1[u], xa, xc, acc1[b]);
+            acc0[b] = dot16_b8<WQ>(w0[u], xa, xc, acc0[b]);
+            acc1[b] = dot16_b8<WQ>(w1[u], xa, xc, acc1[b]);
           } else {
             const u32x4 xa = gld16(xb);
             acc0[b] = dot8_bf16(w0[u], xa, acc0[b]);
@@ -123,10 +121,10 @@ __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
 // <= NORM_IPW_MAX waves per work group.
 constexpr int NORM_IPW_MAX = 10;
 
-template <int BT, bool FP8, int EPI, bool KVFP8, int U>
+template <int BT, int WQ, int EPI, bool KVFP8, int U>
 __global__ __launch_bounds__(WAVE * NORM_IPW_MAX) void k_gemv_norm(MatmulParams p, int n_items, int ipw) {
   extern __shared__ __align__(16) uint8_t gemv_smem[];
-  gemv_norm_group<BT, FP8, EPI, KVFP8, U, NORM_IPW_MAX, false>(p, n_items, blockIdx.x,
+  gemv_norm_group<BT, WQ, EPI, KVFP8, U, NORM_IPW_MAX>(p, n_items, blockIdx.x,
                                                                reinterpret_cast<uint16_t*>(gemv_smem), ipw);
 }
 
@@ -139,18 +137,18 @@ namespace {
 // a long static share at the end.  Rows longer than one pass of a wave (64 U vectors)
 // are split over S <= 8 waves of the work group (a wave takes more than one pass only
 // beyond 8 passes' worth).
-template <int BT, bool FP8, int EPI, bool KVFP8, int U>
+template <int BT, int WQ, int EPI, bool KVFP8, int U>
 hipError_t gemv_s(const MatmulParams& p, int n_items, int kv, hipStream_t s) {
   const int need = (kv + WAVE * U - 1) / (WAVE * U);
   const dim3 grid(n_items);
   if (need <= 1)
-    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, U, 1>), grid, dim3(WAVE), 0, s, p);
+    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 1>), grid, dim3(WAVE), 0, s, p);
   else if (need <= 2)
-    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, U, 2>), grid, dim3(2 * WAVE), 0, s, p);
+    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 2>), grid, dim3(2 * WAVE), 0, s, p);
   else if (need <= 4)
-    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, U, 4>), grid, dim3(4 * WAVE), 0, s, p);
+    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 4>), grid, dim3(4 * WAVE), 0, s, p);
   else
-    hipLaunchKernelGGL((k_gemv<BT, FP8, EPI, KVFP8, U, 8>), grid, dim3(8 * WAVE), 0, s, p);
+    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 8>), grid, dim3(8 * WAVE), 0, s, p);
   return hipGetLastError();
 }
 
@@ -180,9 +178,9 @@ int norm_ipw(const void* kern, int n_items, size_t lds) {
   return w;
 }
 
-template <int BT, bool FP8, int EPI, bool KVFP8, int U>
+template <int BT, int WQ, int EPI, bool KVFP8, int U>
 hipError_t gemv_norm_go(const MatmulParams& p, int n_items, hipStream_t s) {
-  auto kern = k_gemv_norm<BT, FP8, EPI, KVFP8, U>;
+  auto kern = k_gemv_norm<BT, WQ, EPI, KVFP8, U>;
   const size_t lds = (size_t)BT * p.K * 2;
   static size_t allowed = 64 * 1024;  // per instance: the dynamic LDS size enabled so far
   if (lds > allowed) {
@@ -207,29 +205,29 @@ hipError_t gemv_norm_go(const MatmulParams& p, int n_items, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BT, bool FP8, int EPI, bool KVFP8>
+template <int BT, int WQ, int EPI, bool KVFP8>
 hipError_t gemv_go(const MatmulParams& p, hipStream_t s) {
   const int n_items = EPI == EPI_SILU ? p.d_ff : p.N / 2;
   if (n_items <= 0) return hipSuccess;
-  const int kv = p.K / (FP8 ? 16 : 8);
+  const int kv = p.K / (WQ != W_BF16 ? 16 : 8);
   // one wave per row pair, 4 loads per row per lane in flight and as many passes as the
   // row needs (measured faster than one deeper pass, or than splitting the row over
   // waves, which multiplies the normalizations per row pair)
-  if (p.nh) return gemv_norm_go<BT, FP8, EPI, KVFP8, 4>(p, n_items, s);
+  if (p.nh) return gemv_norm_go<BT, WQ, EPI, KVFP8, 4>(p, n_items, s);
   // shallow per-wave load depth and many waves measured best (more waves resident per
   // CU): U = 4 for rows up to 1024 vectors (two waves per row pair at K = 4096 bf16),
   // U = 2 beyond (eight waves, two passes each, for the d_ff-long rows)
-  if (kv <= 1024) return gemv_s<BT, FP8, EPI, KVFP8, 4>(p, n_items, kv, s);
-  return gemv_s<BT, FP8, EPI, KVFP8, 2>(p, n_items, kv, s);
+  if (kv <= 1024) return gemv_s<BT, WQ, EPI, KVFP8, 4>(p, n_items, kv, s);
+  return gemv_s<BT, WQ, EPI, KVFP8, 2>(p, n_items, kv, s);
 }
 
-template <bool FP8, int EPI, bool KVFP8>
+template <int WQ, int EPI, bool KVFP8>
 hipError_t dispatch_bt(const MatmulParams& p, bool mfma, hipStream_t s) {
   if (!mfma) {
-    if (p.Bp <= 1) return gemv_go<1, FP8, EPI, KVFP8>(p, s);
-    if (p.Bp <= 2) return gemv_go<2, FP8, EPI, KVFP8>(p, s);
-    if (p.Bp <= 4) return gemv_go<4, FP8, EPI, KVFP8>(p, s);
-    if (p.Bp <= 8) return gemv_go<8, FP8, EPI, KVFP8>(p, s);
+    if (p.Bp <= 1) return gemv_go<1, WQ, EPI, KVFP8>(p, s);
+    if (p.Bp <= 2) return gemv_go<2, WQ, EPI, KVFP8>(p, s);
+    if (p.Bp <= 4) return gemv_go<4, WQ, EPI, KVFP8>(p, s);
+    if (p.Bp <= 8) return gemv_go<8, WQ, EPI, KVFP8>(p, s);
     // no-MFMA mode above 8 rows: run the 8-row gemv on slices of the batch
     for (int b0 = 0; b0 < p.Bp; b0 += 8) {
       MatmulParams q = p;
@@ -242,34 +240,42 @@ hipError_t dispatch_bt(const MatmulParams& p, bool mfma, hipStream_t s) {
       q.seq_lens = p.seq_lens ? p.seq_lens + b0 : nullptr;
       q.bt = p.bt ? p.bt + (int64_t)b0 * p.bps : nullptr;
       hipError_t e;
-      if (q.Bp <= 1) e = gemv_go<1, FP8, EPI, KVFP8>(q, s);
-      else if (q.Bp <= 2) e = gemv_go<2, FP8, EPI, KVFP8>(q, s);
-      else if (q.Bp <= 4) e = gemv_go<4, FP8, EPI, KVFP8>(q, s);
-      else e = gemv_go<8, FP8, EPI, KVFP8>(q, s);
+      if (q.Bp <= 1) e = gemv_go<1, WQ, EPI, KVFP8>(q, s);
+      else if (q.Bp <= 2) e = gemv_go<2, WQ, EPI, KVFP8>(q, s);
+      else if (q.Bp <= 4) e = gemv_go<4, WQ, EPI, KVFP8>(q, s);
+      else e = gemv_go<8, WQ, EPI, KVFP8>(q, s);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
   }
-  return launch_gemm_mfma(p, EPI, FP8, KVFP8, s);
+  return launch_gemm_mfma(p, EPI, (WFmt)WQ, KVFP8, s);
 }
 
-template <bool FP8, bool KVFP8>
+template <int WQ, bool KVFP8>
 hipError_t dispatch_epi(const MatmulParams& p, int epi, bool mfma, hipStream_t s) {
   switch (epi) {
-    case EPI_LOGITS: return dispatch_bt<FP8, EPI_LOGITS, KVFP8>(p, mfma, s);
-    case EPI_RESID: return dispatch_bt<FP8, EPI_RESID, KVFP8>(p, mfma, s);
-    case EPI_SILU: return dispatch_bt<FP8, EPI_SILU, KVFP8>(p, mfma, s);
-    default: return dispatch_bt<FP8, EPI_QKV, KVFP8>(p, mfma, s);
+    case EPI_LOGITS: return dispatch_bt<WQ, EPI_LOGITS, KVFP8>(p, mfma, s);
+    case EPI_RESID: return dispatch_bt<WQ, EPI_RESID, KVFP8>(p, mfma, s);
+    case EPI_SILU: return dispatch_bt<WQ, EPI_SILU, KVFP8>(p, mfma, s);
+    default: return dispatch_bt<WQ, EPI_QKV, KVFP8>(p, mfma, s);
   }
+}
+
+template <int WQ>
+hipError_t dispatch_kv(const MatmulParams& p, int epi, bool kv_fp8, bool mfma, hipStream_t s) {
+  return kv_fp8 ? dispatch_epi<WQ, true>(p, epi, mfma, s) : dispatch_epi<WQ, false>(p, epi, mfma, s);
 }
 
 }  // namespace
 
-hipError_t launch_matmul(const MatmulParams& p, int epi, bool w_fp8, bool kv_fp8, bool mfma, hipStream_t s) {
+hipError_t launch_matmul(const MatmulParams& p, int epi, WFmt wq, bool kv_fp8, bool mfma, hipStream_t s) {
   // the cache dtype only matters for the QKV epilogue; keep one instance otherwise
   if (epi != EPI_QKV) kv_fp8 = false;
-  if (w_fp8) return kv_fp8 ? dispatch_epi<true, true>(p, epi, mfma, s) : dispatch_epi<true, false>(p, epi, mfma, s);
-  return kv_fp8 ? dispatch_epi<false, true>(p, epi, mfma, s) : dispatch_epi<false, false>(p, epi, mfma, s);
+  switch (wq) {
+    case W_E4M3: return dispatch_kv<W_E4M3>(p, epi, kv_fp8, mfma, s);
+    case W_I8: return dispatch_kv<W_I8>(p, epi, kv_fp8, mfma, s);
+    default: return dispatch_kv<W_BF16>(p, epi, kv_fp8, mfma, s);
+  }
 }
 
 }  // namespace dec

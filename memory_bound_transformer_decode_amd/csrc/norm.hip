@@ -12,7 +12,7 @@ namespace dec {
 // One work group of 256 threads per batch row.  Each thread keeps its NV float4 of the
 // row in registers, so the row is read once and the kernel costs one load round trip
 // plus a block reduction (NV * 1024 >= d; NV = 0 selects a two-pass loop for wider rows).
-template <bool EMBED, bool FP8, int NV>
+template <bool EMBED, int WQ, int NV>
 __global__ __launch_bounds__(256) void k_norm(NormParams p) {
   __shared__ float red[4];
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -21,14 +21,14 @@ __global__ __launch_bounds__(256) void k_norm(NormParams p) {
   float* hout = p.h_out ? p.h_out + (int64_t)b * d : nullptr;
   uint16_t* xrow = p.x + (int64_t)b * d;
   const int64_t id = EMBED ? (int64_t)p.ids[b] : 0;
-  const float e_scale = (EMBED && FP8) ? p.E_scale[id] : 1.f;
+  const float e_scale = (EMBED && WQ != W_BF16) ? p.E_scale[id] : 1.f;
   // 4 consecutive elements of the row starting at i (embedding rows are dequantized)
   auto load4 = [&](int i) -> f32x4 {
     if (!EMBED) return *reinterpret_cast<const f32x4*>(hrow + i);
     f32x4 v;
-    if (FP8) {
+    if constexpr (WQ != W_BF16) {
       const uint32_t c = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.E) + id * d + i);
-      const f32x2 lo = e4m3x2_to_f32x2<false>(c), hi = e4m3x2_to_f32x2<true>(c);
+      const f32x2 lo = b8x2_to_f32x2<WQ, false>(c), hi = b8x2_to_f32x2<WQ, true>(c);
       v = f32x4{lo.x * e_scale, lo.y * e_scale, hi.x * e_scale, hi.y * e_scale};
     } else {
       const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.E) + id * d + i);
@@ -72,23 +72,27 @@ __global__ __launch_bounds__(256) void k_norm(NormParams p) {
 }
 
 namespace {
-template <bool EMBED, bool FP8>
+template <bool EMBED, int WQ>
 hipError_t norm_go(const NormParams& p, hipStream_t s) {
   const int nv = (p.d + 1023) / 1024;
-  if (nv <= 1) hipLaunchKernelGGL((k_norm<EMBED, FP8, 1>), dim3(p.Bp), dim3(256), 0, s, p);
-  else if (nv <= 2) hipLaunchKernelGGL((k_norm<EMBED, FP8, 2>), dim3(p.Bp), dim3(256), 0, s, p);
-  else if (nv <= 4) hipLaunchKernelGGL((k_norm<EMBED, FP8, 4>), dim3(p.Bp), dim3(256), 0, s, p);
-  else if (nv <= 8) hipLaunchKernelGGL((k_norm<EMBED, FP8, 8>), dim3(p.Bp), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((k_norm<EMBED, FP8, 0>), dim3(p.Bp), dim3(256), 0, s, p);
+  if (nv <= 1) hipLaunchKernelGGL((k_norm<EMBED, WQ, 1>), dim3(p.Bp), dim3(256), 0, s, p);
+  else if (nv <= 2) hipLaunchKernelGGL((k_norm<EMBED, WQ, 2>), dim3(p.Bp), dim3(256), 0, s, p);
+  else if (nv <= 4) hipLaunchKernelGGL((k_norm<EMBED, WQ, 4>), dim3(p.Bp), dim3(256), 0, s, p);
+  else if (nv <= 8) hipLaunchKernelGGL((k_norm<EMBED, WQ, 8>), dim3(p.Bp), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((k_norm<EMBED, WQ, 0>), dim3(p.Bp), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_embed_norm(const NormParams& p, bool w_fp8, hipStream_t s) {
-  return w_fp8 ? norm_go<true, true>(p, s) : norm_go<true, false>(p, s);
+hipError_t launch_embed_norm(const NormParams& p, WFmt wq, hipStream_t s) {
+  switch (wq) {
+    case W_E4M3: return norm_go<true, W_E4M3>(p, s);
+    case W_I8: return norm_go<true, W_I8>(p, s);
+    default: return norm_go<true, W_BF16>(p, s);
+  }
 }
 
-hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s) { return norm_go<false, false>(p, s); }
+hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s) { return norm_go<false, W_BF16>(p, s); }
 
 // RoPE angles phi = p * theta^(-2i/dh) (RoFormer, adjacent pairs), in double precision
 __global__ void k_rope_table(float2* rope, int max_seq, int half, double theta) {

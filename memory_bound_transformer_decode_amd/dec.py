@@ -20,8 +20,9 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdec.so")
 
 DEC_OK, DEC_E_INVALID, DEC_E_STATE, DEC_E_CAPACITY, DEC_E_UNSUPPORTED, DEC_E_HIP = 0, -1, -2, -3, -4, -5
-DEC_BF16, DEC_FP8_E4M3 = 0, 1
-FLAG_EAGER, FLAG_UNFUSED, FLAG_NO_MFMA, FLAG_CAPTURE_ALL, FLAG_PERSISTENT, FLAG_FUSED_QKV_ATTN = 1, 2, 4, 8, 16, 32
+DEC_BF16, DEC_FP8_E4M3, DEC_INT8 = 0, 1, 2
+FLAG_EAGER, FLAG_UNFUSED, FLAG_NO_MFMA, FLAG_CAPTURE_ALL = 1, 2, 4, 8
+PATH_GRAPH, PATH_MFMA_PRODUCTS, PATH_MFMA_ATTENTION, PATH_FOLDED_NORM, PATH_UNFUSED = 1, 2, 4, 8, 16
 LADDER = (1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64)
 BLOCK = 16
 
@@ -49,10 +50,26 @@ class DecStepArgs(Structure):
                 ("seq_lens", POINTER(c_int32)), ("block_tables", POINTER(c_int32))]
 
 
+class DecVerifyArgs(Structure):
+    _fields_ = [("n_seqs", c_int32), ("k", c_int32), ("token_ids", POINTER(c_int32)),
+                ("seq_lens", POINTER(c_int32)), ("block_tables", POINTER(c_int32))]
+
+
+class DecPrefillArgs(Structure):
+    _fields_ = [("n_tokens", c_int32), ("token_ids", POINTER(c_int32)), ("start_pos", c_int32),
+                ("block_table", POINTER(c_int32))]
+
+
 class DecInfo(Structure):
     _fields_ = [("kernels_per_step", c_int32), ("bucket", c_int32), ("attn_splits", c_int32),
                 ("used_mfma", c_int32), ("used_graph", c_int32), ("graphs_captured", c_int32),
-                ("flags", c_uint32), ("persistent", c_int32)]
+                ("flags", c_uint32), ("rows", c_int32), ("launches", c_int32)]
+
+
+class DecAttnDesc(Structure):
+    _fields_ = [("n_rows", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32), ("d_head", c_int32),
+                ("kv_dtype", c_int32), ("n_layers", c_int32), ("layer", c_int32), ("num_blocks", c_int32),
+                ("max_blocks_per_seq", c_int32)]
 
 
 class DecError(RuntimeError):
@@ -61,9 +78,10 @@ class DecError(RuntimeError):
         self.code = code
 
 
-EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_load_weights", "dec_step", "dec_set_flags",
-           "dec_get_info", "dec_destroy", "dec_last_error", "dec_bw_probe", "dec_launch_matmul",
-           "dec_sample_greedy", "dec_sample")
+EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_load_weights", "dec_step", "dec_verify",
+           "dec_prefill", "dec_set_flags", "dec_get_info", "dec_get_step_info", "dec_destroy",
+           "dec_last_error", "dec_bw_probe", "dec_launch_matmul", "dec_sample_greedy", "dec_sample",
+           "dec_attention_workspace_bytes", "dec_attention")
 MAT_QKV, MAT_O, MAT_GATE_UP, MAT_DOWN, MAT_LM_HEAD = 0, 1, 2, 3, 4
 
 _lib = None
@@ -88,10 +106,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dec_load_weights.restype = c_int
     lib.dec_step.argtypes = [c_void_p, POINTER(DecStepArgs)]
     lib.dec_step.restype = c_int
+    lib.dec_verify.argtypes = [c_void_p, POINTER(DecVerifyArgs)]
+    lib.dec_verify.restype = c_int
+    lib.dec_prefill.argtypes = [c_void_p, POINTER(DecPrefillArgs), POINTER(c_int32)]
+    lib.dec_prefill.restype = c_int
     lib.dec_set_flags.argtypes = [c_void_p, c_uint32]
     lib.dec_set_flags.restype = c_int
-    lib.dec_get_info.argtypes = [c_void_p, POINTER(DecInfo)]
+    lib.dec_get_info.argtypes = [c_void_p, POINTER(c_int32), POINTER(c_int32)]
     lib.dec_get_info.restype = c_int
+    lib.dec_get_step_info.argtypes = [c_void_p, POINTER(DecInfo)]
+    lib.dec_get_step_info.restype = c_int
     lib.dec_destroy.argtypes = [c_void_p]
     lib.dec_destroy.restype = c_int
     lib.dec_last_error.argtypes = []
@@ -104,6 +128,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dec_sample.restype = c_int
     lib.dec_launch_matmul.argtypes = [c_void_p, c_int, c_int]
     lib.dec_launch_matmul.restype = c_int
+    lib.dec_attention_workspace_bytes.argtypes = [POINTER(DecAttnDesc)]
+    lib.dec_attention_workspace_bytes.restype = c_size_t
+    lib.dec_attention.argtypes = [POINTER(DecAttnDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_size_t, c_void_p]
+    lib.dec_attention.restype = c_int
     _lib = lib
     return lib
 
@@ -114,7 +143,7 @@ def _check(rc: int) -> None:
 
 
 def _dtype_code(name: str) -> int:
-    return {"bf16": DEC_BF16, "fp8": DEC_FP8_E4M3}[name]
+    return {"bf16": DEC_BF16, "fp8": DEC_FP8_E4M3, "int8": DEC_INT8}[name]
 
 
 def make_config(model, *, num_blocks: int, max_batch: int, max_seq_len: int, flags: int = 0) -> DecConfig:
@@ -209,6 +238,38 @@ class Decoder:
         self._last_n = n
         return self.logits[:n]
 
+    def verify(self, token_ids, seq_lens: Sequence[int], block_tables) -> torch.Tensor:
+        """Enqueue the k-token verify step: token_ids [n][k], seq_lens [n] (position of
+        each sequence's first token), block_tables [n][bps].  Returns the [n, k, vocab]
+        fp32 logits view (row (s, j): after token j of sequence s)."""
+        ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+        lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        if ids.ndim != 2:
+            raise ValueError("token_ids must be [n][k]")
+        n, k = ids.shape
+        if lens.shape != (n,) or bt.shape != (n, self.bps):
+            raise ValueError(f"expected seq_lens [{n}] and block_tables [{n}][{self.bps}]")
+        P = POINTER(c_int32)
+        args = DecVerifyArgs(n, k, ids.ctypes.data_as(P), lens.ctypes.data_as(P), bt.ctypes.data_as(P))
+        _check(self.lib.dec_verify(self.ctx, ctypes.byref(args)))
+        self._last_n = n * k
+        return self.logits[: n * k].view(n, k, -1)
+
+    def prefill(self, token_ids: Sequence[int], start_pos: int, block_table) -> torch.Tensor:
+        """Enqueue chunked prefill of one prompt at positions start_pos, start_pos + 1, ...;
+        returns the [vocab] fp32 logits view after the prompt's last token."""
+        ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        if ids.ndim != 1 or bt.shape != (self.bps,):
+            raise ValueError(f"expected token_ids [n] and block_table [{self.bps}]")
+        P = POINTER(c_int32)
+        row = c_int32(-1)
+        args = DecPrefillArgs(ids.shape[0], ids.ctypes.data_as(P), int(start_pos), bt.ctypes.data_as(P))
+        _check(self.lib.dec_prefill(self.ctx, ctypes.byref(args), ctypes.byref(row)))
+        self._last_n = row.value + 1
+        return self.logits[row.value]
+
     def sample_greedy(self) -> torch.Tensor:
         """Enqueue greedy sampling of the last step: int32 [n] token ids on the device."""
         n = self._last_n
@@ -234,8 +295,14 @@ class Decoder:
 
     def info(self) -> DecInfo:
         out = DecInfo()
-        _check(self.lib.dec_get_info(self.ctx, ctypes.byref(out)))
+        _check(self.lib.dec_get_step_info(self.ctx, ctypes.byref(out)))
         return out
+
+    def path(self):
+        """(kernels per plan, PATH_* bits) of the last call (dec_get_info)."""
+        k, f = c_int32(), c_int32()
+        _check(self.lib.dec_get_info(self.ctx, ctypes.byref(k), ctypes.byref(f)))
+        return k.value, f.value
 
     def close(self) -> None:
         if getattr(self, "ctx", None):
@@ -248,6 +315,38 @@ class Decoder:
             self.close()
         except Exception:
             pass
+
+
+def attn_desc(q: torch.Tensor, pool: torch.Tensor, layer: int, block_tables: torch.Tensor) -> DecAttnDesc:
+    """Descriptor of an attention call from q [n][Hq][dh] fp32, the pool
+    [L][2][num_blocks][Hkv][16][dh] and block tables [n][max_blocks_per_seq]."""
+    n, Hq, dh = q.shape
+    L, _, nb, Hkv, _, dh2 = pool.shape
+    if dh2 != dh:
+        raise ValueError("q and pool disagree on d_head")
+    kv = DEC_BF16 if pool.dtype == torch.bfloat16 else DEC_FP8_E4M3
+    return DecAttnDesc(n, Hq, Hkv, dh, kv, L, layer, nb, block_tables.shape[1])
+
+
+def attention(q: torch.Tensor, pool: torch.Tensor, layer: int, seq_lens: torch.Tensor,
+              block_tables: torch.Tensor, out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dec_attention on the current stream: o [n][Hq * dh] bf16 (device tensors in)."""
+    lib = load_library()
+    desc = attn_desc(q, pool, layer, block_tables)
+    n = load_library().dec_attention_workspace_bytes(ctypes.byref(desc))
+    if n == 0:
+        _check(DEC_E_INVALID)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape[0], q.shape[1] * q.shape[2], dtype=torch.bfloat16, device=q.device)
+    _check(lib.dec_attention(ctypes.byref(desc), c_void_p(q.data_ptr()), c_void_p(pool.data_ptr()),
+                             c_void_p(seq_lens.data_ptr()), c_void_p(block_tables.data_ptr()),
+                             c_void_p(out.data_ptr()), c_void_p(workspace.data_ptr()),
+                             workspace.numel() * workspace.element_size(),
+                             c_void_p(torch.cuda.current_stream(q.device).cuda_stream)))
+    return out
 
 
 def bw_probe(buf: torch.Tensor, reps: int = 5) -> float:

@@ -18,7 +18,7 @@ them.
 * Step ledger D_step(B, S) ~ W + B S K + D_activation, F_step ~ 2 P B
   ("GPU Inference Internals", Batching Economics).
 * Launch tax, two forms: T_eager ~ T_compute + N tau, T_graph ~ T_compute +
-  tau ("CUDA graphs & kernel fusion", Direct answer and Code); and eager step
+  tau ("CUDA graphs & kernel fusion", Direct answer); and eager step
   = max(GPU work, launches x CPU cost per launch) ("Kernels, Fusion & CUDA
   Graphs", Fix 2: CUDA graphs).
 
@@ -145,13 +145,36 @@ def roofline_step_time(flops: float, hbm_bytes: float, peak_flops: float, bandwi
                link_bytes / link_bw if link_bytes else 0.0)
 
 
-def launch_tax_step_ms(weight_gib: float, n_kernels: int = 430, tau_us: float = 5.0,
-                       bw: float = 1e12):
-    """Additive launch-tax model: (compute, eager, graph, eager/graph) in ms."""
-    compute = weight_gib * 1024 ** 3 / bw * 1e3
-    eager = compute + n_kernels * tau_us / 1e3
-    graph = compute + tau_us / 1e3
-    return compute, eager, graph, eager / graph
+@dataclass(frozen=True)
+class LaunchTax:
+    """Seconds per step: the GPU work alone, with one launch per kernel, with one graph launch."""
+
+    compute_s: float
+    eager_s: float
+    graph_s: float
+
+    @property
+    def graph_gain(self) -> float:
+        return self.eager_s / self.graph_s
+
+    @property
+    def tax_share(self) -> float:
+        """Launch overhead of the eager step relative to the GPU work."""
+        return (self.eager_s - self.compute_s) / self.compute_s
+
+
+def launch_tax(compute_s: float, kernels: int, per_launch_s: float) -> LaunchTax:
+    """The additive launch-tax model ("CUDA graphs & kernel fusion", Direct answer): a
+    step launched kernel by kernel costs its GPU work plus one launch cost per kernel;
+    replayed as one graph it costs the GPU work plus a single launch."""
+    return LaunchTax(compute_s, compute_s + kernels * per_launch_s, compute_s + per_launch_s)
+
+
+def weight_streaming_launch_tax(weight_bytes: float, bandwidth: float, kernels: int,
+                                per_launch_s: float) -> LaunchTax:
+    """launch_tax for a step whose GPU work is one read of the weights at `bandwidth`
+    (the memory term of roofline_step_time, no compute term)."""
+    return launch_tax(roofline_step_time(0.0, weight_bytes, float("inf"), bandwidth), kernels, per_launch_s)
 
 
 def overlapped_eager_step_s(weight_bytes: float, flops: float, bw: float, peak_flops: float,

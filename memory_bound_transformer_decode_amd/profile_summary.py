@@ -18,9 +18,9 @@ known size (the same counters; they give the bytes-per-reported-unit factors)::
         --fetch DIR1 --write DIR2 --copy-fetch DIR3 --copy-write DIR4 --copy-bytes N \
         --kernel SUBSTRING --commands "<...>" > profiles/<kernel>_<workload>_traffic.txt
 
-The traffic file ends with ``source_sha256`` of the kernel's sources, which bench.py
-compares with the tree it runs from: counters taken on another version of the kernel
-are not reported.
+The traffic file ends with ``source_sha256`` of the kernel family's sources (``--family``
+gemv, gemm or attn), which bench.py compares with the tree it runs from: counters taken
+on another version of the kernel are not reported.
 """
 
 from __future__ import annotations
@@ -33,14 +33,18 @@ import os
 import sys
 from typing import Dict, List
 
-# sources of the matrix-vector kernels (the benchmark's dominant kernel)
-KERNEL_SOURCES = ("csrc/matmul.hip", "csrc/gemv_norm.h", "csrc/epilogue.h", "csrc/common.h", "csrc/kernels.h")
+# sources of each kernel family whose traffic is summarized
+KERNEL_SOURCES = {
+    "gemv": ("csrc/matmul.hip", "csrc/gemv_norm.h", "csrc/epilogue.h", "csrc/common.h", "csrc/kernels.h"),
+    "gemm": ("csrc/gemm_mfma.hip", "csrc/epilogue.h", "csrc/common.h", "csrc/kernels.h"),
+    "attn": ("csrc/attention.hip", "csrc/attn_unit.h", "csrc/common.h", "csrc/kernels.h"),
+}
 
 
-def kernel_source_sha256() -> str:
+def kernel_source_sha256(family: str = "gemv") -> str:
     here = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(here, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -128,6 +132,7 @@ def traffic(args) -> None:
     print("# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
     print(f"# commands: {args.commands}")
     print(f"kernel: {args.kernel}")
+    print(f"family: {args.family}")
     print(f"dispatches: {len(f)} (fetch), {len(w)} (write)")
     print(f"fetch_kib_per_dispatch: {sum(f) / len(f):.1f}")
     print(f"write_kib_per_dispatch: {sum(w) / len(w):.1f}")
@@ -139,7 +144,7 @@ def traffic(args) -> None:
     print(f"fetch_bytes_per_dispatch: {fetch:.0f}")
     print(f"write_bytes_per_dispatch: {write:.0f}")
     print(f"traffic_bytes_per_dispatch: {fetch + write:.0f}")
-    print(f"source_sha256: {kernel_source_sha256()}")
+    print(f"source_sha256: {kernel_source_sha256(args.family)}")
 
 
 def read_traffic(path: str) -> Dict[str, str]:
@@ -170,6 +175,7 @@ def main(argv=None) -> int:
         t.add_argument(name, required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--copy-kernel", default="copyBuffer")
+    t.add_argument("--family", choices=sorted(KERNEL_SOURCES), default="gemv")
     args = ap.parse_args(argv)
     {"stats": stats, "counters": counters, "traffic": traffic}[args.cmd](args)
     return 0

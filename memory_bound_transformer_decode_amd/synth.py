@@ -15,6 +15,9 @@ CPU oracle decode these bits themselves):
     is E4M3 as defined by Micikevicius et al., "FP8 Formats for Deep
     Learning" (cited by the kernel-fusion architecture study's reference
     list): bias 7, max 448, no infinities.
+  * int8 weights (weight-only INT8): N(0, 0.02) drawn in fp32, then per output
+    row s = max|w| / 127 (s = 1 for an all-zero row), code = round-half-even
+    (w / s) clamped to [-127, 127]; scales kept as fp32.
   * context K/V: N(0, 1) rounded to the cache dtype.
   * block tables: a seeded random permutation of the pool's block ids.
 
@@ -54,7 +57,7 @@ class ModelConfig:
     vocab: int
     rms_eps: float = 1e-5
     rope_theta: float = 1e4
-    weight_dtype: str = "bf16"  # "bf16" | "fp8"
+    weight_dtype: str = "bf16"  # "bf16" | "fp8" | "int8"
     kv_dtype: str = "bf16"  # "bf16" | "fp8"
     block_size: int = BLOCK
 
@@ -102,7 +105,11 @@ M70B = ModelConfig("70B", 4, n_layers=80, d_model=8192, n_q_heads=64, n_kv_heads
                    d_head=128, d_ff=28672, vocab=128256,
                    weight_dtype="fp8", kv_dtype="fp8")
 
-MODELS: Dict[str, ModelConfig] = {m.name: m for m in (TINY, M1B, M8B, M32B, M70B)}
+# The 8B shape with weight-only INT8 (per-row scales) and a bf16 cache: the second
+# one-byte weight format through the same dequantizing kernels.
+M8B_I8 = dataclasses.replace(M8B, name="8B-int8", config_id=5, weight_dtype="int8")
+
+MODELS: Dict[str, ModelConfig] = {m.name: m for m in (TINY, M1B, M8B, M32B, M70B, M8B_I8)}
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload(TINY, (1,), 32, 32, 8,
@@ -115,6 +122,8 @@ WORKLOADS: Dict[str, Workload] = {
                     "32B-class decoder, fp8 weights and KV, prompts U[64,256], 40 decode steps"),
     "70B": Workload(M70B, (1, 64), 2048, 2048, 40,
                     "70B-class decoder, fp8 weights and KV, context 2048, 40 decode steps"),
+    "8B-int8": Workload(M8B_I8, (1, 8, 32), 256, 1024, 40,
+                        "8B-class decoder, int8 weights, bf16 KV, context U[256,1024], 40 decode steps"),
 }
 
 
@@ -152,19 +161,31 @@ def quantize_rows_fp8(w32: torch.Tensor):
     return q, s.to(torch.float32)
 
 
+def quantize_rows_int8(w32: torch.Tensor):
+    """Per-output-row absmax scaling to symmetric int8: returns (int8 codes, fp32 scales)."""
+    amax = w32.abs().amax(dim=1)
+    s = torch.where(amax > 0, amax / torch.full_like(amax, 127.0), torch.ones_like(amax))
+    q = torch.round(w32 / s[:, None]).clamp_(-127.0, 127.0).to(torch.int8)
+    return q, s.to(torch.float32)
+
+
+_FMT_OF_DTYPE = {torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8", torch.int8: "int8"}
+_DTYPE_OF_FMT = {v: k for k, v in _FMT_OF_DTYPE.items()}
+
+
 @dataclass
 class StoredMatrix:
     """A weight matrix [rows][cols] in its storage format (row = output channel)."""
 
-    w: torch.Tensor  # torch.bfloat16 or torch.float8_e4m3fn, contiguous
-    scale: Optional[torch.Tensor]  # fp32 [rows] for fp8, None for bf16
+    w: torch.Tensor  # torch.bfloat16, torch.float8_e4m3fn or torch.int8, contiguous
+    scale: Optional[torch.Tensor]  # fp32 [rows] for fp8 / int8, None for bf16
 
     @property
     def fmt(self) -> str:
-        return "fp8" if self.w.dtype == torch.float8_e4m3fn else "bf16"
+        return _FMT_OF_DTYPE[self.w.dtype]
 
     def codes_numpy(self, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
-        """Raw storage bits of rows [r0, r1) as uint16 (bf16) or uint8 (fp8), on the host."""
+        """Raw storage bits of rows [r0, r1) as uint16 (bf16) or uint8 (fp8, int8), on the host."""
         part = self.w[r0:r1]
         if self.fmt == "bf16":
             return part.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -178,11 +199,9 @@ class StoredMatrix:
 
 def _draw_matrix(rows: int, cols: int, fmt: str, gen: torch.Generator,
                  device, std: float = 0.02, chunk_rows: int = 8192) -> StoredMatrix:
-    """N(0, std) in fp32, stored as bf16 or fp8+per-row scale, drawn in row chunks."""
-    if fmt == "bf16":
-        out = torch.empty(rows, cols, dtype=torch.bfloat16, device=device)
-    else:
-        out = torch.empty(rows, cols, dtype=torch.float8_e4m3fn, device=device)
+    """N(0, std) in fp32, stored as bf16 or fp8 / int8 + per-row scale, drawn in row chunks."""
+    out = torch.empty(rows, cols, dtype=_DTYPE_OF_FMT[fmt], device=device)
+    if fmt != "bf16":
         scale = torch.empty(rows, dtype=torch.float32, device=device)
     for r0 in range(0, rows, chunk_rows):
         r1 = min(rows, r0 + chunk_rows)
@@ -191,7 +210,7 @@ def _draw_matrix(rows: int, cols: int, fmt: str, gen: torch.Generator,
         if fmt == "bf16":
             out[r0:r1] = w32.to(torch.bfloat16)
         else:
-            q, s = quantize_rows_fp8(w32)
+            q, s = quantize_rows_fp8(w32) if fmt == "fp8" else quantize_rows_int8(w32)
             out[r0:r1] = q
             scale[r0:r1] = s
         del w32

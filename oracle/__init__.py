@@ -14,12 +14,15 @@ The pages this follows state that fusion, FlashAttention and CUDA graphs
 change how the mathematics executes, not what it computes (kernel-fusion
 architecture study, section 11 "Kernel-fusion strategy" and Figure 4), so the
 plain definition is the reference; FP8 storage is the one change to *what* is
-computed, and the oracle therefore takes the already-quantized model as the
-model's definition.
+computed (as is INT8 weight-only storage), and the oracle therefore takes the
+already-quantized model as the model's definition.
 
 Modules:
-  codecs   -- bf16 and FP8-E4M3 decode/encode from the bit definitions
-  decoder  -- the fp64 decode step over a paged KV cache, plus the MAC ledger
+  codecs   -- bf16, FP8-E4M3 and int8 decode/encode from the bit definitions
+  decoder  -- the fp64 decode step over a paged KV cache, the multi-token step
+              (verify, prefill) as its causal generalisation, plus the MAC ledger
+  sampling -- the top-k / top-p rule after the LM head
+  inputs   -- adapters from the seeded inputs to the oracle's objects
 
 Every function is pinned by the `-m "not gpu"` tests against closed forms,
 worked examples printed on the pages, invariants and brute force; the one

@@ -13,6 +13,10 @@ Learning" (reference list of the kernel-fusion architecture study): 1 sign,
 subnormals m * 2^-9; the all-ones pattern S.1111.111 is NaN; there are no
 infinities, so the largest finite magnitude is 1.75 * 2^8 = 448.  Encoding
 rounds to nearest-even and saturates finite values to +-448 (never NaN).
+
+int8: two's complement, bit 7 the sign: a byte b >= 128 stands for b - 256.
+The weight-only INT8 format of the stored models (per-row scale, symmetric
+codes -127..127) is a scale times this integer.
 """
 
 from __future__ import annotations
@@ -111,6 +115,29 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return code
 
 
+# ------------------------------------------------------------------ int8
+
+def int8_decode(codes: np.ndarray) -> np.ndarray:
+    """uint8 bytes -> float64 two's-complement integers (exact)."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(b >= 128, b - 256, b).astype(np.float64)
+
+
+def int8_quantize_rows(w32: np.ndarray):
+    """Per-row absmax scaling to symmetric int8, as the stored int8 models are built:
+    s = max|w|/127 (1 for an all-zero row) in binary32, q = round-half-even(fl32(w / s))
+    clamped to [-127, 127].  Returns (codes as uint8 bytes, s).
+
+    Used only to check that the stored int8 models are what their recipe says."""
+    w32 = np.asarray(w32, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=1)
+    s = np.where(amax > 0, (amax.astype(np.float64) / 127.0).astype(np.float32),
+                 np.float32(1.0)).astype(np.float32)
+    ratio = (w32.astype(np.float64) / s[:, None].astype(np.float64)).astype(np.float32)
+    q = np.clip(np.rint(ratio.astype(np.float64)), -127, 127).astype(np.int64)
+    return (q & 0xFF).astype(np.uint8), s
+
+
 # ------------------------------------------------------------------ dispatch
 
 def decode(codes: np.ndarray, fmt: str) -> np.ndarray:
@@ -118,6 +145,8 @@ def decode(codes: np.ndarray, fmt: str) -> np.ndarray:
         return bf16_decode(codes)
     if fmt == "fp8":
         return e4m3_decode(codes)
+    if fmt == "int8":
+        return int8_decode(codes)
     if fmt == "f64":
         return np.asarray(codes, dtype=np.float64)
     raise ValueError(fmt)

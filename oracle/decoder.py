@@ -46,12 +46,27 @@ forward-pass value.
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Callable, List, Optional, Sequence
 
 import numpy as np
 
 from . import codecs
+
+# Host threads for the matrix products: row chunks of a product are independent, so
+# they are decoded and multiplied in parallel (each output row's sum is the same
+# computation whichever thread runs it).
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+_POOL: Optional[ThreadPoolExecutor] = None
+
+
+def _pool() -> ThreadPoolExecutor:
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(max_workers=_THREADS)
+    return _POOL
 
 
 # ---------------------------------------------------------------- building blocks
@@ -112,21 +127,23 @@ class Matrix:
 
     rows: int
     cols: int
-    fmt: str  # "bf16" | "fp8" | "f64"
+    fmt: str  # "bf16" | "fp8" | "int8" | "f64"
     codes: Optional[np.ndarray] = None
     scale: Optional[np.ndarray] = None  # float32 [rows] or None (implicit 1)
     fetch: Optional[Callable[[int, int], np.ndarray]] = None
-    chunk_rows: int = 4096
+    chunk_rows: int = 512
     _cache: Optional[np.ndarray] = field(default=None, repr=False)
+
+    def _codes(self, r0: int, r1: int) -> np.ndarray:
+        return self.codes[r0:r1] if self.codes is not None else self.fetch(r0, r1)
 
     def decoded(self, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
         """Rows [r0, r1) as float64 values, scale applied (exact: an E4M3 value has at
-        most 4 significant bits and the scale 24, well inside float64)."""
+        most 4 significant bits, an int8 value 7, and the scale 24, well inside float64)."""
         r1 = self.rows if r1 is None else r1
         if self._cache is not None:
             return self._cache[r0:r1]
-        codes = self.codes[r0:r1] if self.codes is not None else self.fetch(r0, r1)
-        w = codecs.decode(codes, self.fmt)
+        w = codecs.decode(self._codes(r0, r1), self.fmt)
         if self.scale is not None:
             w = w * self.scale[r0:r1].astype(np.float64)[:, None]
         return w
@@ -137,12 +154,25 @@ class Matrix:
         return self
 
     def matvec(self, X: np.ndarray, ledger: Optional["Ledger"] = None) -> np.ndarray:
-        """Y[b] = W X[b] for X [B][cols] -> Y [B][rows], decoding row chunks as it goes."""
+        """Y[b] = s (.) (C X[b]) for X [B][cols] -> Y [B][rows]: the stored values C
+        times X, each output row times its scale s (1 without scales) -- the per-row
+        scale written as the definition of the scaled format.  Row chunks are fetched,
+        decoded and multiplied independently (in parallel)."""
         X = np.asarray(X, dtype=np.float64)
         Y = np.empty((X.shape[0], self.rows), dtype=np.float64)
-        for r0 in range(0, self.rows, self.chunk_rows):
+        # a streamed matrix is fetched once per product, then decoded chunk by chunk
+        codes = self.codes if self.codes is not None or self._cache is not None else self.fetch(0, self.rows)
+
+        def chunk(r0: int) -> None:
             r1 = min(self.rows, r0 + self.chunk_rows)
-            Y[:, r0:r1] = X @ self.decoded(r0, r1).T
+            if self._cache is not None:
+                Y[:, r0:r1] = X @ self._cache[r0:r1].T
+                return
+            Y[:, r0:r1] = X @ codecs.decode(codes[r0:r1], self.fmt).T
+            if self.scale is not None:
+                Y[:, r0:r1] *= self.scale[r0:r1].astype(np.float64)[None, :]
+
+        list(_pool().map(chunk, range(0, self.rows, self.chunk_rows)))
         if ledger is not None:
             ledger.macs += X.shape[0] * self.rows * self.cols
         return Y
@@ -222,15 +252,19 @@ class PagedKVCache:
 def decode_step(m: Model, cache: PagedKVCache, token_ids: Sequence[int],
                 seq_lens: Sequence[int], block_tables: np.ndarray,
                 ledger: Optional[Ledger] = None, n_layers: Optional[int] = None,
-                lm_rows: Optional[Sequence[int]] = None) -> np.ndarray:
-    """One decode step for B live sequences; returns logits [B][V] (float64).
+                on_layer: Optional[Callable[[int], None]] = None) -> np.ndarray:
+    """One pass of the model over B rows; returns logits [B][V] (float64).
 
-    token_ids[b]: the new token of sequence b.  seq_lens[b]: tokens already in
-    the cache, which is also the 0-based position of the new token.
-    block_tables[b]: physical block ids of sequence b's logical blocks.
-    Writes the new token's K and V of every layer into `cache`.
+    Row b is token token_ids[b] at 0-based position seq_lens[b] (= tokens of its
+    sequence already cached) of the sequence whose block table is block_tables[b].
+    In a decode step every row is a different sequence.  Rows may also be several
+    tokens of one sequence at consecutive positions (the verify step, a prefill
+    chunk): in every layer the K and V of all rows are written first, then each row
+    attends to positions 0 .. p of its sequence, so a token sees itself and the
+    tokens before it and none after -- the causal mask, from the positions alone.
+    Writes every row's K and V of every layer into `cache`.
     n_layers: run only the first n layers (default: all).
-    lm_rows: compute only these vocabulary rows of the LM head (others are NaN).
+    on_layer: called with l after each layer (progress reports of long runs).
     """
     B = len(token_ids)
     L = m.n_layers if n_layers is None else n_layers
@@ -241,21 +275,25 @@ def decode_step(m: Model, cache: PagedKVCache, token_ids: Sequence[int],
     for l in range(L):
         x = rmsnorm(h, m.attn_norm[l], eps)
         qkv = m.qkv[l].matvec(x, ledger)
-        o = np.zeros((B, Hq, dh), dtype=np.float64)
+        qs = []
         for b in range(B):
             p = int(seq_lens[b])
             bt = block_tables[b]
-            q = rope(qkv[b, : Hq * dh].reshape(Hq, dh), p, theta)
+            qs.append(rope(qkv[b, : Hq * dh].reshape(Hq, dh), p, theta))
             k = rope(qkv[b, Hq * dh:(Hq + Hkv) * dh].reshape(Hkv, dh), p, theta)
             v = qkv[b, (Hq + Hkv) * dh:].reshape(Hkv, dh)
             for c in range(Hkv):
                 cache.write(l, 0, bt, p, c, k[c])
                 cache.write(l, 1, bt, p, c, v[c])
+        o = np.zeros((B, Hq, dh), dtype=np.float64)
+        for b in range(B):
+            p = int(seq_lens[b])
+            bt = block_tables[b]
             for c in range(Hkv):
                 Kc = cache.read(l, 0, bt, p + 1, c)
                 Vc = cache.read(l, 1, bt, p + 1, c)
                 for j in range(c * g, (c + 1) * g):
-                    o[b, j] = attend(q[j], Kc, Vc)
+                    o[b, j] = attend(qs[b][j], Kc, Vc)
             if ledger is not None:
                 ledger.attn_macs += 2 * Hq * dh * (p + 1)
         h = h + m.o[l].matvec(o.reshape(B, Hq * dh), ledger)
@@ -263,13 +301,37 @@ def decode_step(m: Model, cache: PagedKVCache, token_ids: Sequence[int],
         gu = m.gate_up[l].matvec(x, ledger)
         a = silu(gu[:, : m.d_ff]) * gu[:, m.d_ff:]
         h = h + m.down[l].matvec(a, ledger)
+        if on_layer is not None:
+            on_layer(l)
     xf = rmsnorm(h, m.final_norm, eps)
-    if lm_rows is None:
-        return m.lm_head.matvec(xf, ledger)
-    out = np.full((B, m.vocab), np.nan)
-    for r in lm_rows:
-        out[:, r] = xf @ m.lm_head.row(int(r))
-    return out
+    return m.lm_head.matvec(xf, ledger)
+
+
+def verify_step(m: Model, cache: PagedKVCache, tokens: np.ndarray, seq_lens: Sequence[int],
+                block_tables: np.ndarray) -> np.ndarray:
+    """The verification step of speculative decoding ("GPU Inference Internals",
+    Roofline: Why Decode Is Memory-Bound, speculative-decoding paragraph): k tokens
+    per sequence, tokens[s][j] at position seq_lens[s] + j, in one pass.  Returns
+    logits [n][k][V]: row (s, j) is the distribution after token j of sequence s."""
+    tokens = np.asarray(tokens)
+    n, k = tokens.shape
+    rows_ids = [int(tokens[s, j]) for s in range(n) for j in range(k)]
+    rows_pos = [int(seq_lens[s]) + j for s in range(n) for j in range(k)]
+    rows_bt = np.stack([block_tables[s] for s in range(n) for _ in range(k)])
+    z = decode_step(m, cache, rows_ids, rows_pos, rows_bt)
+    return z.reshape(n, k, -1)
+
+
+def prefill(m: Model, cache: PagedKVCache, tokens: Sequence[int], start_pos: int,
+            block_table: Sequence[int]) -> np.ndarray:
+    """Prefill of one sequence's prompt ("GPU Inference Internals", Roofline: Why
+    Decode Is Memory-Bound, the Prefill paragraph): every prompt token at positions
+    start_pos, start_pos + 1, ... in one causal pass, writing its K and V into the
+    cache.  Returns the logits after the last prompt token [V]."""
+    n = len(tokens)
+    bts = np.stack([np.asarray(block_table)] * n)
+    z = decode_step(m, cache, [int(t) for t in tokens], [start_pos + i for i in range(n)], bts)
+    return z[-1]
 
 
 def kv_bytes_per_token(n_layers: int, n_kv_heads: int, d_head: int, bytes_per_elem: int) -> int:

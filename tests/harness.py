@@ -2,21 +2,21 @@
 oracle on the same seeded inputs, compare logits and KV-cache bits.
 
 Tolerances (relative to each row's oracle logit range R = max - min):
-  bf16 weights and cache: max |z_gpu - z_oracle| <= 2e-2 R; fp8 weights or fp8
-  cache: <= 6e-2 R.
+  bf16 or int8 weights with a bf16 cache: max |z_gpu - z_oracle| <= 2e-2 R; fp8
+  weights or fp8 cache: <= 6e-2 R.  (int8 storage is part of the model both sides
+  compute, so what differs is the same bf16 activation rounding as for bf16
+  weights; the fp8 bar is kept for an fp8 cache.)
 Greedy agreement: wherever the oracle's top-1 minus top-2 exceeds tol * R, the
 HIP path's argmax equals the oracle's.
 KV cache: placement is exact -- every slot the oracle never wrote still holds
 the canary and every slot it wrote holds a value.  A written element must be
-the oracle's code or an adjacent one, or lie within tol_l * max|v| of the
-oracle's value, v being the head vector it belongs to: the kernels form K and V
-from bf16 activations, so an element near zero can sit many codes away from
-the fp64 value while its absolute error stays at the activation-rounding level.
-tol_l = tol in layer 0 (K, V straight from the embedding: one rounding of the
-normalized input) and 3 tol in deeper layers, where the activation rounding of
-every earlier layer has accumulated (measured on the 1B shape: 0.6% of the
-vector absmax in layer 0 growing to 1.8% in layer 15; the logits stay below
-0.8% of their range).
+the oracle's code or an adjacent one, or lie within tol * max|v| of the
+oracle's value, v being the head vector it belongs to, at every depth.  The
+kernels form K and V from bf16 activations, so an element near zero can sit
+many codes away from the fp64 value while its absolute error stays at the
+activation-rounding level; the bar is the logits' own (the same relative
+error, measured against the vector's largest element instead of the row's
+range).  The worst error per layer is logged.
 """
 
 from __future__ import annotations
@@ -35,11 +35,12 @@ from memory_bound_transformer_decode_amd import synth
 from oracle import decoder as OD
 from oracle import inputs as OI
 
-TOL = {"bf16": 2e-2, "fp8": 6e-2}
+TOL = {"bf16": 2e-2, "int8": 2e-2, "fp8": 6e-2}
 
 
 def tol_of(cfg: synth.ModelConfig) -> float:
-    """The bf16 bar for an all-bf16 model, the fp8 bar as soon as weights or cache are fp8."""
+    """The bf16 bar for bf16 / int8 weights and a bf16 cache, the fp8 bar as soon as
+    weights or cache are fp8."""
     return max(TOL[cfg.weight_dtype], TOL[cfg.kv_dtype])
 
 
@@ -98,6 +99,9 @@ class Report:
     argmax_checked: int = 0
     argmax_mismatch: int = 0
     kv_neighbour: int = 0  # written elements that differ from the oracle's code
+    kv_worst: float = 0.0  # largest |dv| / max|v| over written elements
+    kv_worst_layer: int = -1
+    kv_by_layer: dict = field(default_factory=dict)  # layer -> largest |dv| / max|v|
     rows: int = 0
     errs: List[float] = field(default_factory=list)
 
@@ -137,15 +141,28 @@ def compare_kv(pool_gpu: torch.Tensor, ocache: OD.PagedKVCache, fmt: str, rep: R
     ov = codecs.decode(o[vec], fmt)
     gap = np.abs(ordered(g[vec], fmt) - ordered(o[vec], fmt))
     scale = np.max(np.abs(ov), axis=-1, keepdims=True)
-    layer = np.argwhere(vec)[:, 0][:, None]
-    tol_l = np.where(layer == 0, tol, 3 * tol)
-    ok = (gap <= 1) | (np.abs(gv - ov) <= tol_l * scale)
+    rel = np.abs(gv - ov) / scale
+    layer = np.argwhere(vec)[:, 0]
+    worst = rel.max(axis=-1)
+    for l in np.unique(layer):
+        wl = float(worst[layer == l].max())
+        rep.kv_by_layer[int(l)] = max(wl, rep.kv_by_layer.get(int(l), 0.0))
+        if wl > rep.kv_worst:
+            rep.kv_worst, rep.kv_worst_layer = wl, int(l)
+    ok = (gap <= 1) | (rel <= tol)
     if not ok.all():
         where = np.argwhere(vec)[np.argwhere(~ok)[0][0]].tolist()
-        worst = float(np.max(np.abs(gv - ov) / scale))
-        raise AssertionError(f"KV values differ beyond tolerance (worst {worst:.3e} of the vector "
-                             f"absmax) e.g. at {where}")
+        bad_rel = float(np.max(np.where(ok, 0.0, rel)))
+        raise AssertionError(f"KV values differ beyond tolerance ({bad_rel:.3e} of the vector "
+                             f"absmax, more than one code away) e.g. at {where}")
     rep.kv_neighbour += int(diff.sum())
+
+
+def progress(cfg: synth.ModelConfig, step: int):
+    """A per-layer progress line every 8 layers for deep models (long oracle runs)."""
+    if cfg.n_layers < 16:
+        return None
+    return lambda l: log(f"{cfg.name} step {step}: oracle layer {l + 1}/{cfg.n_layers}") if (l + 1) % 8 == 0 else None
 
 
 def run_parity(case: Case, batch_ids: np.ndarray, *, flags: int = 0, max_batch: Optional[int] = None,
@@ -165,7 +182,10 @@ def run_parity(case: Case, batch_ids: np.ndarray, *, flags: int = 0, max_batch: 
     rep = Report()
     for t in range(steps):
         z = d.step(batch_ids[t], lens, case.block_tables).double().cpu().numpy()
-        zo = OD.decode_step(om, oc, batch_ids[t], lens, case.block_tables)
+        t0 = time.time()
+        zo = OD.decode_step(om, oc, batch_ids[t], lens, case.block_tables, on_layer=progress(cfg, t))
+        if cfg.n_layers >= 8:
+            log(f"{cfg.name} step {t}: oracle {time.time() - t0:.1f}s")
         assert np.all(np.isfinite(z)), f"non-finite logits at step {t}"
         compare_logits(z, zo, tol, rep, t)
         if cfg.n_layers > 0 and (kv_every_step or t == steps - 1):
@@ -173,10 +193,14 @@ def run_parity(case: Case, batch_ids: np.ndarray, *, flags: int = 0, max_batch: 
         lens = lens + 1
     info = d.info()
     d.close()
-    log(f"{cfg.name} B={B} steps={steps} flags={flags} persistent={info.persistent} "
+    log(f"{cfg.name} B={B} steps={steps} flags={flags} "
         f"mfma={info.used_mfma}: max rel err {rep.max_rel_err:.3e} "
         f"(tol {tol}), argmax {rep.argmax_checked - rep.argmax_mismatch}/{rep.argmax_checked}, "
-        f"kv elements off the oracle's code {rep.kv_neighbour}")
+        f"kv elements off the oracle's code {rep.kv_neighbour}, worst kv |dv|/absmax "
+        f"{rep.kv_worst:.3e} (layer {rep.kv_worst_layer})")
+    if len(rep.kv_by_layer) > 2:
+        log(f"{cfg.name} worst kv |dv|/absmax by layer: " +
+            " ".join(f"{l}:{v:.2e}" for l, v in sorted(rep.kv_by_layer.items())))
     return rep
 
 

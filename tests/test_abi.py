@@ -66,6 +66,9 @@ def test_workspace_bytes_valid_and_invalid():
     ("vocab", 1001, -1, b"vocab"),
     ("weight_dtype", 7, -1, b"dtype"),
     ("flags", 1 << 9, -1, b"flag"),
+    ("flags", 16, -1, b"flag"),
+    ("kv_dtype", 2, -1, b"dtype"),
+    ("max_seq_len", 524289, -4, b"max_seq_len"),
     ("rms_eps", 0.0, -1, b"rms_eps"),
     ("num_blocks", 0, -1, b"num_blocks"),
 ])
@@ -104,7 +107,10 @@ def test_null_context_calls():
     lib = dec.load_library()
     assert lib.dec_step(None, None) == dec.DEC_E_INVALID
     assert lib.dec_load_weights(None, None) == dec.DEC_E_INVALID
-    assert lib.dec_get_info(None, None) == dec.DEC_E_INVALID
+    assert lib.dec_get_info(None, None, None) == dec.DEC_E_INVALID
+    assert lib.dec_get_step_info(None, None) == dec.DEC_E_INVALID
+    assert lib.dec_verify(None, None) == dec.DEC_E_INVALID
+    assert lib.dec_prefill(None, None, None) == dec.DEC_E_INVALID
     assert lib.dec_set_flags(None, 0) == dec.DEC_E_INVALID
     assert lib.dec_sample_greedy(None, None) == dec.DEC_E_INVALID
     assert lib.dec_destroy(None) == dec.DEC_OK
@@ -121,6 +127,14 @@ def test_unknown_flag_bits_rejected():
                         ctypes.c_void_p(16), ctypes.byref(ctx))
     assert rc == dec.DEC_E_INVALID
     assert b"flag" in lib.dec_last_error()
+
+
+def test_int8_weights_accepted_by_the_workspace_query():
+    from memory_bound_transformer_decode_amd import dec
+    lib = dec.load_library()
+    c = _cfg()
+    c.weight_dtype = dec.DEC_INT8
+    assert lib.dec_workspace_bytes(ctypes.byref(c)) > 0
 
 
 def test_unfused_flag_accepted_by_the_workspace_query():

@@ -24,8 +24,7 @@ MINI = synth.ModelConfig("mini", 7, n_layers=2, d_model=320, n_q_heads=10, n_kv_
                          d_head=64, d_ff=1040, vocab=1000)
 MINI128 = synth.ModelConfig("mini128", 8, n_layers=2, d_model=256, n_q_heads=8, n_kv_heads=1,
                             d_head=128, d_ff=512, vocab=512)
-# g = 4 query heads per KV head: with FLAG_FUSED_QKV_ATTN, the matrix-vector path runs
-# QKV and attention as one kernel
+# g = 4 query heads per KV head
 MINI4 = synth.ModelConfig("mini4", 9, n_layers=2, d_model=320, n_q_heads=8, n_kv_heads=2,
                           d_head=64, d_ff=1040, vocab=1000)
 MINI4_128 = synth.ModelConfig("mini4x128", 10, n_layers=2, d_model=256, n_q_heads=8, n_kv_heads=2,
@@ -33,7 +32,7 @@ MINI4_128 = synth.ModelConfig("mini4x128", 10, n_layers=2, d_model=256, n_q_head
 
 
 LADDER = (1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64)
-FLAG_NO_MFMA, FLAG_FUSED = 4, 32  # dec.FLAG_NO_MFMA, dec.FLAG_FUSED_QKV_ATTN
+FLAG_NO_MFMA = 4  # dec.FLAG_NO_MFMA
 
 
 def bucket(B):
@@ -42,28 +41,16 @@ def bucket(B):
 
 def uses_mfma(cfg, B, flags=0):
     """Whether the library runs the products on MFMA tiles: from the bucket of 8 rows
-    with bf16 weights, of 4 with E4M3 weights, unless FLAG_NO_MFMA."""
-    return not flags & FLAG_NO_MFMA and bucket(B) >= (4 if cfg.weight_dtype == "fp8" else 8)
-
-
-def fused_qkv_attn(cfg, B, flags=0):
-    """Whether the library runs QKV and attention as one kernel for this batch (the
-    matrix-vector path of buckets <= 8, g <= 4)."""
-    return (bool(flags & FLAG_FUSED) and not uses_mfma(cfg, B, flags) and bucket(B) <= 8
-            and cfg.n_q_heads // cfg.n_kv_heads <= 4 and cfg.d_head % 16 == 0)
+    with bf16 weights, of 4 with one-byte weights, unless FLAG_NO_MFMA."""
+    return not flags & FLAG_NO_MFMA and bucket(B) >= (8 if cfg.weight_dtype == "bf16" else 4)
 
 
 def kernels_per_step(cfg, B, flags=0):
-    """Kernels of one step: per layer QKV, attention, O, gate+up, down, plus two RMSNorm
-    kernels unless the matrix-vector kernels normalize their own input or the MFMA
-    products fold the norms (d_model <= 8192); embedding and LM head."""
-    if uses_mfma(cfg, B, flags):
-        per_layer = 5 if cfg.d_model <= 8192 else 7
-    elif bucket(B) <= 8:
-        per_layer = 4 if fused_qkv_attn(cfg, B, flags) else 5
-    else:
-        per_layer = 7
-    return per_layer * cfg.n_layers + 2
+    """Kernels of one step: per layer QKV, attention, O, gate+up, down (the matrix-vector
+    kernels normalize their own input, the MFMA products fold the norms); embedding and
+    LM head."""
+    assert uses_mfma(cfg, B, flags) or bucket(B) <= 8
+    return 5 * cfg.n_layers + 2
 
 
 def fmt(cfg, w, kv):
@@ -118,15 +105,64 @@ def test_mini_model(dec, w, kv, B):
     assert_ok(run_parity(case, ids), cfg)
 
 
+@pytest.mark.parametrize("flags", [0, FLAG_NO_MFMA])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("B", [1, 5, 16])
-def test_mini_dh128_group8(dec, kv, B):
+def test_mini_dh128_group8(dec, kv, B, flags):
+    """d_head 128 with 8 query heads per KV head, on the MFMA path and (FLAG_NO_MFMA) on
+    the matrix-vector kernels and the vector attention (the wide-group branch that holds
+    one block per wave)."""
     cfg = fmt(MINI128, "bf16" if kv == "bf16" else "fp8", kv)
     rng = np.random.default_rng(10 + B)
     case = make_case(cfg, ctx_mix(B, rng, hi=200), 256, seed=3, gains="random")
     ids = synth.make_token_ids(cfg, 3, B, seed=3)
-    log(f"mini128 {kv} B={B}")
+    log(f"mini128 {kv} B={B} flags={flags}")
+    assert_ok(run_parity(case, ids, flags=flags), cfg)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_vector_attention_long_context_group8(dec, kv):
+    """The vector attention (FLAG_NO_MFMA) at g = 8, d_head 128 with contexts long
+    enough for several splits per KV head (the last arrival combines them)."""
+    cfg = fmt(MINI128, "bf16" if kv == "bf16" else "fp8", kv)
+    lens = [1500, 37, 999]
+    case = make_case(cfg, lens, 1600, seed=24, gains="random")
+    ids = synth.make_token_ids(cfg, 2, 3, seed=24)
+    log(f"mini128 {kv} long contexts, vector attention")
+    assert_ok(run_parity(case, ids, flags=FLAG_NO_MFMA), cfg)
+
+
+# ------------------------------------------------------------------ weight-only INT8
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("B", [1, 2, 3, 8, 13, 64])
+def test_mini_model_int8_weights(dec, kv, B):
+    """int8 weights with per-row scales: the matrix-vector kernels below 4 rows, the MFMA
+    tiles from 4 (one-byte weights), the embedding dequantized by the first kernel."""
+    cfg = fmt(MINI, "int8", kv)
+    rng = np.random.default_rng(140 + B)
+    case = make_case(cfg, ctx_mix(B, rng), 128, seed=25, gains="random")
+    ids = synth.make_token_ids(cfg, 3, B, seed=25)
+    log(f"mini int8/{kv} B={B}")
     assert_ok(run_parity(case, ids), cfg)
+
+
+@pytest.mark.parametrize("B", [1, 3, 16])
+def test_zero_layer_int8(dec, B):
+    cfg = fmt(MINI, "int8", "bf16").with_layers(0)
+    case = make_case(cfg, [0] * B, 16, seed=26, gains="random")
+    ids = synth.make_token_ids(cfg, 1, B, seed=26)
+    assert_ok(run_parity(case, ids), cfg)
+
+
+@pytest.mark.parametrize("B", [1, 5])
+def test_int8_unfused_and_no_mfma(dec, B):
+    cfg = fmt(MINI, "int8", "bf16")
+    rng = np.random.default_rng(150 + B)
+    case = make_case(cfg, ctx_mix(B, rng), 128, seed=27, gains="random")
+    ids = synth.make_token_ids(cfg, 2, B, seed=27)
+    assert_ok(run_parity(case, ids, flags=dec.FLAG_UNFUSED), cfg)
+    assert_ok(run_parity(case, ids, flags=FLAG_NO_MFMA), cfg)
 
 
 def test_decode_from_empty_cache(dec):
@@ -153,108 +189,41 @@ def _one_step(dec, case, ids, lens, flags, max_batch=None):
     return z, pool, info
 
 
-@pytest.mark.parametrize("B,persist", [(5, False), (5, True), (24, False)])
-def test_graph_replay_equals_eager_bitwise(dec, B, persist):
+@pytest.mark.parametrize("B", [5, 24])
+def test_graph_replay_equals_eager_bitwise(dec, B):
     cfg = fmt(MINI, "bf16", "bf16")
     rng = np.random.default_rng(20)
     case = make_case(cfg, ctx_mix(B, rng), 128, seed=5)
     ids = synth.make_token_ids(cfg, 1, B, seed=5)[0]
-    base = dec.FLAG_PERSISTENT if persist else 0
-    ze, pe, ie = _one_step(dec, case, ids, case.ctx_lens, base | dec.FLAG_EAGER)
-    zg, pg, ig = _one_step(dec, case, ids, case.ctx_lens, base)
+    ze, pe, ie = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_EAGER)
+    zg, pg, ig = _one_step(dec, case, ids, case.ctx_lens, 0)
     assert ie.used_graph == 0 and ig.used_graph == 1
     assert torch.equal(ze.view(torch.int32), zg.view(torch.int32))
     assert torch.equal(pe.view(torch.uint8), pg.view(torch.uint8))
-    persistent = B <= 8 and persist
-    assert ie.persistent == ig.persistent == int(persistent)
-    # per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the
-    # matrix-vector kernels (buckets below the MFMA threshold) normalize their own input
-    expect = 1 if persistent else kernels_per_step(cfg, B)
-    assert ie.kernels_per_step == ig.kernels_per_step == expect
+    assert ie.kernels_per_step == ig.kernels_per_step == kernels_per_step(cfg, B)
 
 
-@pytest.mark.parametrize("w,kv", [("bf16", "bf16"), ("fp8", "fp8")])
-@pytest.mark.parametrize("B", [1, 3, 8])
-def test_mini_model_persistent_plan(dec, w, kv, B):
-    """The persistent one-kernel step at small batches (opt-in)."""
-    cfg = fmt(MINI, w, kv)
-    rng = np.random.default_rng(50 + B)
-    case = make_case(cfg, ctx_mix(B, rng), 128, seed=12, gains="random")
-    ids = synth.make_token_ids(cfg, 3, B, seed=12)
-    log(f"mini persistent {w}/{kv} B={B}")
-    assert_ok(run_parity(case, ids, flags=dec.FLAG_PERSISTENT), cfg)
-
-
-@pytest.mark.parametrize("w,kv", [("bf16", "bf16"), ("fp8", "fp8"), ("bf16", "fp8")])
-@pytest.mark.parametrize("B", [1, 3, 8])
-def test_fused_qkv_attention(dec, w, kv, B):
-    """QKV projection and attention as one kernel (g = 4), against the oracle."""
-    cfg = fmt(MINI4, w, kv)
-    rng = np.random.default_rng(100 + B)
-    case = make_case(cfg, ctx_mix(B, rng), 128, seed=18, gains="random")
-    ids = synth.make_token_ids(cfg, 3, B, seed=18)
-    log(f"mini4 fused qkv+attention {w}/{kv} B={B}")
-    assert_ok(run_parity(case, ids, flags=dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_NO_MFMA), cfg)
-
-
-@pytest.mark.parametrize("cfg0", [MINI4, MINI4_128])
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
-@pytest.mark.parametrize("B", [1, 5, 8])
-def test_fused_qkv_attention_matches_separate(dec, cfg0, kv, B):
-    """One kernel or two for QKV + attention: the same arithmetic up to the order of the
-    RMSNorm sum (the two kernels give its work groups different widths), the same cache
-    slots; one kernel fewer per layer."""
-    cfg = fmt(cfg0, "bf16", kv)
-    rng = np.random.default_rng(110 + B)
-    # contexts long enough that the attention splits (several work groups per kv head
-    # wait, and the last one combines)
-    lens = [int(x) for x in rng.integers(0, 500, size=B)]
-    lens[0] = 499
-    case = make_case(cfg, lens, 512, seed=19, gains="random")
-    ids = synth.make_token_ids(cfg, 1, B, seed=19)[0]
-    log(f"{cfg.name} fused vs separate B={B}")
-    mv = dec.FLAG_NO_MFMA  # the matrix-vector path, where the fused kernel applies
-    zf, pf, inf_ = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_FUSED_QKV_ATTN | mv)
-    zs, ps, ins = _one_step(dec, case, ids, case.ctx_lens, mv)
-    assert inf_.kernels_per_step == kernels_per_step(cfg, B, dec.FLAG_FUSED_QKV_ATTN | mv) == 4 * cfg.n_layers + 2
-    assert ins.kernels_per_step == kernels_per_step(cfg, B, mv) == 5 * cfg.n_layers + 2
-    a, b = zf.double().cpu().numpy(), zs.double().cpu().numpy()
-    R = a.max(axis=1) - a.min(axis=1)
-    assert np.max(np.abs(a - b) / R[:, None]) < 5e-3
-    canary = synth.KV_CANARY_BF16 if kv == "bf16" else synth.KV_CANARY_FP8
-    assert np.array_equal(synth.kv_codes_numpy(pf) != canary, synth.kv_codes_numpy(ps) != canary)
-
-
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_fused_qkv_attention_several_blocks_per_wave(dec, kv):
-    """Long contexts at batch 8: each attention wave takes two or more KV blocks, so the
-    second pair of heads of a group re-reads the wave's first block."""
-    cfg = fmt(MINI4, "bf16", kv)
-    B = 8
-    rng = np.random.default_rng(120)
-    lens = [int(x) for x in rng.integers(2600, 4000, size=B)]
-    case = make_case(cfg, lens, 4096, seed=21)
-    ids = synth.make_token_ids(cfg, 2, B, seed=21)
-    log(f"{cfg.name} long contexts B={B}")
-    assert_ok(run_parity(case, ids, flags=dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_NO_MFMA), cfg)
-
-
-def test_fused_qkv_attention_repeated_steps(dec):
-    """The kernel's wait counters are cleared by the O projection after it: many launches
-    in a row (graph replays, every layer) keep giving the eager result."""
-    cfg = fmt(MINI4, "fp8", "fp8")
+def test_graph_replays_repeat_the_eager_result(dec):
+    """Many replays of one captured graph, with eager steps and synchronizations between
+    them, each give the eager step's bits (the split counters reset themselves)."""
+    cfg = fmt(MINI, "fp8", "fp8")
     B = 3
     case = make_case(cfg, [40, 7, 100], 128, seed=20)
     ids = synth.make_token_ids(cfg, 1, B, seed=20)[0]
     d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=4,
-                    max_seq_len=128, kv_pool=case.pool.clone(), flags=dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_NO_MFMA)
-    outs = [d.step(ids, case.ctx_lens, case.block_tables).clone() for _ in range(6)]
-    d.set_flags(dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_NO_MFMA | dec.FLAG_EAGER)
+                    max_seq_len=128, kv_pool=case.pool.clone())
+    outs = []
+    for _ in range(4):
+        outs.append(d.step(ids, case.ctx_lens, case.block_tables).clone())
+        torch.cuda.synchronize()
+    d.set_flags(dec.FLAG_EAGER)
     ref = d.step(ids, case.ctx_lens, case.block_tables).clone()
-    d.set_flags(dec.FLAG_FUSED_QKV_ATTN | dec.FLAG_NO_MFMA)
+    d.set_flags(0)
     outs.append(d.step(ids, case.ctx_lens, case.block_tables).clone())
     torch.cuda.synchronize()
+    k, f = d.path()
     d.close()
+    assert f & dec.PATH_GRAPH and k == kernels_per_step(cfg, B)
     for z in outs:
         assert torch.equal(z.view(torch.int32), ref.view(torch.int32))
 
@@ -396,7 +365,7 @@ def test_mini_model_unfused_plan(dec, w, kv, B):
 
 def test_unfused_step_matches_fused(dec):
     """Same step, fused and unfused: close results (summation and rounding order only),
-    the same cache slots, and 11 kernels per layer unfused."""
+    the same cache slots, and 13 kernels per layer unfused (attention as three)."""
     cfg = fmt(MINI, "bf16", "bf16")
     B = 5
     rng = np.random.default_rng(80)
@@ -404,7 +373,7 @@ def test_unfused_step_matches_fused(dec):
     ids = synth.make_token_ids(cfg, 1, B, seed=15)[0]
     zf, pf, inf_ = _one_step(dec, case, ids, case.ctx_lens, 0)
     zu, pu, inu = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_UNFUSED)
-    assert inu.kernels_per_step == 11 * cfg.n_layers + 2
+    assert inu.kernels_per_step == 13 * cfg.n_layers + 2
     a, b = zf.double().cpu().numpy(), zu.double().cpu().numpy()
     R = a.max(axis=1) - a.min(axis=1)
     assert np.max(np.abs(a - b) / R[:, None]) < 5e-3
@@ -412,24 +381,6 @@ def test_unfused_step_matches_fused(dec):
     gf = synth.kv_codes_numpy(pf) != canary
     gu = synth.kv_codes_numpy(pu) != canary
     assert np.array_equal(gf, gu)
-
-
-@pytest.mark.parametrize("B", [1, 2, 4, 8])
-def test_persistent_step_matches_multi_kernel(dec, B):
-    """Both plans of the same step agree closely (different summation orders only)."""
-    cfg = fmt(MINI, "bf16", "bf16")
-    rng = np.random.default_rng(60 + B)
-    case = make_case(cfg, ctx_mix(B, rng), 128, seed=13, gains="random")
-    ids = synth.make_token_ids(cfg, 1, B, seed=13)[0]
-    zp, pp, ip = _one_step(dec, case, ids, case.ctx_lens, dec.FLAG_PERSISTENT)
-    zm, pm, im = _one_step(dec, case, ids, case.ctx_lens, 0)
-    assert ip.persistent == 1 and im.persistent == 0
-    a, b = zp.double().cpu().numpy(), zm.double().cpu().numpy()
-    R = a.max(axis=1) - a.min(axis=1)
-    assert np.max(np.abs(a - b) / R[:, None]) < 5e-3
-    # same cache slots written
-    canary = synth.KV_CANARY_BF16
-    assert torch.equal(pp.view(torch.int16) == canary, pm.view(torch.int16) == canary)
 
 
 def test_repeated_steps_are_deterministic(dec):
@@ -517,7 +468,8 @@ def test_1b_workload_shapes(dec):
 
 @pytest.mark.parametrize("name,layers,B", [("8B", 2, 1), ("8B", 2, 8), ("8B", 1, 32),
                                            ("32B", 1, 1), ("32B", 1, 13), ("32B", 1, 64),
-                                           ("70B", 1, 1), ("70B", 1, 64)])
+                                           ("70B", 1, 1), ("70B", 1, 64),
+                                           ("8B-int8", 2, 1), ("8B-int8", 2, 2), ("8B-int8", 1, 32)])
 def test_large_workload_widths(dec, name, layers, B):
     """Full widths and vocabulary of the 8B / 32B / 70B workloads at truncated depth,
     at each workload's batch sizes and context mix, 2 decode steps."""
@@ -530,13 +482,3 @@ def test_large_workload_widths(dec, name, layers, B):
     assert_ok(run_parity(case, ids, stream_weights=True, kv_every_step=False), cfg)
 
 
-@pytest.mark.parametrize("name,B", [("8B", 1), ("70B", 1)])
-def test_large_workload_widths_persistent(dec, name, B):
-    """The persistent step at the same widths (the benchmark reports both plans)."""
-    wl = synth.WORKLOADS[name]
-    cfg = wl.model.with_layers(1)
-    lens = synth.make_context_lengths(wl, B, seed=0)
-    case = make_case(cfg, lens, wl.max_seq_len, seed=0)
-    ids = synth.make_token_ids(cfg, 2, B, seed=0)
-    assert_ok(run_parity(case, ids, flags=dec.FLAG_PERSISTENT, stream_weights=True,
-                         kv_every_step=False), cfg)

@@ -1,0 +1,233 @@
+"""Parity of the multi-token calls with the oracle (needs an MI355X): the k-token verify
+step of speculative decoding (dec_verify) and chunked prefill (dec_prefill).
+
+The oracle runs the same tokens through its causal multi-token step (every row's K/V
+written, then each row attends to positions 0..p of its sequence), which its CPU pins
+tie to a cache-free full causal recompute.  Bars as in harness.py: logits per row,
+greedy argmax, KV placement bit-exact and values within the bar.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from memory_bound_transformer_decode_amd import synth
+from oracle import decoder as OD
+from oracle import inputs as OI
+
+from harness import Report, assert_ok, compare_kv, compare_logits, log, make_case, require_gpu, tol_of
+
+pytestmark = pytest.mark.gpu
+
+MINI = synth.ModelConfig("mini", 7, n_layers=2, d_model=320, n_q_heads=10, n_kv_heads=2,
+                         d_head=64, d_ff=1040, vocab=1000)
+MINI128 = synth.ModelConfig("mini128", 8, n_layers=2, d_model=256, n_q_heads=8, n_kv_heads=1,
+                            d_head=128, d_ff=512, vocab=512)
+
+
+def fmt(cfg, w, kv):
+    return dataclasses.replace(cfg, weight_dtype=w, kv_dtype=kv, name=f"{cfg.name}-{w}-{kv}")
+
+
+@pytest.fixture(scope="module")
+def dec():
+    return require_gpu()
+
+
+# ------------------------------------------------------------------ verify
+
+def run_verify(dec, case, tokens, flags=0, max_batch=None, stream=False):
+    cfg = case.cfg
+    n, k = tokens.shape
+    tol = tol_of(cfg)
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks,
+                    max_batch=max_batch or dec.ladder_bucket(n * k), max_seq_len=case.max_seq_len,
+                    flags=flags, kv_pool=case.pool.clone())
+    z = d.verify(tokens, case.ctx_lens, case.block_tables).double().cpu().numpy()
+    info = d.info()
+    om = OI.model(case.weights, keep=not stream, stream=stream)
+    oc = OI.cache(cfg, synth.kv_codes_numpy(case.pool))
+    zo = OD.verify_step(om, oc, tokens, case.ctx_lens, case.block_tables)
+    rep = Report()
+    assert np.all(np.isfinite(z))
+    compare_logits(z.reshape(n * k, -1), zo.reshape(n * k, -1), tol, rep, 0)
+    compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol)
+    d.close()
+    log(f"verify {cfg.name} n={n} k={k} flags={flags}: max rel err {rep.max_rel_err:.3e}, "
+        f"argmax {rep.argmax_checked - rep.argmax_mismatch}/{rep.argmax_checked}, "
+        f"worst kv {rep.kv_worst:.3e}")
+    assert info.rows == n * k and info.launches == 1 and info.bucket == dec.ladder_bucket(n * k)
+    return rep
+
+
+@pytest.mark.parametrize("w,kv", [("bf16", "bf16"), ("fp8", "fp8"), ("int8", "bf16")])
+@pytest.mark.parametrize("n,k", [(1, 1), (1, 4), (3, 4), (5, 3), (2, 8), (8, 8)])
+def test_verify_mini(dec, w, kv, n, k):
+    cfg = fmt(MINI, w, kv)
+    rng = np.random.default_rng(200 + n * 10 + k)
+    lens = [int(x) for x in rng.integers(0, 120, size=n)]
+    lens[0] = 15  # the k tokens cross a block boundary
+    case = make_case(cfg, lens, 136, seed=30, gains="random")
+    tokens = synth.make_token_ids(cfg, k, n, seed=30).T.copy()  # [n][k]
+    assert_ok(run_verify(dec, case, tokens), cfg)
+
+
+@pytest.mark.parametrize("flags", [0, 4])
+def test_verify_group8_dh128(dec, flags):
+    cfg = fmt(MINI128, "bf16", "bf16")
+    case = make_case(cfg, [300, 5], 400, seed=31, gains="random")
+    tokens = synth.make_token_ids(cfg, 5, 2, seed=31).T.copy()
+    assert_ok(run_verify(dec, case, tokens, flags=flags), cfg)
+
+
+def test_verify_unfused(dec):
+    cfg = fmt(MINI, "bf16", "bf16")
+    case = make_case(cfg, [20, 60], 128, seed=32)
+    tokens = synth.make_token_ids(cfg, 4, 2, seed=32).T.copy()
+    assert_ok(run_verify(dec, case, tokens, flags=dec.FLAG_UNFUSED), cfg)
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_verify_8b_widths(dec, n):
+    """The 8B widths (2 layers), 8 proposed tokens per sequence."""
+    wl = synth.WORKLOADS["8B"]
+    cfg = wl.model.with_layers(2)
+    lens = synth.make_context_lengths(wl, n, seed=0)
+    case = make_case(cfg, lens, wl.max_seq_len, seed=0)
+    tokens = synth.make_token_ids(cfg, 8, n, seed=33).T.copy()
+    assert_ok(run_verify(dec, case, tokens, stream=True), cfg)
+
+
+def test_verify_k1_equals_step_bitwise(dec):
+    """A verify step of one token per sequence is the decode step: the same rows, the
+    same plan, the same bits."""
+    cfg = fmt(MINI, "bf16", "bf16")
+    case = make_case(cfg, [9, 40, 3], 128, seed=34)
+    ids = synth.make_token_ids(cfg, 1, 3, seed=34)[0]
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=4, max_seq_len=128,
+                    kv_pool=case.pool.clone())
+    zs = d.step(ids, case.ctx_lens, case.block_tables).clone()
+    torch.cuda.synchronize()
+    ps = d.kv_pool.clone()
+    d.kv_pool.copy_(case.pool)
+    zv = d.verify(ids[:, None], case.ctx_lens, case.block_tables).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(zs.view(torch.int32), zv[:, 0].view(torch.int32))
+    assert torch.equal(ps.view(torch.uint8), d.kv_pool.view(torch.uint8))
+    d.close()
+
+
+def test_verify_argument_errors(dec):
+    cfg = fmt(MINI, "bf16", "bf16")
+    case = make_case(cfg, [3, 5], 64, seed=35)
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=8, max_seq_len=64,
+                    kv_pool=case.pool.clone())
+    bt = case.block_tables
+    ok = np.ones((2, 4), np.int32)
+    for tokens, lens, code in [(np.ones((2, 9), np.int32), [3, 5], dec.DEC_E_INVALID),   # k > 8
+                               (np.ones((3, 4), np.int32)[:2], [3, 61], dec.DEC_E_CAPACITY),  # past max_seq_len
+                               (np.full((2, 4), cfg.vocab, np.int32), [3, 5], dec.DEC_E_INVALID)]:
+        with pytest.raises(dec.DecError) as e:
+            d.verify(tokens, lens, bt)
+        assert e.value.code == code
+    with pytest.raises(dec.DecError) as e:  # 3 x 4 rows > max_batch 8
+        d.verify(np.ones((3, 4), np.int32), [1, 2, 3], np.concatenate([bt, bt[:1]]))
+    assert e.value.code == dec.DEC_E_CAPACITY
+    z = d.verify(ok, [3, 5], bt)  # a rejected call has no side effects
+    torch.cuda.synchronize()
+    assert torch.isfinite(z).all()
+    d.close()
+
+
+# ------------------------------------------------------------------ prefill
+
+def run_prefill(dec, cfg, n_tokens, start, max_batch, max_seq_len, seed, stream=False, decode_after=2,
+                flags=0):
+    tol = tol_of(cfg)
+    case = make_case(cfg, [start], max_seq_len, seed=seed, gains="random" if cfg.n_layers <= 2 else "ones")
+    tokens = synth.make_token_ids(cfg, n_tokens, 1, seed=seed)[:, 0].copy()
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=max_batch,
+                    max_seq_len=max_seq_len, flags=flags, kv_pool=case.pool.clone())
+    z = d.prefill(tokens, start, case.block_tables[0]).double().cpu().numpy()
+    info = d.info()
+    om = OI.model(case.weights, keep=not stream, stream=stream)
+    oc = OI.cache(cfg, synth.kv_codes_numpy(case.pool))
+    zo = OD.prefill(om, oc, tokens, start, case.block_tables[0])
+    rep = Report()
+    assert np.all(np.isfinite(z))
+    compare_logits(z[None], zo[None], tol, rep, 0)
+    compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol)
+    chunks = -(-n_tokens // max_batch)
+    assert info.launches == chunks and info.rows == n_tokens
+    # decode on from the prefilled cache, both sides
+    p = start + n_tokens
+    after = synth.make_token_ids(cfg, decode_after, 1, seed=seed + 1)
+    for t in range(decode_after):
+        zd = d.step(after[t], [p + t], case.block_tables[:1]).double().cpu().numpy()
+        zdo = OD.decode_step(om, oc, after[t], [p + t], case.block_tables[:1])
+        compare_logits(zd, zdo, tol, rep, t + 1)
+    if decode_after:
+        compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol)
+    d.close()
+    log(f"prefill {cfg.name} n={n_tokens} start={start} chunk={max_batch} ({chunks} chunks): "
+        f"max rel err {rep.max_rel_err:.3e}, argmax {rep.argmax_checked - rep.argmax_mismatch}/"
+        f"{rep.argmax_checked}, worst kv {rep.kv_worst:.3e}")
+    return rep
+
+
+def test_prefill_tiny(dec):
+    cfg = synth.TINY
+    assert_ok(run_prefill(dec, cfg, 32, 0, 8, 48, seed=40), cfg)
+
+
+@pytest.mark.parametrize("w,kv,n,start,mb", [("bf16", "bf16", 50, 0, 16), ("fp8", "fp8", 70, 13, 64),
+                                             ("int8", "bf16", 40, 0, 8), ("bf16", "fp8", 33, 31, 32),
+                                             ("bf16", "bf16", 5, 100, 1)])
+def test_prefill_mini(dec, w, kv, n, start, mb):
+    """Ragged last chunks, prefill after an existing context, chunk of one token."""
+    cfg = fmt(MINI, w, kv)
+    assert_ok(run_prefill(dec, cfg, n, start, mb, 160, seed=41), cfg)
+
+
+def test_prefill_unfused_and_no_mfma(dec):
+    cfg = fmt(MINI128, "bf16", "bf16")
+    assert_ok(run_prefill(dec, cfg, 45, 0, 16, 64, seed=42, flags=dec.FLAG_UNFUSED), cfg)
+    assert_ok(run_prefill(dec, cfg, 45, 0, 16, 64, seed=42, flags=4), cfg)
+
+
+def test_prefill_1b(dec):
+    """The ~1B workload's 128-token prompt in two chunks of 64, then decode."""
+    wl = synth.WORKLOADS["1B"]
+    assert_ok(run_prefill(dec, wl.model, 128, 0, 64, wl.max_seq_len, seed=43), wl.model)
+
+
+@pytest.mark.parametrize("name,layers,n", [("8B", 2, 200), ("70B", 1, 130)])
+def test_prefill_large_widths(dec, name, layers, n):
+    wl = synth.WORKLOADS[name]
+    cfg = wl.model.with_layers(layers)
+    assert_ok(run_prefill(dec, cfg, n, 0, 64, n + 16, seed=44, stream=True), cfg)
+
+
+def test_prefill_argument_errors(dec):
+    cfg = fmt(MINI, "bf16", "bf16")
+    case = make_case(cfg, [0], 64, seed=45)
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=16, max_seq_len=64,
+                    kv_pool=case.pool.clone())
+    bt = case.block_tables[0]
+    with pytest.raises(dec.DecError) as e:
+        d.prefill(np.ones(60, np.int32), 10, bt)  # reaches position 69 >= 64
+    assert e.value.code == dec.DEC_E_CAPACITY
+    with pytest.raises(dec.DecError) as e:
+        d.prefill(np.zeros(0, np.int32), 0, bt)
+    assert e.value.code == dec.DEC_E_INVALID
+    bad = bt.copy()
+    bad[2] = case.num_blocks
+    with pytest.raises(dec.DecError) as e:
+        d.prefill(np.ones(40, np.int32), 0, bad)
+    assert e.value.code == dec.DEC_E_CAPACITY
+    z = d.prefill(np.ones(20, np.int32), 0, bt)
+    torch.cuda.synchronize()
+    assert torch.isfinite(z).all()
+    d.close()

@@ -122,3 +122,51 @@ def test_stored_matrix_decode_is_exact_product(fmt):
         v = codecs.e4m3_decode(q.view(torch.uint8).numpy()) * s.numpy().astype(np.float64)[:, None]
         ref = (q.to(torch.float64) * s.to(torch.float64)[:, None]).numpy()
         assert np.array_equal(v, ref)
+
+
+# ------------------------------------------------------------------ int8
+
+def test_int8_decode_twos_complement():
+    """Every byte from the two's-complement definition: 0x00 = 0, 0x7F = 127, 0x80 = -128,
+    0xFF = -1; agrees with numpy's own int8 view of the same bytes."""
+    b = np.arange(256, dtype=np.uint8)
+    v = codecs.int8_decode(b)
+    assert v[0] == 0 and v[0x7F] == 127 and v[0x80] == -128 and v[0xFF] == -1 and v[0x81] == -127
+    assert np.array_equal(v, b.view(np.int8).astype(np.float64))
+    assert codecs.decode(b, "int8").dtype == np.float64
+
+
+def test_int8_model_recipe_reproduced_by_oracle_encoder():
+    """The stored int8 models are exactly per-row absmax/127 + round-half-even codes in
+    [-127, 127]; the row's largest magnitude maps to +-127."""
+    g = torch.Generator().manual_seed(6)
+    w32 = torch.randn(64, 200, generator=g) * 0.02
+    w32[5] = 0.0
+    q, s = synth.quantize_rows_int8(w32)
+    codes, s_ref = codecs.int8_quantize_rows(w32.numpy())
+    assert np.array_equal(s.numpy(), s_ref)
+    assert s_ref[5] == 1.0
+    assert np.array_equal(q.view(torch.uint8).numpy(), codes)
+    qi = codecs.int8_decode(codes)
+    assert qi.min() >= -127 and qi.max() <= 127
+    amax_col = np.argmax(np.abs(w32.numpy()), axis=1)
+    for r in range(64):
+        if r != 5:
+            assert abs(qi[r, amax_col[r]]) == 127
+
+
+def test_int8_round_half_even_ties():
+    """Ties go to the even code: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -0.5 -> 0, -1.5 -> -2."""
+    w = np.array([[127.0, 0.5, 1.5, 2.5, -0.5, -1.5]], dtype=np.float32)  # scale exactly 1
+    codes, s = codecs.int8_quantize_rows(w)
+    assert s[0] == 1.0
+    assert codecs.int8_decode(codes).tolist() == [[127, 0, 2, 2, 0, -2]]
+
+
+def test_int8_stored_matrix_decode_is_exact_product():
+    g = torch.Generator().manual_seed(8)
+    w32 = torch.randn(16, 64, generator=g) * 0.02
+    q, s = synth.quantize_rows_int8(w32)
+    v = codecs.int8_decode(q.view(torch.uint8).numpy()) * s.numpy().astype(np.float64)[:, None]
+    ref = (q.to(torch.float64) * s.to(torch.float64)[:, None]).numpy()
+    assert np.array_equal(v, ref)

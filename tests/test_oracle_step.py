@@ -123,6 +123,52 @@ def test_cached_decode_equals_full_causal_recompute():
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
 
 
+def test_prefill_equals_full_causal_recompute_at_every_position():
+    """All prompt tokens in one causal pass (the prefill / verify definition) give the
+    brute-force logits of the last token, and the cache then serves a decode step."""
+    m = tiny_model(seed=9)
+    bt = [2, 0, 4]
+    cache = new_cache(m, 6)
+    last = D.prefill(m, cache, TOKENS[:7], 0, bt)
+    ref = brute_force_logits(m, TOKENS)
+    np.testing.assert_allclose(last, ref[6], rtol=0, atol=1e-11)
+    nxt = D.decode_step(m, cache, [TOKENS[7]], [7], np.array([bt]))[0]
+    np.testing.assert_allclose(nxt, ref[7], rtol=0, atol=1e-11)
+
+
+def test_verify_step_equals_full_causal_recompute():
+    """Two sequences, k = 3 proposed tokens after different contexts: every row's logits
+    equal the brute force at its position; the cache equals sequential decode's."""
+    m = tiny_model(seed=10)
+    bts = np.array([[1, 4, 6], [0, 2, 5]])
+    seqs = [TOKENS[:8], TOKENS[2:7]]
+    ctx = [5, 2]
+    cache_v, cache_s = new_cache(m, 7), new_cache(m, 7)
+    for b, seq in enumerate(seqs):
+        for p in range(ctx[b]):
+            for cache in (cache_v, cache_s):
+                D.decode_step(m, cache, [seq[p]], [p], bts[b:b + 1])
+    tokens = np.array([seqs[0][5:8], seqs[1][2:5]])
+    z = D.verify_step(m, cache_v, tokens, ctx, bts)
+    for b, seq in enumerate(seqs):
+        ref = brute_force_logits(m, seq)
+        for j in range(3):
+            np.testing.assert_allclose(z[b, j], ref[ctx[b] + j], rtol=0, atol=1e-11)
+            D.decode_step(m, cache_s, [seq[ctx[b] + j]], [ctx[b] + j], bts[b:b + 1])
+    np.testing.assert_allclose(cache_v.pool, cache_s.pool, rtol=0, atol=1e-12)
+
+
+def test_multi_token_rows_in_any_order():
+    """The rows of one pass may come in any order: K/V of every row are written before
+    any row attends, so the causal result does not depend on the row order."""
+    m = tiny_model(seed=11)
+    bt = np.array([[3, 1]])
+    a = D.decode_step(m, new_cache(m, 4), TOKENS[:6], list(range(6)), np.repeat(bt, 6, axis=0))
+    perm = [4, 0, 5, 2, 1, 3]
+    b = D.decode_step(m, new_cache(m, 4), [TOKENS[i] for i in perm], perm, np.repeat(bt, 6, axis=0))
+    np.testing.assert_allclose(b, a[perm], rtol=0, atol=1e-12)
+
+
 def test_batched_step_equals_single_sequence_steps():
     m = tiny_model(seed=1)
     bts = np.array([[1, 4], [0, 2], [5, 3]])

@@ -16,14 +16,27 @@ GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
                                    "pages_worked_examples.json")))
 
 
-def test_launch_tax_step_ms_printed_outputs():
+def _page_model(weight_gib, n_kernels=430, tau_us=5.0, bw=1e12):
+    return P.weight_streaming_launch_tax(weight_gib * 2 ** 30, bw, n_kernels, tau_us * 1e-6)
+
+
+def test_launch_tax_printed_outputs():
+    """The page's model at its printed inputs gives its printed figures (ms, 1 decimal;
+    the gain to 2 decimals)."""
     g = GOLD["launch_tax_step_ms"]
     for c in g["cases"]:
-        comp, eager, graph, spd = P.launch_tax_step_ms(c["weight_gib"], **g["params"])
-        assert f"{comp:4.1f}".strip() == f"{c['compute_ms']:.1f}"
-        assert f"{eager:4.1f}".strip() == f"{c['eager_ms']:.1f}"
-        assert f"{graph:4.1f}".strip() == f"{c['graph_ms']:.1f}"
-        assert f"{spd:.2f}" == f"{c['speedup']:.2f}"
+        t = _page_model(c["weight_gib"], **g["params"])
+        assert f"{1e3 * t.compute_s:.1f}" == f"{c['compute_ms']:.1f}"
+        assert f"{1e3 * t.eager_s:.1f}" == f"{c['eager_ms']:.1f}"
+        assert f"{1e3 * t.graph_s:.1f}" == f"{c['graph_ms']:.1f}"
+        assert f"{t.graph_gain:.2f}" == f"{c['speedup']:.2f}"
+
+
+def test_launch_tax_is_additive():
+    t = P.launch_tax(2e-3, 100, 4e-6)
+    assert t.eager_s == pytest.approx(2.4e-3) and t.graph_s == pytest.approx(2.004e-3)
+    assert t.tax_share == pytest.approx(0.2)
+    assert P.launch_tax(1.0, 0, 1e-6).eager_s == 1.0
 
 
 def test_launch_tax_direct_answer_and_share():
@@ -32,8 +45,8 @@ def test_launch_tax_direct_answer_and_share():
     assert tax_ms == pytest.approx(2.15)
     assert round(tax_ms) == g["approx_ms"]
     for c in GOLD["launch_share_quantized"]["cases"]:
-        comp, eager, graph, _ = P.launch_tax_step_ms(c["weight_gib"])
-        assert round(100 * (eager - comp) / comp) == c["share_pct"]  # share of the compute time
+        t = _page_model(c["weight_gib"])
+        assert round(100 * t.tax_share) == c["share_pct"]  # share of the compute time
 
 
 def test_machine_balance_h100():
