@@ -143,8 +143,9 @@ __device__ __forceinline__ f32x2 e4m3x2_to_f32x2(uint32_t w) {
 // instruction (a byte-select on the conversion's source), the pair packed by another.
 template <bool HI>
 __device__ __forceinline__ f32x2 i8x2_to_f32x2(uint32_t w) {
-  const uint32_t v = HI ? w >> 16 : w;
-  return f32x2{(float)(int8_t)v, (float)(int8_t)(v >> 8)};
+  // written so that each conversion selects its byte directly (no shifts)
+  if constexpr (HI) return f32x2{(float)(int8_t)(w >> 16), (float)((int32_t)w >> 24)};
+  else return f32x2{(float)(int8_t)w, (float)(int8_t)(w >> 8)};
 }
 template <bool HI>
 __device__ __forceinline__ bf16x2 i8x2_to_bf16x2(uint32_t w) {
@@ -189,6 +190,20 @@ __device__ __forceinline__ float dot4_b8(uint32_t w, uint32_t x01, uint32_t x23,
   acc = dot2_bf16v(b8x2_to_bf16x2<WQ, false>(w), x01, acc);
   acc = dot2_bf16v(b8x2_to_bf16x2<WQ, true>(w), x23, acc);
   return acc;
+}
+
+// 16 one-byte codes -> 16 bf16 (exact): elements 0..7 in a, 8..15 in b
+template <int WQ>
+__device__ __forceinline__ void widen16_b8(const u32x4& w, u32x4& a, u32x4& b) {
+  const uint32_t c[4] = {w.x, w.y, w.z, w.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __builtin_bit_cast(uint32_t, b8x2_to_bf16x2<WQ, false>(c[i]));
+    o[2 * i + 1] = __builtin_bit_cast(uint32_t, b8x2_to_bf16x2<WQ, true>(c[i]));
+  }
+  a = u32x4{o[0], o[1], o[2], o[3]};
+  b = u32x4{o[4], o[5], o[6], o[7]};
 }
 
 // 16 one-byte weights . 16 bf16 activations (xa: elements 0..7, xb: 8..15)

@@ -74,7 +74,7 @@ dec::AttnShape attn_shape(const dec_config& c) {
 
 struct Layout {
   size_t ids, lens, bt, static_bytes;  // static region: ids | lens | block tables
-  size_t h, x, q, part_o, part_ml, o, a, rope;
+  size_t h, x, xl, q, part_o, part_ml, o, a, rope;  // xl: the QKV input's second bf16 part
   size_t uf;                           // unfused step: fp32 product rows [MB][max(N)]
   size_t us;                           // unfused step: attention scores [MB][Hq][max_seq_len]
   size_t attn_cnt;                     // attention split arrival counters
@@ -100,6 +100,8 @@ Layout layout_of(const dec_config& c) {
   L.h = off;
   off = align256(off + MB * c.d_model * 4);
   L.x = off;
+  off = align256(off + MB * c.d_model * 2);
+  L.xl = off;
   off = align256(off + MB * c.d_model * 2);
   L.q = off;
   off = align256(off + MB * c.n_q_heads * c.d_head * 4);
@@ -270,12 +272,13 @@ dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) 
   uint16_t* x = ws_ptr<uint16_t>(c, c->L.x);
   float* h = ws_ptr<float>(c, c->L.h);
   switch (which) {
-    case DEC_MAT_QKV:  // [q; k; v] = W_qkv x, RoPE, K/V -> cache
+    case DEC_MAT_QKV:  // [q; k; v] = W_qkv (x + xl), RoPE, K/V -> cache
       p.W = c->qkv[l].w;
       p.scale = c->qkv[l].scale;
       p.N = (Hq + 2 * Hkv) * dh;
       p.K = d;
       p.x = x;
+      p.xl = ws_ptr<uint16_t>(c, c->L.xl);
       p.ldx = d;
       *epi = dec::EPI_QKV;
       break;
@@ -366,6 +369,8 @@ void set_fold_norm(dec_ctx* c, int which, int l, int Bp, dec::MatmulParams& p) {
   p.eps = g.rms_eps;
   if (which == DEC_MAT_O || which == DEC_MAT_DOWN) {
     p.xout = ws_ptr<uint16_t>(c, c->L.x);
+    // down before the next layer's QKV also writes the second part of its input
+    if (which == DEC_MAT_DOWN && l + 1 < g.n_layers) p.xout_lo = ws_ptr<uint16_t>(c, c->L.xl);
     p.ldxo = d;
     p.xg = which == DEC_MAT_O ? c->mlp_norm + (size_t)l * d
            : l + 1 < g.n_layers ? c->attn_norm + (size_t)(l + 1) * d : c->final_norm;
@@ -401,9 +406,9 @@ hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const
 }
 
 // Batches of <= 8 rows on the matrix-vector kernels normalize their own input in LDS
-// ([Bp][d] bf16 must fit in 128 KB)
+// ([Bp][d] bf16 in two parts for QKV must fit in 128 KB)
 bool fused_norm(const dec_config& g, int Bp) {
-  return !use_mfma(g, Bp) && Bp <= 8 && (size_t)Bp * g.d_model * 2 <= 128 * 1024;
+  return !use_mfma(g, Bp) && Bp <= 8 && (size_t)Bp * g.d_model * 4 <= 128 * 1024;
 }
 
 dec::AttnParams attn_params(dec_ctx* c, int Bp, int layer) {
@@ -452,6 +457,8 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   np.E_scale = c->embed.scale;
   np.ids = ws_ptr<int32_t>(c, c->L.ids);
   np.gain = g.n_layers > 0 ? c->attn_norm : c->final_norm;
+  uint16_t* xl = ws_ptr<uint16_t>(c, c->L.xl);
+  np.x_lo = g.n_layers > 0 ? xl : nullptr;  // layer 0's QKV input
   if ((e = dec::launch_embed_norm(np, wq, s)) != hipSuccess) return e;
   // the product of `which` with its rows written plainly to uf [Bp][N]
   auto plain = [&](int which, int l, dec::MatmulParams* keep) -> hipError_t {
@@ -465,6 +472,7 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   for (int l = 0; l < g.n_layers; ++l) {
     if (l > 0) {
       np.gain = c->attn_norm + (size_t)l * d;
+      np.x_lo = xl;
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
     dec::MatmulParams qp{};
@@ -476,6 +484,7 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
     if ((e = plain(DEC_MAT_O, l, nullptr)) != hipSuccess) return e;
     if ((e = dec::launch_add(h, uf, Bp * d, s)) != hipSuccess) return e;
     np.gain = c->mlp_norm + (size_t)l * d;
+    np.x_lo = nullptr;
     if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     if ((e = plain(DEC_MAT_GATE_UP, l, nullptr)) != hipSuccess) return e;
     if ((e = dec::launch_silu_mul(uf, g.d_ff, Bp, ws_ptr<uint16_t>(c, c->L.a), g.d_ff, s)) != hipSuccess) return e;
@@ -485,6 +494,7 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   if (skip_lm) return hipSuccess;
   if (g.n_layers > 0) {
     np.gain = c->final_norm;
+    np.x_lo = nullptr;
     if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
   }
   return run_matmul(c, DEC_MAT_LM_HEAD, 0, Bp, s);
@@ -513,6 +523,8 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   np.E_scale = c->embed.scale;
   np.ids = ws_ptr<int32_t>(c, c->L.ids);
   np.gain = g.n_layers > 0 ? c->attn_norm : c->final_norm;
+  uint16_t* xl = ws_ptr<uint16_t>(c, c->L.xl);
+  np.x_lo = g.n_layers > 0 ? xl : nullptr;  // layer 0's QKV input
   if ((e = dec::launch_embed_norm(np, wq, s)) != hipSuccess) return e;
 
   // no RMSNorm kernels: the matrix-vector kernels normalize their own input (fn), or the
@@ -523,6 +535,7 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
     const float* an = c->attn_norm + (size_t)l * d;
     if (l > 0 && nk) {
       np.gain = an;
+      np.x_lo = xl;
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
     if ((e = run_matmul(c, DEC_MAT_QKV, l, Bp, s, fn ? an : nullptr)) != hipSuccess) return e;
@@ -533,6 +546,7 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
     const float* mn = c->mlp_norm + (size_t)l * d;
     if (nk) {
       np.gain = mn;
+      np.x_lo = nullptr;
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
     if ((e = run_matmul(c, DEC_MAT_GATE_UP, l, Bp, s, fn ? mn : nullptr)) != hipSuccess) return e;
@@ -541,6 +555,7 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   if (skip_lm) return hipSuccess;
   if (g.n_layers > 0 && nk) {
     np.gain = c->final_norm;
+    np.x_lo = nullptr;
     if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
   }
   if ((e = run_matmul(c, DEC_MAT_LM_HEAD, 0, Bp, s, fn ? c->final_norm : nullptr)) != hipSuccess) return e;

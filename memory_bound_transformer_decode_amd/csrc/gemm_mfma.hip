@@ -47,8 +47,10 @@ constexpr int tile_bytes() { return B8 ? 256 : 16 * (64 / RPL_BF16); }  // of a 
 template <bool B8>
 constexpr int tile_row() { return tile_bytes<B8>() + 16; }  // LDS row of a wave's weight tile (padded)
 // x chunk buffers: two (the next chunk is staged while this one is read) up to 32 batch
-// columns; one beyond, where two would hold the LDS to one work group per CU
-constexpr int x_buffers(int NT) { return NT >= 3 ? 1 : 2; }
+// columns; one beyond, where two would hold the LDS to one work group per CU.  XLO: x
+// comes in two bf16 parts (the QKV input, see MatmulParams::xl), each with its buffers,
+// and one buffer from 32 columns.
+constexpr int x_buffers(int NT, bool XLO) { return (NT >= 3 || (XLO && NT >= 2)) ? 1 : 2; }
 // 16-row tiles per wave (measured on the 8B, 32B and 70B shapes at 48-64 rows): with
 // one-byte (E4M3) weights each x operand read from LDS (NT per k-step) costs the LDS more than the
 // weights do, so from 48 columns a wave takes two tiles that share those reads -- on
@@ -65,9 +67,11 @@ int tiles_per_wave(int NT, bool byte_weights, int n_rows_total, int K) {
 // D[4 (l / 16) + j][l % 16], j = 0..3.  Which k-values a lane group covers is free as long
 // as A and B agree: in k-step s of a group of GK k-values, lane group g takes the 8
 // k-values s 32 + 8 g + [0, 8).
-template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW>
+// XLO: the input is x + p.xl, two bf16 parts; every product is made with each part.
+template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW, bool XLO>
 __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n) {
-  extern __shared__ __align__(16) uint8_t lds[];  // x: [XBUFS][NT 16][XROW] bf16; tiles: [W][TPW][16][TROW]
+  // x: [XP][XBUFS][NT 16][XROW] bf16 (XP parts); tiles: [W][TPW][16][TROW]
+  extern __shared__ __align__(16) uint8_t lds[];
   constexpr bool B8 = WQ != W_BF16;  // one-byte weights (E4M3 or int8 codes)
   constexpr bool SILU = EPI == EPI_SILU;
   constexpr int RPL = B8 ? 4 : RPL_BF16;          // rows per weight load instruction
@@ -81,12 +85,13 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   constexpr int XSEG = KC / 8;                     // 16-byte pieces per staged x row
   constexpr int XL = (COLS * XSEG + W * WAVE - 1) / (W * WAVE);  // x staging loads per thread
   constexpr int XBUF = COLS * XROW;                // bf16 per x buffer
-  constexpr int XBUFS = x_buffers(NT);
+  constexpr int XBUFS = x_buffers(NT, XLO);
+  constexpr int XP = XLO ? 2 : 1;                  // parts of x
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int lane = tid % WAVE, m = lane % 16, kg = lane / 16;
-  uint8_t* tile = lds + (size_t)XBUFS * XBUF * 2 + (size_t)wave * TPW * 16 * tile_row<B8>();
+  uint8_t* tile = lds + (size_t)XP * XBUFS * XBUF * 2 + (size_t)wave * TPW * 16 * tile_row<B8>();
   // rows: output rows of the product (d_ff intermediate indices for gate+up); a tile
   // covers TR of them, a wave TPW tiles (TPW > 1: each x operand read from LDS feeds
   // TPW tiles' products)
@@ -129,23 +134,29 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
         for (int q = 0; q < NQ; ++q) wr[tt][gi][q] = ld_stream(reinterpret_cast<const u32x4*>(wp[tt][q] + off));
     }
   };
-  // x loads of chunk c into registers (rows past Bp read row Bp - 1; k past K is zero)
-  auto load_x = [&](int c, u32x4 (&xr)[XL]) {
+  // x loads of chunk c into registers, each part (rows past Bp read row Bp - 1; k past
+  // K is zero)
+  auto load_x = [&](int c, u32x4 (&xr)[XP][XL]) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j) {
-      const int i = tid + j * W * WAVE;
-      const int b = min(i / XSEG, p.Bp - 1), k = c * KC + (i % XSEG) * 8;
-      const u32x4 v = gld16(p.x + (int64_t)b * p.ldx + min(k, p.K - 8));
-      xr[j] = k < p.K ? v : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int part = 0; part < XP; ++part)
+#pragma unroll
+      for (int j = 0; j < XL; ++j) {
+        const int i = tid + j * W * WAVE;
+        const int b = min(i / XSEG, p.Bp - 1), k = c * KC + (i % XSEG) * 8;
+        const u32x4 v = gld16((part ? p.xl : p.x) + (int64_t)b * p.ldx + min(k, p.K - 8));
+        xr[part][j] = k < p.K ? v : u32x4{0u, 0u, 0u, 0u};
+      }
   };
-  auto store_x = [&](int buf, const u32x4 (&xr)[XL]) {
+  auto store_x = [&](int buf, const u32x4 (&xr)[XP][XL]) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j) {
-      const int i = tid + j * W * WAVE;
-      if (XL * W * WAVE == COLS * XSEG || i < COLS * XSEG)
-        *reinterpret_cast<u32x4*>(xs + buf * XBUF + (i / XSEG) * XROW + (i % XSEG) * 8) = xr[j];
-    }
+    for (int part = 0; part < XP; ++part)
+#pragma unroll
+      for (int j = 0; j < XL; ++j) {
+        const int i = tid + j * W * WAVE;
+        if (XL * W * WAVE == COLS * XSEG || i < COLS * XSEG)
+          *reinterpret_cast<u32x4*>(xs + (part * XBUFS + buf) * XBUF + (i / XSEG) * XROW + (i % XSEG) * 8) =
+              xr[part][j];
+      }
   };
 
   f32x4 acc[TPW][NT];
@@ -155,7 +166,6 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
     for (int t = 0; t < NT; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto mma_chunk = [&](int buf, const u32x4 (&wr)[TPW][NGRP][NQ]) {
-    const uint16_t* xb = xs + buf * XBUF;
 #pragma unroll
     for (int gi = 0; gi < NGRP; ++gi) {
       // this wave's TPW 16 x TB-byte tiles of the group, then each lane's operands from them
@@ -180,11 +190,15 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
           }
         }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const bf16x8 bv = __builtin_bit_cast(bf16x8, ld16(xb + (t * 16 + m) * XROW + gi * GK + s * 32 + kg * 8));
+        for (int part = 0; part < XP; ++part) {
+          const uint16_t* xb = xs + (part * XBUFS + buf) * XBUF;
 #pragma unroll
-          for (int tt = 0; tt < TPW; ++tt)
-            acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bv, acc[tt][t], 0, 0, 0);
+          for (int t = 0; t < NT; ++t) {
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, ld16(xb + (t * 16 + m) * XROW + gi * GK + s * 32 + kg * 8));
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+              acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bv, acc[tt][t], 0, 0, 0);
+          }
         }
       }
     }
@@ -249,7 +263,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   constexpr int SPER = (GEMM_SSQ_MAX + W - 1) / W;
   {
     constexpr int B1 = XBUFS == 2 ? 1 : 0;
-    u32x4 wa[TPW][NGRP][NQ], wb[TPW][NGRP][NQ], xr[XL];
+    u32x4 wa[TPW][NGRP][NQ], wb[TPW][NGRP][NQ], xr[XP][XL];
     const int scol = tid % GEMM_SSQ_STRIDE, spart = tid / GEMM_SSQ_STRIDE;
     float sv[SPER];
     if (p.ssq_n > 0) {
@@ -418,7 +432,10 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
             const float hn = (full[tt] ? e_h[tt][t][j] : gld(o + r)) + y;
             gst(o + r, hn);
             if (p.xout) {
-              gst(p.xout + (int64_t)col * p.ldxo + r, f32_to_bf16(hn * (full[tt] ? e_g[tt][j] : gld(p.xg + r))));
+              const float xv = hn * (full[tt] ? e_g[tt][j] : gld(p.xg + r));
+              const uint16_t xh = f32_to_bf16(xv);
+              gst(p.xout + (int64_t)col * p.ldxo + r, xh);
+              if (p.xout_lo) gst(p.xout_lo + (int64_t)col * p.ldxo + r, f32_to_bf16(xv - bf16_to_f32(xh)));
               sq[t] += hn * hn;
             }
           } else {
@@ -448,14 +465,14 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
 }
 
 template <bool B8>
-constexpr size_t lds_bytes(int NT, int W, int TPW) {
-  return (size_t)x_buffers(NT) * NT * 16 * XROW * 2 + (size_t)W * TPW * 16 * tile_row<B8>();
+constexpr size_t lds_bytes(int NT, int W, int TPW, bool XLO) {
+  return (size_t)(XLO ? 2 : 1) * x_buffers(NT, XLO) * NT * 16 * XROW * 2 + (size_t)W * TPW * 16 * tile_row<B8>();
 }
 
-template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW>
-hipError_t go_tpw(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
-  auto kern = k_gemm_lds<NT, WQ, EPI, KVFP8, W, TPW>;
-  constexpr size_t lds = lds_bytes<WQ != W_BF16>(NT, W, TPW);
+template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW, bool XLO>
+hipError_t go_tpwx(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
+  auto kern = k_gemm_lds<NT, WQ, EPI, KVFP8, W, TPW, XLO>;
+  constexpr size_t lds = lds_bytes<WQ != W_BF16>(NT, W, TPW, XLO);
   static_assert(lds <= 160 * 1024, "LDS of one work group");
   static bool attr = false;
   if (!attr && lds > 64 * 1024) {
@@ -466,6 +483,20 @@ hipError_t go_tpw(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
   }
   hipLaunchKernelGGL(kern, dim3(g.n_rb * g.ks), dim3(WAVE * W), lds, s, p, g.ks);
   return hipGetLastError();
+}
+
+// QKV always takes its input in two parts; a plain product (the unfused step's QKV)
+// does when given p.xl; the others never do
+template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW>
+hipError_t go_tpw(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
+  if constexpr (EPI == EPI_QKV) {
+    return go_tpwx<NT, WQ, EPI, KVFP8, W, TPW, true>(p, g, s);
+  } else if constexpr (EPI == EPI_LOGITS) {
+    return p.xl ? go_tpwx<NT, WQ, EPI, KVFP8, W, TPW, true>(p, g, s)
+                : go_tpwx<NT, WQ, EPI, KVFP8, W, TPW, false>(p, g, s);
+  } else {
+    return go_tpwx<NT, WQ, EPI, KVFP8, W, TPW, false>(p, g, s);
+  }
 }
 
 template <int NT, int WQ, int EPI, bool KVFP8, int W>

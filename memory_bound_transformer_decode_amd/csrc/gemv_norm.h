@@ -13,10 +13,12 @@ namespace dec {
 // weight loads are issued before the norm, so the norm runs under the weight stream.
 //
 // The work of work group `group`: ipw <= IPW_MAX waves, items group ipw .. group ipw +
-// ipw - 1; xs is LDS of BT K bf16.
+// ipw - 1; xs is LDS of BT K bf16, twice that for QKV, whose input is kept as two bf16
+// parts (x, then the remainder bf16(v - x) at xs + BT K: see MatmulParams::xl).
 template <int BT, int WQ, int EPI, bool KVFP8, int U, int IPW_MAX>
 __device__ __forceinline__ void gemv_norm_group(const MatmulParams& p, int n_items, int group, uint16_t* xs,
                                                 int ipw) {
+  constexpr bool XL = EPI == EPI_QKV;
   __shared__ float red[IPW_MAX][BT];
   constexpr int EPV = WQ != W_BF16 ? 16 : 8;
   const int NT = WAVE * ipw;
@@ -85,17 +87,28 @@ __device__ __forceinline__ void gemv_norm_group(const MatmulParams& p, int n_ite
     for (int u = 0; u < U; ++u) {
       const int kk = k0 + WAVE * u;
       if (kk < KV) {
+        // one-byte weights widened once to bf16 (elements 0..7, 8..15 of the vector)
+        u32x4 v0a, v0b, v1a, v1b;
+        if constexpr (WQ != W_BF16) {
+          widen16_b8<WQ>(w0[u], v0a, v0b);
+          widen16_b8<WQ>(w1[u], v1a, v1b);
+        } else {
+          v0a = w0[u];
+          v1a = w1[u];
+        }
 #pragma unroll
-        for (int b = 0; b < BT; ++b) {
-          const uint16_t* xb = xs + b * K + kk * EPV;
-          if constexpr (WQ != W_BF16) {
-            const u32x4 xa = *reinterpret_cast<const u32x4*>(xb), xc = *reinterpret_cast<const u32x4*>(xb + 8);
-            acc0[b] = dot16_b8<WQ>(w0[u], xa, xc, acc0[b]);
-            acc1[b] = dot16_b8<WQ>(w1[u], xa, xc, acc1[b]);
-          } else {
+        for (int part = 0; part < (XL ? 2 : 1); ++part) {
+#pragma unroll
+          for (int b = 0; b < BT; ++b) {
+            const uint16_t* xb = xs + (part * BT + b) * K + kk * EPV;
             const u32x4 xa = *reinterpret_cast<const u32x4*>(xb);
-            acc0[b] = dot8_bf16(w0[u], xa, acc0[b]);
-            acc1[b] = dot8_bf16(w1[u], xa, acc1[b]);
+            acc0[b] = dot8_bf16(v0a, xa, acc0[b]);
+            acc1[b] = dot8_bf16(v1a, xa, acc1[b]);
+            if constexpr (WQ != W_BF16) {
+              const u32x4 xc = *reinterpret_cast<const u32x4*>(xb + 8);
+              acc0[b] = dot8_bf16(v0b, xc, acc0[b]);
+              acc1[b] = dot8_bf16(v1b, xc, acc1[b]);
+            }
           }
         }
       }
@@ -119,9 +132,19 @@ __device__ __forceinline__ void gemv_norm_group(const MatmulParams& p, int n_ite
     r[b] = 1.0f / sqrtf(t / (float)K + p.eps);
   }
   auto put_x = [&](int i, int b, const f32x4& v, const f32x4& g) {
-    const uint32_t lo = (uint32_t)f32_to_bf16(v.x * r[b] * g.x) | ((uint32_t)f32_to_bf16(v.y * r[b] * g.y) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(v.z * r[b] * g.z) | ((uint32_t)f32_to_bf16(v.w * r[b] * g.w) << 16);
-    *reinterpret_cast<u32x2*>(xs + b * K + i) = u32x2{lo, hi};
+    const float y[4] = {v.x * r[b] * g.x, v.y * r[b] * g.y, v.z * r[b] * g.z, v.w * r[b] * g.w};
+    uint16_t hb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hb[j] = f32_to_bf16(y[j]);
+    *reinterpret_cast<u32x2*>(xs + b * K + i) =
+        u32x2{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+    if constexpr (XL) {
+      uint16_t lb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lb[j] = f32_to_bf16(y[j] - bf16_to_f32(hb[j]));
+      *reinterpret_cast<u32x2*>(xs + (BT + b) * K + i) =
+          u32x2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
+    }
   };
   if (held) {
 #pragma unroll

@@ -32,6 +32,12 @@ struct MatmulParams {
   int d_ff;              // EPI_SILU: up rows start at d_ff (N = 2 d_ff)
   const uint16_t* x;     // bf16 activations [Bp][ldx]
   int ldx;
+  // The QKV product takes its input as two bf16 parts, x + xl (xl = bf16(v - x) of the
+  // fp32 value v): q and k feed a softmax whose logits can be large, which turns a
+  // relative error of q or k into a larger one of the attention weights, so their
+  // input keeps about 16 significant bits instead of 8.  xl: [Bp][ldx], or the kernel
+  // forms both parts itself (norm-fused kernels).
+  const uint16_t* xl;
   int Bp;                // padded batch (bucket)
   float* out;            // EPI_LOGITS / EPI_RESID: [Bp][ldo]
   int ldo;
@@ -64,6 +70,7 @@ struct MatmulParams {
   // its sums for batch row b by 1 / sqrt(sum_{i < ssq_n} ssq_in[i GEMM_SSQ_STRIDE + b] / K
   // + eps).
   uint16_t* xout;
+  uint16_t* xout_lo;     // with xout: also bf16(h_new xg - xout) (the next product is QKV)
   int ldxo;
   const float* xg;
   float* ssq_out;
@@ -99,6 +106,7 @@ struct NormParams {
   float* h_out;         // embed: h written here
   const float* gain;    // [d]
   uint16_t* x;          // [Bp][d] bf16 out
+  uint16_t* x_lo;       // [Bp][d] bf16(x_fp32 - x) out, or nullptr (the next product is QKV)
   int d, Bp;
   float eps;
   // embedding

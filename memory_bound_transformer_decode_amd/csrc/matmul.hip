@@ -31,7 +31,8 @@ namespace dec {
 // Work group = one row pair (item blockIdx.x), S waves; wave w takes the contiguous
 // slice [KV w / S, KV (w + 1) / S) of the 16-byte vectors of both rows, with U loads
 // per row per lane in flight; the slices' sums are added in LDS in wave order.
-template <int BT, int WQ, int EPI, bool KVFP8, int U, int S>
+// XL: the input is x + p.xl (two bf16 parts, see MatmulParams::xl).
+template <int BT, int WQ, int EPI, bool KVFP8, int U, int S, bool XL>
 __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
   constexpr int EPV = WQ != W_BF16 ? 16 : 8;  // weight elements per 16-byte vector
   const int lane = threadIdx.x % WAVE;
@@ -64,17 +65,27 @@ __global__ __launch_bounds__(WAVE * S) void k_gemv(MatmulParams p) {
     for (int u = 0; u < U; ++u) {
       const int kk = k0 + WAVE * u;
       if (kk < ke) {
+        u32x4 v0a, v0b, v1a, v1b;  // the weights as bf16 (one-byte codes widened once)
+        if constexpr (WQ != W_BF16) {
+          widen16_b8<WQ>(w0[u], v0a, v0b);
+          widen16_b8<WQ>(w1[u], v1a, v1b);
+        } else {
+          v0a = w0[u];
+          v1a = w1[u];
+        }
 #pragma unroll
-        for (int b = 0; b < BT; ++b) {
-          const uint16_t* xb = p.x + (int64_t)b * p.ldx + (int64_t)kk * EPV;
-          if constexpr (WQ != W_BF16) {
-            const u32x4 xa = gld16(xb), xc = gld16(xb + 8);
-            acc0[b] = dot16_b8<WQ>(w0[u], xa, xc, acc0[b]);
-            acc1[b] = dot16_b8<WQ>(w1[u], xa, xc, acc1[b]);
-          } else {
+        for (int part = 0; part < (XL ? 2 : 1); ++part) {
+#pragma unroll
+          for (int b = 0; b < BT; ++b) {
+            const uint16_t* xb = (part ? p.xl : p.x) + (int64_t)b * p.ldx + (int64_t)kk * EPV;
             const u32x4 xa = gld16(xb);
-            acc0[b] = dot8_bf16(w0[u], xa, acc0[b]);
-            acc1[b] = dot8_bf16(w1[u], xa, acc1[b]);
+            acc0[b] = dot8_bf16(v0a, xa, acc0[b]);
+            acc1[b] = dot8_bf16(v1a, xa, acc1[b]);
+            if constexpr (WQ != W_BF16) {
+              const u32x4 xc = gld16(xb + 8);
+              acc0[b] = dot8_bf16(v0b, xc, acc0[b]);
+              acc1[b] = dot8_bf16(v1b, xc, acc1[b]);
+            }
           }
         }
       }
@@ -137,19 +148,33 @@ namespace {
 // a long static share at the end.  Rows longer than one pass of a wave (64 U vectors)
 // are split over S <= 8 waves of the work group (a wave takes more than one pass only
 // beyond 8 passes' worth).
-template <int BT, int WQ, int EPI, bool KVFP8, int U>
-hipError_t gemv_s(const MatmulParams& p, int n_items, int kv, hipStream_t s) {
+template <int BT, int WQ, int EPI, bool KVFP8, int U, bool XL>
+hipError_t gemv_sx(const MatmulParams& p, int n_items, int kv, hipStream_t s) {
   const int need = (kv + WAVE * U - 1) / (WAVE * U);
   const dim3 grid(n_items);
   if (need <= 1)
-    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 1>), grid, dim3(WAVE), 0, s, p);
+    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 1, XL>), grid, dim3(WAVE), 0, s, p);
   else if (need <= 2)
-    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 2>), grid, dim3(2 * WAVE), 0, s, p);
+    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 2, XL>), grid, dim3(2 * WAVE), 0, s, p);
   else if (need <= 4)
-    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 4>), grid, dim3(4 * WAVE), 0, s, p);
+    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 4, XL>), grid, dim3(4 * WAVE), 0, s, p);
   else
-    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 8>), grid, dim3(8 * WAVE), 0, s, p);
+    hipLaunchKernelGGL((k_gemv<BT, WQ, EPI, KVFP8, U, 8, XL>), grid, dim3(8 * WAVE), 0, s, p);
   return hipGetLastError();
+}
+
+// QKV always takes its input in two parts; a plain product (the unfused step's QKV)
+// does when given p.xl; the others never do
+template <int BT, int WQ, int EPI, bool KVFP8, int U>
+hipError_t gemv_s(const MatmulParams& p, int n_items, int kv, hipStream_t s) {
+  if constexpr (EPI == EPI_QKV) {
+    return gemv_sx<BT, WQ, EPI, KVFP8, U, true>(p, n_items, kv, s);
+  } else if constexpr (EPI == EPI_LOGITS) {
+    return p.xl ? gemv_sx<BT, WQ, EPI, KVFP8, U, true>(p, n_items, kv, s)
+                : gemv_sx<BT, WQ, EPI, KVFP8, U, false>(p, n_items, kv, s);
+  } else {
+    return gemv_sx<BT, WQ, EPI, KVFP8, U, false>(p, n_items, kv, s);
+  }
 }
 
 // Waves (row pairs) per work group of the norm-fused kernel.  Where every work group
@@ -181,7 +206,7 @@ int norm_ipw(const void* kern, int n_items, size_t lds) {
 template <int BT, int WQ, int EPI, bool KVFP8, int U>
 hipError_t gemv_norm_go(const MatmulParams& p, int n_items, hipStream_t s) {
   auto kern = k_gemv_norm<BT, WQ, EPI, KVFP8, U>;
-  const size_t lds = (size_t)BT * p.K * 2;
+  const size_t lds = (size_t)BT * p.K * 2 * (EPI == EPI_QKV ? 2 : 1);  // QKV: two bf16 parts
   static size_t allowed = 64 * 1024;  // per instance: the dynamic LDS size enabled so far
   if (lds > allowed) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -232,6 +257,7 @@ hipError_t dispatch_bt(const MatmulParams& p, bool mfma, hipStream_t s) {
     for (int b0 = 0; b0 < p.Bp; b0 += 8) {
       MatmulParams q = p;
       q.x = p.x + (int64_t)b0 * p.ldx;
+      q.xl = p.xl ? p.xl + (int64_t)b0 * p.ldx : nullptr;
       q.nh = p.nh ? p.nh + (int64_t)b0 * p.K : nullptr;
       q.Bp = p.Bp - b0 < 8 ? p.Bp - b0 : 8;
       q.out = p.out ? p.out + (int64_t)b0 * p.ldo : nullptr;
@@ -269,6 +295,8 @@ hipError_t dispatch_kv(const MatmulParams& p, int epi, bool kv_fp8, bool mfma, h
 }  // namespace
 
 hipError_t launch_matmul(const MatmulParams& p, int epi, WFmt wq, bool kv_fp8, bool mfma, hipStream_t s) {
+  // the QKV input comes in two parts: computed by the norm-fused kernel, or given
+  if (epi == EPI_QKV && !(p.xl || (p.nh && !mfma))) return hipErrorInvalidValue;
   // the cache dtype only matters for the QKV epilogue; keep one instance otherwise
   if (epi != EPI_QKV) kv_fp8 = false;
   switch (wq) {

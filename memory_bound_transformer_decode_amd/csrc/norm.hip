@@ -37,11 +37,22 @@ __global__ __launch_bounds__(256) void k_norm(NormParams p) {
     *reinterpret_cast<f32x4*>(hout + i) = v;
     return v;
   };
+  // x = bf16(y), y = h r g; with x_lo also the remainder bf16(y - x)
+  uint16_t* xlrow = p.x_lo ? p.x_lo + (int64_t)b * d : nullptr;
   auto store4 = [&](int i, f32x4 v, float r) {
     const f32x4 g = *reinterpret_cast<const f32x4*>(p.gain + i);
-    const uint32_t lo = (uint32_t)f32_to_bf16(v.x * r * g.x) | ((uint32_t)f32_to_bf16(v.y * r * g.y) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(v.z * r * g.z) | ((uint32_t)f32_to_bf16(v.w * r * g.w) << 16);
-    *reinterpret_cast<u32x2*>(xrow + i) = u32x2{lo, hi};
+    const float y[4] = {v.x * r * g.x, v.y * r * g.y, v.z * r * g.z, v.w * r * g.w};
+    uint16_t hb[4], lb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hb[j] = f32_to_bf16(y[j]);
+      lb[j] = f32_to_bf16(y[j] - bf16_to_f32(hb[j]));
+    }
+    *reinterpret_cast<u32x2*>(xrow + i) =
+        u32x2{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+    if (xlrow)
+      *reinterpret_cast<u32x2*>(xlrow + i) =
+          u32x2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
   };
   float ss = 0.f;
   if (NV > 0) {

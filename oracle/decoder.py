@@ -52,12 +52,14 @@ from dataclasses import dataclass, field
 from typing import Callable, List, Optional, Sequence
 
 import numpy as np
+from threadpoolctl import threadpool_limits
 
 from . import codecs
 
 # Host threads for the matrix products: row chunks of a product are independent, so
 # they are decoded and multiplied in parallel (each output row's sum is the same
-# computation whichever thread runs it).
+# computation whichever thread runs it), each chunk's product by a single-threaded BLAS
+# call (a threaded BLAS inside every worker would oversubscribe the cores).
 _THREADS = max(1, min(16, os.cpu_count() or 1))
 _POOL: Optional[ThreadPoolExecutor] = None
 
@@ -172,7 +174,8 @@ class Matrix:
             if self.scale is not None:
                 Y[:, r0:r1] *= self.scale[r0:r1].astype(np.float64)[None, :]
 
-        list(_pool().map(chunk, range(0, self.rows, self.chunk_rows)))
+        with threadpool_limits(limits=1, user_api="blas"):
+            list(_pool().map(chunk, range(0, self.rows, self.chunk_rows)))
         if ledger is not None:
             ledger.macs += X.shape[0] * self.rows * self.cols
         return Y

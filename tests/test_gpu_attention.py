@@ -4,10 +4,11 @@ attention on the same cache bits (needs an MI355X).
 Inputs: q ~ N(0, 1) fp32 (scaled so the softmax is neither flat nor one-hot), K/V
 ~ N(0, 1) in the cache format, block tables a seeded permutation of the pool, a
 length mix with empty rows (-1), one position, block edges, and contexts long enough
-for several splits.  Bar: the output is bf16, so each element may differ from the fp64
-value by its bf16 rounding (2^-9 relative) plus the kernel's rounding of q and the
-probabilities into bf16 high + low parts (about 2^-16): |o - o_ref| <= 4e-3 times the
-head vector's largest |o_ref|, and exactly 0 for an empty row.
+for several splits.  Bar: the output is bf16 (8 significant bits), so each element may
+differ from the fp64 value by its rounding, up to 2^-8 of its magnitude, plus the
+kernel's arithmetic (q and the probabilities kept as bf16 high + low parts, about 2^-16;
+fp32 exponentials and sums): |o - o_ref| <= 2^-8 |o_ref| + 2^-10 max|o_ref| over the
+head vector, and exactly 0 for an empty row.
 """
 
 import numpy as np
@@ -21,7 +22,7 @@ from oracle import decoder as OD
 from harness import log, require_gpu
 
 pytestmark = pytest.mark.gpu
-BAR = 4e-3
+REL, ABS = 2.0 ** -8, 2.0 ** -10
 
 
 @pytest.fixture(scope="module")
@@ -76,10 +77,10 @@ def test_attention_matches_oracle(dec, kv, Hq, Hkv, dh):
             continue
         for j in range(Hq):
             scale = np.max(np.abs(ref[r, j]))
-            err = np.max(np.abs(got[r, j] - ref[r, j])) / scale
-            worst = max(worst, err)
-    log(f"attention {kv} Hq={Hq} Hkv={Hkv} dh={dh}: worst |do| / max|o| {worst:.2e}")
-    assert worst <= BAR
+            err = np.abs(got[r, j] - ref[r, j])
+            worst = max(worst, float(np.max(err / (REL * np.abs(ref[r, j]) + ABS * scale))))
+    log(f"attention {kv} Hq={Hq} Hkv={Hkv} dh={dh}: worst error / bar {worst:.3f}")
+    assert worst <= 1.0
 
 
 def test_attention_workspace_and_argument_errors(dec):

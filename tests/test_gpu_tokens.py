@@ -49,11 +49,12 @@ def run_verify(dec, case, tokens, flags=0, max_batch=None, stream=False):
     info = d.info()
     om = OI.model(case.weights, keep=not stream, stream=stream)
     oc = OI.cache(cfg, synth.kv_codes_numpy(case.pool))
+    before = oc.pool.copy()
     zo = OD.verify_step(om, oc, tokens, case.ctx_lens, case.block_tables)
     rep = Report()
     assert np.all(np.isfinite(z))
     compare_logits(z.reshape(n * k, -1), zo.reshape(n * k, -1), tol, rep, 0)
-    compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol)
+    compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol, before)
     d.close()
     log(f"verify {cfg.name} n={n} k={k} flags={flags}: max rel err {rep.max_rel_err:.3e}, "
         f"argmax {rep.argmax_checked - rep.argmax_mismatch}/{rep.argmax_checked}, "
@@ -154,11 +155,13 @@ def run_prefill(dec, cfg, n_tokens, start, max_batch, max_seq_len, seed, stream=
     info = d.info()
     om = OI.model(case.weights, keep=not stream, stream=stream)
     oc = OI.cache(cfg, synth.kv_codes_numpy(case.pool))
+    before = oc.pool.copy()
     zo = OD.prefill(om, oc, tokens, start, case.block_tables[0])
     rep = Report()
     assert np.all(np.isfinite(z))
     compare_logits(z[None], zo[None], tol, rep, 0)
-    compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol)
+    compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol, before)
+    before = oc.pool.copy()
     chunks = -(-n_tokens // max_batch)
     assert info.launches == chunks and info.rows == n_tokens
     # decode on from the prefilled cache, both sides
@@ -169,7 +172,7 @@ def run_prefill(dec, cfg, n_tokens, start, max_batch, max_seq_len, seed, stream=
         zdo = OD.decode_step(om, oc, after[t], [p + t], case.block_tables[:1])
         compare_logits(zd, zdo, tol, rep, t + 1)
     if decode_after:
-        compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol)
+        compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol, before)
     d.close()
     log(f"prefill {cfg.name} n={n_tokens} start={start} chunk={max_batch} ({chunks} chunks): "
         f"max rel err {rep.max_rel_err:.3e}, argmax {rep.argmax_checked - rep.argmax_mismatch}/"
