@@ -343,6 +343,20 @@ int dec_attention(const dec_attn_desc* desc, const float* q, const void* kv_pool
                   const int32_t* block_tables, uint16_t* o, void* workspace, size_t workspace_bytes,
                   void* hip_stream);
 
+/* dec_attention for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and
+ * arguments without the workspace, which comes from a static scratch area of the
+ * library -- DEC_ATTN_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  The
+ * call allocates nothing (its first call on a GPU looks up that GPU's scratch address);
+ * it clears the split counters it uses with a kernel on hip_stream.  Shapes whose
+ * workspace (dec_attention_workspace_bytes) exceeds the scratch are refused with
+ * DEC_E_CAPACITY.  Calls on one GPU share its scratch: calls that can overlap (other
+ * streams, other threads) race and must be serialized by the caller. */
+#define DEC_ATTN_NOALLOC_SCRATCH_BYTES (8u << 20)
+int dec_attention_noalloc(const dec_attn_desc* desc, const float* q, const void* kv_pool,
+                          const int32_t* seq_lens, const int32_t* block_tables, uint16_t* o,
+                          void* hip_stream);
+
 /* Streaming read of `bytes` of device memory at `buf` (16-byte aligned, a
  * multiple of 16), `reps` times, on `hip_stream`; returns the best observed
  * read bandwidth in bytes/s through *out.  Measures the HBM read rate the

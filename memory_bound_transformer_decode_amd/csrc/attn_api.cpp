@@ -1,5 +1,7 @@
 // The attention step of decode as a call of its own: split-K paged GQA attention of
-// query rows over a paged KV cache, with the caller's workspace (dec_attention).
+// query rows over a paged KV cache, with the caller's workspace (dec_attention) or a
+// statically allocated scratch area (dec_attention_noalloc, for callers that cannot
+// allocate device memory).
 //
 // Exact softmax attention computed tile by tile over a paged cache (FlashAttention and
 // PagedAttention as cited by "GPU Inference Internals", Kernels: FlashAttention and the
@@ -9,12 +11,23 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "dec.h"
 #include "kernels.h"
 
 namespace {
+
+// Scratch of dec_attention_noalloc: attention partials and split counters, one copy per
+// GPU the library runs on, held until the process ends.  Host code never uses the
+// array's name as an address: each device's address comes from hipGetSymbolAddress.
+constexpr size_t NOALLOC_SCRATCH_BYTES = DEC_ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
 
 int afail(int code, const char* fmt, ...) {
   char buf[512];
@@ -112,6 +125,36 @@ int dec_attention(const dec_attn_desc* d, const float* q, const void* kv_pool, c
     return afail(DEC_E_INVALID, "workspace must be non-NULL and 256-byte aligned");
   if (workspace_bytes < need) return afail(DEC_E_INVALID, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   return enqueue(d, q, kv_pool, seq_lens, block_tables, o, static_cast<uint8_t*>(workspace),
+                 static_cast<hipStream_t>(hip_stream));
+}
+
+int dec_attention_noalloc(const dec_attn_desc* d, const float* q, const void* kv_pool, const int32_t* seq_lens,
+                          const int32_t* block_tables, uint16_t* o, void* hip_stream) {
+  int rc = check_desc(d);
+  if (rc != DEC_OK) return rc;
+  if ((rc = check_ptrs(q, kv_pool, seq_lens, block_tables, o)) != DEC_OK) return rc;
+  const size_t need = dec::attn_scratch(shape_of(d), d->n_rows).total;
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return afail(DEC_E_CAPACITY, "this shape needs %zu bytes of scratch; the static area holds %zu", need,
+                 NOALLOC_SCRATCH_BYTES);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return afail(DEC_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return afail(DEC_E_UNSUPPORTED, "device %d beyond %d", dev, MAX_DEVICES);
+  void* ptr = nullptr;
+  {
+    // the device's own address of its copy of the array, looked up once per device
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        g_scratch_ptr[dev] = nullptr;
+        return afail(DEC_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      }
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  return enqueue(d, q, kv_pool, seq_lens, block_tables, o, static_cast<uint8_t*>(ptr),
                  static_cast<hipStream_t>(hip_stream));
 }
 

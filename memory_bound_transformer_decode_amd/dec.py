@@ -81,7 +81,7 @@ class DecError(RuntimeError):
 EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_load_weights", "dec_step", "dec_verify",
            "dec_prefill", "dec_set_flags", "dec_get_info", "dec_get_step_info", "dec_destroy",
            "dec_last_error", "dec_bw_probe", "dec_launch_matmul", "dec_sample_greedy", "dec_sample",
-           "dec_attention_workspace_bytes", "dec_attention")
+           "dec_attention_workspace_bytes", "dec_attention", "dec_attention_noalloc")
 MAT_QKV, MAT_O, MAT_GATE_UP, MAT_DOWN, MAT_LM_HEAD = 0, 1, 2, 3, 4
 
 _lib = None
@@ -133,6 +133,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dec_attention.argtypes = [POINTER(DecAttnDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_size_t, c_void_p]
     lib.dec_attention.restype = c_int
+    lib.dec_attention_noalloc.argtypes = [POINTER(DecAttnDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p]
+    lib.dec_attention_noalloc.restype = c_int
     _lib = lib
     return lib
 
