@@ -12,6 +12,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -110,6 +112,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// fp32 -> fp16 bits, round to nearest even; magnitudes beyond the largest finite fp16
+// (65504) saturate to it (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  const float c = __builtin_fminf(__builtin_fmaxf(f, -65504.0f), 65504.0f);
+  return __builtin_bit_cast(uint16_t, (_Float16)(f != f ? f : c));
+}
+
 // fp32 -> OCP E4M3 code: round to nearest even, finite values saturate to +-448.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
   uint32_t u = __float_as_uint(f);
@@ -163,6 +172,23 @@ template <int WQ, bool HI>
 __device__ __forceinline__ f32x2 b8x2_to_f32x2(uint32_t w) {
   if constexpr (WQ == W_I8) return i8x2_to_f32x2<HI>(w);
   else return e4m3x2_to_f32x2<HI>(w);
+}
+
+// Weights as fp16 operands.  E4M3 and int8 values are fp16 values (exact).  bf16 values
+// are exact in fp16 from 2^-14 to 65504 in magnitude (8 significant bits fit fp16's 11);
+// smaller ones are cut to a multiple of 2^-24 (the conversion rounds toward zero), an
+// absolute change below 2^-24.
+__device__ __forceinline__ f16x2 bf16x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w), bf16_hi(w)));
+}
+template <int WQ, bool HI>
+__device__ __forceinline__ f16x2 b8x2_to_f16x2(uint32_t w) {
+  if constexpr (WQ == W_I8) {
+    const f32x2 f = i8x2_to_f32x2<HI>(w);
+    return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(f.x, f.y));
+  } else {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+  }
 }
 
 // ---------------------------------------------------------------- dot products

@@ -247,6 +247,19 @@ int hip_fail(dec_ctx* c, hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(ctx, e_, what); \
   } while (0)
 
+// Buckets from 8 rows (bf16 weights) or 4 rows (one-byte weights) up run the products on
+// the matrix cores (unless DEC_FLAG_NO_MFMA); smaller ones run the matrix-vector
+// kernels.  Measured on the 8B and 32B shapes: the vector kernels' activation reads from
+// LDS (Bp per weight vector) and, for E4M3, the widening of every weight once per batch
+// row make them slower than the MFMA tiles from these batches on; the MFMA tiles pad the
+// batch to 16 columns at no extra HBM traffic.
+constexpr int MFMA_MIN_BATCH_BF16 = 8;
+constexpr int MFMA_MIN_BATCH_BYTE = 4;
+bool use_mfma(const dec_config& g, int Bp) {
+  return !(g.flags & DEC_FLAG_NO_MFMA) &&
+         Bp >= (g.weight_dtype != DEC_BF16 ? MFMA_MIN_BATCH_BYTE : MFMA_MIN_BATCH_BF16);
+}
+
 // Parameters of the matrix kernel `which` (dec_matrix) of layer l for a padded batch Bp.
 dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) {
   const dec_config& g = c->cfg;
@@ -272,13 +285,14 @@ dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) 
   uint16_t* x = ws_ptr<uint16_t>(c, c->L.x);
   float* h = ws_ptr<float>(c, c->L.h);
   switch (which) {
-    case DEC_MAT_QKV:  // [q; k; v] = W_qkv (x + xl), RoPE, K/V -> cache
+    case DEC_MAT_QKV:  // [q; k; v] = W_qkv x, RoPE, K/V -> cache (x: fp16, or x + xl)
       p.W = c->qkv[l].w;
       p.scale = c->qkv[l].scale;
       p.N = (Hq + 2 * Hkv) * dh;
       p.K = d;
       p.x = x;
-      p.xl = ws_ptr<uint16_t>(c, c->L.xl);
+      if (use_mfma(g, Bp)) p.x_f16 = 1;
+      else p.xl = ws_ptr<uint16_t>(c, c->L.xl);
       p.ldx = d;
       *epi = dec::EPI_QKV;
       break;
@@ -330,19 +344,6 @@ dec::MatmulParams matmul_params(dec_ctx* c, int which, int l, int Bp, int* epi) 
   return p;
 }
 
-// Buckets from 8 rows (bf16 weights) or 4 rows (one-byte weights) up run the products on
-// the matrix cores (unless DEC_FLAG_NO_MFMA); smaller ones run the matrix-vector
-// kernels.  Measured on the 8B and 32B shapes: the vector kernels' activation reads from
-// LDS (Bp per weight vector) and, for E4M3, the widening of every weight once per batch
-// row make them slower than the MFMA tiles from these batches on; the MFMA tiles pad the
-// batch to 16 columns at no extra HBM traffic.
-constexpr int MFMA_MIN_BATCH_BF16 = 8;
-constexpr int MFMA_MIN_BATCH_BYTE = 4;
-bool use_mfma(const dec_config& g, int Bp) {
-  return !(g.flags & DEC_FLAG_NO_MFMA) &&
-         Bp >= (g.weight_dtype != DEC_BF16 ? MFMA_MIN_BATCH_BYTE : MFMA_MIN_BATCH_BF16);
-}
-
 // Row blocks of a residual product on the MFMA tiles -- O (K = Hq dh) or down (K = d_ff)
 // -- : the number of row-block sums of squares it writes for the folded RMSNorm that
 // follows it.
@@ -369,8 +370,9 @@ void set_fold_norm(dec_ctx* c, int which, int l, int Bp, dec::MatmulParams& p) {
   p.eps = g.rms_eps;
   if (which == DEC_MAT_O || which == DEC_MAT_DOWN) {
     p.xout = ws_ptr<uint16_t>(c, c->L.x);
-    // down before the next layer's QKV also writes the second part of its input
-    if (which == DEC_MAT_DOWN && l + 1 < g.n_layers) p.xout_lo = ws_ptr<uint16_t>(c, c->L.xl);
+    // down before the next layer's QKV (on the matrix cores, as all products of a folded
+    // plan) writes its input as fp16
+    if (which == DEC_MAT_DOWN && l + 1 < g.n_layers) p.xout_f16 = 1;
     p.ldxo = d;
     p.xg = which == DEC_MAT_O ? c->mlp_norm + (size_t)l * d
            : l + 1 < g.n_layers ? c->attn_norm + (size_t)(l + 1) * d : c->final_norm;
@@ -457,8 +459,13 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   np.E_scale = c->embed.scale;
   np.ids = ws_ptr<int32_t>(c, c->L.ids);
   np.gain = g.n_layers > 0 ? c->attn_norm : c->final_norm;
+  // layer 0's QKV input: fp16 for the matrix cores, else two bf16 parts
   uint16_t* xl = ws_ptr<uint16_t>(c, c->L.xl);
-  np.x_lo = g.n_layers > 0 ? xl : nullptr;  // layer 0's QKV input
+  auto qkv_input = [&](bool on) {
+    np.x_f16 = on && mfma;
+    np.x_lo = on && !mfma ? xl : nullptr;
+  };
+  qkv_input(g.n_layers > 0);
   if ((e = dec::launch_embed_norm(np, wq, s)) != hipSuccess) return e;
   // the product of `which` with its rows written plainly to uf [Bp][N]
   auto plain = [&](int which, int l, dec::MatmulParams* keep) -> hipError_t {
@@ -472,7 +479,7 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   for (int l = 0; l < g.n_layers; ++l) {
     if (l > 0) {
       np.gain = c->attn_norm + (size_t)l * d;
-      np.x_lo = xl;
+      qkv_input(true);
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
     dec::MatmulParams qp{};
@@ -484,7 +491,7 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
     if ((e = plain(DEC_MAT_O, l, nullptr)) != hipSuccess) return e;
     if ((e = dec::launch_add(h, uf, Bp * d, s)) != hipSuccess) return e;
     np.gain = c->mlp_norm + (size_t)l * d;
-    np.x_lo = nullptr;
+    qkv_input(false);
     if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     if ((e = plain(DEC_MAT_GATE_UP, l, nullptr)) != hipSuccess) return e;
     if ((e = dec::launch_silu_mul(uf, g.d_ff, Bp, ws_ptr<uint16_t>(c, c->L.a), g.d_ff, s)) != hipSuccess) return e;
@@ -494,7 +501,7 @@ hipError_t enqueue_unfused(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   if (skip_lm) return hipSuccess;
   if (g.n_layers > 0) {
     np.gain = c->final_norm;
-    np.x_lo = nullptr;
+    qkv_input(false);
     if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
   }
   return run_matmul(c, DEC_MAT_LM_HEAD, 0, Bp, s);
@@ -523,8 +530,14 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   np.E_scale = c->embed.scale;
   np.ids = ws_ptr<int32_t>(c, c->L.ids);
   np.gain = g.n_layers > 0 ? c->attn_norm : c->final_norm;
+  // layer 0's QKV input: fp16 for the matrix cores, else two bf16 parts
+  const bool mfma = use_mfma(g, Bp);
   uint16_t* xl = ws_ptr<uint16_t>(c, c->L.xl);
-  np.x_lo = g.n_layers > 0 ? xl : nullptr;  // layer 0's QKV input
+  auto qkv_input = [&](bool on) {
+    np.x_f16 = on && mfma;
+    np.x_lo = on && !mfma ? xl : nullptr;
+  };
+  qkv_input(g.n_layers > 0);
   if ((e = dec::launch_embed_norm(np, wq, s)) != hipSuccess) return e;
 
   // no RMSNorm kernels: the matrix-vector kernels normalize their own input (fn), or the
@@ -535,7 +548,7 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
     const float* an = c->attn_norm + (size_t)l * d;
     if (l > 0 && nk) {
       np.gain = an;
-      np.x_lo = xl;
+      qkv_input(true);
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
     if ((e = run_matmul(c, DEC_MAT_QKV, l, Bp, s, fn ? an : nullptr)) != hipSuccess) return e;
@@ -546,7 +559,7 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
     const float* mn = c->mlp_norm + (size_t)l * d;
     if (nk) {
       np.gain = mn;
-      np.x_lo = nullptr;
+      qkv_input(false);
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
     if ((e = run_matmul(c, DEC_MAT_GATE_UP, l, Bp, s, fn ? mn : nullptr)) != hipSuccess) return e;
@@ -555,7 +568,7 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   if (skip_lm) return hipSuccess;
   if (g.n_layers > 0 && nk) {
     np.gain = c->final_norm;
-    np.x_lo = nullptr;
+    qkv_input(false);
     if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
   }
   if ((e = run_matmul(c, DEC_MAT_LM_HEAD, 0, Bp, s, fn ? c->final_norm : nullptr)) != hipSuccess) return e;

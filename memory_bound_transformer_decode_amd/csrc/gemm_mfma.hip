@@ -14,6 +14,9 @@
 //  * One-byte codes (E4M3 or int8) are widened to bf16 in registers (exact), and the
 //    per-row scale is applied once in the epilogue (dequantization fused into the
 //    matmul: kernel-fusion architecture study, section 11).
+//  * QKV runs on v_mfma_f32_16x16x32_f16 instead: its input x comes as fp16 (more
+//    significant bits for q and k, see MatmulParams::xl), and the weights are widened
+//    to fp16 in registers (exact for E4M3 and int8; bf16 see bf16x2_to_f16x2).
 //  * The activations x [Bp][K] are the other operand of every tile.  A work group owns
 //    W 16-row tiles (one per wave) and stages x through LDS in chunks of KC k-values
 //    shared by all of its waves, so its L2 reads of x are Bp / 16 W of the weight bytes
@@ -47,10 +50,8 @@ constexpr int tile_bytes() { return B8 ? 256 : 16 * (64 / RPL_BF16); }  // of a 
 template <bool B8>
 constexpr int tile_row() { return tile_bytes<B8>() + 16; }  // LDS row of a wave's weight tile (padded)
 // x chunk buffers: two (the next chunk is staged while this one is read) up to 32 batch
-// columns; one beyond, where two would hold the LDS to one work group per CU.  XLO: x
-// comes in two bf16 parts (the QKV input, see MatmulParams::xl), each with its buffers,
-// and one buffer from 32 columns.
-constexpr int x_buffers(int NT, bool XLO) { return (NT >= 3 || (XLO && NT >= 2)) ? 1 : 2; }
+// columns; one beyond, where two would hold the LDS to one work group per CU.
+constexpr int x_buffers(int NT) { return NT >= 3 ? 1 : 2; }
 // 16-row tiles per wave (measured on the 8B, 32B and 70B shapes at 48-64 rows): with
 // one-byte (E4M3) weights each x operand read from LDS (NT per k-step) costs the LDS more than the
 // weights do, so from 48 columns a wave takes two tiles that share those reads -- on
@@ -66,11 +67,11 @@ int tiles_per_wave(int NT, bool byte_weights, int n_rows_total, int K) {
 // the four lane groups l / 16 four disjoint sets of 8 k-values; lane l receives
 // D[4 (l / 16) + j][l % 16], j = 0..3.  Which k-values a lane group covers is free as long
 // as A and B agree: in k-step s of a group of GK k-values, lane group g takes the 8
-// k-values s 32 + 8 g + [0, 8).
-// XLO: the input is x + p.xl, two bf16 parts; every product is made with each part.
-template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW, bool XLO>
+// k-values s 32 + 8 g + [0, 8).  v_mfma_f32_16x16x32_f16 has the same operand layout.
+// F16: x holds fp16 codes and the weights enter the products as fp16 (the QKV input).
+template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW, bool F16>
 __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n) {
-  // x: [XP][XBUFS][NT 16][XROW] bf16 (XP parts); tiles: [W][TPW][16][TROW]
+  // x: [XBUFS][NT 16][XROW] bf16 or fp16; tiles: [W][TPW][16][TROW]
   extern __shared__ __align__(16) uint8_t lds[];
   constexpr bool B8 = WQ != W_BF16;  // one-byte weights (E4M3 or int8 codes)
   constexpr bool SILU = EPI == EPI_SILU;
@@ -84,14 +85,13 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   constexpr int COLS = NT * 16;
   constexpr int XSEG = KC / 8;                     // 16-byte pieces per staged x row
   constexpr int XL = (COLS * XSEG + W * WAVE - 1) / (W * WAVE);  // x staging loads per thread
-  constexpr int XBUF = COLS * XROW;                // bf16 per x buffer
-  constexpr int XBUFS = x_buffers(NT, XLO);
-  constexpr int XP = XLO ? 2 : 1;                  // parts of x
+  constexpr int XBUF = COLS * XROW;                // elements per x buffer
+  constexpr int XBUFS = x_buffers(NT);
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int lane = tid % WAVE, m = lane % 16, kg = lane / 16;
-  uint8_t* tile = lds + (size_t)XP * XBUFS * XBUF * 2 + (size_t)wave * TPW * 16 * tile_row<B8>();
+  uint8_t* tile = lds + (size_t)XBUFS * XBUF * 2 + (size_t)wave * TPW * 16 * tile_row<B8>();
   // rows: output rows of the product (d_ff intermediate indices for gate+up); a tile
   // covers TR of them, a wave TPW tiles (TPW > 1: each x operand read from LDS feeds
   // TPW tiles' products)
@@ -134,29 +134,23 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
         for (int q = 0; q < NQ; ++q) wr[tt][gi][q] = ld_stream(reinterpret_cast<const u32x4*>(wp[tt][q] + off));
     }
   };
-  // x loads of chunk c into registers, each part (rows past Bp read row Bp - 1; k past
-  // K is zero)
-  auto load_x = [&](int c, u32x4 (&xr)[XP][XL]) {
+  // x loads of chunk c into registers (rows past Bp read row Bp - 1; k past K is zero)
+  auto load_x = [&](int c, u32x4 (&xr)[XL]) {
 #pragma unroll
-    for (int part = 0; part < XP; ++part)
-#pragma unroll
-      for (int j = 0; j < XL; ++j) {
-        const int i = tid + j * W * WAVE;
-        const int b = min(i / XSEG, p.Bp - 1), k = c * KC + (i % XSEG) * 8;
-        const u32x4 v = gld16((part ? p.xl : p.x) + (int64_t)b * p.ldx + min(k, p.K - 8));
-        xr[part][j] = k < p.K ? v : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int j = 0; j < XL; ++j) {
+      const int i = tid + j * W * WAVE;
+      const int b = min(i / XSEG, p.Bp - 1), k = c * KC + (i % XSEG) * 8;
+      const u32x4 v = gld16(p.x + (int64_t)b * p.ldx + min(k, p.K - 8));
+      xr[j] = k < p.K ? v : u32x4{0u, 0u, 0u, 0u};
+    }
   };
-  auto store_x = [&](int buf, const u32x4 (&xr)[XP][XL]) {
+  auto store_x = [&](int buf, const u32x4 (&xr)[XL]) {
 #pragma unroll
-    for (int part = 0; part < XP; ++part)
-#pragma unroll
-      for (int j = 0; j < XL; ++j) {
-        const int i = tid + j * W * WAVE;
-        if (XL * W * WAVE == COLS * XSEG || i < COLS * XSEG)
-          *reinterpret_cast<u32x4*>(xs + (part * XBUFS + buf) * XBUF + (i / XSEG) * XROW + (i % XSEG) * 8) =
-              xr[part][j];
-      }
+    for (int j = 0; j < XL; ++j) {
+      const int i = tid + j * W * WAVE;
+      if (XL * W * WAVE == COLS * XSEG || i < COLS * XSEG)
+        *reinterpret_cast<u32x4*>(xs + buf * XBUF + (i / XSEG) * XROW + (i % XSEG) * 8) = xr[j];
+    }
   };
 
   f32x4 acc[TPW][NT];
@@ -176,28 +170,46 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
           *reinterpret_cast<u32x4*>(tile + (tt * 16 + RPL * q + lr) * TROW + lj * 16) = wr[tt][gi][q];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        bf16x8 av[TPW];
+        // the lane's 8 weights of each tile as bf16, or fp16 (F16), bits
+        u32x4 av[TPW];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const uint8_t* tr = tile + (tt * 16 + m) * TROW;
           if (B8) {
             const u32x2 c8 = *reinterpret_cast<const u32x2*>(tr + s * 32 + kg * 8);
-            const bf16x2 q0 = b8x2_to_bf16x2<WQ, false>(c8.x), q1 = b8x2_to_bf16x2<WQ, true>(c8.x);
-            const bf16x2 q2 = b8x2_to_bf16x2<WQ, false>(c8.y), q3 = b8x2_to_bf16x2<WQ, true>(c8.y);
-            av[tt] = bf16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+            if constexpr (F16)
+              av[tt] = u32x4{__builtin_bit_cast(uint32_t, b8x2_to_f16x2<WQ, false>(c8.x)),
+                             __builtin_bit_cast(uint32_t, b8x2_to_f16x2<WQ, true>(c8.x)),
+                             __builtin_bit_cast(uint32_t, b8x2_to_f16x2<WQ, false>(c8.y)),
+                             __builtin_bit_cast(uint32_t, b8x2_to_f16x2<WQ, true>(c8.y))};
+            else
+              av[tt] = u32x4{__builtin_bit_cast(uint32_t, b8x2_to_bf16x2<WQ, false>(c8.x)),
+                             __builtin_bit_cast(uint32_t, b8x2_to_bf16x2<WQ, true>(c8.x)),
+                             __builtin_bit_cast(uint32_t, b8x2_to_bf16x2<WQ, false>(c8.y)),
+                             __builtin_bit_cast(uint32_t, b8x2_to_bf16x2<WQ, true>(c8.y))};
           } else {
-            av[tt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tr + s * 64 + kg * 16));
+            const u32x4 wv = *reinterpret_cast<const u32x4*>(tr + s * 64 + kg * 16);
+            if constexpr (F16)
+              av[tt] = u32x4{__builtin_bit_cast(uint32_t, bf16x2_to_f16x2(wv.x)),
+                             __builtin_bit_cast(uint32_t, bf16x2_to_f16x2(wv.y)),
+                             __builtin_bit_cast(uint32_t, bf16x2_to_f16x2(wv.z)),
+                             __builtin_bit_cast(uint32_t, bf16x2_to_f16x2(wv.w))};
+            else
+              av[tt] = wv;
           }
         }
+        const uint16_t* xb = xs + buf * XBUF;
 #pragma unroll
-        for (int part = 0; part < XP; ++part) {
-          const uint16_t* xb = xs + (part * XBUFS + buf) * XBUF;
+        for (int t = 0; t < NT; ++t) {
+          const u32x4 bv = ld16(xb + (t * 16 + m) * XROW + gi * GK + s * 32 + kg * 8);
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const bf16x8 bv = __builtin_bit_cast(bf16x8, ld16(xb + (t * 16 + m) * XROW + gi * GK + s * 32 + kg * 8));
-#pragma unroll
-            for (int tt = 0; tt < TPW; ++tt)
-              acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bv, acc[tt][t], 0, 0, 0);
+          for (int tt = 0; tt < TPW; ++tt) {
+            if constexpr (F16)
+              acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[tt]),
+                                                                  __builtin_bit_cast(f16x8, bv), acc[tt][t], 0, 0, 0);
+            else
+              acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[tt]),
+                                                                   __builtin_bit_cast(bf16x8, bv), acc[tt][t], 0, 0, 0);
           }
         }
       }
@@ -263,7 +275,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   constexpr int SPER = (GEMM_SSQ_MAX + W - 1) / W;
   {
     constexpr int B1 = XBUFS == 2 ? 1 : 0;
-    u32x4 wa[TPW][NGRP][NQ], wb[TPW][NGRP][NQ], xr[XP][XL];
+    u32x4 wa[TPW][NGRP][NQ], wb[TPW][NGRP][NQ], xr[XL];
     const int scol = tid % GEMM_SSQ_STRIDE, spart = tid / GEMM_SSQ_STRIDE;
     float sv[SPER];
     if (p.ssq_n > 0) {
@@ -433,9 +445,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
             gst(o + r, hn);
             if (p.xout) {
               const float xv = hn * (full[tt] ? e_g[tt][j] : gld(p.xg + r));
-              const uint16_t xh = f32_to_bf16(xv);
-              gst(p.xout + (int64_t)col * p.ldxo + r, xh);
-              if (p.xout_lo) gst(p.xout_lo + (int64_t)col * p.ldxo + r, f32_to_bf16(xv - bf16_to_f32(xh)));
+              gst(p.xout + (int64_t)col * p.ldxo + r, p.xout_f16 ? f32_to_f16(xv) : f32_to_bf16(xv));
               sq[t] += hn * hn;
             }
           } else {
@@ -465,14 +475,14 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
 }
 
 template <bool B8>
-constexpr size_t lds_bytes(int NT, int W, int TPW, bool XLO) {
-  return (size_t)(XLO ? 2 : 1) * x_buffers(NT, XLO) * NT * 16 * XROW * 2 + (size_t)W * TPW * 16 * tile_row<B8>();
+constexpr size_t lds_bytes(int NT, int W, int TPW) {
+  return (size_t)x_buffers(NT) * NT * 16 * XROW * 2 + (size_t)W * TPW * 16 * tile_row<B8>();
 }
 
-template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW, bool XLO>
+template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW, bool F16>
 hipError_t go_tpwx(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
-  auto kern = k_gemm_lds<NT, WQ, EPI, KVFP8, W, TPW, XLO>;
-  constexpr size_t lds = lds_bytes<WQ != W_BF16>(NT, W, TPW, XLO);
+  auto kern = k_gemm_lds<NT, WQ, EPI, KVFP8, W, TPW, F16>;
+  constexpr size_t lds = lds_bytes<WQ != W_BF16>(NT, W, TPW);
   static_assert(lds <= 160 * 1024, "LDS of one work group");
   static bool attr = false;
   if (!attr && lds > 64 * 1024) {
@@ -485,15 +495,15 @@ hipError_t go_tpwx(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-// QKV always takes its input in two parts; a plain product (the unfused step's QKV)
-// does when given p.xl; the others never do
+// QKV always takes an fp16 input; a plain product (the unfused step's QKV) does when
+// p.x_f16 says so; the others never do
 template <int NT, int WQ, int EPI, bool KVFP8, int W, int TPW>
 hipError_t go_tpw(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
   if constexpr (EPI == EPI_QKV) {
     return go_tpwx<NT, WQ, EPI, KVFP8, W, TPW, true>(p, g, s);
   } else if constexpr (EPI == EPI_LOGITS) {
-    return p.xl ? go_tpwx<NT, WQ, EPI, KVFP8, W, TPW, true>(p, g, s)
-                : go_tpwx<NT, WQ, EPI, KVFP8, W, TPW, false>(p, g, s);
+    return p.x_f16 ? go_tpwx<NT, WQ, EPI, KVFP8, W, TPW, true>(p, g, s)
+                   : go_tpwx<NT, WQ, EPI, KVFP8, W, TPW, false>(p, g, s);
   } else {
     return go_tpwx<NT, WQ, EPI, KVFP8, W, TPW, false>(p, g, s);
   }

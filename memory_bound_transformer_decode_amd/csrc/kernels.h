@@ -32,12 +32,15 @@ struct MatmulParams {
   int d_ff;              // EPI_SILU: up rows start at d_ff (N = 2 d_ff)
   const uint16_t* x;     // bf16 activations [Bp][ldx]
   int ldx;
-  // The QKV product takes its input as two bf16 parts, x + xl (xl = bf16(v - x) of the
-  // fp32 value v): q and k feed a softmax whose logits can be large, which turns a
-  // relative error of q or k into a larger one of the attention weights, so their
-  // input keeps about 16 significant bits instead of 8.  xl: [Bp][ldx], or the kernel
-  // forms both parts itself (norm-fused kernels).
+  // The QKV product's input keeps more than bf16's 8 significant bits: q and k feed a
+  // softmax whose logits can be large, which turns a relative error of q or k into a
+  // larger one of the attention weights.  On the matrix-vector kernels it comes as two
+  // bf16 parts, x + xl (xl = bf16(v - x) of the fp32 value v, about 16 significant
+  // bits; xl: [Bp][ldx], or the norm-fused kernels form both parts in LDS).  On the
+  // matrix cores it comes as fp16 codes in x (x_f16 set: 11 significant bits, one
+  // operand instead of two), and the weights enter the products as fp16 too.
   const uint16_t* xl;
+  int x_f16;
   int Bp;                // padded batch (bucket)
   float* out;            // EPI_LOGITS / EPI_RESID: [Bp][ldo]
   int ldo;
@@ -65,12 +68,13 @@ struct MatmulParams {
   // RMSNorm folded into the MFMA products (the norm's 1 / rms is one factor per batch
   // row, so it can be applied to the products' sums).  A residual-add product (O, down)
   // with xout set also writes xout[b][r] = bf16(h_new[b][r] xg[r]) -- the next norm's
-  // input times its gain -- and, for its row block rb, ssq_out[rb GEMM_SSQ_STRIDE + b] =
+  // input times its gain; fp16 when xout_f16 (the next product is QKV) -- and, for its
+  // row block rb, ssq_out[rb GEMM_SSQ_STRIDE + b] =
   // the sum of h_new[b][r]^2 over the block's rows.  A product with ssq_n > 0 multiplies
   // its sums for batch row b by 1 / sqrt(sum_{i < ssq_n} ssq_in[i GEMM_SSQ_STRIDE + b] / K
   // + eps).
   uint16_t* xout;
-  uint16_t* xout_lo;     // with xout: also bf16(h_new xg - xout) (the next product is QKV)
+  int xout_f16;
   int ldxo;
   const float* xg;
   float* ssq_out;
@@ -105,8 +109,10 @@ struct NormParams {
   const float* h;       // [Bp][d] fp32 (input, or output for the embedding kernel)
   float* h_out;         // embed: h written here
   const float* gain;    // [d]
-  uint16_t* x;          // [Bp][d] bf16 out
-  uint16_t* x_lo;       // [Bp][d] bf16(x_fp32 - x) out, or nullptr (the next product is QKV)
+  uint16_t* x;          // [Bp][d] bf16 out (fp16 when x_f16)
+  uint16_t* x_lo;       // [Bp][d] bf16(x_fp32 - x) out, or nullptr (the next product is QKV
+                        // on the matrix-vector kernels)
+  int x_f16;            // x as fp16 codes (the next product is QKV on the matrix cores)
   int d, Bp;
   float eps;
   // embedding

@@ -295,8 +295,10 @@ hipError_t dispatch_kv(const MatmulParams& p, int epi, bool kv_fp8, bool mfma, h
 }  // namespace
 
 hipError_t launch_matmul(const MatmulParams& p, int epi, WFmt wq, bool kv_fp8, bool mfma, hipStream_t s) {
-  // the QKV input comes in two parts: computed by the norm-fused kernel, or given
-  if (epi == EPI_QKV && !(p.xl || (p.nh && !mfma))) return hipErrorInvalidValue;
+  // fp16 activations are read by the matrix cores only; the QKV input is fp16 there, and
+  // two bf16 parts on the matrix-vector kernels (given, or formed by the norm-fused kernel)
+  if (p.x_f16 && (!mfma || p.xl)) return hipErrorInvalidValue;
+  if (epi == EPI_QKV && (mfma ? !p.x_f16 : !(p.xl || p.nh))) return hipErrorInvalidValue;
   // the cache dtype only matters for the QKV epilogue; keep one instance otherwise
   if (epi != EPI_QKV) kv_fp8 = false;
   switch (wq) {

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void k_norm(NormParams p) {
     *reinterpret_cast<f32x4*>(hout + i) = v;
     return v;
   };
-  // x = bf16(y), y = h r g; with x_lo also the remainder bf16(y - x)
+  // x = bf16(y), y = h r g; with x_lo also the remainder bf16(y - x); fp16(y) if x_f16
   uint16_t* xlrow = p.x_lo ? p.x_lo + (int64_t)b * d : nullptr;
   auto store4 = [&](int i, f32x4 v, float r) {
     const f32x4 g = *reinterpret_cast<const f32x4*>(p.gain + i);
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void k_norm(NormParams p) {
     uint16_t hb[4], lb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      hb[j] = f32_to_bf16(y[j]);
+      hb[j] = p.x_f16 ? f32_to_f16(y[j]) : f32_to_bf16(y[j]);
       lb[j] = f32_to_bf16(y[j] - bf16_to_f32(hb[j]));
     }
     *reinterpret_cast<u32x2*>(xrow + i) =
@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void k_norm(NormParams p) {
 namespace {
 template <bool EMBED, int WQ>
 hipError_t norm_go(const NormParams& p, hipStream_t s) {
+  if (p.x_f16 && p.x_lo) return hipErrorInvalidValue;  // fp16 x is one part
   const int nv = (p.d + 1023) / 1024;
   if (nv <= 1) hipLaunchKernelGGL((k_norm<EMBED, WQ, 1>), dim3(p.Bp), dim3(256), 0, s, p);
   else if (nv <= 2) hipLaunchKernelGGL((k_norm<EMBED, WQ, 2>), dim3(p.Bp), dim3(256), 0, s, p);
