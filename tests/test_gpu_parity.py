@@ -189,7 +189,7 @@ def _one_step(dec, case, ids, lens, flags, max_batch=None):
     return z, pool, info
 
 
-@pytest.mark.parametrize("B", [5, 24])
+@pytest.mark.parametrize("B", [1, 5, 24])
 def test_graph_replay_equals_eager_bitwise(dec, B):
     cfg = fmt(MINI, "bf16", "bf16")
     rng = np.random.default_rng(20)
@@ -383,11 +383,12 @@ def test_unfused_step_matches_fused(dec):
     assert np.array_equal(gf, gu)
 
 
-def test_repeated_steps_are_deterministic(dec):
+@pytest.mark.parametrize("lens", [[9, 40, 3], [40]])
+def test_repeated_steps_are_deterministic(dec, lens):
     cfg = fmt(MINI, "fp8", "fp8")
-    case = make_case(cfg, [9, 40, 3], 128, seed=6)
-    ids = synth.make_token_ids(cfg, 1, 3, seed=6)[0]
-    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=4,
+    case = make_case(cfg, lens, 128, seed=6)
+    ids = synth.make_token_ids(cfg, 1, len(lens), seed=6)[0]
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=dec.ladder_bucket(len(lens)),
                     max_seq_len=128, kv_pool=case.pool.clone())
     outs = [d.step(ids, case.ctx_lens, case.block_tables).clone() for _ in range(3)]
     torch.cuda.synchronize()
