@@ -21,6 +21,10 @@
 //    W 16-row tiles (one per wave) and stages x through LDS in chunks of KC k-values
 //    shared by all of its waves, so its L2 reads of x are Bp / 16 W of the weight bytes
 //    instead of Bp / 16 of them for a work group of one tile.
+//  * Every wave keeps the next chunk's weights in flight while it multiplies the
+//    current one.  For the compiler's waits to allow that, every path issues the same
+//    loads in a fixed order and no loaded value is looked at before it is needed (a
+//    select on the just-loaded x made each chunk wait for all loads in flight).
 //  * Matrices with too few row blocks to fill the chip also split K over KS work
 //    groups.  Each writes its partial tiles; the last one of a row block to arrive sums
 //    the KS partials in split order (so the result does not depend on arrival order)
@@ -62,6 +66,12 @@ constexpr size_t TPW2_MIN_WEIGHTS = (size_t)200 << 20;
 int tiles_per_wave(int NT, bool byte_weights, int n_rows_total, int K) {
   return byte_weights && NT >= 3 && (size_t)n_rows_total * (size_t)K >= TPW2_MIN_WEIGHTS ? 2 : 1;
 }
+
+// Weight chunks each wave keeps in flight (the chunk being multiplied and D - 1 ahead).
+// Measured at 8B and 70B widths, batches 8 to 64: two (one chunk ahead) beat three and
+// four, whose registers cost more than their extra loads in flight bring.
+constexpr int GEMM_DEPTH = 2;
+constexpr int gemm_depth(int) { return GEMM_DEPTH; }
 
 // v_mfma_f32_16x16x32_bf16: lane l supplies A[l % 16][8 k-values] and B[8 k-values][l % 16],
 // the four lane groups l / 16 four disjoint sets of 8 k-values; lane l receives
@@ -124,32 +134,44 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
 
   // weight loads of chunk c, unconditional: pieces past K are read at the row's last
   // piece (x is zero there, so they add nothing)
+  // A chunk past this work group's last (c >= c1) reads the matrix's first bytes instead,
+  // the same few lines for every wave (cache hits), so that every path issues the same
+  // loads: the compiler's waits for a chunk then let the later chunks' loads stay in
+  // flight (a load issued on only some paths makes it wait for all of them).
   auto load_w = [&](int c, u32x4 (&wr)[TPW][NGRP][NQ]) {
+    const bool real = c < c1;
 #pragma unroll
     for (int gi = 0; gi < NGRP; ++gi) {
       const int off = min(c * KC * (B8 ? 1 : 2) + gi * TB + lj * 16, lastv);
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) wr[tt][gi][q] = ld_stream(reinterpret_cast<const u32x4*>(wp[tt][q] + off));
+        for (int q = 0; q < NQ; ++q) {
+          const uint8_t* a = real ? wp[tt][q] + off : static_cast<const uint8_t*>(p.W) + lj * 16;
+          wr[tt][gi][q] = ld_stream(reinterpret_cast<const u32x4*>(a));
+        }
     }
   };
-  // x loads of chunk c into registers (rows past Bp read row Bp - 1; k past K is zero)
+  // x loads of chunk c into registers (rows past Bp read row Bp - 1, k past K the row's
+  // last piece).  The loaded values are not looked at before store_x: a use right after
+  // the load would wait for it, and so for every weight load issued before it.
   auto load_x = [&](int c, u32x4 (&xr)[XL]) {
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
       const int i = tid + j * W * WAVE;
       const int b = min(i / XSEG, p.Bp - 1), k = c * KC + (i % XSEG) * 8;
-      const u32x4 v = gld16(p.x + (int64_t)b * p.ldx + min(k, p.K - 8));
-      xr[j] = k < p.K ? v : u32x4{0u, 0u, 0u, 0u};
+      xr[j] = gld16(p.x + (int64_t)b * p.ldx + min(k, p.K - 8));
     }
   };
-  auto store_x = [&](int buf, const u32x4 (&xr)[XL]) {
+  // x of chunk c into LDS buffer buf, zero for k past K
+  auto store_x = [&](int buf, int c, const u32x4 (&xr)[XL]) {
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
       const int i = tid + j * W * WAVE;
+      const int k = c * KC + (i % XSEG) * 8;
       if (XL * W * WAVE == COLS * XSEG || i < COLS * XSEG)
-        *reinterpret_cast<u32x4*>(xs + buf * XBUF + (i / XSEG) * XROW + (i % XSEG) * 8) = xr[j];
+        *reinterpret_cast<u32x4*>(xs + buf * XBUF + (i / XSEG) * XROW + (i % XSEG) * 8) =
+            k < p.K ? xr[j] : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -232,38 +254,41 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   f32x4 e_h[TPW][EPI == EPI_RESID ? NT : 1];
   f32x4 e_cs[TPW][EPI == EPI_QKV ? NT : 1];
   int e_pos[EPI == EPI_QKV ? NT : 1], e_blk[EPI == EPI_QKV ? NT : 1];
-  auto epi_prefetch = [&]() {
+  // As with the weights, every path issues the same loads here (rows clamped into the
+  // matrix, absent scale or gain arrays replaced by the matrix's first bytes), and the
+  // values are looked at only in the epilogue, where they are selected.  The tokens'
+  // positions, which the cache-block and RoPE addresses need, are loaded before the first
+  // weights (pos_prefetch), so that waiting for them leaves the weight loads in flight.
+  const float* fdummy = static_cast<const float*>(p.W);
+  auto pos_prefetch = [&]() {
     if (EPI == EPI_QKV) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) e_pos[t] = gld(p.seq_lens + min(t * 16 + m, p.Bp - 1));
     }
+  };
+  auto epi_prefetch = [&]() {
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-      e_sc[tt] = e_su[tt] = f32x4{1.f, 1.f, 1.f, 1.f};
-      if (!full[tt]) continue;
-      if (p.scale) {
-        e_sc[tt] = gld(reinterpret_cast<const f32x4*>(p.scale + er0[tt]));
-        if (SILU) e_su[tt] = gld(reinterpret_cast<const f32x4*>(p.scale + p.d_ff + er0[tt]));
-      }
+      const int rc = min(er0[tt], rows - 4);
+      e_sc[tt] = gld(reinterpret_cast<const f32x4*>(p.scale ? p.scale + rc : fdummy));
+      if (SILU) e_su[tt] = gld(reinterpret_cast<const f32x4*>(p.scale ? p.scale + p.d_ff + rc : fdummy));
       if (EPI == EPI_RESID) {
-        if (p.xout) e_g[tt] = gld(reinterpret_cast<const f32x4*>(p.xg + er0[tt]));
+        e_g[tt] = gld(reinterpret_cast<const f32x4*>(p.xout ? p.xg + rc : fdummy));
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          e_h[tt][t] = gld(reinterpret_cast<const f32x4*>(p.out + (int64_t)min(t * 16 + m, p.Bp - 1) * p.ldo + er0[tt]));
+          e_h[tt][t] = gld(reinterpret_cast<const f32x4*>(p.out + (int64_t)min(t * 16 + m, p.Bp - 1) * p.ldo + rc));
       }
     }
     if (EPI == EPI_QKV) {
-      const int qrows = p.Hq * p.dh, krows = p.Hkv * p.dh;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int col = min(t * 16 + m, p.Bp - 1);
         const int pr = e_pos[t] < 0 ? 0 : e_pos[t];
-        e_blk[t] = e_pos[t] >= 0 ? gld(p.bt + (int64_t)col * p.bps + e_pos[t] / KV_BLOCK) : 0;
+        e_blk[t] = gld(p.bt + (int64_t)col * p.bps + pr / KV_BLOCK);  // used only where e_pos >= 0
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
-          e_cs[tt][t] = full[tt] && er0[tt] < qrows + krows
-                            ? gld(reinterpret_cast<const f32x4*>(p.rope + (int64_t)pr * (p.dh / 2) + ((er0[tt] % p.dh) >> 1)))
-                            : f32x4{1.f, 0.f, 1.f, 0.f};
+          e_cs[tt][t] = gld(reinterpret_cast<const f32x4*>(p.rope + (int64_t)pr * (p.dh / 2) +
+                                                             ((min(er0[tt], rows - 4) % p.dh) >> 1)));
       }
     }
   };
@@ -274,45 +299,53 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
   __shared__ float ssq_s[W][GEMM_SSQ_STRIDE];
   constexpr int SPER = (GEMM_SSQ_MAX + W - 1) / W;
   {
-    constexpr int B1 = XBUFS == 2 ? 1 : 0;
-    u32x4 wa[TPW][NGRP][NQ], wb[TPW][NGRP][NQ], xr[XL];
+    // weight chunks in flight: chunk c + D - 1 is requested before chunk c is multiplied
+    constexpr int D = gemm_depth(TPW);
+    u32x4 wr[D][TPW][NGRP][NQ], xr[XL];
     const int scol = tid % GEMM_SSQ_STRIDE, spart = tid / GEMM_SSQ_STRIDE;
     float sv[SPER];
-    if (p.ssq_n > 0) {
-      const float* sp = p.ssq_in + min(scol, p.Bp - 1);
+    {
+      const float* sp = p.ssq_n > 0 ? p.ssq_in + min(scol, p.Bp - 1) : fdummy;
+      const int last = p.ssq_n > 0 ? p.ssq_n - 1 : 0;
 #pragma unroll
-      for (int j = 0; j < SPER; ++j) sv[j] = gld(sp + (size_t)min(spart + j * W, p.ssq_n - 1) * GEMM_SSQ_STRIDE);
+      for (int j = 0; j < SPER; ++j) sv[j] = gld(sp + (size_t)min(spart + j * W, last) * GEMM_SSQ_STRIDE);
     }
+    pos_prefetch();
     load_x(c0, xr);
-    load_w(c0, wa);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j + 1 < D; ++j) load_w(c0 + j, wr[j]);
+    __builtin_amdgcn_sched_barrier(0);
     epi_prefetch();
+    __builtin_amdgcn_sched_barrier(0);
     if (p.ssq_n > 0) {
       float ss = 0.f;
 #pragma unroll
       for (int j = 0; j < SPER; ++j) ss += spart + j * W < p.ssq_n ? sv[j] : 0.f;
       ssq_s[spart][scol] = ss;
     }
-    store_x(0, xr);
+    store_x(0, c0, xr);
     __syncthreads();
-    for (int c = c0; c < c1; c += 2) {
-      if (c + 1 < c1) {
-        load_x(c + 1, xr);
-        load_w(c + 1, wb);
+    // chunk c = c0 + D i + j sits in weight buffer j and in x buffer (c - c0) % XBUFS.  The
+    // x of chunk c + 1 is requested before the weights of chunk c + D - 1, so that storing
+    // it to LDS (which waits for it) does not wait for those weights.
+    for (int c = c0; c < c1; c += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int cc = c + j;
+        if (cc >= c1) break;
+        // the order of the loads (and that they precede the products) is kept by
+        // scheduling barriers: the compiler would otherwise sink them past the products
+        load_x(cc + 1, xr);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(cc + D - 1, wr[(j + D - 1) % D]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_chunk(XBUFS == 2 ? (cc - c0) & 1 : 0, wr[j]);
+        if (cc + 1 >= c1) break;
+        if (XBUFS == 1) __syncthreads();
+        store_x(XBUFS == 2 ? (cc + 1 - c0) & 1 : 0, cc + 1, xr);
+        __syncthreads();
       }
-      mma_chunk(0, wa);
-      if (c + 1 >= c1) break;
-      if (XBUFS == 1) __syncthreads();
-      store_x(B1, xr);
-      __syncthreads();
-      if (c + 2 < c1) {
-        load_x(c + 2, xr);
-        load_w(c + 2, wa);
-      }
-      mma_chunk(B1, wb);
-      if (c + 2 >= c1) break;
-      if (XBUFS == 1) __syncthreads();
-      store_x(0, xr);
-      __syncthreads();
     }
   }
 
@@ -385,8 +418,8 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
         for (int j = 0; j < 4; ++j) {
           const int r = r0 + j;
           if (r >= rows) break;
-          const float sg = full[tt] ? e_sc[tt][j] : p.scale ? gld(p.scale + r) : 1.f;
-          const float su = full[tt] ? e_su[tt][j] : p.scale ? gld(p.scale + p.d_ff + r) : 1.f;
+          const float sg = !p.scale ? 1.f : full[tt] ? e_sc[tt][j] : gld(p.scale + r);
+          const float su = !p.scale ? 1.f : full[tt] ? e_su[tt][j] : gld(p.scale + p.d_ff + r);
           gst(o + r, f32_to_bf16(silu_f(acc[tt][t][j] * sg) * (up[j] * su)));
         }
         continue;
@@ -398,7 +431,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
           const int qrows = p.Hq * p.dh, krows = p.Hkv * p.dh, dh = p.dh;
           float y[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = acc[tt][t][j] * e_sc[tt][j];
+          for (int j = 0; j < 4; ++j) y[j] = acc[tt][t][j] * (p.scale ? e_sc[tt][j] : 1.f);
           if (r0 < qrows + krows) {  // q or k: rotate the adjacent pairs
             const f32x4 cs = e_cs[tt][t];
             const float a0 = y[0] * cs.x - y[1] * cs.y, a1 = y[0] * cs.y + y[1] * cs.x;
@@ -439,7 +472,7 @@ __global__ __launch_bounds__(WAVE * W) void k_gemm_lds(MatmulParams p, int ks_n)
         for (int j = 0; j < 4; ++j) {
           const int r = r0 + j;
           if (r >= rows) break;
-          const float y = acc[tt][t][j] * (full[tt] ? e_sc[tt][j] : p.scale ? gld(p.scale + r) : 1.f);
+          const float y = acc[tt][t][j] * (!p.scale ? 1.f : full[tt] ? e_sc[tt][j] : gld(p.scale + r));
           if (EPI == EPI_RESID) {
             const float hn = (full[tt] ? e_h[tt][t][j] : gld(o + r)) + y;
             gst(o + r, hn);
