@@ -247,10 +247,12 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
       o[t] *= alpha;
-      // V^T[dim 16 t + m][positions 4 g .. 4 g + 3] from the tile
-      bf16x4 va;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) va[j] = *reinterpret_cast<const __bf16*>(vt + (4 * g + j) * TR + (16 * t + m) * 2);
+      // V^T[dim 16 t + m][positions 4 g .. 4 g + 3] from the tile by one transposing LDS
+      // read (ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i % 4
+      // of the 4 elements that lane 4 j + i / 4 points at, j = 0..3): lane 16 g + i
+      // points at position row 4 g + i / 4, dims 16 t + 4 (i % 4) .. + 3
+      const uint8_t* src = vt + (4 * g + m / 4) * TR + (16 * t + 4 * (m % 4)) * 2;
+      const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)src);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, o[t], 0, 0, 0);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, o[t], 0, 0, 0);
     }
