@@ -141,8 +141,12 @@ class Leg:
         self.pool = synth.empty_kv_pool(cfg, nb, device="cuda", canary=False)
         synth.fill_context_kv(cfg, self.pool, self.bt, self.lens0, seed=seed)
         self.ids = synth.make_token_ids(cfg, steps + 8, B, seed=seed)
-        self.d = dec.Decoder(cfg, weights, num_blocks=nb, max_batch=max(max_batch, dec.ladder_bucket(B)),
-                             max_seq_len=self.max_seq, kv_pool=self.pool, flags=flags)
+        # the decoder's stream: a stream of its own, so that its launches can be captured
+        self.stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            self.d = dec.Decoder(cfg, weights, num_blocks=nb, max_batch=max(max_batch, dec.ladder_bucket(B)),
+                                 max_seq_len=self.max_seq, kv_pool=self.pool, flags=flags)
         self.shape = perfmodel.Shape.of(cfg)
         torch.cuda.synchronize()
 
@@ -159,12 +163,12 @@ class Leg:
         evs = None
         if per_step:
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(self.steps + 1)]
-            evs[0].record()
+            evs[0].record(self.stream)
         t0 = time.perf_counter()
         for t in range(self.steps):
             d.step(self.ids[t], self.lens0 + t, self.bt)
             if per_step:
-                evs[t + 1].record()
+                evs[t + 1].record(self.stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         steps_s = [evs[t].elapsed_time(evs[t + 1]) / 1e3 for t in range(self.steps)] if per_step else None
@@ -198,25 +202,32 @@ class Leg:
         return res
 
     def gate_up_kernel(self) -> dict:
-        """The gate+up kernel alone: one launch per layer back to back (distinct weights
-        each launch, so none is served from a cache), timed with events on the
-        library's stream (the torch stream the decoder was created on) around all L
-        launches; the average includes the short gaps between launches."""
+        """The gate+up kernel alone: one launch per layer (distinct weights each launch,
+        so none is served from a cache), the L launches captured into a graph on the
+        decoder's stream -- as the step runs them -- and the graph's replays timed with
+        events on that stream (three, after one warm-up replay); the average includes
+        the graph's short gaps between kernels."""
         import torch
 
         from memory_bound_transformer_decode_amd import dec
 
         L = self.cfg.n_layers
-        durs = []
-        for rep in range(4):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
             for l in range(L):
                 self.d.launch_matmul(dec.MAT_GATE_UP, l)
-            e1.record()
-            torch.cuda.synchronize()
-            if rep > 0:
-                durs.append(e0.elapsed_time(e1) / 1e3 / L)
+        durs = []
+        with torch.cuda.stream(self.stream):
+            for rep in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(self.stream)
+                g.replay()
+                e1.record(self.stream)
+                torch.cuda.synchronize()
+                if rep > 0:
+                    durs.append(e0.elapsed_time(e1) / 1e3 / L)
+        del g
         avg = float(np.mean(durs))
         mfma = bool(self.d.info().used_mfma)
         nbytes = gate_up_bytes(self.cfg, self.B, mfma)

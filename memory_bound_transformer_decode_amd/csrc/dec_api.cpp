@@ -247,13 +247,13 @@ int hip_fail(dec_ctx* c, hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(ctx, e_, what); \
   } while (0)
 
-// Buckets from 8 rows (bf16 weights) or 4 rows (one-byte weights) up run the products on
-// the matrix cores (unless DEC_FLAG_NO_MFMA); smaller ones run the matrix-vector
-// kernels.  Measured on the 8B and 32B shapes: the vector kernels' activation reads from
-// LDS (Bp per weight vector) and, for E4M3, the widening of every weight once per batch
-// row make them slower than the MFMA tiles from these batches on; the MFMA tiles pad the
-// batch to 16 columns at no extra HBM traffic.
-constexpr int MFMA_MIN_BATCH_BF16 = 8;
+// Buckets from 4 rows up run the products on the matrix cores (unless
+// DEC_FLAG_NO_MFMA); smaller ones run the matrix-vector kernels.  Measured on the 8B and
+// 32B shapes: the vector kernels' activation reads from LDS (Bp per weight vector) and,
+// for one-byte codes, the widening of every weight once per batch row make them slower
+// than the MFMA tiles from 4 rows on (8B bf16, batch 4: 3.73 against 4.09 ms per step);
+// the MFMA tiles pad the batch to 16 columns at no extra HBM traffic.
+constexpr int MFMA_MIN_BATCH_BF16 = 4;
 constexpr int MFMA_MIN_BATCH_BYTE = 4;
 bool use_mfma(const dec_config& g, int Bp) {
   return !(g.flags & DEC_FLAG_NO_MFMA) &&

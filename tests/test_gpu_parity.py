@@ -40,9 +40,9 @@ def bucket(B):
 
 
 def uses_mfma(cfg, B, flags=0):
-    """Whether the library runs the products on MFMA tiles: from the bucket of 8 rows
-    with bf16 weights, of 4 with one-byte weights, unless FLAG_NO_MFMA."""
-    return not flags & FLAG_NO_MFMA and bucket(B) >= (8 if cfg.weight_dtype == "bf16" else 4)
+    """Whether the library runs the products on MFMA tiles: from the bucket of 4 rows,
+    unless FLAG_NO_MFMA."""
+    return not flags & FLAG_NO_MFMA and bucket(B) >= 4
 
 
 def kernels_per_step(cfg, B, flags=0):
