@@ -20,7 +20,8 @@ read over every position plus the new tokens' K/V, and the fp32 logits.
 
 Further legs on the same line (each a dict; `--legs none` skips them):
   batch32      the 8B model at batch 32 (the metric's second batch size)
-  plans        8B batch 1: eager launches and the unfused plan (graph and eager)
+  plans        8B batch 1: eager launches, attention and O as separate launches, and
+               the unfused plan (graph and eager)
   workloads    1B batch 1 (graph and eager: the launch-bound regime), 32B and 70B
                at batch 1, 70B at batch 64, the 8B model with int8 weights; each
                with its dominant kernel's roofline
@@ -408,7 +409,9 @@ def main() -> int:
     plans = None
     if "plans" in legs:
         plans = {"multi_kernel_graph": summary(main_res)}
-        for name, flags in (("multi_kernel_eager", dec.FLAG_EAGER), ("unfused_graph", dec.FLAG_UNFUSED),
+        for name, flags in (("multi_kernel_eager", dec.FLAG_EAGER),
+                            ("separate_attention_o_graph", dec.FLAG_NO_ATTN_O),
+                            ("unfused_graph", dec.FLAG_UNFUSED),
                             ("unfused_eager", dec.FLAG_UNFUSED | dec.FLAG_EAGER)):
             plans[name] = summary(main_leg.measure(flags, args.warmup, 2))
         main_leg.d.set_flags(0)

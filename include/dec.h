@@ -79,7 +79,8 @@ enum {
                                 KV write, attention as scores -> softmax -> P V with the scores in
                                 HBM, SiLU x mul and residual adds as kernels of their own */
   DEC_FLAG_NO_MFMA = 4u,     /* matrix-vector kernels and vector attention at every batch size (no MFMA) */
-  DEC_FLAG_CAPTURE_ALL = 8u  /* capture every batch bucket at the first step instead of lazily */
+  DEC_FLAG_CAPTURE_ALL = 8u, /* capture every batch bucket at the first step instead of lazily */
+  DEC_FLAG_NO_ATTN_O = 16u   /* attention and the O projection as separate launches at batch 1 */
 };
 
 /* Bits of dec_get_info's path_flags: how the last call ran. */
@@ -88,7 +89,8 @@ enum {
   DEC_PATH_MFMA_PRODUCTS = 2,   /* the matrix products ran on MFMA tiles (else matrix-vector kernels) */
   DEC_PATH_MFMA_ATTENTION = 4,  /* attention's arithmetic ran on MFMA */
   DEC_PATH_FOLDED_NORM = 8,     /* RMSNorm folded into the MFMA products (no norm kernels) */
-  DEC_PATH_UNFUSED = 16         /* the unfused plan (DEC_FLAG_UNFUSED) */
+  DEC_PATH_UNFUSED = 16,        /* the unfused plan (DEC_FLAG_UNFUSED) */
+  DEC_PATH_ATTN_O = 32          /* attention and the O projection ran as one launch per layer */
 };
 
 typedef struct dec_config {
@@ -234,9 +236,24 @@ int dec_verify(dec_ctx* ctx, const dec_verify_args* args);
  * enqueueing every chunk. */
 int dec_prefill(dec_ctx* ctx, const dec_prefill_args* args, int32_t* logits_row);
 
-/* Change DEC_FLAG_EAGER / DEC_FLAG_UNFUSED / DEC_FLAG_NO_MFMA between steps
- * (captured graphs of the other mode are kept). */
+/* Change DEC_FLAG_EAGER / DEC_FLAG_UNFUSED / DEC_FLAG_NO_MFMA / DEC_FLAG_NO_ATTN_O
+ * between steps (captured graphs of the other mode are kept). */
 int dec_set_flags(dec_ctx* ctx, uint32_t flags);
+
+/* Wait for the context's stream, then report whether every device-side wait of the
+ * calls so far ended normally.  At batch 1, attention and the O projection run as one
+ * launch (DEC_PATH_ATTN_O; "Kernels, Fusion & CUDA Graphs", Fix 1, the fused-kernel
+ * table) whose O work groups wait on a device counter for attention's output; that wait
+ * is bounded, and one that gives up sets a device flag instead of hanging: the launch
+ * ends with wrong values.  Returns DEC_OK, or DEC_E_HIP when a wait gave up (the
+ * context is then failed: destroy it) or the stream reported an error. */
+int dec_check(dec_ctx* ctx);
+
+/* Polls a device-side wait makes before it gives up (default 32768, each about a
+ * memory round trip: tens of milliseconds; 0 gives up at once).  For exercising the
+ * failure path of dec_check; captured graphs are dropped (they hold the limit).
+ * DEC_E_INVALID for a NULL ctx or a negative limit. */
+int dec_set_wait_limit(dec_ctx* ctx, int32_t polls);
 
 /* Matrix kernels of the step, for dec_launch_matmul. */
 typedef enum {

@@ -293,11 +293,12 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
 
 // One work group computes one (split, kv head c, sequence b) unit of attention.  With
 // one split it writes o; otherwise it writes its partial, and the last split of the
-// group to arrive combines.  o is written device-coherently.
+// group to arrive combines.  o is written device-coherently.  Returns, in every thread,
+// whether this work group wrote the group's o.
 // MF: the wave's blocks in the MFMA form (attn_wave_mfma), with the wave's V tile at
 // vtile + wave 16 attn_vt_row<DH>() bytes of LDS.
 template <int DH, bool FP8, int G, int NW, bool MF = false>
-__device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c, int b, AttnSmem<DH, G, NW>& S,
+__device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c, int b, AttnSmem<DH, G, NW>& S,
                                           uint8_t* vtile = nullptr) {
   constexpr int EPL = 8;             // cache elements per lane per row
   constexpr int LPP = DH / EPL;      // lanes per position row
@@ -429,10 +430,10 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
     cst(p.part_o + row * DH + e, O);
     if (e == 0) cst_f2(p.part_ml + row * 2, M, L);
   }
-  if (single) return;
+  if (single) return true;
 
   // arrival: the partial stores of every wave complete before this work group counts
-  if (!arrive_after_stores(p.cnt + (int64_t)b * p.Hkv + c, (unsigned)p.n_split, &S.last)) return;
+  if (!arrive_after_stores(p.cnt + (int64_t)b * p.Hkv + c, (unsigned)p.n_split, &S.last)) return false;
 
   // combine the n_split partials of the group's G heads.  The partial max and sum of
   // (head, split) pair threadIdx.x are loaded first; with at most ATTN_COMBINE_PRE
@@ -502,6 +503,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams& p, int split, int c,
     }
     cst(p.o + ((int64_t)b * p.Hq + c * G + h) * DH + e, f32_to_bf16(out));
   }
+  return true;
 }
 
 }  // namespace dec

@@ -271,6 +271,17 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Sum over the wave, the same value in every lane: 16-lane row sums by DPP, then the four
+// row sums read into scalar registers and added in a fixed order.
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v = group_sum<16>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

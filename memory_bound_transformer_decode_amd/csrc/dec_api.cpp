@@ -47,15 +47,22 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int LADDER[] = {1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64};
 constexpr int N_BUCKETS = sizeof(LADDER) / sizeof(LADDER[0]);
-constexpr uint32_t KNOWN_FLAGS = DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL;
-// Plans: the flags that change the kernels (UNFUSED, NO_MFMA) and whether the LM head
-// runs (prefill chunks before the last skip it).
+constexpr uint32_t KNOWN_FLAGS =
+    DEC_FLAG_EAGER | DEC_FLAG_UNFUSED | DEC_FLAG_NO_MFMA | DEC_FLAG_CAPTURE_ALL | DEC_FLAG_NO_ATTN_O;
+// Plans: the flags that change the kernels (UNFUSED, NO_MFMA, NO_ATTN_O) and whether the
+// LM head runs (prefill chunks before the last skip it).
 constexpr int MODE_SKIP_LM = 4;
-constexpr int N_MODES = 8;
+constexpr int MODE_NO_ATTN_O = 8;
+constexpr int N_MODES = 16;
 constexpr int MAX_VERIFY_K = 8;
+// Polls before a fused attention + O launch's wait gives up (each poll is a memory round
+// trip of about a microsecond plus a short sleep: tens of milliseconds, against
+// microseconds for the attention it waits for).
+constexpr int ATTN_O_SPIN = 1 << 15;
 
 int mode_of(uint32_t flags, bool skip_lm) {
-  return ((flags & DEC_FLAG_UNFUSED) ? 1 : 0) | ((flags & DEC_FLAG_NO_MFMA) ? 2 : 0) | (skip_lm ? MODE_SKIP_LM : 0);
+  return ((flags & DEC_FLAG_UNFUSED) ? 1 : 0) | ((flags & DEC_FLAG_NO_MFMA) ? 2 : 0) | (skip_lm ? MODE_SKIP_LM : 0) |
+         ((flags & DEC_FLAG_NO_ATTN_O) ? MODE_NO_ATTN_O : 0);
 }
 
 int bucket_index(int n) {
@@ -78,6 +85,7 @@ struct Layout {
   size_t uf;                           // unfused step: fp32 product rows [MB][max(N)]
   size_t us;                           // unfused step: attention scores [MB][Hq][max_seq_len]
   size_t attn_cnt;                     // attention split arrival counters
+  size_t attn_o_cnt, attn_o_abort;     // fused attention + O launches: a done counter per layer; abort flag
   size_t ssq;                          // folded RMSNorm: row-block sums of squares
   size_t gpart, gcnt;                  // MFMA products split over K: partial tiles, row-block counters
   size_t gpart_floats, gcnt_n;
@@ -151,6 +159,10 @@ Layout layout_of(const dec_config& c) {
   off = align256(off + part_floats * 4);
   L.attn_cnt = off;
   off = align256(off + MB * c.n_kv_heads * 4);
+  L.attn_o_cnt = off;  // one 256-byte line per layer (every O work group polls it)
+  off = align256(off + (size_t)c.n_layers * 256);
+  L.attn_o_abort = off;
+  off = align256(off + 4);
   L.ssq = off;
   off = align256(off + (size_t)dec::GEMM_SSQ_MAX * dec::GEMM_SSQ_STRIDE * 4);
   L.gcnt = off;
@@ -213,6 +225,7 @@ struct dec_ctx {
   bool loaded = false;
   bool failed = false;
   int last_n = 0;  // rows with logits after the last call (0: none yet)
+  int wait_limit = ATTN_O_SPIN;  // polls of a device-side wait before it gives up
   // weights
   dec_mat embed{}, lm{};
   std::vector<dec_mat> qkv, o, gu, down;
@@ -393,6 +406,18 @@ void set_fold_norm(dec_ctx* c, int which, int l, int Bp, dec::MatmulParams& p) {
 // arithmetic sits on each wave's chain of blocks.
 bool attn_mfma(const dec_config& g) { return !(g.flags & DEC_FLAG_NO_MFMA); }
 
+int device_cus() {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      v = 256;
+    n_cu = v > 0 ? v : 256;
+  }
+  return n_cu;
+}
+
+
 // norm_gain: when set, the kernel computes x = RMSNorm(h) norm_gain itself (fused_norm)
 hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const float* norm_gain = nullptr) {
   const dec_config& g = c->cfg;
@@ -411,6 +436,17 @@ hipError_t run_matmul(dec_ctx* c, int which, int l, int Bp, hipStream_t s, const
 // ([Bp][d] bf16 in two parts for QKV must fit in 128 KB)
 bool fused_norm(const dec_config& g, int Bp) {
   return !use_mfma(g, Bp) && Bp <= 8 && (size_t)Bp * g.d_model * 4 <= 128 * 1024;
+}
+
+// Rows of W_o per wave of the fused attention + O launch (attn_o.hip), or 0 where the two
+// run as separate launches: a single sequence on the matrix-vector kernels, MFMA
+// attention, and O work groups that fit beside attention's on the chip.
+int attn_o_rows(const dec_config& g, int Bp) {
+  if (Bp != 1 || g.n_layers == 0 || use_mfma(g, Bp) || !attn_mfma(g) || !fused_norm(g, Bp) ||
+      (g.flags & (DEC_FLAG_UNFUSED | DEC_FLAG_NO_ATTN_O)) || !dec::attn_o_supported(g.n_q_heads, g.n_kv_heads, g.d_head))
+    return 0;
+  const int n_attn = dec::attn_splits(attn_shape(g), Bp) * g.n_kv_heads * Bp;
+  return dec::attn_o_rows_per_wave(n_attn, g.d_model, g.n_q_heads * g.d_head, wfmt_of(g.weight_dtype), device_cus());
 }
 
 dec::AttnParams attn_params(dec_ctx* c, int Bp, int layer) {
@@ -538,7 +574,15 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
     np.x_lo = on && !mfma ? xl : nullptr;
   };
   qkv_input(g.n_layers > 0);
+  // the fused attention + O launches' done counters start the step at zero
+  const int ao_rows = attn_o_rows(g, Bp);
+  if (ao_rows > 0) {
+    np.zero = ws_ptr<unsigned>(c, c->L.attn_o_cnt);
+    np.n_zero = g.n_layers * 64;
+  }
   if ((e = dec::launch_embed_norm(np, wq, s)) != hipSuccess) return e;
+  np.zero = nullptr;
+  np.n_zero = 0;
 
   // no RMSNorm kernels: the matrix-vector kernels normalize their own input (fn), or the
   // MFMA products fold the norms
@@ -552,9 +596,23 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
       if ((e = dec::launch_rmsnorm(np, s)) != hipSuccess) return e;
     }
     if ((e = run_matmul(c, DEC_MAT_QKV, l, Bp, s, fn ? an : nullptr)) != hipSuccess) return e;
-    // attention over positions 0..p
-    if ((e = dec::launch_attention(attn_params(c, Bp, l), kvfp8, s)) != hipSuccess) return e;
-    if ((e = run_matmul(c, DEC_MAT_O, l, Bp, s)) != hipSuccess) return e;
+    // attention over positions 0..p, then h += W_o o
+    if (ao_rows > 0) {
+      dec::AttnOParams P{};
+      P.a = attn_params(c, Bp, l);
+      int epi = 0;
+      P.m = matmul_params(c, DEC_MAT_O, l, Bp, &epi);
+      P.done = ws_ptr<unsigned>(c, c->L.attn_o_cnt) + (size_t)l * 64;
+      P.need = (unsigned)(P.a.Hkv * Bp);
+      P.abort = ws_ptr<int>(c, c->L.attn_o_abort);
+      P.spin = c->wait_limit;
+      P.n_attn = P.a.n_split * P.a.Hkv * Bp;
+      P.rows = ao_rows;
+      if ((e = dec::launch_attn_o(P, wq, kvfp8, s)) != hipSuccess) return e;
+    } else {
+      if ((e = dec::launch_attention(attn_params(c, Bp, l), kvfp8, s)) != hipSuccess) return e;
+      if ((e = run_matmul(c, DEC_MAT_O, l, Bp, s)) != hipSuccess) return e;
+    }
     // x = RMSNorm(h) g_mlp
     const float* mn = c->mlp_norm + (size_t)l * d;
     if (nk) {
@@ -588,10 +646,12 @@ int kernels_of_plan(const dec_config& g, int Bp, bool skip_lm) {
     if (!skip_lm) n += (L > 0 ? 1 : 0) + slices;
     return n;
   }
-  // per layer: QKV, attention, O, gate+up, down, and two RMSNorm kernels unless the
-  // matrix-vector kernels fuse them or the MFMA products fold them
+  // per layer: QKV, attention, O (one launch with attention at batch 1 where it fits),
+  // gate+up, down, and two RMSNorm kernels unless the matrix-vector kernels fuse them or
+  // the MFMA products fold them
   const bool norms = !fused_norm(g, Bp) && !fold_norm(g, Bp);
-  int n = 1 + (5 + (norms ? 2 : 0) + 4 * (slices - 1)) * L - (norms && L > 0 ? 1 : 0);
+  const int per_layer = (attn_o_rows(g, Bp) > 0 ? 4 : 5) + (norms ? 2 : 0) + 4 * (slices - 1);
+  int n = 1 + per_layer * L - (norms && L > 0 ? 1 : 0);
   if (!skip_lm) n += slices + (norms && L > 0 ? 1 : 0);
   return n;
 }
@@ -823,6 +883,31 @@ int dec_set_flags(dec_ctx* c, uint32_t flags) {
   return DEC_OK;
 }
 
+int dec_check(dec_ctx* c) {
+  if (!c) return fail(DEC_E_INVALID, "ctx is NULL");
+  if (c->failed) return fail(DEC_E_STATE, "context has failed; destroy it");
+  HIPCHK(c, hipStreamSynchronize(c->stream), "hipStreamSynchronize");
+  int gave_up = 0;
+  HIPCHK(c, hipMemcpy(&gave_up, c->ws + c->L.attn_o_abort, sizeof gave_up, hipMemcpyDeviceToHost),
+         "reading the device wait flag");
+  if (gave_up) {
+    c->failed = true;
+    return fail(DEC_E_HIP,
+                "a fused attention + O launch gave up waiting for attention's output after %d polls; "
+                "its results are wrong",
+                c->wait_limit);
+  }
+  return DEC_OK;
+}
+
+int dec_set_wait_limit(dec_ctx* c, int32_t polls) {
+  if (!c) return fail(DEC_E_INVALID, "ctx is NULL");
+  if (polls < 0) return fail(DEC_E_INVALID, "the wait limit must be >= 0 (got %d)", polls);
+  c->wait_limit = polls;
+  drop_graphs(c);
+  return DEC_OK;
+}
+
 int dec_step(dec_ctx* c, const dec_step_args* a) {
   if (!c || !a) return fail(DEC_E_INVALID, "ctx or args is NULL");
   int rc = check_ready(c);
@@ -985,6 +1070,7 @@ int dec_get_info(const dec_ctx* c, int32_t* kernels_per_step, int32_t* path_flag
   if (i.bucket > 0 && !(i.flags & DEC_FLAG_NO_MFMA)) f |= DEC_PATH_MFMA_ATTENTION;
   if (i.flags & DEC_FLAG_UNFUSED) f |= DEC_PATH_UNFUSED;
   else if (i.bucket > 0 && fold_norm(c->cfg, i.bucket)) f |= DEC_PATH_FOLDED_NORM;
+  if (i.bucket > 0 && attn_o_rows(c->cfg, i.bucket) > 0) f |= DEC_PATH_ATTN_O;
   *path_flags = f;
   return DEC_OK;
 }

@@ -117,6 +117,8 @@ struct NormParams {
   float eps;
   // embedding
   const void* E; const float* E_scale; const int32_t* ids;
+  unsigned* zero;       // embedding kernel: n_zero counters set to zero (the step's first kernel)
+  int n_zero;
 };
 
 // h = E[ids[b]] (dequantized), x = RMSNorm(h) g
@@ -158,6 +160,29 @@ AttnScratch attn_scratch(const AttnShape& s, int Bp);
 hipError_t launch_attention(const AttnParams& p, bool kv_fp8, hipStream_t s);
 // zero n 32-bit counters with a kernel (safe inside a captured graph)
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t s);
+
+// Attention and the O projection of one layer in one launch (a single sequence on the
+// matrix-vector path, attn_o.hip): attention's n_attn work groups first, then work
+// groups that hold `rows` rows of W_o per wave in registers and wait for attention.
+constexpr int ATTN_O_RMAX = 3;  // rows of W_o per wave
+constexpr int ATTN_O_VMAX = 8;  // 16-byte vectors of a row per lane
+struct AttnOParams {
+  AttnParams a;       // Bp = 1, MFMA form
+  MatmulParams m;     // the O product: x = a.o, out = h (EPI_RESID), Bp = 1
+  unsigned* done;     // (sequence, kv head) groups whose output is written; zero at launch
+  unsigned need;      // a.Bp a.Hkv
+  int* abort;         // set by a wait that gave up (the launch's values are then wrong)
+  int spin;           // polls before a wait gives up
+  int n_attn;         // attention work groups: a.n_split a.Hkv a.Bp
+  int rows;           // rows of W_o per wave, 1 .. ATTN_O_RMAX
+};
+// Rows per wave that let every O work group be resident beside the attention work groups
+// (one work group per CU), or 0 when the shape does not fit the fused launch.
+int attn_o_rows_per_wave(int n_attn, int N, int K, WFmt wq, int n_cu);
+// The head shapes the fused launch is built for (d_head 64 or 128, 4, 5 or 8 query heads
+// per kv head).
+bool attn_o_supported(int Hq, int Hkv, int dh);
+hipError_t launch_attn_o(const AttnOParams& p, WFmt wq, bool kv_fp8, hipStream_t s);
 
 // The unfused form for the unfused step (measurement only): scores S = q K^T / sqrt(dh)
 // written to HBM (scores [Bp][Hq][ld_s] fp32, ld_s >= the longest context), a softmax

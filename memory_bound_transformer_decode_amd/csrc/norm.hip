@@ -16,6 +16,8 @@ template <bool EMBED, int WQ, int NV>
 __global__ __launch_bounds__(256) void k_norm(NormParams p) {
   __shared__ float red[4];
   const int b = blockIdx.x, tid = threadIdx.x;
+  if (EMBED && b == 0)
+    for (int i = tid; i < p.n_zero; i += 256) cst(p.zero + i, 0u);
   const int d = p.d;  // a multiple of 16
   const float* hrow = p.h + (int64_t)b * d;
   float* hout = p.h_out ? p.h_out + (int64_t)b * d : nullptr;

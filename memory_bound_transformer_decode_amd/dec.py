@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdec.so")
 
 DEC_OK, DEC_E_INVALID, DEC_E_STATE, DEC_E_CAPACITY, DEC_E_UNSUPPORTED, DEC_E_HIP = 0, -1, -2, -3, -4, -5
 DEC_BF16, DEC_FP8_E4M3, DEC_INT8 = 0, 1, 2
-FLAG_EAGER, FLAG_UNFUSED, FLAG_NO_MFMA, FLAG_CAPTURE_ALL = 1, 2, 4, 8
-PATH_GRAPH, PATH_MFMA_PRODUCTS, PATH_MFMA_ATTENTION, PATH_FOLDED_NORM, PATH_UNFUSED = 1, 2, 4, 8, 16
+FLAG_EAGER, FLAG_UNFUSED, FLAG_NO_MFMA, FLAG_CAPTURE_ALL, FLAG_NO_ATTN_O = 1, 2, 4, 8, 16
+PATH_GRAPH, PATH_MFMA_PRODUCTS, PATH_MFMA_ATTENTION, PATH_FOLDED_NORM, PATH_UNFUSED, PATH_ATTN_O = 1, 2, 4, 8, 16, 32
 LADDER = (1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64)
 BLOCK = 16
 
@@ -79,8 +79,8 @@ class DecError(RuntimeError):
 
 
 EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_load_weights", "dec_step", "dec_verify",
-           "dec_prefill", "dec_set_flags", "dec_get_info", "dec_get_step_info", "dec_destroy",
-           "dec_last_error", "dec_bw_probe", "dec_launch_matmul", "dec_sample_greedy", "dec_sample",
+           "dec_prefill", "dec_set_flags", "dec_check", "dec_set_wait_limit", "dec_get_info",
+           "dec_get_step_info", "dec_destroy", "dec_last_error", "dec_bw_probe", "dec_launch_matmul", "dec_sample_greedy", "dec_sample",
            "dec_attention_workspace_bytes", "dec_attention", "dec_attention_noalloc")
 MAT_QKV, MAT_O, MAT_GATE_UP, MAT_DOWN, MAT_LM_HEAD = 0, 1, 2, 3, 4
 
@@ -112,6 +112,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dec_prefill.restype = c_int
     lib.dec_set_flags.argtypes = [c_void_p, c_uint32]
     lib.dec_set_flags.restype = c_int
+    lib.dec_check.argtypes = [c_void_p]
+    lib.dec_check.restype = c_int
+    lib.dec_set_wait_limit.argtypes = [c_void_p, c_int32]
+    lib.dec_set_wait_limit.restype = c_int
     lib.dec_get_info.argtypes = [c_void_p, POINTER(c_int32), POINTER(c_int32)]
     lib.dec_get_info.restype = c_int
     lib.dec_get_step_info.argtypes = [c_void_p, POINTER(DecInfo)]
@@ -295,6 +299,13 @@ class Decoder:
 
     def set_flags(self, flags: int) -> None:
         _check(self.lib.dec_set_flags(self.ctx, flags))
+
+    def check(self) -> None:
+        """dec_check: wait for the stream; raise if a device-side wait gave up."""
+        _check(self.lib.dec_check(self.ctx))
+
+    def set_wait_limit(self, polls: int) -> None:
+        _check(self.lib.dec_set_wait_limit(self.ctx, polls))
 
     def info(self) -> DecInfo:
         out = DecInfo()

@@ -212,6 +212,7 @@ def run_parity(case: Case, batch_ids: np.ndarray, *, flags: int = 0, max_batch: 
             compare_kv(d.kv_pool, oc, cfg.kv_dtype, rep, tol, before)
             before = oc.pool.copy()
         lens = lens + 1
+    d.check()  # no device-side wait gave up
     info = d.info()
     d.close()
     log(f"{cfg.name} B={B} steps={steps} flags={flags} "

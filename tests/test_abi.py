@@ -66,7 +66,7 @@ def test_workspace_bytes_valid_and_invalid():
     ("vocab", 1001, -1, b"vocab"),
     ("weight_dtype", 7, -1, b"dtype"),
     ("flags", 1 << 9, -1, b"flag"),
-    ("flags", 16, -1, b"flag"),
+    ("flags", 32, -1, b"flag"),
     ("kv_dtype", 2, -1, b"dtype"),
     ("max_seq_len", 524289, -4, b"max_seq_len"),
     ("rms_eps", 0.0, -1, b"rms_eps"),

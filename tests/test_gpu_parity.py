@@ -50,7 +50,20 @@ def kernels_per_step(cfg, B, flags=0):
     kernels normalize their own input, the MFMA products fold the norms); embedding and
     LM head."""
     assert uses_mfma(cfg, B, flags) or bucket(B) <= 8
-    return 5 * cfg.n_layers + 2
+    return (4 if attn_o_fits(cfg, B, flags) else 5) * cfg.n_layers + 2
+
+
+def attn_o_fits(cfg, B, flags=0):
+    """Whether attention and the O projection run as one launch: one sequence on the
+    matrix-vector kernels with MFMA attention, 4, 5 or 8 query heads per KV head, d_head
+    64 or 128, and O rows of K = Hq d_head elements that a wave covers in 1 to 8 16-byte
+    vectors per lane (the small models here also fit the O work groups on the chip)."""
+    if bucket(B) != 1 or flags & (FLAG_NO_MFMA | 2 | 16) or cfg.n_layers == 0:  # NO_MFMA, UNFUSED, NO_ATTN_O
+        return False
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    epv = 8 if cfg.weight_dtype == "bf16" else 16
+    K = cfg.n_q_heads * cfg.d_head
+    return g in (4, 5, 8) and cfg.d_head in (64, 128) and K % (64 * epv) == 0 and K // (64 * epv) <= 8
 
 
 def fmt(cfg, w, kv):
@@ -381,6 +394,74 @@ def test_unfused_step_matches_fused(dec):
     gf = synth.kv_codes_numpy(pf) != canary
     gu = synth.kv_codes_numpy(pu) != canary
     assert np.array_equal(gf, gu)
+
+
+# ------------------------------------------------------------------ attention + O, one launch
+
+@pytest.mark.parametrize("base,w,kv", [(MINI4_128, "bf16", "bf16"), (MINI128, "fp8", "fp8"),
+                                       (MINI4, "bf16", "fp8"), (MINI4_128, "int8", "bf16")])
+def test_attention_and_o_in_one_launch(dec, base, w, kv):
+    """At batch 1, where the shape fits, attention and the O projection run as one launch
+    (its O work groups wait on a device counter for attention's output): parity with the
+    oracle over several steps with split contexts, the path bit and one kernel less per
+    layer; DEC_FLAG_NO_ATTN_O gives the separate launches, also at parity."""
+    cfg = fmt(base, w, kv)
+    assert attn_o_fits(cfg, 1)
+    case = make_case(cfg, [300], 512, seed=31)
+    ids = synth.make_token_ids(cfg, 3, 1, seed=31)
+    for flags in (0, dec.FLAG_NO_ATTN_O):
+        assert_ok(run_parity(case, ids, flags=flags), cfg)
+        d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=1, max_seq_len=512,
+                        flags=flags, kv_pool=case.pool.clone())
+        d.step(ids[0], case.ctx_lens, case.block_tables)
+        d.check()
+        k, f = d.path()
+        splits = d.info().attn_splits
+        d.close()
+        assert splits > 1  # the combine, and its signal, run
+        assert bool(f & dec.PATH_ATTN_O) == (flags == 0)
+        assert k == kernels_per_step(cfg, 1, flags)
+
+
+def test_attention_and_o_one_launch_graph_equals_eager(dec):
+    """The fused launch is deterministic: graph replay and eager launches give the same bits,
+    and the done counters start every step at zero (several steps in a row)."""
+    cfg = fmt(MINI4_128, "bf16", "bf16")
+    case = make_case(cfg, [200], 512, seed=33)
+    ids = synth.make_token_ids(cfg, 3, 1, seed=33)
+    outs = {}
+    for flags in (dec.FLAG_EAGER, 0):
+        d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=1, max_seq_len=512,
+                        flags=flags, kv_pool=case.pool.clone())
+        outs[flags] = [d.step(ids[t], case.ctx_lens + t, case.block_tables).clone() for t in range(3)]
+        d.check()
+        assert d.path()[1] & dec.PATH_ATTN_O
+        d.close()
+    for ze, zg in zip(outs[dec.FLAG_EAGER], outs[0]):
+        assert torch.equal(ze.view(torch.int32), zg.view(torch.int32))
+
+
+def test_attention_and_o_wait_limit_is_reported(dec):
+    """A device-side wait that gives up (forced from the host with a limit of 0 polls: the
+    O work groups stop waiting at once, every kernel still ends) is reported by dec_check,
+    which then fails the context."""
+    cfg = fmt(MINI4_128, "bf16", "bf16")
+    case = make_case(cfg, [300], 512, seed=34)
+    ids = synth.make_token_ids(cfg, 1, 1, seed=34)[0]
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=1, max_seq_len=512,
+                    kv_pool=case.pool.clone())
+    d.step(ids, case.ctx_lens, case.block_tables)
+    d.check()
+    with pytest.raises(dec.DecError):
+        d.set_wait_limit(-1)
+    d.set_wait_limit(0)
+    d.step(ids, case.ctx_lens, case.block_tables)
+    assert d.path()[1] & dec.PATH_ATTN_O
+    with pytest.raises(dec.DecError, match="gave up"):
+        d.check()
+    with pytest.raises(dec.DecError):
+        d.step(ids, case.ctx_lens, case.block_tables)  # the context has failed
+    d.close()
 
 
 @pytest.mark.parametrize("lens", [[9, 40, 3], [40]])
