@@ -88,14 +88,14 @@ __device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const Q
 #pragma unroll
     for (int off = LPP; off < WAVE; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
     const float mn = fmaxf(m[h], bm);  // finite: the block's first position is valid
-    const float alpha = exp2f(m[h] - mn);
+    const float alpha = exp2_hw(m[h] - mn);
     m[h] = mn;
     l[h] *= alpha;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      sc[ps][h] = exp2f(sc[ps][h] - mn);  // the probability, in place of the score
+      sc[ps][h] = exp2_hw(sc[ps][h] - mn);  // the probability, in place of the score
       l[h] += sc[ps][h];
     }
   }
@@ -232,13 +232,13 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     const float mn = fmaxf(mrun, bm);  // finite: the block's first position is valid
-    const float alpha = exp2f(mrun - mn);
+    const float alpha = exp2_hw(mrun - mn);
     mrun = mn;
     bf16x4 ph, pl;
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float pj = exp2f(sc[j] - mn);
+      const float pj = exp2_hw(sc[j] - mn);
       ps += pj;
       ph[j] = (__bf16)pj;  // the hardware conversion (round to nearest even), two per instruction
       pl[j] = (__bf16)(pj - (float)ph[j]);
@@ -416,7 +416,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c,
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float f = exp2f(sm[w][h] - M);
+        const float f = exp2_hw(sm[w][h] - M);
         O = fmaf(f, so[w][h][e], O);
         L = fmaf(f, sl[w][h], L);
       }
@@ -486,7 +486,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c,
 #pragma unroll
         for (int sp = 0; sp < PRE; ++sp) {
           if (sp < p.n_split) {
-            const float f = exp2f(cm[h][sp] - M);
+            const float f = exp2_hw(cm[h][sp] - M);
             O = fmaf(f, po[i][sp], O);
             L = fmaf(f, cl[h][sp], L);
           }
@@ -494,7 +494,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c,
       } else {
 #pragma unroll 8
         for (int sp = 0; sp < p.n_split; ++sp) {
-          const float f = exp2f(cm[h][sp] - M);
+          const float f = exp2_hw(cm[h][sp] - M);
           O = fmaf(f, cld(p.part_o + (row0 + sp) * DH + e), O);
           L = fmaf(f, cl[h][sp], L);
         }

@@ -271,6 +271,10 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// 2^x by the hardware instruction (v_exp_f32, about 1 ulp): results below 2^-126 flush to
+// zero, which softmax weights (x <= 0) lose nothing by; 2^-inf = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Sum over the wave, the same value in every lane: 16-lane row sums by DPP, then the four
 // row sums read into scalar registers and added in a fixed order.
 __device__ __forceinline__ float wave_sum_rows(float v) {
