@@ -9,9 +9,9 @@
 namespace dec {
 
 
-// most splits whose partial outputs the combine loads ahead of their max and sum
-// (measured: a gain with 3 splits, a loss with 8 or more held in registers)
-constexpr int ATTN_COMBINE_PRE = 4;
+// splits whose partial outputs the combine loads together with every split's max and
+// sum (one round trip for up to this many splits)
+constexpr int ATTN_COMBINE_PRE = 16;
 
 // LDS of one attention work group
 template <int DH, int G, int NW>
@@ -435,40 +435,34 @@ __device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c,
   // arrival: the partial stores of every wave complete before this work group counts
   if (!arrive_after_stores(p.cnt + (int64_t)b * p.Hkv + c, (unsigned)p.n_split, &S.last)) return false;
 
-  // combine the n_split partials of the group's G heads.  The partial max and sum of
-  // (head, split) pair threadIdx.x are loaded first; with at most ATTN_COMBINE_PRE
-  // splits each thread's partial outputs follow at once, before the max and sum reach
-  // LDS, so that their round trip overlaps that of the max and sum.
+  // combine the n_split partials of the group's G heads: thread -> (head h, element e).
+  // One round trip brings the max and sum of every (head, split) pair (into LDS) together
+  // with each thread's partial outputs of the first ATTN_COMBINE_PRE splits (registers);
+  // the partial outputs of further splits follow once the maximum is known.
   constexpr int PRE = ATTN_COMBINE_PRE;
   constexpr int NI = (G * DH + NW * WAVE - 1) / (NW * WAVE);  // outputs per thread
   auto& cm = S.cm;
   auto& cl = S.cl;
   auto& cM = S.cM;
-  const int nml = G * p.n_split;
-  const int64_t row_g = ((int64_t)b * p.Hq + c * G) * p.n_split;  // (head c G, split 0)
-  uint64_t ml0 = 0;
-  if (threadIdx.x < nml) ml0 = cld(reinterpret_cast<const uint64_t*>(p.part_ml + (row_g + threadIdx.x) * 2));
-  const bool pre = p.n_split <= PRE;
+  const int ns = p.n_split;
+  const int64_t row_g = ((int64_t)b * p.Hq + c * G) * ns;  // (head c G, split 0)
   float po[NI][PRE];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int idx = threadIdx.x + i * NW * WAVE;
-    const int64_t row0 = row_g + (int64_t)(idx / DH) * p.n_split;
+    const int idx = min((int)threadIdx.x + i * NW * WAVE, G * DH - 1);  // past the end: a re-read
+    const int64_t row0 = row_g + (int64_t)(idx / DH) * ns;
 #pragma unroll
-    for (int sp = 0; sp < PRE; ++sp)
-      if (pre && idx < G * DH && sp < p.n_split) po[i][sp] = cld(p.part_o + (row0 + sp) * DH + idx % DH);
+    for (int sp = 0; sp < PRE; ++sp) po[i][sp] = cld(p.part_o + (row0 + min(sp, ns - 1)) * DH + idx % DH);
   }
-  for (int idx = threadIdx.x; idx < nml; idx += NW * WAVE) {
-    const int h = idx / p.n_split, sp = idx % p.n_split;
-    const uint64_t ml =
-        idx == (int)threadIdx.x ? ml0 : cld(reinterpret_cast<const uint64_t*>(p.part_ml + (row_g + idx) * 2));
-    cm[h][sp] = __uint_as_float((uint32_t)ml);
-    cl[h][sp] = __uint_as_float((uint32_t)(ml >> 32));
+  for (int t = threadIdx.x; t < G * ns; t += NW * WAVE) {
+    const uint64_t ml = cld(reinterpret_cast<const uint64_t*>(p.part_ml + (row_g + t) * 2));
+    cm[t / ns][t % ns] = __uint_as_float((uint32_t)ml);
+    cl[t / ns][t % ns] = __uint_as_float((uint32_t)(ml >> 32));
   }
   __syncthreads();
   if (threadIdx.x < G) {
     float M = -INFINITY;
-    for (int sp = 0; sp < p.n_split; ++sp) M = fmaxf(M, cm[threadIdx.x][sp]);
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, cm[threadIdx.x][sp]);
     cM[threadIdx.x] = M;
   }
   __syncthreads();
@@ -478,26 +472,22 @@ __device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c,
     if (idx >= G * DH) break;
     const int h = idx / DH, e = idx % DH;
     const float M = cM[h];
-    const int64_t row0 = ((int64_t)b * p.Hq + c * G + h) * p.n_split;
+    const int64_t row0 = row_g + (int64_t)h * ns;
     float out = 0.f;
     if (M != -INFINITY) {
       float O = 0.f, L = 0.f;
-      if (pre) {
 #pragma unroll
-        for (int sp = 0; sp < PRE; ++sp) {
-          if (sp < p.n_split) {
-            const float f = exp2_hw(cm[h][sp] - M);
-            O = fmaf(f, po[i][sp], O);
-            L = fmaf(f, cl[h][sp], L);
-          }
-        }
-      } else {
-#pragma unroll 8
-        for (int sp = 0; sp < p.n_split; ++sp) {
+      for (int sp = 0; sp < PRE; ++sp) {
+        if (sp < ns) {
           const float f = exp2_hw(cm[h][sp] - M);
-          O = fmaf(f, cld(p.part_o + (row0 + sp) * DH + e), O);
+          O = fmaf(f, po[i][sp], O);
           L = fmaf(f, cl[h][sp], L);
         }
+      }
+      for (int sp = PRE; sp < ns; ++sp) {
+        const float f = exp2_hw(cm[h][sp] - M);
+        O = fmaf(f, cld(p.part_o + (row0 + sp) * DH + e), O);
+        L = fmaf(f, cl[h][sp], L);
       }
       out = O / L;
     }
