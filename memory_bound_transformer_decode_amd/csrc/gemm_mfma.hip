@@ -571,8 +571,8 @@ hipError_t go_epi(const MatmulParams& p, const GemmPlan& g, int epi, bool kv_fp8
 
 // Row blocks of GEMM_WAVES tiles and the K split: where the row blocks alone would leave
 // the chip under-filled (fewer than GEMM_TARGET_GROUPS work groups for MI355X's 256
-// CUs), K is split so that about that many work groups run, with at least two chunks
-// each.  A pure function of the shape: the workspace is sized with it.
+// CUs), K is split, at least two chunks per work group and at most one work group per
+// CU.  A pure function of the shape: the workspace is sized with it.
 GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool byte_weights) {
   GemmPlan g{};
   const int NT = (Bp + 15) / 16;
@@ -582,7 +582,10 @@ GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool byte_weights) {
   const int nch = (K + KC - 1) / KC;
   int ks = 1;
   if (g.n_rb < GEMM_TARGET_GROUPS) {
-    ks = (GEMM_TARGET_GROUPS + g.n_rb - 1) / g.n_rb;
+    // as many splits as fit the CUs without a second work group on any of them: a grid
+    // just past a multiple of the CU count doubles the work of some CUs while the others
+    // wait (8B QKV at 32 rows: 3 splits, 288 work groups, measured slower than 2)
+    ks = GEMM_TARGET_GROUPS / g.n_rb;
     const int cap = nch / 2 > 1 ? nch / 2 : 1;
     if (ks > cap) ks = cap;
     if (ks > GEMM_MAX_SPLIT) ks = GEMM_MAX_SPLIT;
