@@ -551,6 +551,15 @@ hipError_t go(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
 
 template <int WQ, int EPI, bool KVFP8>
 hipError_t go_nt(const MatmulParams& p, const GemmPlan& g, hipStream_t s) {
+  if constexpr (EPI == EPI_SILU) {
+    if (g.waves == GEMM_WAVES_WIDE) {
+      if (p.Bp <= 16) return go<1, WQ, EPI, KVFP8, GEMM_WAVES_WIDE>(p, g, s);
+      if (p.Bp <= 32) return go<2, WQ, EPI, KVFP8, GEMM_WAVES_WIDE>(p, g, s);
+      if (p.Bp <= 48) return go<3, WQ, EPI, KVFP8, GEMM_WAVES_WIDE>(p, g, s);
+      return go<4, WQ, EPI, KVFP8, GEMM_WAVES_WIDE>(p, g, s);
+    }
+  }
+  if (g.waves != GEMM_WAVES) return hipErrorInvalidValue;
   if (p.Bp <= 16) return go<1, WQ, EPI, KVFP8, GEMM_WAVES>(p, g, s);
   if (p.Bp <= 32) return go<2, WQ, EPI, KVFP8, GEMM_WAVES>(p, g, s);
   if (p.Bp <= 48) return go<3, WQ, EPI, KVFP8, GEMM_WAVES>(p, g, s);
@@ -578,8 +587,22 @@ GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool byte_weights) {
   const int NT = (Bp + 15) / 16;
   const int tpw = tiles_per_wave(NT, byte_weights, rows * n_groups, K);
   const int tile_rows = (n_groups == 2 ? 8 : 16) * tpw;  // gate+up tiles hold 8 of each
+  g.waves = GEMM_WAVES;
   g.n_rb = (rows + tile_rows * GEMM_WAVES - 1) / (tile_rows * GEMM_WAVES);
   const int nch = (K + KC - 1) / KC;
+  if (n_groups == 2 && g.n_rb >= GEMM_TARGET_GROUPS) {
+    // gate+up without a K split: the row-block size whose busiest CU streams the fewest
+    // wave tiles (work groups past a multiple of the CU count double up on some CUs)
+    const int units = (rows + tile_rows - 1) / tile_rows;
+    auto busiest = [&](int w) {
+      const int n = (units + w - 1) / w;
+      return ((n + GEMM_TARGET_GROUPS - 1) / GEMM_TARGET_GROUPS) * w;
+    };
+    if (busiest(GEMM_WAVES_WIDE) < busiest(GEMM_WAVES)) {
+      g.waves = GEMM_WAVES_WIDE;
+      g.n_rb = (units + GEMM_WAVES_WIDE - 1) / GEMM_WAVES_WIDE;
+    }
+  }
   int ks = 1;
   if (g.n_rb < GEMM_TARGET_GROUPS) {
     // as many splits as fit the CUs without a second work group on any of them: a grid

@@ -85,11 +85,15 @@ struct MatmulParams {
 // MFMA products (Bp up to 64): row blocks of GEMM_WAVES waves of 16-row tiles, K split over
 // ks work groups where the row blocks alone leave the chip under-filled.
 constexpr int GEMM_WAVES = 4;
+// gate+up's alternative row block: 7 waves, so that d_ff = 14336 or 28672 splits into one
+// row block per CU (1792 wave tiles = 256 x 7) instead of 448 of 4 waves (1.75 per CU)
+constexpr int GEMM_WAVES_WIDE = 7;
 constexpr int GEMM_MAX_SPLIT = 16;
 constexpr int GEMM_TARGET_GROUPS = 256;  // one per CU of MI355X
 struct GemmPlan {
   int n_rb;            // row blocks
   int ks;              // work groups per row block (K split)
+  int waves;           // waves per work group (tiles per row block / tpw)
   int tpw;             // 16-row tiles per wave
   size_t part_floats;  // partial-tile floats the launch needs (0 when ks == 1)
 };
