@@ -40,7 +40,7 @@ __global__ __launch_bounds__(WAVE * NW) void k_attn_split(AttnParams p) {
 template <int DH, bool FP8, int G, int NW>
 __global__ __launch_bounds__(WAVE * NW) void k_attn_mfma(AttnParams p) {
   __shared__ AttnSmem<DH, G, NW> S;
-  __shared__ __align__(16) uint8_t vt[NW * 16 * attn_vt_row<DH>()];
+  __shared__ __align__(16) uint8_t vt[NW * attn_wave_lds<DH>()];
   attn_unit<DH, FP8, G, NW, true>(p, blockIdx.x, blockIdx.y, blockIdx.z, S, vt);
 }
 

@@ -134,7 +134,7 @@ __device__ __forceinline__ void attn_o_rows(const AttnOParams& P, int grp, uint1
 template <int DH, bool FP8, int G, int WQ>
 __global__ __launch_bounds__(WAVE * ATTN_WAVES) void k_attn_o(AttnOParams P) {
   __shared__ AttnSmem<DH, G, ATTN_WAVES> S;
-  __shared__ __align__(16) uint8_t vt[ATTN_WAVES * 16 * attn_vt_row<DH>()];
+  __shared__ __align__(16) uint8_t vt[ATTN_WAVES * attn_wave_lds<DH>()];
   const int bid = blockIdx.x;
   if (bid < P.n_attn) {
     const int ns = P.a.n_split;

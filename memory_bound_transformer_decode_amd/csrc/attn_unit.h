@@ -117,15 +117,19 @@ __device__ __forceinline__ void attn_update(int blk, int ntok, int prow, const Q
 // 32 and 64: the registers they take)
 constexpr int ATTN_MFMA_DEPTH = 2;
 
-// V tile of one wave for the MFMA form: 16 position rows of DH bf16, padded by 16 bytes
+// Tiles of one wave for the MFMA form: K then V, 16 position rows of DH bf16 each, a row
+// padded by 16 bytes
 template <int DH>
 constexpr int attn_vt_row() { return DH * 2 + 16; }
+template <int DH>
+constexpr int attn_wave_lds() { return 2 * 16 * attn_vt_row<DH>(); }
 
 // The MFMA form of one wave's blocks (batches where attention's arithmetic, not its
 // memory latency, sets the pace: the scores and the P V products on the matrix cores).
 // Per block of 16 positions:
-//   S^T = K q^T     v_mfma_f32_16x16x32_bf16, A = K rows (the 16 positions), B = the
-//                   group's queries as 16 columns (heads >= G are zero); lane l ends with
+//   S^T = K q^T     v_mfma_f32_16x16x32_bf16, A = K rows (the 16 positions, from the
+//                   wave's K tile), B = the group's queries as 16 columns (heads >= G
+//                   are zero); lane l ends with
 //                   S[position 4 (l / 16) + j][head l % 16], j < 4;
 //   online softmax per head (column): the block's max over the lane's 4 positions and the
 //                   four lane groups; running max, this lane's share of the sum, and the
@@ -166,15 +170,20 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
     }
   }
 
-  // the lane's 8 elements of K and V row m per k-step: bf16 (16 bytes) or E4M3 (8 bytes)
+  // K and V of a block are read row-contiguously: load instruction s covers rows RPI s ..
+  // RPI s + RPI - 1 whole (512 elements, lane l the 8 at element 8 l), which the memory
+  // system serves in full lines; the tiles in LDS then give each lane its MFMA operands.
+  // A lane holds 8 elements per instruction: bf16 (16 bytes) or E4M3 (8 bytes).
+  constexpr int RPI = 512 / DH;  // rows per load instruction
+  const int lrow = lane / (DH / 8), lcol = (lane % (DH / 8)) * 8;
   typedef u32x4 KVReg[2][NS];
   auto load = [&](int i, KVReg& r) {
     const int phys = __shfl(my_phys, i);
-    const int64_t kb = kv_offset(p.layer, 0, phys, c, 0, 0, p.num_blocks, p.Hkv, DH) + (int64_t)m * DH;
-    const int64_t vb = kv_offset(p.layer, 1, phys, c, 0, 0, p.num_blocks, p.Hkv, DH) + (int64_t)m * DH;
+    const int64_t kb = kv_offset(p.layer, 0, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
+    const int64_t vb = kv_offset(p.layer, 1, phys, c, 0, 0, p.num_blocks, p.Hkv, DH);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int e = s * 32 + g * 8;
+      const int e = (s * RPI + lrow) * DH + lcol;
       if (FP8) {
         const u32x2 k2 = gld(reinterpret_cast<const u32x2*>(pool + kb + e));
         const u32x2 v2 = gld(reinterpret_cast<const u32x2*>(pool + vb + e));
@@ -200,26 +209,29 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
 #pragma unroll
   for (int t = 0; t < NC; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  uint8_t* kt = vt + 16 * TR;  // the wave's K tile
   auto block = [&](int i, const KVReg& r) {
     const int pos0 = (bfirst + i * NW) * KV_BLOCK;
-    // V row m into the tile; zeros past the last position (those slots may hold
-    // anything, even NaN, which a zero probability would not cancel in the product)
-    const bool rv = pos0 + m < ntok;
-    // the previous block's reads of the tile come before these writes (LDS serves one
+    // the previous block's reads of the tiles come before these writes (LDS serves one
     // wave's accesses in order; the wave barrier keeps the compiler from reordering them)
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const bf16x8 v = as_bf16x8(r[1][s]);
-      *reinterpret_cast<u32x4*>(vt + m * TR + (s * 32 + g * 8) * 2) =
-          rv ? __builtin_bit_cast(u32x4, v) : u32x4{0u, 0u, 0u, 0u};
+      const int row = s * RPI + lrow;
+      // K rows past the last position only feed scores that are masked below; V rows
+      // there are zeroed (those slots may hold anything, even NaN, which a zero
+      // probability would not cancel in the product)
+      *reinterpret_cast<u32x4*>(kt + row * TR + lcol * 2) = __builtin_bit_cast(u32x4, as_bf16x8(r[0][s]));
+      *reinterpret_cast<u32x4*>(vt + row * TR + lcol * 2) =
+          pos0 + row < ntok ? __builtin_bit_cast(u32x4, as_bf16x8(r[1][s])) : u32x4{0u, 0u, 0u, 0u};
     }
     // ... and these writes before this block's transposed reads below
     __builtin_amdgcn_wave_barrier();
     f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const bf16x8 kv = as_bf16x8(r[0][s]);
+      // A operand: K row m, elements 32 s + 8 g .. + 7
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(kt + m * TR + (s * 32 + g * 8) * 2);
       sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[s], sa, 0, 0, 0);
       sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[s], sa, 0, 0, 0);
     }
@@ -244,9 +256,15 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
       pl[j] = (__bf16)(pj - (float)ph[j]);
     }
     lrun = lrun * alpha + ps;
+    // the output is rescaled only when some head's running max rose in this block (once
+    // the context's largest scores have been seen it rarely does): multiplying by exactly
+    // 1 would change no bit, and the wave-uniform branch skips NC x 4 products
+    if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int t = 0; t < NC; ++t) o[t] *= alpha;
+    }
 #pragma unroll
     for (int t = 0; t < NC; ++t) {
-      o[t] *= alpha;
       // V^T[dim 16 t + m][positions 4 g .. 4 g + 3] from the tile by one transposing LDS
       // read (ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i % 4
       // of the 4 elements that lane 4 j + i / 4 points at, j = 0..3): lane 16 g + i
@@ -295,8 +313,8 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
 // one split it writes o; otherwise it writes its partial, and the last split of the
 // group to arrive combines.  o is written device-coherently.  Returns, in every thread,
 // whether this work group wrote the group's o.
-// MF: the wave's blocks in the MFMA form (attn_wave_mfma), with the wave's V tile at
-// vtile + wave 16 attn_vt_row<DH>() bytes of LDS.
+// MF: the wave's blocks in the MFMA form (attn_wave_mfma), with the wave's V and K tiles
+// at vtile + wave attn_wave_lds<DH>() bytes of LDS.
 template <int DH, bool FP8, int G, int NW, bool MF = false>
 __device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c, int b, AttnSmem<DH, G, NW>& S,
                                           uint8_t* vtile = nullptr) {
@@ -333,7 +351,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c,
   };
   if constexpr (MF) {
     attn_wave_mfma<DH, FP8, G, NW>(p, b, c, lane, nb, blk0 + wave, ntok, my_phys,
-                                   vtile + wave * 16 * attn_vt_row<DH>(), S.sm[wave], S.sl[wave], S.so[wave]);
+                                   vtile + wave * attn_wave_lds<DH>(), S.sm[wave], S.sl[wave], S.so[wave]);
   } else {
     const float qscale = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
     float qv[G][EPL];  // the lane's 8 elements of each head's query, scaled
