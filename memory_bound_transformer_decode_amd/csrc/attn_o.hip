@@ -11,7 +11,7 @@
 //  * work groups 0 .. n_attn - 1 run the attention units exactly as k_attn_mfma does
 //    (attn_unit, MFMA form); a unit that writes its (sequence, kv head) group's output
 //    counts it on `done` once its stores are acknowledged;
-//  * every later work group takes R rows of W_o per wave, loads them whole into
+//  * every later work group takes R <= 6 rows of W_o per wave, loads them whole into
 //    registers (the weights depend on nothing), then waits until all groups are done,
 //    stages the attention output in LDS and finishes h += s (W_o o) for its rows.  The
 //    O weights thus stream while attention runs.
@@ -69,12 +69,13 @@ __device__ __forceinline__ void attn_o_wait(const unsigned* done, unsigned need,
 }
 
 // h[r] += s_r sum_k W_o[r][k] o[k] for the rows of O work group `grp`: wave w takes rows
-// (grp NW + w) R .. + R - 1; lane l holds 16-byte vectors l, l + 64, ..., of each row
-// (V = K / (64 EPV) of them), so that a row is reduced once over the wave.
-template <int WQ, int NW>
+// (grp NW + w) R .. + R - 1 (R <= RM); lane l holds 16-byte vectors l, l + 64, ..., of
+// each row (V = K / (64 EPV) of them), so that a row is reduced once over the wave.
+template <int WQ, int NW, int RM>
 __device__ __forceinline__ void attn_o_rows(const AttnOParams& P, int grp, uint16_t* xs) {
   constexpr int EPV = WQ != W_BF16 ? 16 : 8;  // weight elements per 16-byte vector
-  constexpr int RM = ATTN_O_RMAX, VM = ATTN_O_VMAX;
+  constexpr int VM = ATTN_O_VMAX;
+  static_assert(RM * VM <= ATTN_O_WREGS, "weights held per lane");
   const MatmulParams& p = P.m;
   const int lane = threadIdx.x % WAVE;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
@@ -101,37 +102,39 @@ __device__ __forceinline__ void attn_o_rows(const AttnOParams& P, int grp, uint1
   for (int i = threadIdx.x; i < p.K / 8; i += NW * WAVE)
     *reinterpret_cast<u32x4*>(xs + i * 8) = gld16(p.x + (int64_t)i * 8);
   __syncthreads();
-  u32x4 xa[VM], xb[VM];  // o elements of the lane's vectors (bf16; xb: the second 8 of 16)
+  // vector by vector: the lane's o elements of vector v serve every row
+  float acc[RM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r) acc[r] = 0.f;
 #pragma unroll
   for (int v = 0; v < VM; ++v) {
     if (v < V) {
       const uint16_t* xp = xs + (lane + v * WAVE) * EPV;
-      xa[v] = *reinterpret_cast<const u32x4*>(xp);
-      if constexpr (WQ != W_BF16) xb[v] = *reinterpret_cast<const u32x4*>(xp + 8);
+      const u32x4 xa = *reinterpret_cast<const u32x4*>(xp);  // bf16; xb: the second 8 of 16
+      const u32x4 xb = WQ != W_BF16 ? *reinterpret_cast<const u32x4*>(xp + 8) : xa;
+#pragma unroll
+      for (int r = 0; r < RM; ++r) {
+        if (r < R) {
+          if constexpr (WQ != W_BF16)
+            acc[r] = dot16_b8<WQ>(wr[r][v], xa, xb, acc[r]);
+          else
+            acc[r] = dot8_bf16(wr[r][v], xa, acc[r]);
+        }
+      }
     }
   }
   float mine = 0.f;  // lane r: the sum of row row0 + r
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
     if (r < R) {
-      float acc = 0.f;
-#pragma unroll
-      for (int v = 0; v < VM; ++v) {
-        if (v < V) {
-          if constexpr (WQ != W_BF16)
-            acc = dot16_b8<WQ>(wr[r][v], xa[v], xb[v], acc);
-          else
-            acc = dot8_bf16(wr[r][v], xa[v], acc);
-        }
-      }
-      acc = wave_sum_rows(acc);
-      mine = lane == r ? acc : mine;
+      const float t = wave_sum_rows(acc[r]);
+      mine = lane == r ? t : mine;
     }
   }
   if (lane < R && row0 + lane < p.N) gst(p.out + row0 + lane, h_old + mine * sc);
 }
 
-template <int DH, bool FP8, int G, int WQ>
+template <int DH, bool FP8, int G, int WQ, int RM>
 __global__ __launch_bounds__(WAVE * ATTN_WAVES) void k_attn_o(AttnOParams P) {
   __shared__ AttnSmem<DH, G, ATTN_WAVES> S;
   __shared__ __align__(16) uint8_t vt[ATTN_WAVES * attn_wave_lds<DH>()];
@@ -143,18 +146,24 @@ __global__ __launch_bounds__(WAVE * ATTN_WAVES) void k_attn_o(AttnOParams P) {
     return;
   }
   static_assert(sizeof(vt) >= ATTN_O_VMAX * WAVE * 16 * 2, "o staging must fit the V tiles' LDS");
-  attn_o_rows<WQ, ATTN_WAVES>(P, bid - P.n_attn, reinterpret_cast<uint16_t*>(vt));
+  attn_o_rows<WQ, ATTN_WAVES, RM>(P, bid - P.n_attn, reinterpret_cast<uint16_t*>(vt));
 }
 
-template <int DH, bool FP8, int G>
-hipError_t attn_o_wq(const AttnOParams& P, WFmt wq, int grid, hipStream_t s) {
+template <int DH, bool FP8, int G, int RM>
+hipError_t attn_o_rm(const AttnOParams& P, WFmt wq, int grid, hipStream_t s) {
   const dim3 blk(WAVE * ATTN_WAVES);
   switch (wq) {
-    case W_E4M3: hipLaunchKernelGGL((k_attn_o<DH, FP8, G, W_E4M3>), dim3(grid), blk, 0, s, P); break;
-    case W_I8: hipLaunchKernelGGL((k_attn_o<DH, FP8, G, W_I8>), dim3(grid), blk, 0, s, P); break;
-    default: hipLaunchKernelGGL((k_attn_o<DH, FP8, G, W_BF16>), dim3(grid), blk, 0, s, P); break;
+    case W_E4M3: hipLaunchKernelGGL((k_attn_o<DH, FP8, G, W_E4M3, RM>), dim3(grid), blk, 0, s, P); break;
+    case W_I8: hipLaunchKernelGGL((k_attn_o<DH, FP8, G, W_I8, RM>), dim3(grid), blk, 0, s, P); break;
+    default: hipLaunchKernelGGL((k_attn_o<DH, FP8, G, W_BF16, RM>), dim3(grid), blk, 0, s, P); break;
   }
   return hipGetLastError();
+}
+
+// up to 3 rows per wave, or up to ATTN_O_RMAX (the larger register set only when needed)
+template <int DH, bool FP8, int G>
+hipError_t attn_o_wq(const AttnOParams& P, WFmt wq, int grid, hipStream_t s) {
+  return P.rows <= 3 ? attn_o_rm<DH, FP8, G, 3>(P, wq, grid, s) : attn_o_rm<DH, FP8, G, ATTN_O_RMAX>(P, wq, grid, s);
 }
 
 template <int DH, bool FP8>
@@ -169,12 +178,22 @@ hipError_t attn_o_g(const AttnOParams& P, WFmt wq, int grid, hipStream_t s) {
 
 }  // namespace
 
-int attn_o_rows_per_wave(int n_attn, int N, int K, WFmt wq, int n_cu) {
+AttnOPlan attn_o_plan(const AttnShape& sh, int Bp, int N, WFmt wq, int n_cu) {
   const int epv = wq != W_BF16 ? 16 : 8;
-  if (K % (epv * WAVE) != 0 || K / (epv * WAVE) > ATTN_O_VMAX || n_attn >= n_cu) return 0;
-  const int free_wg = n_cu - n_attn;  // one work group per CU (the attention units' registers)
-  const int R = (N + free_wg * ATTN_WAVES - 1) / (free_wg * ATTN_WAVES);
-  return R <= ATTN_O_RMAX ? R : 0;
+  const int K = sh.Hq * sh.dh;
+  if (Bp != 1 || !attn_o_supported(sh.Hq, sh.Hkv, sh.dh) || K % (epv * WAVE) != 0 ||
+      K / (epv * WAVE) > ATTN_O_VMAX || N <= 0)
+    return AttnOPlan{0, 0};
+  const int V = K / (epv * WAVE);
+  const int min_ns = (sh.bps + WAVE * ATTN_WAVES - 1) / (WAVE * ATTN_WAVES);
+  // the most splits (from the standalone launch's count down) whose work groups leave room
+  for (int ns = attn_splits(sh, Bp); ns >= min_ns && ns >= 1; --ns) {
+    const int free_wg = n_cu - ns * sh.Hkv * Bp;  // one work group per CU (attention's registers)
+    if (free_wg <= 0) continue;
+    const int R = (N + free_wg * ATTN_WAVES - 1) / (free_wg * ATTN_WAVES);
+    if (R <= ATTN_O_RMAX && R * V <= ATTN_O_WREGS) return AttnOPlan{R, ns};
+  }
+  return AttnOPlan{0, 0};
 }
 
 bool attn_o_supported(int Hq, int Hkv, int dh) {

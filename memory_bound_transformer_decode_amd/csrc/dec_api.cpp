@@ -438,16 +438,16 @@ bool fused_norm(const dec_config& g, int Bp) {
   return !use_mfma(g, Bp) && Bp <= 8 && (size_t)Bp * g.d_model * 4 <= 128 * 1024;
 }
 
-// Rows of W_o per wave of the fused attention + O launch (attn_o.hip), or 0 where the two
-// run as separate launches: a single sequence on the matrix-vector kernels, MFMA
-// attention, and O work groups that fit beside attention's on the chip.
-int attn_o_rows(const dec_config& g, int Bp) {
+// The fused attention + O launch's shape (attn_o.hip): rows of W_o per wave (0 where the
+// two run as separate launches) and attention splits.  A single sequence on the
+// matrix-vector kernels, MFMA attention, and O work groups that fit beside attention's.
+dec::AttnOPlan attn_o_plan(const dec_config& g, int Bp) {
   if (Bp != 1 || g.n_layers == 0 || use_mfma(g, Bp) || !attn_mfma(g) || !fused_norm(g, Bp) ||
-      (g.flags & (DEC_FLAG_UNFUSED | DEC_FLAG_NO_ATTN_O)) || !dec::attn_o_supported(g.n_q_heads, g.n_kv_heads, g.d_head))
-    return 0;
-  const int n_attn = dec::attn_splits(attn_shape(g), Bp) * g.n_kv_heads * Bp;
-  return dec::attn_o_rows_per_wave(n_attn, g.d_model, g.n_q_heads * g.d_head, wfmt_of(g.weight_dtype), device_cus());
+      (g.flags & (DEC_FLAG_UNFUSED | DEC_FLAG_NO_ATTN_O)))
+    return dec::AttnOPlan{0, 0};
+  return dec::attn_o_plan(attn_shape(g), Bp, g.d_model, wfmt_of(g.weight_dtype), device_cus());
 }
+int attn_o_rows(const dec_config& g, int Bp) { return attn_o_plan(g, Bp).rows; }
 
 dec::AttnParams attn_params(dec_ctx* c, int Bp, int layer) {
   const dec_config& g = c->cfg;
@@ -575,7 +575,8 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   };
   qkv_input(g.n_layers > 0);
   // the fused attention + O launches' done counters start the step at zero
-  const int ao_rows = attn_o_rows(g, Bp);
+  const dec::AttnOPlan ao = attn_o_plan(g, Bp);
+  const int ao_rows = ao.rows;
   if (ao_rows > 0) {
     np.zero = ws_ptr<unsigned>(c, c->L.attn_o_cnt);
     np.n_zero = g.n_layers * 64;
@@ -600,6 +601,7 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
     if (ao_rows > 0) {
       dec::AttnOParams P{};
       P.a = attn_params(c, Bp, l);
+      P.a.n_split = ao.n_split;  // no more than attn_splits: the workspace holds the partials
       int epi = 0;
       P.m = matmul_params(c, DEC_MAT_O, l, Bp, &epi);
       P.done = ws_ptr<unsigned>(c, c->L.attn_o_cnt) + (size_t)l * 64;
@@ -772,7 +774,8 @@ int run_plan(dec_ctx* c, int Bp, bool skip_lm) {
     for (auto& ge : row) ncap += ge != nullptr;
   c->info.kernels_per_step = kernels_of_plan(g, Bp, skip_lm);
   c->info.bucket = Bp;
-  c->info.attn_splits = dec::attn_splits(attn_shape(g), Bp);
+  const dec::AttnOPlan aop = attn_o_plan(g, Bp);
+  c->info.attn_splits = aop.rows > 0 ? aop.n_split : dec::attn_splits(attn_shape(g), Bp);
   c->info.used_mfma = use_mfma(g, Bp) ? 1 : 0;
   c->info.graphs_captured = ncap;
   c->info.flags = g.flags;

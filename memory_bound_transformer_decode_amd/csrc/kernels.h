@@ -168,8 +168,9 @@ hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t s);
 // Attention and the O projection of one layer in one launch (a single sequence on the
 // matrix-vector path, attn_o.hip): attention's n_attn work groups first, then work
 // groups that hold `rows` rows of W_o per wave in registers and wait for attention.
-constexpr int ATTN_O_RMAX = 3;  // rows of W_o per wave
+constexpr int ATTN_O_RMAX = 6;  // rows of W_o per wave
 constexpr int ATTN_O_VMAX = 8;  // 16-byte vectors of a row per lane
+constexpr int ATTN_O_WREGS = 48;  // 16-byte weight vectors a lane may hold (192 VGPRs)
 struct AttnOParams {
   AttnParams a;       // Bp = 1, MFMA form
   MatmulParams m;     // the O product: x = a.o, out = h (EPI_RESID), Bp = 1
@@ -180,9 +181,13 @@ struct AttnOParams {
   int n_attn;         // attention work groups: a.n_split a.Hkv a.Bp
   int rows;           // rows of W_o per wave, 1 .. ATTN_O_RMAX
 };
-// Rows per wave that let every O work group be resident beside the attention work groups
-// (one work group per CU), or 0 when the shape does not fit the fused launch.
-int attn_o_rows_per_wave(int n_attn, int N, int K, WFmt wq, int n_cu);
+// The fused launch's shape: rows of W_o per wave and attention splits such that every O
+// work group is resident beside the attention work groups (one work group per CU), the
+// most splits (up to attn_splits) that allow it; rows = 0 when the shape does not fit.
+struct AttnOPlan {
+  int rows, n_split;
+};
+AttnOPlan attn_o_plan(const AttnShape& s, int Bp, int N, WFmt wq, int n_cu);
 // The head shapes the fused launch is built for (d_head 64 or 128, 4, 5 or 8 query heads
 // per kv head).
 bool attn_o_supported(int Hq, int Hkv, int dh);
