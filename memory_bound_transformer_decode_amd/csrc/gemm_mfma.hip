@@ -615,7 +615,7 @@ GemmPlan gemm_plan(int rows, int n_groups, int K, int Bp, bool byte_weights) {
   }
   g.ks = ks;
   g.tpw = tpw;
-  g.part_floats = ks > 1 ? (size_t)g.n_rb * ks * GEMM_WAVES * tpw * NT * WAVE * 4 : 0;
+  g.part_floats = ks > 1 ? (size_t)g.n_rb * ks * g.waves * tpw * NT * WAVE * 4 : 0;
   return g;
 }
 
