@@ -239,6 +239,7 @@ class Leg:
     def close(self) -> None:
         import torch
 
+        self.d.check()  # every device-side wait of the measured steps ended normally
         self.d.close()
         del self.pool
         torch.cuda.empty_cache()
