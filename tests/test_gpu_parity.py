@@ -564,3 +564,27 @@ def test_large_workload_widths(dec, name, layers, B):
     assert_ok(run_parity(case, ids, stream_weights=True, kv_every_step=False), cfg)
 
 
+@pytest.mark.parametrize("name,splits", [("8B", 9), ("32B", 3), ("70B", 10), ("8B-int8", 9)])
+def test_batch1_attention_o_plans_of_the_workloads(dec, name, splits):
+    """At batch 1 the benchmarked workloads run attention and O as one launch: the path
+    bit, four kernels per layer and the plan's attention splits on MI355X's 256 CUs -- the
+    standalone count where W_o fits beside attention (8B: 9 splits, 3 rows per wave), fewer
+    where it does not (70B: 10 instead of 17, 6 rows per wave)."""
+    wl = synth.WORKLOADS[name]
+    cfg = wl.model.with_layers(1)
+    lens = synth.make_context_lengths(wl, 1, seed=0)
+    case = make_case(cfg, lens, wl.max_seq_len, seed=0)
+    ids = synth.make_token_ids(cfg, 1, 1, seed=0)[0]
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=1, max_seq_len=wl.max_seq_len,
+                    kv_pool=case.pool.clone())
+    d.step(ids, case.ctx_lens, case.block_tables)
+    d.check()
+    k, f = d.path()
+    seen = d.info().attn_splits
+    d.close()
+    log(f"{name} batch 1: {k} kernels per step, path bits {f:#x}, {seen} attention splits")
+    assert f & dec.PATH_ATTN_O
+    assert k == 4 * cfg.n_layers + 2
+    assert seen == splits
+
+
