@@ -9,19 +9,20 @@
 // table; the kernel-fusion architecture study on launch overhead).  Here:
 //
 //  * work groups 0 .. n_attn - 1 run the attention units exactly as k_attn_mfma does
-//    (attn_unit, MFMA form); a unit that writes its (sequence, kv head) group's output
-//    counts it on `done` once its stores are acknowledged;
+//    (attn_unit, MFMA form), writing o;
 //  * every later work group takes R <= 6 rows of W_o per wave, loads them whole into
-//    registers (the weights depend on nothing), then waits until all groups are done,
-//    stages the attention output in LDS and finishes h += s (W_o o) for its rows.  The
-//    O weights thus stream while attention runs.
+//    registers (the weights depend on nothing), then polls o until every element is
+//    written, and finishes h += s (W_o o) for its rows.  The O weights thus stream while
+//    attention runs.
 //
-// The attention output is read with ordinary (L2-cached) loads, so that each XCD's L2
-// fetches it once for all its work groups: no XCD holds a line of it from before this
-// launch (caches are invalidated between launches, as for every buffer one launch writes
-// and the next reads), and within the launch it is read only after the wait, by which
-// time its writers' stores have reached memory; each (sequence, kv head) group's output
-// is G d_head bf16 = a whole number of 128-byte lines, so no line mixes two writers.
+// o is its own completion flag: it holds ATTN_O_PENDING in every element when the launch
+// starts (stored by an earlier launch: the step's embedding kernel for the first layer,
+// the previous layer's launch otherwise; two buffers alternate by layer), each element is
+// written once, by one two-byte device-coherent store of its final value, which is never
+// that pattern, and the O work groups read o with device-coherent loads, so a 16-byte
+// slice without the pattern holds final values.  Against a counter that the writers
+// would raise after their stores are acknowledged, this saves the acknowledgement, the
+// counter's round trip and the separate read of o.
 //
 // Forward progress: the attention work groups come first in block order and the
 // dispatcher hands out each XCD's work groups in block order, so every attention work
@@ -35,37 +36,56 @@ namespace dec {
 
 namespace {
 
-// Count the group's output on `done` once every thread's stores are acknowledged (the
-// ordering argument of arrive_after_stores: vmcnt(0) also counts stores here, the
-// barrier orders every thread's wait before thread 0's update, and the update is one
-// agent-scope atomic).
-__device__ __forceinline__ void attn_o_signal(unsigned* done) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited on
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Whether any of the 8 bf16 of v is ATTN_O_PENDING
+__device__ __forceinline__ bool o_pending(const u32x4& v) {
+  bool any = false;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) any |= (w[j] & 0xFFFFu) == ATTN_O_PENDING || (w[j] >> 16) == ATTN_O_PENDING;
+  return any;
 }
 
-// Wave 0 polls `done` until it reaches `need` (or gives up after `spin` polls, or once
-// another wait has given up), then the work group goes on.  Loads issued after the
-// barrier see what the counted work groups stored: their stores had reached memory before
-// they counted (the compiler-only fences keep the loads below the wait).
-__device__ __forceinline__ void attn_o_wait(const unsigned* done, unsigned need, int* abort, int spin) {
-  if (threadIdx.x < WAVE) {
-    for (int it = 0;; ++it) {
-      if (it >= spin) {  // spin 0: give up at once (the failure path's own test)
-        if (threadIdx.x == 0) cst(abort, 1);
-        break;
-      }
-      if (cld(done) >= need) break;
-      if ((it & 15) == 15 && cld(abort) != 0) break;
-      __builtin_amdgcn_s_sleep(2);
+// Copy o [K] bf16 into LDS (xs) once every element is written: each thread polls its
+// 16-byte slices with device-coherent loads, keeps the complete ones and polls the rest
+// again, until no thread of the work group has a slice pending (or `spin` polls have
+// passed, or another work group has given up).  SPT: slices per thread, K <= SPT 8 NT.
+template <int NT, int SPT>
+__device__ __forceinline__ void attn_o_stage(const uint16_t* o, int K, uint16_t* xs, int* abort, int spin) {
+  const int tid = threadIdx.x;
+  unsigned pending = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+    if ((tid + j * NT) * 8 < K) pending |= 1u << j;
+  for (int it = 0;; ++it) {
+    if (it >= spin) {  // spin 0: give up at once (the failure path's own test)
+      if (tid == 0) cst(abort, 1);
+      break;
     }
+    u32x4 v[SPT];
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+      if (pending >> j & 1u) v[j] = cld16(o + (tid + j * NT) * 8);
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      if ((pending >> j & 1u) && !o_pending(v[j])) {
+        *reinterpret_cast<u32x4*>(xs + (tid + j * NT) * 8) = v[j];
+        pending &= ~(1u << j);
+      }
+    }
+    if (!__syncthreads_or(pending != 0)) break;
+    if ((it & 15) == 15 && __syncthreads_or(tid == 0 && cld(abort) != 0)) break;
+    __builtin_amdgcn_s_sleep(1);
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Mark the next layer's o as not yet written: the O work groups share its 16-byte slices.
+__device__ __forceinline__ void attn_o_mark_next(uint16_t* next, int K, int grp, int n_grp, int NT) {
+  for (int i = grp * NT + (int)threadIdx.x; i < K / 8; i += n_grp * NT) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(next + (int64_t)i * 8);
+    cst(q, (uint64_t)ATTN_O_PENDING2 << 32 | ATTN_O_PENDING2);
+    cst(q + 1, (uint64_t)ATTN_O_PENDING2 << 32 | ATTN_O_PENDING2);
+  }
 }
 
 // h[r] += s_r sum_k W_o[r][k] o[k] for the rows of O work group `grp`: wave w takes rows
@@ -96,12 +116,10 @@ __device__ __forceinline__ void attn_o_rows(const AttnOParams& P, int grp, uint1
   const float h_old = gld(p.out + my_row);
   const float sc = p.scale ? gld(p.scale + my_row) : 1.f;
 
-  attn_o_wait(P.done, P.need, P.abort, P.spin);
+  attn_o_mark_next(P.next, p.K, grp, (int)gridDim.x - P.n_attn, NW * WAVE);
+  attn_o_stage<NW * WAVE, (ATTN_O_VMAX * WAVE * 16 + NW * WAVE * 8 - 1) / (NW * WAVE * 8)>(p.x, p.K, xs, P.abort,
+                                                                                       P.spin);
 
-  // o [K] bf16 into LDS, 16 bytes per thread per pass
-  for (int i = threadIdx.x; i < p.K / 8; i += NW * WAVE)
-    *reinterpret_cast<u32x4*>(xs + i * 8) = gld16(p.x + (int64_t)i * 8);
-  __syncthreads();
   // vector by vector: the lane's o elements of vector v serve every row
   float acc[RM];
 #pragma unroll
@@ -142,7 +160,7 @@ __global__ __launch_bounds__(WAVE * ATTN_WAVES) void k_attn_o(AttnOParams P) {
   if (bid < P.n_attn) {
     const int ns = P.a.n_split;
     const int split = bid % ns, c = (bid / ns) % P.a.Hkv, b = bid / (ns * P.a.Hkv);
-    if (attn_unit<DH, FP8, G, ATTN_WAVES, true>(P.a, split, c, b, S, vt)) attn_o_signal(P.done);
+    attn_unit<DH, FP8, G, ATTN_WAVES, true>(P.a, split, c, b, S, vt);
     return;
   }
   static_assert(sizeof(vt) >= ATTN_O_VMAX * WAVE * 16 * 2, "o staging must fit the V tiles' LDS");
@@ -205,8 +223,8 @@ bool attn_o_supported(int Hq, int Hkv, int dh) {
 hipError_t launch_attn_o(const AttnOParams& P, WFmt wq, bool kv_fp8, hipStream_t s) {
   const AttnParams& a = P.a;
   const MatmulParams& m = P.m;
-  if (!attn_o_supported(a.Hq, a.Hkv, a.dh) || a.Bp != 1 || !a.mfma || m.Bp != 1 || !P.done || !P.abort ||
-      P.rows < 1 || P.rows > ATTN_O_RMAX || P.n_attn != a.n_split * a.Hkv * a.Bp || P.need != (unsigned)(a.Hkv * a.Bp))
+  if (!attn_o_supported(a.Hq, a.Hkv, a.dh) || a.Bp != 1 || !a.mfma || m.Bp != 1 || !P.abort || !P.next ||
+      P.next == a.o || m.x != a.o || P.rows < 1 || P.rows > ATTN_O_RMAX || P.n_attn != a.n_split * a.Hkv * a.Bp)
     return hipErrorInvalidValue;
   const int epv = wq != W_BF16 ? 16 : 8;
   if (m.K != a.Hq * a.dh || m.K % (epv * WAVE) || m.K / (epv * WAVE) > ATTN_O_VMAX || m.N <= 0 || !m.x || !m.out)

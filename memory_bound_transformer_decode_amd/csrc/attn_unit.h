@@ -315,6 +315,13 @@ __device__ __forceinline__ void attn_wave_mfma(const AttnParams& p, int b, int c
 // whether this work group wrote the group's o.
 // MF: the wave's blocks in the MFMA form (attn_wave_mfma), with the wave's V and K tiles
 // at vtile + wave attn_wave_lds<DH>() bytes of LDS.
+// An attention output element as stored: bf16, with the NaN pattern that marks an
+// unwritten element in the fused attention + O launch replaced by another NaN
+__device__ __forceinline__ uint16_t o_bits(float v) {
+  const uint16_t h = f32_to_bf16(v);
+  return h == ATTN_O_PENDING ? (uint16_t)0xFFBFu : h;
+}
+
 template <int DH, bool FP8, int G, int NW, bool MF = false>
 __device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c, int b, AttnSmem<DH, G, NW>& S,
                                           uint8_t* vtile = nullptr) {
@@ -441,7 +448,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c,
     }
     if (single) {
       // the whole context in this work group: o directly
-      cst(p.o + ((int64_t)b * p.Hq + c * G + h) * DH + e, f32_to_bf16(M != -INFINITY ? O / L : 0.f));
+      cst(p.o + ((int64_t)b * p.Hq + c * G + h) * DH + e, o_bits(M != -INFINITY ? O / L : 0.f));
       continue;
     }
     const int64_t row = ((int64_t)b * p.Hq + c * G + h) * p.n_split + split;
@@ -509,7 +516,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams& p, int split, int c,
       }
       out = O / L;
     }
-    cst(p.o + ((int64_t)b * p.Hq + c * G + h) * DH + e, f32_to_bf16(out));
+    cst(p.o + ((int64_t)b * p.Hq + c * G + h) * DH + e, o_bits(out));
   }
   return true;
 }

@@ -85,7 +85,7 @@ struct Layout {
   size_t uf;                           // unfused step: fp32 product rows [MB][max(N)]
   size_t us;                           // unfused step: attention scores [MB][Hq][max_seq_len]
   size_t attn_cnt;                     // attention split arrival counters
-  size_t attn_o_cnt, attn_o_abort;     // fused attention + O launches: a done counter per layer; abort flag
+  size_t attn_o_buf, attn_o_abort;     // fused attention + O launches: o of even and odd layers; abort flag
   size_t ssq;                          // folded RMSNorm: row-block sums of squares
   size_t gpart, gcnt;                  // MFMA products split over K: partial tiles, row-block counters
   size_t gpart_floats, gcnt_n;
@@ -159,8 +159,8 @@ Layout layout_of(const dec_config& c) {
   off = align256(off + part_floats * 4);
   L.attn_cnt = off;
   off = align256(off + MB * c.n_kv_heads * 4);
-  L.attn_o_cnt = off;  // one 256-byte line per layer (every O work group polls it)
-  off = align256(off + (size_t)c.n_layers * 256);
+  L.attn_o_buf = off;  // two buffers of Hq d_head bf16 (one sequence)
+  off = align256(off + 2 * align256((size_t)c.n_q_heads * c.d_head * 2));
   L.attn_o_abort = off;
   off = align256(off + 4);
   L.ssq = off;
@@ -449,6 +449,12 @@ dec::AttnOPlan attn_o_plan(const dec_config& g, int Bp) {
 }
 int attn_o_rows(const dec_config& g, int Bp) { return attn_o_plan(g, Bp).rows; }
 
+// The fused attention + O launch's attention output for layer l (buffers alternate by layer)
+uint16_t* attn_o_buf(dec_ctx* c, int l) {
+  const size_t n = align256((size_t)c->cfg.n_q_heads * c->cfg.d_head * 2);
+  return reinterpret_cast<uint16_t*>(c->ws + c->L.attn_o_buf + (size_t)(l & 1) * n);
+}
+
 dec::AttnParams attn_params(dec_ctx* c, int Bp, int layer) {
   const dec_config& g = c->cfg;
   dec::AttnParams ap{};
@@ -578,12 +584,12 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
   const dec::AttnOPlan ao = attn_o_plan(g, Bp);
   const int ao_rows = ao.rows;
   if (ao_rows > 0) {
-    np.zero = ws_ptr<unsigned>(c, c->L.attn_o_cnt);
-    np.n_zero = g.n_layers * 64;
+    np.pend = reinterpret_cast<unsigned*>(attn_o_buf(c, 0));
+    np.n_pend = g.n_q_heads * g.d_head / 2;
   }
   if ((e = dec::launch_embed_norm(np, wq, s)) != hipSuccess) return e;
-  np.zero = nullptr;
-  np.n_zero = 0;
+  np.pend = nullptr;
+  np.n_pend = 0;
 
   // no RMSNorm kernels: the matrix-vector kernels normalize their own input (fn), or the
   // MFMA products fold the norms
@@ -602,10 +608,11 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
       dec::AttnOParams P{};
       P.a = attn_params(c, Bp, l);
       P.a.n_split = ao.n_split;  // no more than attn_splits: the workspace holds the partials
+      P.a.o = attn_o_buf(c, l);
       int epi = 0;
       P.m = matmul_params(c, DEC_MAT_O, l, Bp, &epi);
-      P.done = ws_ptr<unsigned>(c, c->L.attn_o_cnt) + (size_t)l * 64;
-      P.need = (unsigned)(P.a.Hkv * Bp);
+      P.m.x = P.a.o;
+      P.next = attn_o_buf(c, l + 1);
       P.abort = ws_ptr<int>(c, c->L.attn_o_abort);
       P.spin = c->wait_limit;
       P.n_attn = P.a.n_split * P.a.Hkv * Bp;

@@ -121,8 +121,8 @@ struct NormParams {
   float eps;
   // embedding
   const void* E; const float* E_scale; const int32_t* ids;
-  unsigned* zero;       // embedding kernel: n_zero counters set to zero (the step's first kernel)
-  int n_zero;
+  unsigned* pend;       // embedding kernel: n_pend words set to ATTN_O_PENDING2 (the step's first
+  int n_pend;           // kernel marks the first layer's attention output as not yet written)
 };
 
 // h = E[ids[b]] (dequantized), x = RMSNorm(h) g
@@ -171,11 +171,15 @@ hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t s);
 constexpr int ATTN_O_RMAX = 6;  // rows of W_o per wave
 constexpr int ATTN_O_VMAX = 8;  // 16-byte vectors of a row per lane
 constexpr int ATTN_O_WREGS = 48;  // 16-byte weight vectors a lane may hold (192 VGPRs)
+// The attention output's "not yet written" value in the fused launch: a bf16 NaN pattern
+// that the attention kernels never store (they store 0xFFBF in its place)
+constexpr uint16_t ATTN_O_PENDING = 0xFFFFu;
+constexpr unsigned ATTN_O_PENDING2 = 0xFFFFFFFFu;  // two of them
 struct AttnOParams {
-  AttnParams a;       // Bp = 1, MFMA form
+  AttnParams a;       // Bp = 1, MFMA form; a.o holds ATTN_O_PENDING in every element at launch
   MatmulParams m;     // the O product: x = a.o, out = h (EPI_RESID), Bp = 1
-  unsigned* done;     // (sequence, kv head) groups whose output is written; zero at launch
-  unsigned need;      // a.Bp a.Hkv
+  uint16_t* next;     // the next layer's attention output (a.Hq a.dh bf16, not a.o): set to
+                      // ATTN_O_PENDING by this launch
   int* abort;         // set by a wait that gave up (the launch's values are then wrong)
   int spin;           // polls before a wait gives up
   int n_attn;         // attention work groups: a.n_split a.Hkv a.Bp

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void k_norm(NormParams p) {
   __shared__ float red[4];
   const int b = blockIdx.x, tid = threadIdx.x;
   if (EMBED && b == 0)
-    for (int i = tid; i < p.n_zero; i += 256) cst(p.zero + i, 0u);
+    for (int i = tid; i < p.n_pend; i += 256) cst(p.pend + i, ATTN_O_PENDING2);
   const int d = p.d;  // a multiple of 16
   const float* hrow = p.h + (int64_t)b * d;
   float* hout = p.h_out ? p.h_out + (int64_t)b * d : nullptr;
