@@ -243,7 +243,7 @@ int dec_set_flags(dec_ctx* ctx, uint32_t flags);
 /* Wait for the context's stream, then report whether every device-side wait of the
  * calls so far ended normally.  At batch 1, attention and the O projection run as one
  * launch (DEC_PATH_ATTN_O; "Kernels, Fusion & CUDA Graphs", Fix 1, the fused-kernel
- * table) whose O work groups wait on a device counter for attention's output; that wait
+ * table) whose O work groups poll attention's output until every element is written; that wait
  * is bounded, and one that gives up sets a device flag instead of hanging: the launch
  * ends with wrong values.  Returns DEC_OK, or DEC_E_HIP when a wait gave up (the
  * context is then failed: destroy it) or the stream reported an error. */
