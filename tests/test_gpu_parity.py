@@ -402,9 +402,9 @@ def test_unfused_step_matches_fused(dec):
                                        (MINI4, "bf16", "fp8"), (MINI4_128, "int8", "bf16")])
 def test_attention_and_o_in_one_launch(dec, base, w, kv):
     """At batch 1, where the shape fits, attention and the O projection run as one launch
-    (its O work groups wait on a device counter for attention's output): parity with the
-    oracle over several steps with split contexts, the path bit and one kernel less per
-    layer; DEC_FLAG_NO_ATTN_O gives the separate launches, also at parity."""
+    (its O work groups poll attention's output until every element is written): parity
+    with the oracle over several steps with split contexts, the path bit and one kernel
+    less per layer; DEC_FLAG_NO_ATTN_O gives the separate launches, also at parity."""
     cfg = fmt(base, w, kv)
     assert attn_o_fits(cfg, 1)
     case = make_case(cfg, [300], 512, seed=31)
@@ -418,14 +418,15 @@ def test_attention_and_o_in_one_launch(dec, base, w, kv):
         k, f = d.path()
         splits = d.info().attn_splits
         d.close()
-        assert splits > 1  # the combine, and its signal, run
+        assert splits > 1  # the split combine runs
         assert bool(f & dec.PATH_ATTN_O) == (flags == 0)
         assert k == kernels_per_step(cfg, 1, flags)
 
 
 def test_attention_and_o_one_launch_graph_equals_eager(dec):
     """The fused launch is deterministic: graph replay and eager launches give the same bits,
-    and the done counters start every step at zero (several steps in a row)."""
+    and every step finds its attention outputs marked as not yet written (several steps in
+    a row)."""
     cfg = fmt(MINI4_128, "bf16", "bf16")
     case = make_case(cfg, [200], 512, seed=33)
     ids = synth.make_token_ids(cfg, 3, 1, seed=33)
@@ -439,6 +440,33 @@ def test_attention_and_o_one_launch_graph_equals_eager(dec):
         d.close()
     for ze, zg in zip(outs[dec.FLAG_EAGER], outs[0]):
         assert torch.equal(ze.view(torch.int32), zg.view(torch.int32))
+
+
+@pytest.mark.parametrize("flags", [0, 1])  # graph replay, FLAG_EAGER
+def test_attention_and_o_state_across_plans(dec, flags):
+    """The fused launch's outputs do not depend on what ran before on the context: with an
+    odd number of layers (the two attention-output buffers wrap within a step), a fused
+    step, a step with separate launches (which leaves those buffers alone) and the fused
+    step again give the same bits, and the fused step is at parity with the oracle."""
+    assert flags in (0, dec.FLAG_EAGER)
+    cfg = fmt(MINI4_128, "bf16", "bf16").with_layers(3)
+    assert attn_o_fits(cfg, 1)
+    case = make_case(cfg, [230], 512, seed=35)
+    ids = synth.make_token_ids(cfg, 1, 1, seed=35)
+    assert_ok(run_parity(case, ids, flags=flags), cfg)
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=1, max_seq_len=512,
+                    flags=flags, kv_pool=case.pool.clone())
+    first = d.step(ids[0], case.ctx_lens, case.block_tables).clone()
+    assert d.path()[1] & dec.PATH_ATTN_O
+    d.set_flags(flags | dec.FLAG_NO_ATTN_O)
+    d.step(ids[0], case.ctx_lens, case.block_tables)
+    assert not d.path()[1] & dec.PATH_ATTN_O
+    d.set_flags(flags)
+    again = d.step(ids[0], case.ctx_lens, case.block_tables).clone()
+    assert d.path()[1] & dec.PATH_ATTN_O
+    d.check()
+    d.close()
+    assert torch.equal(first.view(torch.int32), again.view(torch.int32))
 
 
 def test_attention_and_o_wait_limit_is_reported(dec):
