@@ -580,7 +580,8 @@ hipError_t enqueue_step(dec_ctx* c, int Bp, bool skip_lm, hipStream_t s) {
     np.x_lo = on && !mfma ? xl : nullptr;
   };
   qkv_input(g.n_layers > 0);
-  // the fused attention + O launches' done counters start the step at zero
+  // the fused attention + O launches: the first layer's attention output starts the
+  // step marked as not yet written (each launch marks the next layer's)
   const dec::AttnOPlan ao = attn_o_plan(g, Bp);
   const int ao_rows = ao.rows;
   if (ao_rows > 0) {
