@@ -194,6 +194,22 @@ def test_prefill_mini(dec, w, kv, n, start, mb):
     assert_ok(run_prefill(dec, cfg, n, start, mb, 160, seed=41), cfg)
 
 
+def test_prefill_chunks_of_one_fused(dec):
+    """Chunks of one token on a model whose batch-1 step runs attention and O as one launch
+    (d_head 128, 8 query heads per KV head): every chunk and the decode steps after it
+    take the fused launch, whose attention outputs are marked as not yet written anew by
+    each step."""
+    cfg = fmt(MINI128, "bf16", "bf16")
+    assert_ok(run_prefill(dec, cfg, 6, 300, 1, 512, seed=43), cfg)
+    case = make_case(cfg, [300], 512, seed=43)
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=1, max_seq_len=512,
+                    kv_pool=case.pool.clone())
+    d.prefill(synth.make_token_ids(cfg, 2, 1, seed=43)[:, 0].copy(), 300, case.block_tables[0])
+    assert d.path()[1] & dec.PATH_ATTN_O
+    d.check()
+    d.close()
+
+
 def test_prefill_unfused_and_no_mfma(dec):
     cfg = fmt(MINI128, "bf16", "bf16")
     assert_ok(run_prefill(dec, cfg, 45, 0, 16, 64, seed=42, flags=dec.FLAG_UNFUSED), cfg)
