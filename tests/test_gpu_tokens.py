@@ -101,13 +101,15 @@ def test_verify_8b_widths(dec, n):
     assert_ok(run_verify(dec, case, tokens, stream=True), cfg)
 
 
-def test_verify_k1_equals_step_bitwise(dec):
+@pytest.mark.parametrize("which,lens", [("mini", [9, 40, 3]), ("mini128", [300])])
+def test_verify_k1_equals_step_bitwise(dec, which, lens):
     """A verify step of one token per sequence is the decode step: the same rows, the
-    same plan, the same bits."""
-    cfg = fmt(MINI, "bf16", "bf16")
-    case = make_case(cfg, [9, 40, 3], 128, seed=34)
-    ids = synth.make_token_ids(cfg, 1, 3, seed=34)[0]
-    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=4, max_seq_len=128,
+    same plan, the same bits (one sequence of the d_head-128 model: the fused attention
+    + O launch)."""
+    cfg = fmt(MINI if which == "mini" else MINI128, "bf16", "bf16")
+    case = make_case(cfg, lens, 512, seed=34)
+    ids = synth.make_token_ids(cfg, 1, len(lens), seed=34)[0]
+    d = dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=4, max_seq_len=512,
                     kv_pool=case.pool.clone())
     zs = d.step(ids, case.ctx_lens, case.block_tables).clone()
     torch.cuda.synchronize()
@@ -115,6 +117,7 @@ def test_verify_k1_equals_step_bitwise(dec):
     d.kv_pool.copy_(case.pool)
     zv = d.verify(ids[:, None], case.ctx_lens, case.block_tables).clone()
     torch.cuda.synchronize()
+    assert bool(d.path()[1] & dec.PATH_ATTN_O) == (len(lens) == 1)
     assert torch.equal(zs.view(torch.int32), zv[:, 0].view(torch.int32))
     assert torch.equal(ps.view(torch.uint8), d.kv_pool.view(torch.uint8))
     d.close()
