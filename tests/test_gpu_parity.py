@@ -492,6 +492,40 @@ def test_attention_and_o_wait_limit_is_reported(dec):
     d.close()
 
 
+@pytest.mark.parametrize("which,lens", [("mini4x128", [230]), ("mini-fp8", [9, 40, 3])])
+def test_destroy_and_recreate_resumes_bitwise(dec, which, lens):
+    """Decoding resumes across contexts: two steps on one context, destroyed, then two
+    more on a new context over the same KV pool give the bits of four steps on one
+    context (the cache is the only state a step carries to the next; batch 1 of the
+    d_head-128 model takes the fused attention + O launch)."""
+    cfg = fmt(MINI4_128, "bf16", "bf16") if which == "mini4x128" else fmt(MINI, "fp8", "fp8")
+    case = make_case(cfg, lens, 512, seed=36)
+    B = len(lens)
+    ids = synth.make_token_ids(cfg, 4, B, seed=36)
+    mb = dec.ladder_bucket(B)
+
+    def new_ctx(pool):
+        return dec.Decoder(cfg, case.weights, num_blocks=case.num_blocks, max_batch=mb, max_seq_len=512,
+                           kv_pool=pool)
+
+    d = new_ctx(case.pool.clone())
+    whole = [d.step(ids[t], case.ctx_lens + t, case.block_tables).clone() for t in range(4)]
+    d.check()
+    d.close()
+    pool = case.pool.clone()
+    d = new_ctx(pool)
+    parts = [d.step(ids[t], case.ctx_lens + t, case.block_tables).clone() for t in range(2)]
+    d.check()
+    d.close()
+    d = new_ctx(pool)
+    parts += [d.step(ids[t], case.ctx_lens + t, case.block_tables).clone() for t in range(2, 4)]
+    assert bool(d.path()[1] & dec.PATH_ATTN_O) == (which == "mini4x128")
+    d.check()
+    d.close()
+    for t, (a, b) in enumerate(zip(whole, parts)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"step {t}"
+
+
 @pytest.mark.parametrize("lens", [[9, 40, 3], [40]])
 def test_repeated_steps_are_deterministic(dec, lens):
     cfg = fmt(MINI, "fp8", "fp8")
