@@ -20,6 +20,7 @@
 // multi-token step comes from the per-row positions alone.
 
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <cmath>
 #include <cstdarg>
@@ -919,7 +920,17 @@ int dec_set_wait_limit(dec_ctx* c, int32_t polls) {
   return DEC_OK;
 }
 
+// A named range around each call that enqueues work, for profilers that record roctx
+// markers (rocprofv3 --marker-trace); without one attached the calls do nothing.
+struct TraceRange {
+  explicit TraceRange(const char* name) { roctxRangePushA(name); }
+  ~TraceRange() { roctxRangePop(); }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
+
 int dec_step(dec_ctx* c, const dec_step_args* a) {
+  TraceRange tr("dec_step");
   if (!c || !a) return fail(DEC_E_INVALID, "ctx or args is NULL");
   int rc = check_ready(c);
   if (rc != DEC_OK) return rc;
@@ -950,6 +961,7 @@ int dec_step(dec_ctx* c, const dec_step_args* a) {
 }
 
 int dec_verify(dec_ctx* c, const dec_verify_args* a) {
+  TraceRange tr("dec_verify");
   if (!c || !a) return fail(DEC_E_INVALID, "ctx or args is NULL");
   int rc = check_ready(c);
   if (rc != DEC_OK) return rc;
@@ -988,6 +1000,7 @@ int dec_verify(dec_ctx* c, const dec_verify_args* a) {
 }
 
 int dec_prefill(dec_ctx* c, const dec_prefill_args* a, int32_t* logits_row) {
+  TraceRange tr("dec_prefill");
   if (!c || !a || !logits_row) return fail(DEC_E_INVALID, "ctx, args or logits_row is NULL");
   int rc = check_ready(c);
   if (rc != DEC_OK) return rc;

@@ -18,6 +18,13 @@ known size (the same counters; they give the bytes-per-reported-unit factors)::
         --fetch DIR1 --write DIR2 --copy-fetch DIR3 --copy-write DIR4 --copy-bytes N \
         --kernel SUBSTRING --commands "<...>" > profiles/<kernel>_<workload>_traffic.txt
 
+Host time of the library's calls, from the roctx ranges it opens around them
+(``rocprofv3 --marker-trace --output-format csv``), skipping each name's first
+``--skip`` calls (the graph captures)::
+
+    python -m memory_bound_transformer_decode_amd.profile_summary markers DIR \
+        --command "<the rocprofv3 command>" [--skip 1] > profiles/<...>_markers.md
+
 The traffic file ends with ``source_sha256`` of the kernel family's sources (``--family``
 gemv, gemm or attn), which bench.py compares with the tree it runs from: counters taken
 on another version of the kernel are not reported.
@@ -147,6 +154,25 @@ def traffic(args) -> None:
     print(f"source_sha256: {kernel_source_sha256(args.family)}")
 
 
+def markers(args) -> None:
+    path = _find(args.dir, "marker_api_trace.csv")
+    spans: Dict[str, List[float]] = {}
+    for r in csv.DictReader(open(path)):
+        name = _col(r, "Function", "Message")
+        d = (int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3
+        spans.setdefault(name, []).append(d)
+    print("# Host time of the library's calls (roctx ranges, rocprofv3 --marker-trace)\n")
+    print(f"Command: `{args.command}`\n")
+    print(f"The first {args.skip} call(s) of each name (graph capture) are left out.\n")
+    print("| range | calls | mean us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|")
+    for name in sorted(spans):
+        d = sorted(spans[name][args.skip:]) if len(spans[name]) > args.skip else []
+        if not d:
+            continue
+        print(f"| `{name}` | {len(d)} | {sum(d) / len(d):.1f} | {d[len(d) // 2]:.1f} | {d[0]:.1f} | {d[-1]:.1f} |")
+
+
 def read_traffic(path: str) -> Dict[str, str]:
     out = {}
     with open(path) as fh:
@@ -176,8 +202,12 @@ def main(argv=None) -> int:
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--copy-kernel", default="copyBuffer")
     t.add_argument("--family", choices=sorted(KERNEL_SOURCES), default="gemv")
+    m = sub.add_parser("markers")
+    m.add_argument("dir")
+    m.add_argument("--command", required=True)
+    m.add_argument("--skip", type=int, default=1, help="leave out each range's first calls")
     args = ap.parse_args(argv)
-    {"stats": stats, "counters": counters, "traffic": traffic}[args.cmd](args)
+    {"stats": stats, "counters": counters, "traffic": traffic, "markers": markers}[args.cmd](args)
     return 0
 
 

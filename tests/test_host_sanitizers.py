@@ -48,7 +48,7 @@ def test_abi_checks_under_host_sanitizers(tmp_path):
         san_objs.append(obj)
     lib = str(tmp_path / "libdec_hostsan.so")
     r = subprocess.run([build.hipcc(), f"--offload-arch={build.ARCH}", "-shared", "-fPIC", *san_objs, *objs,
-                        "-o", lib], capture_output=True, text=True)
+                        *build.LINK_LIBS, "-o", lib], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     # the host code is instrumented: the library calls the sanitizers' report hooks
     syms = subprocess.run(["nm", "-D", lib], capture_output=True, text=True).stdout

@@ -42,3 +42,20 @@ def test_counters_mean_per_dispatch(tmp_path, capsys):
     row = [l for l in out.splitlines() if l.startswith("| `dec::k_attn")][0]
     cells = [c.strip() for c in row.split("|")]
     assert cells[2] == "2" and cells[3] == "6" and cells[4] == "20"
+
+
+def test_markers_per_range_without_the_first_calls(tmp_path, capsys):
+    d = _write(tmp_path, "run_marker_api_trace.csv",
+               ["Domain", "Function", "Process_Id", "Thread_Id", "Correlation_Id", "Start_Timestamp",
+                "End_Timestamp"],
+               [["MARKER_CORE_RANGE_API", "dec_step", 1, 1, 1, 0, 50000000],  # capture: left out
+                ["MARKER_CORE_RANGE_API", "dec_step", 1, 1, 2, 60000000, 60002000],
+                ["MARKER_CORE_RANGE_API", "dec_step", 1, 1, 3, 70000000, 70004000],
+                ["MARKER_CORE_RANGE_API", "dec_step", 1, 1, 4, 80000000, 80003000],
+                ["MARKER_CORE_RANGE_API", "dec_prefill", 1, 1, 5, 0, 1000]])
+    ps.main(["markers", d, "--command", "cmd"])
+    out = capsys.readouterr().out
+    assert "dec_prefill" not in out  # its only call is the left-out first one
+    row = [l for l in out.splitlines() if l.startswith("| `dec_step")][0]
+    cells = [c.strip() for c in row.split("|")]
+    assert cells[2] == "3" and cells[3] == "3.0" and cells[4] == "3.0" and cells[5] == "2.0" and cells[6] == "4.0"
